@@ -1,0 +1,173 @@
+"""fp64 CPU oracle for the batched verify step of speculative decoding.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg may import this package; the product path never does.  It shares
+no code with the GPU library and imports nothing from it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, sequential sums in
+ascending token id, OpenMP across independent requests / rows).  This module
+only compiles it with gcc, loads it with ctypes and marshals numpy arrays.
+
+Inputs are numpy arrays: fp32 logits as ``float32``; bf16 logits as the raw
+``uint16`` bit patterns (the top half of an IEEE binary32), which the C side
+widens exactly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_default = None
+
+FP32 = 0
+BF16 = 1
+
+# Decisions whose uniform lies closer than this to the threshold it is
+# compared with (accept ratio or normalised CDF boundary) are "flagged":
+# a path computing in lower precision may legitimately decide them the
+# other way.
+FLAG_BAND = 1e-6
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one oracle C source into a shared library with gcc.
+    No fast-math: IEEE double semantics are kept."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(
+        ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+         "-Wall", "-Wextra", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` (when missing or stale)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(SOURCE):
+        compile_source(SOURCE, _LIB)
+    return _LIB
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return FP32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("logits must be float32 or uint16 (bf16 bit patterns), got %s" % a.dtype)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dt):
+    a = np.asarray(a)
+    if a.dtype != dt:
+        raise TypeError("expected %s, got %s" % (dt, a.dtype))
+    return np.ascontiguousarray(a)
+
+
+class Oracle:
+    """ctypes handle on one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, dbl, ci = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_double, ctypes.c_int)
+        lib.oracle_softmax_stats.argtypes = [vp, ci, i64, i32, dbl, vp, vp]
+        lib.oracle_softmax_stats.restype = ci
+        lib.oracle_verify.argtypes = [vp, vp, ci, vp, vp, vp, dbl, i32, i32, i32, vp, vp, vp, vp]
+        lib.oracle_verify.restype = ci
+        lib.oracle_verify_greedy.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, vp]
+        lib.oracle_verify_greedy.restype = ci
+        self.lib = lib
+        self.path = path
+
+    def softmax_stats(self, logits: np.ndarray, temperature: float):
+        """Row max and sum_t exp((l_t - max)/T) in fp64 for a [..., V] array."""
+        logits = np.ascontiguousarray(logits)
+        code = _dtype_code(logits)
+        V = logits.shape[-1]
+        rows = logits.size // V
+        m = np.empty(rows, np.float64)
+        z = np.empty(rows, np.float64)
+        rc = self.lib.oracle_softmax_stats(_ptr(logits), code, rows, V, float(temperature),
+                                           _ptr(m), _ptr(z))
+        if rc != 0:
+            raise ValueError("oracle_softmax_stats rejected its arguments")
+        return m.reshape(logits.shape[:-1]), z.reshape(logits.shape[:-1])
+
+    def verify(self, target, draft, draft_tokens, uniforms, temperature, k_per_req=None):
+        """One stochastic verify step.
+
+        target [B, K+1, V], draft [B, K, V] or None (one-hot drafts),
+        draft_tokens [B, K] int32, uniforms [B, K+1] float32, k_per_req [B]
+        int32 or None.  Returns out_tokens [B, K+1], num_accepted [B],
+        accept_prob [B, K] (fp64), min_margin [B] (fp64) and flagged [B].
+        """
+        target = np.ascontiguousarray(target)
+        code = _dtype_code(target)
+        B, K1, V = target.shape
+        K = K1 - 1
+        if draft is not None:
+            draft = np.ascontiguousarray(draft)
+            if draft.dtype != target.dtype or draft.shape != (B, K, V):
+                raise ValueError("draft must match target dtype and be [B, K, V]")
+        draft_tokens = _c(draft_tokens, np.int32).reshape(B, K)
+        uniforms = _c(uniforms, np.float32).reshape(B, K + 1)
+        kp = None if k_per_req is None else _c(k_per_req, np.int32).reshape(B)
+        out = np.empty((B, K + 1), np.int32)
+        nacc = np.empty(B, np.int32)
+        ap = np.empty((B, K), np.float64)
+        mm = np.empty(B, np.float64)
+        rc = self.lib.oracle_verify(_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(kp),
+                                    _ptr(uniforms), float(temperature), B, K, V,
+                                    _ptr(out), _ptr(nacc), _ptr(ap), _ptr(mm))
+        if rc != 0:
+            raise ValueError("oracle_verify rejected its arguments")
+        return {"out_tokens": out, "num_accepted": nacc, "accept_prob": ap, "min_margin": mm,
+                "flagged": mm < FLAG_BAND}
+
+    def verify_greedy(self, target, draft_tokens, k_per_req=None):
+        """One greedy verify step; returns out_tokens, num_accepted, argmax."""
+        target = np.ascontiguousarray(target)
+        code = _dtype_code(target)
+        B, K1, V = target.shape
+        K = K1 - 1
+        draft_tokens = _c(draft_tokens, np.int32).reshape(B, K)
+        kp = None if k_per_req is None else _c(k_per_req, np.int32).reshape(B)
+        out = np.empty((B, K + 1), np.int32)
+        nacc = np.empty(B, np.int32)
+        am = np.empty((B, K + 1), np.int32)
+        rc = self.lib.oracle_verify_greedy(_ptr(target), code, _ptr(draft_tokens), _ptr(kp),
+                                           B, K, V, _ptr(out), _ptr(nacc), _ptr(am))
+        if rc != 0:
+            raise ValueError("oracle_verify_greedy rejected its arguments")
+        return {"out_tokens": out, "num_accepted": nacc, "argmax": am}
+
+
+def default() -> Oracle:
+    global _default
+    with _lock:
+        if _default is None:
+            _default = Oracle(build())
+    return _default
+
+
+def softmax_stats(logits, temperature):
+    return default().softmax_stats(logits, temperature)
+
+
+def verify(target, draft, draft_tokens, uniforms, temperature, k_per_req=None):
+    return default().verify(target, draft, draft_tokens, uniforms, temperature, k_per_req)
+
+
+def verify_greedy(target, draft_tokens, k_per_req=None):
+    return default().verify_greedy(target, draft_tokens, k_per_req)

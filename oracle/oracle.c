@@ -1,0 +1,269 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for the batched verify step of
+ * speculative decoding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or constant with the
+ * GPU library.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [LP]  "3.5 Speculative Decoding" (LLM learning path)
+ *   [AIA] "246 Speculative Decoding" (AI in Action)
+ *   [MF]  "Speculative Decoding: Mathematical Foundations, Rejection Sampling
+ *          Dynamics, Draft Architectures, and Serving Latency"
+ *   [SS]  "Speculative Decoding from First Principles" (The Serving Stack)
+ *
+ * Every value is widened exactly to double before use; every sum runs
+ * sequentially in ascending token id.  There is no blocking, fusion or
+ * reordering.  Readings taken where the pages are silent or disagree:
+ *   - accept iff u < min(1, p/q)  (strict; [LP] "The algorithm (one step)"
+ *     writes "<", [AIA] 3.1 and [MF] write "<=").
+ *   - q(x) == 0 gives ratio 1 ([AIA] 3.1 accept_or_resample).
+ *   - an empty residual (sum <= 0) falls back to p ([AIA] 3.1
+ *     residual_distribution).
+ *   - the residual / bonus draw is an inverse CDF in ascending token id:
+ *     the smallest t with u*S < C_t ([LP], [AIA] only say "sample").
+ *   - uniforms[b, i] (i < k_b) drives the accept test of draft i;
+ *     uniforms[b, k_b] drives the final draw (residual or bonus).
+ *   - argmax ties resolve to the lowest token id.
+ *   - p = softmax(l / T), q = softmax(d / T) with one T per call
+ *     ([LP] "Notation"; [LP] "Common pitfalls": same processing for both).
+ *
+ * Parity pins for each function live in the CPU tests (exact enumeration,
+ * closed forms, worked examples of the pages, library cross-checks).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_FP32 0
+#define ORACLE_BF16 1
+
+/* Exact widening of one stored logit to double.  bf16 is the top half of an
+ * IEEE binary32, so shifting its 16 bits into the high half gives the same
+ * value as a float. */
+static double load_logit(const void *base, int dtype, size_t idx) {
+    if (dtype == ORACLE_FP32) {
+        return (double)((const float *)base)[idx];
+    }
+    uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Row statistics of the temperature softmax p_t = exp((l_t - m)/T) / Z:
+ * m = max_t l_t and Z = sum_t exp((l_t - m)/T).
+ * [LP] "Notation": p is the next-token distribution after temperature. */
+static void row_stats(const void *base, int dtype, size_t row_off, int32_t V,
+                      double T, double *m_out, double *z_out) {
+    double m = -INFINITY;
+    for (int32_t t = 0; t < V; ++t) {
+        double l = load_logit(base, dtype, row_off + (size_t)t);
+        if (l > m) m = l;
+    }
+    double z = 0.0;
+    for (int32_t t = 0; t < V; ++t) {
+        double l = load_logit(base, dtype, row_off + (size_t)t);
+        z += exp((l - m) / T);
+    }
+    *m_out = m;
+    *z_out = z;
+}
+
+/* Probability of token t in a row with known statistics. */
+static double row_prob(const void *base, int dtype, size_t row_off, int32_t t,
+                       double m, double z, double T) {
+    double l = load_logit(base, dtype, row_off + (size_t)t);
+    return exp((l - m) / T) / z;
+}
+
+int oracle_softmax_stats(const void *logits, int dtype, int64_t rows, int32_t V,
+                         double T, double *row_max, double *row_sumexp) {
+    if (!logits || !row_max || !row_sumexp || rows < 0 || V <= 0 || !(T > 0.0))
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        row_stats(logits, dtype, (size_t)r * (size_t)V, V, T, &row_max[r],
+                  &row_sumexp[r]);
+    }
+    return 0;
+}
+
+/*
+ * One batched verify step, request by request, following [LP] "The algorithm
+ * (one step)", [AIA] 2.2 and 3.3, [MF] "The Modified Rejection Sampling
+ * Algorithm".
+ *
+ * Layouts (row-major, contiguous):
+ *   target      [B, K+1, V]   draft  [B, K, V] or NULL (one-hot drafts)
+ *   draft_tokens[B, K] int32  k_per_req [B] or NULL (all K)
+ *   uniforms    [B, K+1] fp32
+ * Outputs:
+ *   out_tokens  [B, K+1]: accepted drafts, then the final token, then -1
+ *   num_accepted[B]
+ *   accept_prob [B, K] (may be NULL): min(1, p_i/q_i) at every drafted
+ *               position i < k_b (also past the first rejection), -1 beyond
+ *   min_margin  [B] (may be NULL): smallest distance of a uniform to the
+ *               threshold it was compared with, along the path taken
+ *               (accept tests up to the first rejection, then the CDF
+ *               boundaries around the drawn token, in normalised units)
+ */
+int oracle_verify(const void *target, const void *draft, int dtype,
+                  const int32_t *draft_tokens, const int32_t *k_per_req,
+                  const float *uniforms, double T, int32_t B, int32_t K,
+                  int32_t V, int32_t *out_tokens, int32_t *num_accepted,
+                  double *accept_prob, double *min_margin) {
+    if (!target || !draft_tokens || !uniforms || !out_tokens || !num_accepted)
+        return -1;
+    if (B < 0 || K < 0 || V <= 0 || !(T > 0.0)) return -1;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t k = k_per_req ? k_per_req[b] : K;
+        if (k < 0 || k > K) { err |= 1; continue; }
+        const int32_t *xt = draft_tokens + (size_t)b * K;
+        const float *u = uniforms + (size_t)b * (K + 1);
+        int32_t *out = out_tokens + (size_t)b * (K + 1);
+        double *r = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!r) { err |= 1; continue; }
+
+        /* Step 1 (processed distributions): row statistics of the k+1 target
+         * rows and the k draft rows. */
+        double pm[K + 1], pz[K + 1], qm[K + 1], qz[K + 1];
+        for (int32_t i = 0; i <= k; ++i)
+            row_stats(target, dtype, ((size_t)b * (K + 1) + i) * (size_t)V, V,
+                      T, &pm[i], &pz[i]);
+        if (draft)
+            for (int32_t i = 0; i < k; ++i)
+                row_stats(draft, dtype, ((size_t)b * K + i) * (size_t)V, V, T,
+                          &qm[i], &qz[i]);
+
+        /* Step 2 (accept / reject left to right): ratio_i = min(1, p_i/q_i)
+         * at the drafted token; accept iff u_i < ratio_i; stop at the first
+         * rejection.  The ratio is also reported past the stop. */
+        double margin = INFINITY;
+        int32_t j = k; /* index of the first rejection, k if none */
+        for (int32_t i = 0; i < k; ++i) {
+            int32_t x = xt[i];
+            size_t prow = ((size_t)b * (K + 1) + i) * (size_t)V;
+            double p = row_prob(target, dtype, prow, x, pm[i], pz[i], T);
+            double q = draft ? row_prob(draft, dtype,
+                                        ((size_t)b * K + i) * (size_t)V, x,
+                                        qm[i], qz[i], T)
+                             : 1.0;
+            double ratio = (q == 0.0) ? 1.0 : fmin(1.0, p / q);
+            if (accept_prob) accept_prob[(size_t)b * K + i] = ratio;
+            if (j == k) { /* still on the path */
+                double d = fabs((double)u[i] - ratio);
+                if (d < margin) margin = d;
+                if (!((double)u[i] < ratio)) j = i;
+            }
+        }
+        if (accept_prob)
+            for (int32_t i = k; i < K; ++i) accept_prob[(size_t)b * K + i] = -1.0;
+
+        /* Step 3 (final draw).  On a rejection at j the draw is from
+         * max(0, p_j - q_j) normalised ([LP] step 3, [AIA] 2.2, [MF]); if
+         * every draft was accepted it is the bonus token from p_{k+1}
+         * ([LP] step 4, [MF] step 4). */
+        size_t prow = ((size_t)b * (K + 1) + j) * (size_t)V;
+        for (int32_t t = 0; t < V; ++t) {
+            double p = row_prob(target, dtype, prow, t, pm[j], pz[j], T);
+            double q = 0.0;
+            if (j < k) {
+                if (draft)
+                    q = row_prob(draft, dtype, ((size_t)b * K + j) * (size_t)V,
+                                 t, qm[j], qz[j], T);
+                else
+                    q = (t == xt[j]) ? 1.0 : 0.0;
+            }
+            r[t] = (p - q > 0.0) ? (p - q) : 0.0;
+        }
+        double S = 0.0;
+        for (int32_t t = 0; t < V; ++t) S += r[t];
+        if (!(S > 0.0)) { /* [AIA] 3.1: p and q coincide, fall back to p */
+            for (int32_t t = 0; t < V; ++t)
+                r[t] = row_prob(target, dtype, prow, t, pm[j], pz[j], T);
+            S = 0.0;
+            for (int32_t t = 0; t < V; ++t) S += r[t];
+        }
+        double uf = (double)u[k];
+        double target_mass = uf * S;
+        double C = 0.0, C_prev = 0.0;
+        int32_t tok = -1;
+        for (int32_t t = 0; t < V; ++t) {
+            C_prev = C;
+            C += r[t];
+            if (target_mass < C) { tok = t; break; }
+        }
+        if (tok < 0) { /* rounding left no t: take the last t with r_t > 0 */
+            for (int32_t t = V - 1; t >= 0; --t)
+                if (r[t] > 0.0) { tok = t; break; }
+            C_prev = C = S;
+        }
+        double d0 = fabs(uf - C_prev / S), d1 = fabs(uf - C / S);
+        double dmin = d0 < d1 ? d0 : d1;
+        if (dmin < margin) margin = dmin;
+
+        /* Step 4 (output): accepted prefix, then the final token. */
+        for (int32_t i = 0; i < j; ++i) out[i] = xt[i];
+        out[j] = tok;
+        for (int32_t i = j + 1; i <= K; ++i) out[i] = -1;
+        num_accepted[b] = j;
+        if (min_margin) min_margin[b] = margin;
+        free(r);
+    }
+    return err ? -1 : 0;
+}
+
+/*
+ * Greedy verify: p and q are point masses, so a draft is kept iff it equals
+ * the target argmax; at the first mismatch the target argmax is emitted; if
+ * all k match, the argmax after the last draft is the extra token.
+ * [LP] "Proof that the output distribution is exactly p" (last sentence) and
+ * "Worked example"; [SS] "Draft, verify, keep what matches".
+ * Ties resolve to the lowest token id.
+ */
+int oracle_verify_greedy(const void *target, int dtype,
+                         const int32_t *draft_tokens, const int32_t *k_per_req,
+                         int32_t B, int32_t K, int32_t V, int32_t *out_tokens,
+                         int32_t *num_accepted, int32_t *argmax_out) {
+    if (!target || !draft_tokens || !out_tokens || !num_accepted) return -1;
+    if (B < 0 || K < 0 || V <= 0) return -1;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t k = k_per_req ? k_per_req[b] : K;
+        if (k < 0 || k > K) { err |= 1; continue; }
+        const int32_t *xt = draft_tokens + (size_t)b * K;
+        int32_t *out = out_tokens + (size_t)b * (K + 1);
+        /* Target argmax of every row that the step may use. */
+        int32_t a[K + 1];
+        for (int32_t i = 0; i <= k; ++i) {
+            size_t off = ((size_t)b * (K + 1) + i) * (size_t)V;
+            int32_t best = 0;
+            double bv = load_logit(target, dtype, off);
+            for (int32_t t = 1; t < V; ++t) {
+                double l = load_logit(target, dtype, off + (size_t)t);
+                if (l > bv) { bv = l; best = t; }
+            }
+            a[i] = best;
+        }
+        if (argmax_out)
+            for (int32_t i = 0; i <= K; ++i)
+                argmax_out[(size_t)b * (K + 1) + i] = (i <= k) ? a[i] : -1;
+        /* First draft that differs from the target argmax; k if none. */
+        int32_t j = k;
+        for (int32_t i = 0; i < k; ++i)
+            if (xt[i] != a[i]) { j = i; break; }
+        int32_t a_j = a[j];
+        for (int32_t i = 0; i < j; ++i) out[i] = xt[i];
+        out[j] = a_j;
+        for (int32_t i = j + 1; i <= K; ++i) out[i] = -1;
+        num_accepted[b] = j;
+    }
+    return err ? -1 : 0;
+}

@@ -1,0 +1,588 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics
+fix, independent of the oracle's own code.
+
+Each ``pin_*`` function takes an oracle handle (``oracle.Oracle``) and raises
+AssertionError when the handle disagrees with the pages.  The same functions
+run against the real oracle (tests/test_oracle_pins.py) and against copies of
+it with planted mistakes (tests/test_oracle_mutants.py), which must fail at
+least one pin each.
+
+Expected values come from the pages' printed numbers (tests/golden/*.json),
+from closed forms, or from library routines (scipy.special.softmax /
+logsumexp, numpy.searchsorted) applied to the same inputs; never from the
+oracle itself.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+from scipy import special, stats
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def grid(M):
+    """Stratified uniforms (m + 1/2) / M, exact in fp32 for M a power of two
+    or a small integer grid used below."""
+    return ((np.arange(M, dtype=np.float64) + 0.5) / M).astype(np.float32)
+
+
+def logits_of(p):
+    """fp32 logits whose softmax at T=1 is p up to fp32 rounding (-inf where
+    p is 0)."""
+    p = np.asarray(p, np.float64)
+    with np.errstate(divide="ignore"):
+        return np.log(p).astype(np.float32)
+
+
+def softmax_T(l, T):
+    return special.softmax(np.asarray(l, np.float64) / T, axis=-1)
+
+
+# --------------------------------------------------------------------------
+# Row statistics
+# --------------------------------------------------------------------------
+
+def pin_stats_logsumexp(o):
+    """m is the exact row max; m/T + log Z equals scipy's logsumexp(l/T)."""
+    rng = np.random.default_rng(11)
+    for T in (1.0, 0.6, 1.7):
+        l32 = (rng.standard_normal((7, 513)) * 3).astype(np.float32)
+        l32[2, 100:200] = -np.inf
+        m, z = o.softmax_stats(l32, T)
+        assert np.array_equal(m, l32.max(axis=1).astype(np.float64))
+        lse = special.logsumexp(l32.astype(np.float64) / T, axis=1)
+        np.testing.assert_allclose(m / T + np.log(z), lse, rtol=1e-13, atol=1e-13)
+        f = (rng.standard_normal((3, 300)) * 4).astype(np.float32)
+        bits = (f.view(np.uint32) >> 16).astype(np.uint16)     # valid bf16 values
+        vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        m, z = o.softmax_stats(bits, T)
+        assert np.array_equal(m, vals.max(axis=1))
+        np.testing.assert_allclose(m / T + np.log(z), special.logsumexp(vals / T, axis=1),
+                                   rtol=1e-13, atol=1e-13)
+
+
+def pin_stats_closed_forms(o):
+    """Constant row: Z = V.  Two-level row {a x n, b x (V-n)}: Z = n +
+    (V-n) exp((b-a)/T)."""
+    V = 1000
+    m, z = o.softmax_stats(np.full((1, V), 2.5, np.float32), 0.8)
+    assert m[0] == 2.5 and z[0] == float(V)
+    row = np.full((1, V), -1.0, np.float32)
+    row[0, :37] = 3.0
+    for T in (1.0, 0.8, 2.0):
+        m, z = o.softmax_stats(row, T)
+        assert m[0] == 3.0
+        assert abs(z[0] - (37 + (V - 37) * np.exp(-4.0 / T))) < 1e-10 * z[0]
+
+
+# --------------------------------------------------------------------------
+# One position: accept test and residual, the pages' worked pairs
+# --------------------------------------------------------------------------
+
+def _one_position_laws(o, p, q, M, T=1.0):
+    """Measure, through the oracle with stratified uniforms, the accept
+    probability of every draft token and the residual law.
+
+    Returns (a, h): a[x] = fraction of u in the grid that accepts draft x;
+    h = token histogram of the final draw after a rejection."""
+    V = len(p)
+    lt = np.stack([logits_of(p), logits_of(p)])[None]        # [1, 2, V]
+    ld = logits_of(q)[None, None]                              # [1, 1, V]
+    u = grid(M)
+    a = np.zeros(V)
+    for x in range(V):
+        tgt = np.repeat(lt, M, axis=0)
+        drf = np.repeat(ld, M, axis=0)
+        toks = np.full((M, 1), x, np.int32)
+        uni = np.stack([u, np.full(M, 0.5, np.float32)], axis=1)
+        r = o.verify(tgt, drf, toks, uni, T)
+        a[x] = np.mean(r["num_accepted"] == 1)
+    # Residual law: draft the token with the smallest p/q (a sure rejection
+    # at u = 1 - 2^-24) and sweep the final uniform.
+    ratios = np.where(np.asarray(q) > 0, np.asarray(p) / np.maximum(q, 1e-300), np.inf)
+    x = int(np.argmin(ratios))
+    tgt = np.repeat(lt, M, axis=0)
+    drf = np.repeat(ld, M, axis=0)
+    toks = np.full((M, 1), x, np.int32)
+    uni = np.stack([np.full(M, 1 - 2**-24, np.float32), u], axis=1)
+    r = o.verify(tgt, drf, toks, uni, T)
+    assert np.all(r["num_accepted"] == 0)
+    h = np.bincount(r["out_tokens"][:, 0], minlength=V)[:V] / M
+    return a, h
+
+
+def pin_check_your_understanding(o):
+    """3.5 Speculative Decoding, 'Check your understanding': beta = 0.7,
+    residual (1, 0, 0), P(a) = 0.3 + 0.3 * 1 = 0.6."""
+    g = golden("check_your_understanding.json")
+    p, q = np.array(g["p"]), np.array(g["q"])
+    M = 4096
+    a, h = _one_position_laws(o, p, q, M)
+    beta = float(np.dot(q, a))
+    assert abs(beta - g["acceptance_beta"]) < 2.0 / M, beta
+    np.testing.assert_allclose(h, g["residual"], atol=2.0 / M)
+    law = q * a + np.dot(q, 1 - a) * h
+    assert abs(law[0] - g["p_emit_a"]) < 3.0 / M
+    np.testing.assert_allclose(law, p, atol=3.0 / M)
+
+
+def pin_single_position_experiment(o):
+    """246 Speculative Decoding, 3.2: accept rate sum min(p, q) = 0.55,
+    residual (2/3, 1/3, 0, 0, 0, 0); emitted law = p.  The printed empirical
+    accept rate (0.551 at N = 200000) lies within 3 sigma of 0.55."""
+    g = golden("single_position_experiment.json")
+    p, q = np.array(g["p"]), np.array(g["q"])
+    M = 4096
+    a, h = _one_position_laws(o, p, q, M)
+    beta = float(np.dot(q, a))
+    assert abs(beta - 0.55) < 2.0 / M, beta
+    np.testing.assert_allclose(h, [2 / 3, 1 / 3, 0, 0, 0, 0], atol=2.0 / M)
+    law = q * a + np.dot(q, 1 - a) * h
+    np.testing.assert_allclose(law, p, atol=3.0 / M)
+    sigma = np.sqrt(0.55 * 0.45 / g["samples"])
+    assert abs(g["printed_accept_rate"] - beta) < 3 * sigma + 0.0005 + 2.0 / M
+
+
+def pin_single_position_chisquare(o):
+    """Random drafts x ~ q and random uniforms: the emitted token passes a
+    chi-square test against p (246 Speculative Decoding, 3.2 experiment,
+    redone through the oracle)."""
+    g = golden("single_position_experiment.json")
+    p, q = np.array(g["p"]), np.array(g["q"])
+    N = 200_000
+    rng = np.random.default_rng(12345)
+    lt = np.stack([logits_of(p), logits_of(p)])
+    tgt = np.ascontiguousarray(np.broadcast_to(lt, (N, 2, 6)))
+    drf = np.ascontiguousarray(np.broadcast_to(logits_of(q), (N, 1, 6)))
+    toks = rng.choice(6, size=(N, 1), p=q).astype(np.int32)
+    uni = rng.random((N, 2), dtype=np.float32)
+    r = o.verify(tgt, drf, toks, uni, 1.0)
+    counts = np.bincount(r["out_tokens"][:, 0], minlength=6)
+    chi = stats.chisquare(counts, N * p)
+    assert chi.pvalue > 1e-3, (counts / N, chi)
+    acc = np.mean(r["num_accepted"])
+    assert abs(acc - 0.55) < 4 * np.sqrt(0.55 * 0.45 / N)
+
+
+# --------------------------------------------------------------------------
+# Several positions: per-position laws, bonus row, uniform indexing
+# --------------------------------------------------------------------------
+
+def _rows(seed, K, V, T):
+    rng = np.random.default_rng(seed)
+    lt = (rng.standard_normal((K + 1, V)) * 1.5).astype(np.float32)
+    ld = (lt[:K] + rng.standard_normal((K, V)) * 1.2).astype(np.float32)
+    return lt, ld, softmax_T(lt, T), softmax_T(ld, T)
+
+
+def pin_multi_position_exact(o):
+    """K=3, V=5, T=0.7.  Forcing acceptance before position i with u = 0,
+    the accept probability at i is min(1, P_i/Q_i), the residual law after a
+    rejection at i is max(0, P_i - Q_i)/S (drawn with uniforms[k]), the bonus
+    law is P_k, and the law of the token emitted at i is P_i
+    (3.5 Speculative Decoding, 'The algorithm (one step)' and 'Proof')."""
+    K, V, T, M = 3, 5, 0.7, 2048
+    lt, ld, P, Q = _rows(5, K, V, T)
+    u = grid(M)
+    base_t = np.repeat(lt[None], M, axis=0)
+    base_d = np.repeat(ld[None], M, axis=0)
+    for i in range(K):
+        a = np.zeros(V)
+        for x in range(V):
+            toks = np.zeros((M, K), np.int32)
+            toks[:, i] = x
+            uni = np.zeros((M, K + 1), np.float32)
+            uni[:, i] = u
+            uni[:, K] = 0.5
+            r = o.verify(base_t, base_d, toks, uni, T)
+            assert np.all(r["num_accepted"] >= i)
+            a[x] = np.mean(r["num_accepted"] > i)
+            np.testing.assert_allclose(r["accept_prob"][0, i], min(1.0, P[i, x] / Q[i, x]),
+                                       rtol=1e-6)
+        np.testing.assert_allclose(a, np.minimum(1.0, P[i] / Q[i]), atol=1.0 / M)
+        x = int(np.argmin(P[i] / Q[i]))
+        toks = np.zeros((M, K), np.int32)
+        toks[:, i] = x
+        uni = np.zeros((M, K + 1), np.float32)
+        uni[:, i] = 1 - 2**-24
+        uni[:, i + 1:K] = 0.25          # unused by the step
+        uni[:, K] = u
+        r = o.verify(base_t, base_d, toks, uni, T)
+        assert np.all(r["num_accepted"] == i)
+        h = np.bincount(r["out_tokens"][:, i], minlength=V)[:V] / M
+        res = np.maximum(P[i] - Q[i], 0)
+        np.testing.assert_allclose(h, res / res.sum(), atol=2.0 / M)
+        law = Q[i] * a + np.dot(Q[i], 1 - a) * h
+        np.testing.assert_allclose(law, P[i], atol=3.0 / M)
+    toks = np.zeros((M, K), np.int32)
+    uni = np.zeros((M, K + 1), np.float32)
+    uni[:, K] = u
+    r = o.verify(base_t, base_d, toks, uni, T)
+    assert np.all(r["num_accepted"] == K)
+    h = np.bincount(r["out_tokens"][:, K], minlength=V)[:V] / M
+    np.testing.assert_allclose(h, P[K], atol=2.0 / M)
+
+
+def pin_multi_position_chisquare(o):
+    """Fixed rows, drafts x_i ~ Q_i, random uniforms: given position i is
+    reached, the emitted token there passes a chi-square test against P_i."""
+    K, V, T, N = 3, 6, 0.9, 120_000
+    lt, ld, P, Q = _rows(9, K, V, T)
+    rng = np.random.default_rng(99)
+    toks = np.stack([rng.choice(V, size=N, p=Q[i]) for i in range(K)], axis=1).astype(np.int32)
+    uni = rng.random((N, K + 1), dtype=np.float32)
+    tgt = np.ascontiguousarray(np.broadcast_to(lt, (N, K + 1, V)))
+    drf = np.ascontiguousarray(np.broadcast_to(ld, (N, K, V)))
+    r = o.verify(tgt, drf, toks, uni, T)
+    n = r["num_accepted"]
+    for i in range(K + 1):
+        reached = n >= i
+        counts = np.bincount(r["out_tokens"][reached, i], minlength=V)[:V]
+        exp = reached.sum() * P[i]
+        keep = exp >= 5
+        c = np.append(counts[keep], counts[~keep].sum())
+        e = np.append(exp[keep], exp[~keep].sum())
+        if e[-1] == 0:
+            c, e = c[:-1], e[:-1]
+        assert stats.chisquare(c, e).pvalue > 1e-3, (i, counts, exp)
+
+
+def pin_k0_is_inverse_cdf(o):
+    """k_b = 0 reduces to plain inverse-CDF sampling from p_1 (the bonus draw
+    with no drafts): token = searchsorted(cumsum(p), u * sum(p), 'right')."""
+    rng = np.random.default_rng(3)
+    V, T, N = 777, 1.3, 4000
+    lt = (rng.standard_normal((1, 1, V)) * 2).astype(np.float32)
+    tgt = np.repeat(lt, N, axis=0)
+    u = rng.random((N, 1), dtype=np.float32)
+    r = o.verify(tgt, None, np.zeros((N, 0), np.int32), u, T)
+    P = softmax_T(lt[0, 0], T)
+    c = np.cumsum(P)
+    ref = np.searchsorted(c, u[:, 0].astype(np.float64) * c[-1], side="right")
+    safe = np.min(np.abs(c[None, :] / c[-1] - u.astype(np.float64)), axis=1) > 1e-9
+    assert safe.mean() > 0.99
+    assert np.array_equal(r["out_tokens"][safe, 0], ref[safe])
+    assert np.all(r["num_accepted"] == 0)
+
+
+def pin_identity(o):
+    """q = p accepts every draft (246 Speculative Decoding, 3.4: noise 0.0
+    gives acceptance 1 and k+1 tokens per call)."""
+    rng = np.random.default_rng(4)
+    B, K, V = 64, 4, 300
+    lt = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    ld = lt[:, :K].copy()
+    toks = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    uni = rng.random((B, K + 1), dtype=np.float32)
+    r = o.verify(lt, ld, toks, uni, 0.9)
+    assert np.all(r["num_accepted"] == K)
+    assert np.array_equal(r["out_tokens"][:, :K], toks)
+    assert np.all(r["accept_prob"] == 1.0)
+
+
+def pin_disjoint_support(o):
+    """Disjoint supports: every draft is rejected at the first position and
+    the replacement is drawn from p_1 itself."""
+    V, M, T = 6, 4096, 1.0
+    p = np.array([0.5, 0.3, 0.2, 0, 0, 0])
+    q = np.array([0, 0, 0, 0.25, 0.75, 0])
+    lt = np.stack([logits_of(p), logits_of(p)])[None]
+    ld = logits_of(q)[None, None]
+    tgt = np.repeat(lt, M, axis=0)
+    drf = np.repeat(ld, M, axis=0)
+    toks = np.full((M, 1), 4, np.int32)
+    uni = np.stack([np.full(M, 0.0, np.float32), grid(M)], axis=1)
+    r = o.verify(tgt, drf, toks, uni, T)
+    assert np.all(r["num_accepted"] == 0)
+    assert np.all(r["accept_prob"][:, 0] == 0.0)
+    h = np.bincount(r["out_tokens"][:, 0], minlength=V) / M
+    np.testing.assert_allclose(h, p, atol=2.0 / M)
+
+
+def pin_strict_comparisons(o):
+    """Readings: accept iff u < ratio (strict), and the draw is the smallest t
+    with u*S < C_t (strict).  With one-hot drafts and p = (1/2, 1/2) both
+    thresholds are exactly 1/2."""
+    lt = np.zeros((2, 2, 2), np.float32)          # p = (0.5, 0.5) exactly
+    toks = np.zeros((2, 1), np.int32)
+    uni = np.array([[0.5, 0.5], [0.5 - 2**-24, 0.5]], np.float32)
+    r = o.verify(lt, None, toks, uni, 1.0)
+    assert list(r["num_accepted"]) == [0, 1]
+    # After the rejection at u = 1/2 the one-hot residual is (0, 1).
+    assert r["out_tokens"][0, 0] == 1
+    # k = 0: the bonus draw from (1/2, 1/2) at u = 1/2 lands on token 1,
+    # just below 1/2 on token 0.
+    lt0 = np.zeros((2, 1, 2), np.float32)
+    r = o.verify(lt0, None, np.zeros((2, 0), np.int32),
+                 np.array([[0.5], [0.5 - 2**-24]], np.float32), 1.0)
+    assert list(r["out_tokens"][:, 0]) == [1, 0]
+
+
+def pin_q_zero_accepts(o):
+    """A draft token with q = 0 gets ratio 1 and is accepted (246 Speculative
+    Decoding, 3.1)."""
+    lt = np.zeros((1, 2, 4), np.float32)
+    ld = np.array([[[0.0, 0.0, -np.inf, 0.0]]], np.float32)
+    r = o.verify(lt, ld, np.array([[2]], np.int32), np.array([[0.999, 0.3]], np.float32), 1.0)
+    assert r["num_accepted"][0] == 1 and r["accept_prob"][0, 0] == 1.0
+    assert r["out_tokens"][0, 0] == 2
+
+
+def pin_one_hot_drafts(o):
+    """One-hot drafts: accept probability p(x); the residual is p with x
+    removed and renormalised (3.5 Speculative Decoding, 'Proof', greedy
+    remark and the n-gram row of 'Choosing a draft')."""
+    V, M, T = 5, 4096, 0.8
+    lt, _, P, _ = _rows(21, 1, V, T)
+    tgt = np.repeat(lt[None], M, axis=0)
+    x = 2
+    uni = np.stack([grid(M), np.full(M, 0.5, np.float32)], axis=1)
+    r = o.verify(tgt, None, np.full((M, 1), x, np.int32), uni, T)
+    assert abs(np.mean(r["num_accepted"] == 1) - P[0, x]) < 1.0 / M
+    uni = np.stack([np.full(M, 1 - 2**-24, np.float32), grid(M)], axis=1)
+    r = o.verify(tgt, None, np.full((M, 1), x, np.int32), uni, T)
+    h = np.bincount(r["out_tokens"][:, 0], minlength=V) / M
+    res = P[0].copy()
+    res[x] = 0
+    np.testing.assert_allclose(h, res / res.sum(), atol=2.0 / M)
+
+
+# --------------------------------------------------------------------------
+# Expected tokens per step: the closed form through the oracle
+# --------------------------------------------------------------------------
+
+def closed_form(alpha, k):
+    return (1 - alpha ** (k + 1)) / (1 - alpha)
+
+
+def pin_closed_form_printed_values(o=None):
+    """The closed form reproduces every value the pages print (to their
+    printed precision)."""
+    for c in golden("tokens_per_step.json")["cases"]:
+        v = closed_form(c["alpha"], c["k"])
+        assert round(v, c["decimals"]) == round(c["value"], c["decimals"]) or \
+            abs(v - c["value"]) <= 0.5 * 10 ** -c["decimals"] + 1e-9, (c, v)
+
+
+def _mean_emitted_grid(o, alpha, M, k):
+    """Exact mean tokens per step over the full product grid of accept
+    uniforms: one-hot drafts whose target probability is alpha (V = 2), and a
+    grid of M values per position on which exactly alpha*M values accept."""
+    lt = logits_of([alpha, 1 - alpha])
+    u = grid(M)
+    mesh = np.stack(np.meshgrid(*([u] * k), indexing="ij"), axis=-1).reshape(-1, k)
+    N = mesh.shape[0]
+    tgt = np.ascontiguousarray(np.broadcast_to(lt, (N, k + 1, 2)))
+    uni = np.concatenate([mesh, np.full((N, 1), 0.5, np.float32)], axis=1)
+    r = o.verify(tgt, None, np.zeros((N, k), np.int32), uni, 1.0)
+    return float(np.mean(r["num_accepted"] + 1))
+
+
+def pin_closed_form_through_oracle(o):
+    """Independent acceptance with probability alpha at each position gives
+    (1 - alpha^(k+1)) / (1 - alpha) tokens per step (3.5 Speculative
+    Decoding, 'Expected tokens per step'; 246 Speculative Decoding, 2.4;
+    Speculative Decoding from First Principles)."""
+    for alpha, M, k in ((0.7, 20, 3), (0.6, 5, 3), (0.8, 5, 4), (0.8, 5, 8), (0.7, 10, 5)):
+        got = _mean_emitted_grid(o, alpha, M, k)
+        assert abs(got - closed_form(alpha, k)) < 1e-9, (alpha, k, got)
+    # alpha = 0.7, k = 8 ("about 3.2") with random uniforms.
+    rng = np.random.default_rng(8)
+    N, k = 200_000, 8
+    tgt = np.ascontiguousarray(np.broadcast_to(logits_of([0.7, 0.3]), (N, k + 1, 2)))
+    r = o.verify(tgt, None, np.zeros((N, k), np.int32),
+                 rng.random((N, k + 1), dtype=np.float32), 1.0)
+    e = r["num_accepted"] + 1.0
+    assert abs(e.mean() - closed_form(0.7, 8)) < 4 * e.std() / np.sqrt(N)
+    assert e.min() >= 1 and e.max() <= k + 1
+
+
+# --------------------------------------------------------------------------
+# Ragged k, invariants
+# --------------------------------------------------------------------------
+
+def pin_ragged_equals_truncated(o):
+    """A request with k_b < K gives the same result as the same request
+    alone with K = k_b (padded rows are never read: they hold NaN)."""
+    rng = np.random.default_rng(6)
+    B, K, V, T = 12, 5, 200, 0.6
+    kp = rng.integers(0, K + 1, size=B).astype(np.int32)
+    lt = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    ld = (lt[:, :K] + rng.standard_normal((B, K, V))).astype(np.float32)
+    toks = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    uni = rng.random((B, K + 1), dtype=np.float32)
+    for b in range(B):
+        lt[b, kp[b] + 1:] = np.nan
+        ld[b, kp[b]:] = np.nan
+        uni[b, kp[b]] = rng.random(dtype=np.float32)
+    r = o.verify(lt, ld, toks, uni, T, k_per_req=kp)
+    for b in range(B):
+        kb = int(kp[b])
+        rb = o.verify(lt[b:b + 1, :kb + 1], ld[b:b + 1, :kb], toks[b:b + 1, :kb],
+                      uni[b:b + 1, :kb + 1], T)
+        assert r["num_accepted"][b] == rb["num_accepted"][0]
+        assert np.array_equal(r["out_tokens"][b, :kb + 1], rb["out_tokens"][0])
+        assert np.all(r["out_tokens"][b, kb + 1:] == -1)
+        assert np.all(r["accept_prob"][b, kb:] == -1.0)
+
+
+def pin_invariants(o):
+    """Every step emits between 1 and k+1 tokens; the accepted prefix is the
+    drafts; a replacement after a rejection is never the rejected draft."""
+    rng = np.random.default_rng(7)
+    B, K, V, T = 500, 6, 50, 1.0
+    lt = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    ld = (lt[:, :K] + rng.standard_normal((B, K, V)) * 2).astype(np.float32)
+    Q = softmax_T(ld, T)
+    toks = np.array([[rng.choice(V, p=Q[b, i]) for i in range(K)] for b in range(B)], np.int32)
+    uni = rng.random((B, K + 1), dtype=np.float32)
+    r = o.verify(lt, ld, toks, uni, T)
+    n = r["num_accepted"]
+    assert n.min() >= 0 and n.max() <= K
+    for b in range(B):
+        out = r["out_tokens"][b]
+        assert np.array_equal(out[:n[b]], toks[b, :n[b]])
+        assert 0 <= out[n[b]] < V
+        assert np.all(out[n[b] + 1:] == -1)
+        if n[b] < K:
+            assert out[n[b]] != toks[b, n[b]]
+
+
+# --------------------------------------------------------------------------
+# Greedy
+# --------------------------------------------------------------------------
+
+def pin_greedy_worked_trace(o):
+    """3.5 Speculative Decoding, 'Worked example': drafts (Paris, ., It, is),
+    target argmax (Paris, ., The, -, -) emit Paris, ., The; no bonus."""
+    g = golden("worked_greedy_trace.json")
+    voc = g["vocabulary"]
+    V = len(voc)
+    rng = np.random.default_rng(1)
+    lt = rng.standard_normal((1, 5, V)).astype(np.float32)
+    for i, w in enumerate(g["target_argmax"]):
+        tok = voc[w] if w is not None else voc["<other>"]
+        lt[0, i, tok] = 10.0
+    drafts = np.array([[voc[w] for w in g["drafts"]]], np.int32)
+    r = o.verify_greedy(lt, drafts)
+    assert r["num_accepted"][0] == g["num_accepted"]
+    emitted = [int(t) for t in r["out_tokens"][0] if t >= 0]
+    assert emitted == [voc[w] for w in g["emitted"]]
+
+
+def pin_greedy_ties_and_bonus(o):
+    """Ties go to the lowest id; when all drafts match, the argmax of the row
+    after the last draft is emitted as the extra token."""
+    lt = np.zeros((1, 3, 10), np.float32)
+    lt[0, 0, [3, 7]] = 5.0
+    lt[0, 1, [8, 2, 9]] = 4.0
+    lt[0, 2, [6, 1]] = 2.0
+    r = o.verify_greedy(lt, np.array([[3, 2]], np.int32))
+    assert r["num_accepted"][0] == 2 and list(r["out_tokens"][0]) == [3, 2, 1]
+    r = o.verify_greedy(lt, np.array([[7, 2]], np.int32))
+    assert r["num_accepted"][0] == 0 and list(r["out_tokens"][0]) == [3, -1, -1]
+    bits = np.zeros((1, 2, 4), np.uint16)
+    bits[0, 0] = [0x4000, 0x4040, 0x4040, 0x3F80]       # 2, 3, 3, 1
+    bits[0, 1] = [0xFF80, 0xC000, 0xBF80, 0xBF80]       # -inf, -2, -1, -1
+    r = o.verify_greedy(bits, np.array([[1]], np.int32))
+    assert list(r["out_tokens"][0]) == [1, 2]
+
+
+def pin_greedy_equals_argmax_decoding(o):
+    """Greedy verification reproduces plain argmax decoding token for token
+    (3.5 Speculative Decoding, 'Proof', greedy remark; Speculative Decoding
+    from First Principles, 'The output does not change').  Toy model: a
+    V x V table of next-token logits (a Markov chain over V = 1000 ids);
+    drafts come from a noisy argmax."""
+    rng = np.random.default_rng(2024)
+    V, K, n_tokens = 1000, 4, 10_000
+    table = (rng.standard_normal((V, V)) * 2).astype(np.float32)
+    table_am = np.argmax(table, axis=1)
+    plain = [0]
+    while len(plain) < n_tokens + 1:
+        plain.append(int(table_am[plain[-1]]))
+    seq, steps = [0], 0
+    while len(seq) < n_tokens + 1:
+        ctx = seq[-1]
+        drafts, c = [], ctx
+        for _ in range(K):
+            c = int(table_am[c]) if rng.random() < 0.75 else int(rng.integers(V))
+            drafts.append(c)
+        rows = table[[ctx] + drafts][None]
+        r = o.verify_greedy(rows, np.array([drafts], np.int32))
+        n = int(r["num_accepted"][0])
+        seq.extend(int(t) for t in r["out_tokens"][0, :n + 1])
+        steps += 1
+    assert seq[:n_tokens + 1] == plain[:n_tokens + 1]
+    assert steps < n_tokens / 1.5
+
+
+# --------------------------------------------------------------------------
+# End to end: the toy Markov chain of 3.5 Speculative Decoding, 'Code'
+# --------------------------------------------------------------------------
+
+def pin_markov_chain_third_token(o):
+    """V = 6, k = 4: a target chain and a draft 0.7 * target + 0.3 * other;
+    drafts are sampled autoregressively from the draft chain, the oracle
+    verifies, and the frequency of the third generated token from start
+    token 0 passes a chi-square test against the third power of the target
+    chain (3.5 Speculative Decoding, 'Code')."""
+    rng = np.random.default_rng(0)
+    V, k, N = 6, 4, 40_000
+
+    def chain(sharp):
+        x = np.exp(rng.standard_normal((V, V)) * sharp)
+        return x / x.sum(1, keepdims=True)
+
+    Pt = chain(2.0)
+    Pd = 0.7 * Pt + 0.3 * chain(2.0)
+    Lt, Ld = logits_of(Pt), logits_of(Pd)
+    cdf_d = np.cumsum(Pd, axis=1)
+    seqs = [[] for _ in range(N)]
+    prev = np.zeros(N, np.int64)
+    active = np.arange(N)
+    while active.size:
+        n = active.size
+        drafts = np.empty((n, k), np.int32)
+        ctx = prev[active].copy()
+        for i in range(k):
+            u = rng.random(n)
+            nxt = (u[:, None] < cdf_d[ctx]).argmax(axis=1)
+            drafts[:, i] = nxt
+            ctx = nxt
+        rows_t = np.concatenate([prev[active][:, None], drafts], axis=1)
+        tgt = Lt[rows_t]
+        drf = Ld[rows_t[:, :k]]
+        r = o.verify(tgt, drf, drafts, rng.random((n, k + 1), dtype=np.float32), 1.0)
+        still = []
+        for j, b in enumerate(active):
+            m = int(r["num_accepted"][j]) + 1
+            seqs[b].extend(int(t) for t in r["out_tokens"][j, :m])
+            prev[b] = seqs[b][-1]
+            if len(seqs[b]) < 3:
+                still.append(b)
+        active = np.array(still, np.int64)
+    counts = np.bincount([s[2] for s in seqs], minlength=V)
+    exact = np.linalg.matrix_power(Pt, 3)[0]
+    assert stats.chisquare(counts, N * exact).pvalue > 1e-3, (counts / N, exact)
+
+
+ALL_PINS = [
+    pin_stats_logsumexp, pin_stats_closed_forms,
+    pin_check_your_understanding, pin_single_position_experiment,
+    pin_single_position_chisquare, pin_multi_position_exact,
+    pin_multi_position_chisquare, pin_k0_is_inverse_cdf, pin_identity,
+    pin_disjoint_support, pin_strict_comparisons, pin_q_zero_accepts,
+    pin_one_hot_drafts, pin_closed_form_printed_values,
+    pin_closed_form_through_oracle, pin_ragged_equals_truncated,
+    pin_invariants, pin_greedy_worked_trace, pin_greedy_ties_and_bonus,
+    pin_greedy_equals_argmax_decoding, pin_markov_chain_third_token,
+]

@@ -1,0 +1,85 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each case copies oracle/oracle.c, applies one textual change that a careless
+reading of the pages could produce (a wrong comparison, a transposed operand,
+a dropped term, an off-by-one row or uniform), compiles the copy with gcc on
+the CPU and runs the whole pin suite against it in a subprocess.  The pins
+are only trusted if every such mutant is caught.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "accept_with_le": ("if (!((double)u[i] < ratio)) j = i;",
+                       "if (!((double)u[i] <= ratio)) j = i;"),
+    "ratio_q_over_p": ("fmin(1.0, p / q)", "fmin(1.0, q / p)"),
+    "residual_abs": ("r[t] = (p - q > 0.0) ? (p - q) : 0.0;", "r[t] = fabs(p - q);"),
+    "residual_is_p": ("r[t] = (p - q > 0.0) ? (p - q) : 0.0;", "r[t] = p + 0.0 * q;"),
+    "residual_q_minus_p": ("r[t] = (p - q > 0.0) ? (p - q) : 0.0;",
+                           "r[t] = (q - p > 0.0) ? (q - p) : 0.0;"),
+    "bonus_row_off_by_one": ("size_t prow = ((size_t)b * (K + 1) + j) * (size_t)V;",
+                             "size_t prow = ((size_t)b * (K + 1) + (j == k && j > 0 ? j - 1 : j)) * (size_t)V;"),
+    "final_uniform_is_u_j": ("double uf = (double)u[k];", "double uf = (double)u[j];"),
+    "temperature_multiplies": ("exp((l - m) / T)", "exp((l - m) * T)"),
+    "normaliser_ignores_T": ("z += exp((l - m) / T);", "z += exp(l - m);"),
+    "cdf_with_le": ("if (target_mass < C)", "if (target_mass <= C)"),
+    "argmax_ties_highest": ("if (l > bv) { bv = l; best = t; }",
+                            "if (l >= bv) { bv = l; best = t; }"),
+    "greedy_emits_draft": ("int32_t a_j = a[j];", "int32_t a_j = (j < k) ? xt[j] : a[j];"),
+    "greedy_no_bonus": ("int32_t a_j = a[j];", "int32_t a_j = (j == k) ? -1 : a[j];"),
+    "greedy_compares_next_row": ("if (xt[i] != a[i]) { j = i; break; }",
+                                 "if (xt[i] != a[i + 1]) { j = i; break; }"),
+    "q_zero_rejects": ("(q == 0.0) ? 1.0 :", "(q == 0.0) ? 0.0 :"),
+    "last_draft_never_tested": ("for (int32_t i = 0; i < k; ++i) {\n            int32_t x = xt[i];",
+                                "for (int32_t i = 0; i < k - 1; ++i) {\n            int32_t x = xt[i];"),
+    "does_not_stop_at_first_rejection": ("if (j == k) { /* still on the path */", "if (1) {"),
+    "rejected_draft_emitted": ("out[j] = tok;", "out[j] = (j < k) ? xt[j] : tok;"),
+    "max_not_subtracted_in_prob": ("return exp((l - m) / T) / z;", "return exp(l / T) / z;"),
+}
+
+RUNNER = r"""
+import sys
+sys.path.insert(0, %(root)r)
+import oracle
+from tests import pins
+o = oracle.Oracle(%(lib)r)
+for pin in pins.ALL_PINS:
+    try:
+        pin(o)
+    except AssertionError as e:
+        print("CAUGHT_BY", pin.__name__)
+        sys.exit(3)
+print("NOT_CAUGHT")
+sys.exit(0)
+"""
+
+
+def test_mutants_patch_cleanly():
+    src = open(oracle.SOURCE).read()
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) >= 1, name
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert old in src, "mutation anchor missing: %s" % name
+    mutated = src.replace(old, new)
+    csrc = tmp_path / "oracle_mutant.c"
+    csrc.write_text(mutated)
+    lib = str(tmp_path / "liboracle_mutant.so")
+    oracle.compile_source(str(csrc), lib)
+    env = dict(os.environ, OMP_NUM_THREADS="4")
+    proc = subprocess.run([sys.executable, "-c", RUNNER % {"root": ROOT, "lib": lib}],
+                          capture_output=True, text=True, timeout=300, env=env)
+    out = proc.stdout + proc.stderr
+    assert "NOT_CAUGHT" not in out, "planted mistake %r passed every pin" % name
+    assert proc.returncode != 0, out[-2000:]
