@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+
+One step = one specdec_verify call over one batch of the headline workload
+(B=64 requests, k=5 drafts, V=128256, bf16 target and draft logits, T=0.8),
+with inputs already resident in HBM.  The timed steps rotate over several
+device-resident copies of the input set, so that the working set (>= 720 MB)
+exceeds the 256 MB Infinity Cache and every step streams its logits from HBM.
+
+Prints one JSON line: verified positions/s (sum over requests of k_b + 1 per
+step), the algorithmic HBM bytes per step and their rate against the MI355X
+peak (8 TB/s), the dominant kernel's roofline, and the fp64 CPU oracle timed
+on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "verified positions/s + HBM GB/s (% of peak), B=64 k=5 V=128256 bf16"
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_headline_counters.txt")
+KERNEL_SOURCES = ["device_common.h", "internal.h", "verify.hip"]
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "speculative_decoding_verification_10_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl, num_accepted) -> int:
+    """Bytes the step must move: every target row i <= k_b and draft row
+    i < k_b once, the final row (pair) of every rejected request once more,
+    plus ids, uniforms and outputs."""
+    import numpy as np
+    s = 2 if wl.dtype == "bf16" else 4
+    k = np.full(wl.B, wl.K) if wl.k_per_req is None else wl.k_per_req.astype(np.int64)
+    rows = int(np.sum(k + 1)) + (int(np.sum(k)) if wl.draft is not None else 0)
+    rejected = int(np.sum(num_accepted < k))
+    reread = rejected * (2 if wl.draft is not None else 1)
+    small = int(np.sum(k)) * 4 + int(np.sum(k + 1)) * 4 + wl.B * (wl.K + 1) * 4 + wl.B * 4
+    return (rows + reread) * wl.V * s + small
+
+
+def read_counters():
+    """Per-launch HBM bytes measured with rocprofv3 (FETCH_SIZE + WRITE_SIZE,
+    scaled by a copy-kernel calibration), if the stored summary was taken on
+    the current kernel sources."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    vals = {}
+    with open(PROFILE_COUNTERS) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_digest") != kernel_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The fp64 oracle as it stands, on the host cores, over a bounded
+    number of steps of the same workload."""
+    import oracle
+    oracle.default()
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.verify(wl.target, wl.draft, wl.draft_tokens, wl.uniforms, wl.temperature, wl.k_per_req)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 5000:
+            break
+    pos = wl.verified_positions() * n
+    return {"value": pos / el, "unit": "verified positions/s", "cores": cores, "kind": "oracle",
+            "sample": "%d full steps of the headline workload (%d verified positions) in %.1f s"
+                      % (n, pos, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="device-resident input copies to rotate over")
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay each call from a captured HIP graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; the verify step shards by request "
+              "across GPUs with no exchange, so a multi-GPU figure is N times the 1-GPU one "
+              "and is not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import speculative_decoding_verification_10_amd as sd
+    from speculative_decoding_verification_10_amd import workloads
+    from tests.gpu_util import dev_logits
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    sd.load(build_if_missing=True)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    wl = workloads.make(args.workload)
+    K = wl.K
+    sets = []
+    base = {
+        "target": dev_logits(wl.target, dev),
+        "draft": None if wl.draft is None else dev_logits(wl.draft, dev),
+    }
+    for r in range(max(1, args.sets)):
+        sets.append({
+            "target": base["target"] if r == 0 else base["target"].clone(),
+            "draft": None if base["draft"] is None else (base["draft"] if r == 0 else base["draft"].clone()),
+        })
+    tokens = torch.from_numpy(wl.draft_tokens).to(dev)
+    unif = torch.from_numpy(wl.uniforms).to(dev)
+    kpr = None if wl.k_per_req is None else torch.from_numpy(wl.k_per_req).to(dev)
+    out = (torch.empty((wl.B, K + 1), dtype=torch.int32, device=dev),
+           torch.empty((wl.B,), dtype=torch.int32, device=dev), None)
+    nbytes = sd._lib.verify_workspace_bytes(wl.B, K, wl.V, 1 if wl.dtype == "bf16" else 0,
+                                            wl.draft is None)
+    ws = sd.Workspace(nbytes, dev)
+
+    greedy = wl.greedy
+
+    def step(r):
+        s = sets[r % len(sets)]
+        if greedy:
+            sd.verify_greedy(s["target"], tokens, k_per_req=kpr, workspace=ws, out=out)
+        else:
+            sd.verify(s["target"], s["draft"], tokens, unif, wl.temperature, k_per_req=kpr,
+                      workspace=ws, out=out)
+
+    stream = torch.cuda.current_stream(dev)
+    graphs = None
+    if args.graph:
+        graphs = []
+        for r in range(len(sets)):
+            step(r)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(r):
+        if graphs is not None:
+            graphs[r % len(graphs)].replay()
+        else:
+            step(r)
+
+    for r in range(args.warmup):
+        run(r)
+    torch.cuda.synchronize()
+    nacc = out[1].cpu().numpy()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(args.steps):
+        starts[r].record(stream)
+        run(r)
+        ends[r].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    ms_per_step = wall * 1e3 / args.steps
+
+    positions = wl.verified_positions()
+    alg = algorithmic_bytes(wl, nacc)
+    value = positions / (ms_per_step * 1e-3)
+    gbps = alg / (ms_per_step * 1e-3) / 1e9
+    achieved = alg / (per_launch_ms * 1e-3) / 1e9
+    traffic = read_counters()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; inputs resident in HBM, %d rotating copies)" % len(sets),
+        "config": {"workload": "%s verify B=%d k=%d V=%d %s T=%g" % (args.workload, wl.B, K, wl.V,
+                                                                        wl.dtype, wl.temperature),
+                   "B": wl.B, "k": K, "V": wl.V, "temperature": wl.temperature,
+                   "graph_replay": bool(args.graph)},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "algorithmic_bytes_per_step": alg,
+        "rejected_requests": int(np.sum(nacc < (wl.K if wl.k_per_req is None else wl.k_per_req))),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic,
+                     "launch_ms": round(per_launch_ms, 5),
+                     "kernel": "specdec_verify (whole call)"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

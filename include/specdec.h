@@ -1,0 +1,146 @@
+/*
+ * specdec.h -- C ABI of the batched verify step of speculative decoding on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (one step, every request b of a batch independently):
+ *   p_i = softmax(target_logits[b, i, :] / T)       i = 0 .. k_b
+ *   q_i = softmax(draft_logits[b, i, :] / T)        i = 0 .. k_b - 1
+ *         (or the point mass on draft_tokens[b, i] when draft_logits is NULL)
+ *   for i = 0 .. k_b-1: accept draft_tokens[b, i] iff u_i < min(1, p_i(x)/q_i(x));
+ *   stop at the first rejection j; emit a replacement drawn from
+ *   max(0, p_j - q_j) normalised; if every draft was accepted emit a bonus
+ *   token drawn from p_{k_b}.
+ * Sources: "3.5 Speculative Decoding" (LLM learning path), sections
+ * "Notation" and "The algorithm (one step)"; "246 Speculative Decoding"
+ * (AI in Action), sections 2.2 and 3.1-3.3; "Speculative Decoding:
+ * Mathematical Foundations, ...", section "The Modified Rejection Sampling
+ * Algorithm".  The greedy variant ("3.5 Speculative Decoding", section
+ * "Proof that the output distribution is exactly p", last paragraph, and the
+ * "Worked example"; "Speculative Decoding from First Principles", section
+ * "Draft, verify, keep what matches") keeps a draft iff it equals the target
+ * argmax and otherwise emits that argmax.
+ *
+ * Conventions shared by every entry point
+ *   - All array pointers are DEVICE pointers (memory of the current HIP
+ *     device), owned by the caller; the library keeps none of them after the
+ *     call returns and allocates no memory.
+ *   - Arrays are row-major and contiguous.  Logits are fp32 or bf16 (raw
+ *     IEEE bfloat16, the top half of a binary32).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise with the host.  Outputs are valid once
+ *     the stream has reached the call.
+ *   - Return value: SPECDEC_OK (0) or a negative specdec_status_t.  Argument
+ *     errors are detected on the host before anything is launched and leave
+ *     every output untouched.  No C++ exception crosses the ABI.
+ *   - Workspace: device memory of at least the size the matching
+ *     *_workspace_bytes() function returns, 256-byte aligned.  It must be
+ *     zero-filled before its first use (specdec_workspace_init does that);
+ *     every call that returns SPECDEC_OK and runs to completion leaves it
+ *     ready for the next call.  Calls that may run concurrently need distinct
+ *     workspaces.  After a failed launch, zero it again.
+ *   - Preconditions not checked on the fast path (a violation gives
+ *     unspecified tokens, never an out-of-bounds access): logits finite or
+ *     -inf (-inf = probability 0; a row may not be all -inf); 0 <=
+ *     draft_tokens < V at the positions that are used; 0 <= uniforms < 1;
+ *     0 <= k_per_req[b] <= K.  Rows past k_b (target rows i > k_b, draft
+ *     rows i >= k_b) are never read.
+ */
+#ifndef SPECDEC_H
+#define SPECDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPECDEC_FP32 = 0,
+    SPECDEC_BF16 = 1
+} specdec_dtype_t;
+
+typedef enum {
+    SPECDEC_OK = 0,
+    SPECDEC_EINVAL = -1,     /* null pointer, bad size, bad temperature */
+    SPECDEC_EDTYPE = -2,     /* unknown dtype */
+    SPECDEC_EWORKSPACE = -3, /* workspace missing, too small or misaligned */
+    SPECDEC_ELAUNCH = -4,    /* a kernel launch failed (HIP error) */
+    SPECDEC_EDEVICE = -5     /* no usable gfx950 device */
+} specdec_status_t;
+
+/* Human-readable name of a status code (static storage). */
+const char *specdec_status_string(int status);
+
+/* Library version string (static storage). */
+const char *specdec_version(void);
+
+/* Zero-fill `bytes` of workspace on `stream` (asynchronous). */
+int specdec_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/*
+ * Row statistics of the temperature softmax ("3.5 Speculative Decoding",
+ * section "Notation": p is the distribution after temperature).
+ *   logits      [rows, V]
+ *   row_max     [rows] fp32 out: max_t l_t (raw logit units, exact)
+ *   row_sumexp  [rows] fp32 out: sum_t exp((l_t - row_max) / T)
+ * rows >= 0, V >= 1, T > 0 and finite.
+ */
+size_t specdec_softmax_stats_workspace_bytes(int64_t rows, int32_t V, specdec_dtype_t dtype);
+int specdec_softmax_stats(const void *logits, specdec_dtype_t dtype, int64_t rows, int32_t V,
+                          float temperature, float *row_max, float *row_sumexp,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Stochastic verify step (the operation above).
+ *   target_logits [B, K+1, V]
+ *   draft_logits  [B, K, V], or NULL: drafts are point masses (n-gram /
+ *                 prompt-lookup drafts), so the accept probability is
+ *                 p_i(x) and the replacement is p_j with x removed,
+ *                 renormalised.
+ *   draft_tokens  [B, K] int32
+ *   k_per_req     [B] int32, or NULL (every request has k_b = K)
+ *   uniforms      [B, K+1] fp32 in [0, 1): uniforms[b, i] (i < k_b) drives
+ *                 the accept test of draft i, uniforms[b, k_b] the final
+ *                 draw (replacement or bonus); the others are ignored.
+ *   temperature   one T > 0 for both distributions of every request.
+ * Outputs:
+ *   out_tokens    [B, K+1] int32: accepted drafts, then the final token,
+ *                 then -1.  Emitted count = num_accepted[b] + 1.
+ *   num_accepted  [B] int32
+ *   accept_prob   [B, K] fp32, or NULL: min(1, p_i(x)/q_i(x)) at every
+ *                 drafted position i < k_b (also past the first rejection),
+ *                 -1 for i >= k_b.
+ * The final draw is an inverse CDF in ascending token id: the smallest t
+ * with u * S < C_t, C_t the running sum of the (unnormalised) replacement or
+ * bonus masses and S their total.  B >= 0, K >= 0, V >= 1.
+ */
+size_t specdec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, specdec_dtype_t dtype,
+                                      int one_hot_drafts);
+int specdec_verify(const void *target_logits, const void *draft_logits, specdec_dtype_t dtype,
+                   const int32_t *draft_tokens, const int32_t *k_per_req, const float *uniforms,
+                   float temperature, int32_t B, int32_t K, int32_t V,
+                   int32_t *out_tokens, int32_t *num_accepted, float *accept_prob,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Greedy verify step: a_i = argmax_t target_logits[b, i, t] (lowest id on
+ * ties); j = first i < k_b with draft_tokens[b, i] != a_i, else k_b;
+ * out_tokens[b] = drafts 0..j-1, then a_j, then -1; num_accepted[b] = j.
+ * No temperature (argmax does not depend on T > 0).
+ *   target_logits [B, K+1, V]; draft_tokens [B, K]; k_per_req [B] or NULL.
+ *   argmax_out    [B, K+1] int32, or NULL: a_i for i <= k_b, -1 beyond.
+ */
+size_t specdec_verify_greedy_workspace_bytes(int32_t B, int32_t K, int32_t V,
+                                             specdec_dtype_t dtype);
+int specdec_verify_greedy(const void *target_logits, specdec_dtype_t dtype,
+                          const int32_t *draft_tokens, const int32_t *k_per_req,
+                          int32_t B, int32_t K, int32_t V,
+                          int32_t *out_tokens, int32_t *num_accepted, int32_t *argmax_out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECDEC_H */

@@ -1,0 +1,242 @@
+"""ctypes binding of libspecdec.so: argument marshalling only.
+
+Every step of the verify path runs in the HIP kernels behind the C ABI
+(include/specdec.h).  This module checks shapes, dtypes, devices and
+contiguity of torch tensors, hands their device pointers and the current HIP
+stream to the library, and turns a negative status into an exception.  When
+the library is not built or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+from . import _build
+
+FP32 = 0
+BF16 = 1
+
+_lock = threading.Lock()
+_lib = None
+_workspaces = {}
+
+
+class SpecdecError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load(build_if_missing: bool = True) -> ctypes.CDLL:
+    """Load libspecdec.so (building it first only if it does not exist)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = _build.LIB
+        if not os.path.exists(path):
+            if not build_if_missing:
+                raise RuntimeError("libspecdec.so is not built; run "
+                                   "python -m speculative_decoding_verification_10_amd._build")
+            _build.build()
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, sz, f32, ci = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_size_t, ctypes.c_float, ctypes.c_int)
+        lib.specdec_status_string.argtypes = [ci]
+        lib.specdec_status_string.restype = ctypes.c_char_p
+        lib.specdec_version.argtypes = []
+        lib.specdec_version.restype = ctypes.c_char_p
+        lib.specdec_workspace_init.argtypes = [vp, sz, vp]
+        lib.specdec_workspace_init.restype = ci
+        lib.specdec_softmax_stats_workspace_bytes.argtypes = [i64, i32, ci]
+        lib.specdec_softmax_stats_workspace_bytes.restype = sz
+        lib.specdec_softmax_stats.argtypes = [vp, ci, i64, i32, f32, vp, vp, vp, sz, vp]
+        lib.specdec_softmax_stats.restype = ci
+        lib.specdec_verify_workspace_bytes.argtypes = [i32, i32, i32, ci, ci]
+        lib.specdec_verify_workspace_bytes.restype = sz
+        lib.specdec_verify.argtypes = [vp, vp, ci, vp, vp, vp, f32, i32, i32, i32,
+                                       vp, vp, vp, vp, sz, vp]
+        lib.specdec_verify.restype = ci
+        lib.specdec_verify_greedy_workspace_bytes.argtypes = [i32, i32, i32, ci]
+        lib.specdec_verify_greedy_workspace_bytes.restype = sz
+        lib.specdec_verify_greedy.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, vp,
+                                              vp, sz, vp]
+        lib.specdec_verify_greedy.restype = ci
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().specdec_status_string(status).decode()
+    except Exception:  # pragma: no cover - only reached when the library is broken
+        return "status %d" % status
+
+
+def version() -> str:
+    return load().specdec_version().decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FP32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("logits must be torch.float32 or torch.bfloat16, got %s" % t.dtype)
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape, device) -> None:
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Workspace:
+    """Device scratch for the library, zero-filled when allocated (the
+    library leaves it reusable after every successful call)."""
+
+    def __init__(self, nbytes: int, device):
+        self.nbytes = int(nbytes)
+        self.tensor = torch.zeros(max(self.nbytes, 256), dtype=torch.uint8, device=torch.device(device))
+        self.device = self.tensor.device
+
+    def ptr(self) -> int:
+        return self.tensor.data_ptr()
+
+
+def _workspace(nbytes: int, device: torch.device, ws: Optional[Workspace]) -> Workspace:
+    if ws is not None:
+        if ws.nbytes < nbytes or ws.device != device:
+            raise ValueError("workspace too small (%d < %d) or on the wrong device" % (ws.nbytes, nbytes))
+        return ws
+    key = (device.index, _stream(device))
+    cur = _workspaces.get(key)
+    if cur is None or cur.nbytes < nbytes:
+        cur = Workspace(nbytes, device)
+        _workspaces[key] = cur
+    return cur
+
+
+def verify_workspace_bytes(B, K, V, dtype_code, one_hot) -> int:
+    return int(load().specdec_verify_workspace_bytes(B, K, V, dtype_code, int(bool(one_hot))))
+
+
+def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+           uniforms: torch.Tensor, temperature: float, k_per_req: Optional[torch.Tensor] = None,
+           accept_prob: bool = False, workspace: Optional[Workspace] = None, out=None):
+    """Stochastic verify step (specdec_verify).
+
+    target [B, K+1, V], draft [B, K, V] or None (one-hot drafts), both fp32 or
+    bf16; draft_tokens [B, K] int32; uniforms [B, K+1] fp32; k_per_req [B]
+    int32 or None.  Returns (out_tokens [B, K+1], num_accepted [B],
+    accept_prob [B, K] or None).  ``out`` may hold preallocated
+    (out_tokens, num_accepted, accept_prob) tensors.
+    """
+    lib = load()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    _check(target, "target", target.dtype, (B, K + 1, V), dev)
+    if draft is not None:
+        _check(draft, "draft", target.dtype, (B, K, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    if k_per_req is not None:
+        _check(k_per_req, "k_per_req", torch.int32, (B,), dev)
+    if out is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+        ap = torch.empty((B, K), dtype=torch.float32, device=dev) if accept_prob else None
+    else:
+        out_tokens, nacc, ap = out
+        _check(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+        _check(nacc, "num_accepted", torch.int32, (B,), dev)
+        if ap is not None:
+            _check(ap, "accept_prob", torch.float32, (B, K), dev)
+    nbytes = verify_workspace_bytes(B, K, V, code, draft is None)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib.specdec_verify(_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(k_per_req),
+                            _ptr(uniforms), float(temperature), B, K, V, _ptr(out_tokens),
+                            _ptr(nacc), _ptr(ap), ws.ptr(), ws.nbytes, _stream(dev))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_verify")
+    return out_tokens, nacc, ap
+
+
+def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
+                  k_per_req: Optional[torch.Tensor] = None, argmax: bool = False,
+                  workspace: Optional[Workspace] = None, out=None):
+    """Greedy verify step (specdec_verify_greedy).  Returns (out_tokens,
+    num_accepted, argmax [B, K+1] or None)."""
+    lib = load()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    _check(target, "target", target.dtype, (B, K + 1, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    if k_per_req is not None:
+        _check(k_per_req, "k_per_req", torch.int32, (B,), dev)
+    if out is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+        am = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if argmax else None
+    else:
+        out_tokens, nacc, am = out
+    nbytes = int(lib.specdec_verify_greedy_workspace_bytes(B, K, V, code))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib.specdec_verify_greedy(_ptr(target), code, _ptr(draft_tokens), _ptr(k_per_req), B, K, V,
+                                   _ptr(out_tokens), _ptr(nacc), _ptr(am), ws.ptr(), ws.nbytes,
+                                   _stream(dev))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_verify_greedy")
+    return out_tokens, nacc, am
+
+
+def softmax_stats(logits: torch.Tensor, temperature: float, workspace: Optional[Workspace] = None):
+    """Row max and sum_t exp((l_t - max)/T) of a [..., V] tensor
+    (specdec_softmax_stats).  Returns two fp32 tensors of shape [...]."""
+    lib = load()
+    if logits.dim() < 1:
+        raise ValueError("logits must have a vocabulary axis")
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V > 0 else 0
+    dev = logits.device
+    code = _dtype_code(logits)
+    if not logits.is_contiguous():
+        raise ValueError("logits must be contiguous")
+    rmax = torch.empty(logits.shape[:-1], dtype=torch.float32, device=dev)
+    rsum = torch.empty(logits.shape[:-1], dtype=torch.float32, device=dev)
+    nbytes = int(lib.specdec_softmax_stats_workspace_bytes(rows, V, code))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib.specdec_softmax_stats(_ptr(logits), code, rows, V, float(temperature), _ptr(rmax),
+                                   _ptr(rsum), ws.ptr(), ws.nbytes, _stream(dev))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_softmax_stats")
+    return rmax, rsum

@@ -1,0 +1,278 @@
+// C ABI of the specdec library: argument validation on the host, workspace
+// layout, temperature scale, and dispatch to the kernel launchers.  Nothing
+// here synchronises with the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/specdec.h"
+#include "internal.h"
+
+namespace specdec {
+namespace {
+
+constexpr int32_t kMaxK = 4096;
+constexpr int32_t kMaxV = 1 << 28;
+constexpr size_t kAlign = 256;
+constexpr size_t kMaxBlocks = (size_t)1 << 24;   // gridDim.x * 256 threads < 2^32
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_size(specdec_dtype_t dt) { return dt == SPECDEC_BF16 ? 2 : 4; }
+int elems_per_vec(specdec_dtype_t dt) { return dt == SPECDEC_BF16 ? 8 : 4; }
+
+bool dtype_ok(int dt) { return dt == SPECDEC_FP32 || dt == SPECDEC_BF16; }
+
+// Vectors per row and whether 16-byte loads can be used for every row.
+void row_geometry(int32_t V, specdec_dtype_t dt, bool aligned, int* NV, bool* vec) {
+    const size_t row_bytes = (size_t)V * elem_size(dt);
+    *vec = aligned && (row_bytes % 16 == 0);
+    *NV = *vec ? (int)(row_bytes / 16) : (V + elems_per_vec(dt) - 1) / elems_per_vec(dt);
+}
+
+int tiles_of(int NV) { return (NV + kTileVec - 1) / kTileVec; }
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % 16) == 0; }
+
+// c = log2(e) / T as hi + lo with hi the largest float strictly below c, so
+// that lo > 0.
+bool make_scale(float temperature, Scale* s) {
+    if (!(temperature > 0.0f) || !std::isfinite(temperature)) return false;
+    const double c = 1.4426950408889634074 / (double)temperature;
+    if (!std::isfinite(c) || c > 1e30) return false;
+    float hi = (float)c;
+    if ((double)hi >= c) hi = std::nextafter(hi, 0.0f);
+    const float lo = (float)(c - (double)hi);
+    if (!(hi > 0.0f) || !(lo > 0.0f)) return false;
+    s->hi = hi;
+    s->lo = lo;
+    s->c = c;
+    return true;
+}
+
+struct VerifyLayout {
+    size_t err, row_done, req_done, slot_m, slot_s, slot_slab, total;
+};
+
+// Header (error bits) + self-validating slots: tile max / tile sum of every
+// row slot of every request, and the slab sums of every request's final row.
+VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, bool one_hot) {
+    int NV, NVv;
+    bool vec;
+    row_geometry(V, dt, false, &NV, &vec);        // scalar geometry >= vector geometry
+    row_geometry(V, dt, true, &NVv, &vec);
+    const size_t C = (size_t)tiles_of(NV > NVv ? NV : NVv);
+    const size_t R = (size_t)K + 1 + (one_hot ? 0 : (size_t)K);
+    const size_t parts = (size_t)B * R * C;
+    VerifyLayout L;
+    size_t off = 0;
+    L.err = off;       off = align_up(off + sizeof(uint32_t));
+    L.row_done = off;  off = align_up(off + (size_t)B * R * sizeof(uint32_t));
+    L.req_done = off;  off = align_up(off + (size_t)B * sizeof(uint32_t));
+    L.slot_m = off;    off = align_up(off + parts * sizeof(uint32_t));
+    L.slot_s = off;    off = align_up(off + parts * sizeof(uint64_t));
+    L.slot_slab = off; off = align_up(off + (size_t)B * C * kUnroll * sizeof(uint64_t));
+    L.total = off;
+    return L;
+}
+
+struct GreedyLayout {
+    size_t part_v, part_i, total;
+};
+
+GreedyLayout greedy_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt) {
+    int NV, NVv;
+    bool vec;
+    row_geometry(V, dt, false, &NV, &vec);
+    row_geometry(V, dt, true, &NVv, &vec);
+    const size_t C = (size_t)tiles_of(NV > NVv ? NV : NVv);
+    const size_t parts = (size_t)B * ((size_t)K + 1) * C;
+    GreedyLayout L;
+    size_t off = 0;
+    L.part_v = off; off = align_up(off + parts * sizeof(float));
+    L.part_i = off; off = align_up(off + parts * sizeof(int32_t));
+    L.total = off < kAlign ? kAlign : off;
+    return L;
+}
+
+struct StatsLayout {
+    size_t part_m, part_s, total;
+};
+
+StatsLayout stats_layout(int64_t rows, int32_t V, specdec_dtype_t dt) {
+    int NV, NVv;
+    bool vec;
+    row_geometry(V, dt, false, &NV, &vec);
+    row_geometry(V, dt, true, &NVv, &vec);
+    const size_t C = (size_t)tiles_of(NV > NVv ? NV : NVv);
+    const size_t parts = (size_t)rows * C;
+    StatsLayout L;
+    size_t off = 0;
+    L.part_m = off; off = align_up(off + parts * sizeof(float));
+    L.part_s = off; off = align_up(off + parts * sizeof(double));
+    L.total = off < kAlign ? kAlign : off;
+    return L;
+}
+
+bool workspace_ok(const void* ws, size_t have, size_t need) {
+    return ws != nullptr && have >= need && (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0;
+}
+
+int map_launch(hipError_t e) { return e == hipSuccess ? SPECDEC_OK : SPECDEC_ELAUNCH; }
+
+}  // namespace
+}  // namespace specdec
+
+using namespace specdec;
+
+extern "C" {
+
+const char* specdec_status_string(int status) {
+    switch (status) {
+        case SPECDEC_OK: return "ok";
+        case SPECDEC_EINVAL: return "invalid argument";
+        case SPECDEC_EDTYPE: return "unknown dtype";
+        case SPECDEC_EWORKSPACE: return "workspace missing, too small or misaligned";
+        case SPECDEC_ELAUNCH: return "kernel launch failed";
+        case SPECDEC_EDEVICE: return "no usable gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+const char* specdec_version(void) { return "specdec 0.1 (gfx950)"; }
+
+int specdec_workspace_init(void* workspace, size_t bytes, void* stream) {
+    if (workspace == nullptr && bytes != 0) return SPECDEC_EINVAL;
+    if (bytes == 0) return SPECDEC_OK;
+    return map_launch(hipMemsetAsync(workspace, 0, bytes, (hipStream_t)stream));
+}
+
+size_t specdec_softmax_stats_workspace_bytes(int64_t rows, int32_t V, specdec_dtype_t dtype) {
+    if (rows < 0 || V < 1 || V > kMaxV || !dtype_ok(dtype)) return 0;
+    return stats_layout(rows, V, dtype).total;
+}
+
+int specdec_softmax_stats(const void* logits, specdec_dtype_t dtype, int64_t rows, int32_t V,
+                          float temperature, float* row_max, float* row_sumexp, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
+    if (rows < 0 || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
+    Scale sc;
+    if (!make_scale(temperature, &sc)) return SPECDEC_EINVAL;
+    if (rows == 0) return SPECDEC_OK;
+    if (!logits || !row_max || !row_sumexp) return SPECDEC_EINVAL;
+    const StatsLayout L = stats_layout(rows, V, dtype);
+    if (!workspace_ok(workspace, workspace_bytes, L.total)) return SPECDEC_EWORKSPACE;
+    StatsParams p{};
+    bool vec;
+    row_geometry(V, dtype, aligned16(logits), &p.NV, &vec);
+    p.C = tiles_of(p.NV);
+    if ((size_t)rows * p.C > kMaxBlocks) return SPECDEC_EINVAL;
+    p.logits = logits;
+    p.rows = rows;
+    p.V = V;
+    p.sc = sc;
+    p.row_max = row_max;
+    p.row_sumexp = row_sumexp;
+    char* ws = static_cast<char*>(workspace);
+    p.part_m = reinterpret_cast<float*>(ws + L.part_m);
+    p.part_s = reinterpret_cast<double*>(ws + L.part_s);
+    return map_launch(launch_stats(p, dtype, vec, (hipStream_t)stream));
+}
+
+size_t specdec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, specdec_dtype_t dtype,
+                                      int one_hot_drafts) {
+    if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV || !dtype_ok(dtype)) return 0;
+    return verify_layout(B, K, V, dtype, one_hot_drafts != 0).total;
+}
+
+int specdec_verify(const void* target_logits, const void* draft_logits, specdec_dtype_t dtype,
+                   const int32_t* draft_tokens, const int32_t* k_per_req, const float* uniforms,
+                   float temperature, int32_t B, int32_t K, int32_t V, int32_t* out_tokens,
+                   int32_t* num_accepted, float* accept_prob, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
+    if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
+    Scale sc;
+    if (!make_scale(temperature, &sc)) return SPECDEC_EINVAL;
+    if (B == 0) return SPECDEC_OK;
+    if (!target_logits || !uniforms || !out_tokens || !num_accepted) return SPECDEC_EINVAL;
+    if (K > 0 && !draft_tokens) return SPECDEC_EINVAL;
+    const bool one_hot = (draft_logits == nullptr);
+    const VerifyLayout L = verify_layout(B, K, V, dtype, one_hot);
+    if (!workspace_ok(workspace, workspace_bytes, L.total)) return SPECDEC_EWORKSPACE;
+    VerifyParams p{};
+    bool vec;
+    row_geometry(V, dtype, aligned16(target_logits) && aligned16(draft_logits), &p.NV, &vec);
+    p.C = tiles_of(p.NV);
+    p.R = K + 1 + (one_hot ? 0 : K);
+    p.NS = (p.NV + kSlab - 1) / kSlab;
+    p.kinds = one_hot ? 1 : 2;
+    const size_t na = (size_t)(K + 1) * B * p.kinds * p.C;
+    const size_t nb = (size_t)B * p.C;
+    if (na + nb + (size_t)B > (size_t)0x7FFFFFFF) return SPECDEC_EINVAL;
+    p.NA = (int)na;
+    p.NB = (int)nb;
+    p.target = target_logits;
+    p.draft = draft_logits;
+    p.tokens = draft_tokens;
+    p.kpr = k_per_req;
+    p.unif = uniforms;
+    p.out = out_tokens;
+    p.nacc = num_accepted;
+    p.aprob = accept_prob;
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.sc = sc;
+    char* ws = static_cast<char*>(workspace);
+    p.err = reinterpret_cast<uint32_t*>(ws + L.err);
+    p.row_done = reinterpret_cast<uint32_t*>(ws + L.row_done);
+    p.req_done = reinterpret_cast<uint32_t*>(ws + L.req_done);
+    p.slot_m = reinterpret_cast<uint32_t*>(ws + L.slot_m);
+    p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);
+    p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
+    return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream));
+}
+
+size_t specdec_verify_greedy_workspace_bytes(int32_t B, int32_t K, int32_t V,
+                                             specdec_dtype_t dtype) {
+    if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV || !dtype_ok(dtype)) return 0;
+    return greedy_layout(B, K, V, dtype).total;
+}
+
+int specdec_verify_greedy(const void* target_logits, specdec_dtype_t dtype,
+                          const int32_t* draft_tokens, const int32_t* k_per_req, int32_t B,
+                          int32_t K, int32_t V, int32_t* out_tokens, int32_t* num_accepted,
+                          int32_t* argmax_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
+    if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
+    if (B == 0) return SPECDEC_OK;
+    if (!target_logits || !out_tokens || !num_accepted) return SPECDEC_EINVAL;
+    if (K > 0 && !draft_tokens) return SPECDEC_EINVAL;
+    const GreedyLayout L = greedy_layout(B, K, V, dtype);
+    if (!workspace_ok(workspace, workspace_bytes, L.total)) return SPECDEC_EWORKSPACE;
+    GreedyParams p{};
+    bool vec;
+    row_geometry(V, dtype, aligned16(target_logits), &p.NV, &vec);
+    p.C = tiles_of(p.NV);
+    if ((size_t)B * (K + 1) * p.C > kMaxBlocks) return SPECDEC_EINVAL;
+    p.target = target_logits;
+    p.tokens = draft_tokens;
+    p.kpr = k_per_req;
+    p.out = out_tokens;
+    p.nacc = num_accepted;
+    p.amax = argmax_out;
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    char* ws = static_cast<char*>(workspace);
+    p.part_v = reinterpret_cast<float*>(ws + L.part_v);
+    p.part_i = reinterpret_cast<int32_t*>(ws + L.part_i);
+    return map_launch(launch_greedy(p, dtype, vec, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,285 @@
+// Device-side building blocks shared by the verify, greedy and row-statistics
+// kernels for gfx950 (wave64, 256-thread workgroups).
+//
+// Streaming model: a row of V logits is read as 16-byte vectors (8 bf16 or 4
+// fp32 values).  A workgroup reads a "tile" of 4 x 256 vectors (16 KB): each
+// thread issues 4 independent 16-byte nontemporal loads before it decodes
+// any of them.  Consecutive threads read consecutive vectors, so each load
+// instruction of a wave covers 1 KB of contiguous memory.  A "slab" is one
+// load instruction of the workgroup: 256 consecutive vectors.
+//
+// Softmax arithmetic: p_t = exp((l_t - m) / T) / Z is evaluated as
+// exp2(l_t * c - M) with c = log2(e) / T split into two floats hi + lo
+// (hi < c strictly, so lo > 0 and a -inf logit gives -inf, never NaN) and
+// M = fp32(m * c), the reference offset of a thread, tile or row.  The
+// exponent is fma(x, lo, fma(x, hi, -M)): two operations, c carried to about
+// 48 bits, and the only rounding that varies from element to element is that
+// of the final float.  The rounding of M itself is the same for every
+// element that shares the reference, and every rescale between references
+// (thread -> tile -> row) uses the same M values, so it cancels in p.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specdec {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 4;                       // vectors per thread per tile
+constexpr int kSlab = kThreads;                  // vectors per slab
+constexpr int kTileVec = kThreads * kUnroll;     // vectors per tile (16 KB)
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum : int { kFP32 = 0, kBF16 = 1 };
+
+template <int DT> struct Elem;
+template <> struct Elem<kFP32> { static constexpr int E = 4; static constexpr int S = 4; };
+template <> struct Elem<kBF16> { static constexpr int E = 8; static constexpr int S = 2; };
+
+struct Scale {
+    float hi;   // largest float strictly below log2(e)/T
+    float lo;   // log2(e)/T - hi, rounded to float (> 0)
+    double c;   // log2(e)/T in double
+};
+
+// The reference offset of a max m: M = fp32(m * c).
+__host__ __device__ __forceinline__ float offset_of(float m, const Scale& s) {
+    return (float)((double)m * s.c);
+}
+
+// Base-2 exponent of exp(x / T) relative to the offset M: x * c - M.
+__device__ __forceinline__ float exponent2(float x, float M, const Scale& s) {
+    return __fmaf_rn(x, s.lo, __fmaf_rn(x, s.hi, -M));
+}
+
+__device__ __forceinline__ float fast_exp2(float a) { return __builtin_amdgcn_exp2f(a); }
+
+// ---------------------------------------------------------------------------
+// Loads
+// ---------------------------------------------------------------------------
+
+template <int DT> __device__ __forceinline__ u32x4 neg_inf_raw() {
+    if (DT == kBF16) return u32x4{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+    return u32x4{0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u};
+}
+
+// Vector v of a row, as raw bits.  VEC: the row start is 16-byte aligned and
+// V * sizeof(elem) is a multiple of 16, so every vector is one 16-byte load.
+// Otherwise elements are loaded one by one and those at index >= V (and the
+// whole vector when v >= NV) read as -inf.  NT selects nontemporal loads.
+template <int DT, bool VEC, bool NT>
+__device__ __forceinline__ u32x4 load_raw(const void* row, int V, int NV, int v) {
+    if (v >= NV) return neg_inf_raw<DT>();
+    if (VEC) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row) + v;
+        if (NT) return __builtin_nontemporal_load(p);
+        return *p;
+    }
+    u32x4 r = neg_inf_raw<DT>();
+    if (DT == kFP32) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(row);
+        const int t0 = v * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (t0 + e < V) r[e] = p[t0 + e];
+    } else {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(row);
+        const int t0 = v * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (t0 + e < V) {
+                const uint32_t h = p[t0 + e];
+                if (e & 1) r[e >> 1] = (r[e >> 1] & 0x0000FFFFu) | (h << 16);
+                else r[e >> 1] = (r[e >> 1] & 0xFFFF0000u) | h;
+            }
+        }
+    }
+    return r;
+}
+
+// Decode raw bits into E floats in ascending token order (exact for bf16:
+// a bf16 value is the top half of the float with the same value).
+template <int DT>
+__device__ __forceinline__ void decode(const u32x4& r, float (&x)[Elem<DT>::E]) {
+    if constexpr (DT == kFP32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(r[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(r[e] << 16);
+            x[2 * e + 1] = __uint_as_float(r[e] & 0xFFFF0000u);
+        }
+    }
+}
+
+// One logit, widened to float (used for gathers at draft tokens).
+template <int DT>
+__device__ __forceinline__ float load_one(const void* row, int t) {
+    if (DT == kFP32) return reinterpret_cast<const float*>(row)[t];
+    return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(row)[t]) << 16);
+}
+
+template <int E>
+__device__ __forceinline__ float pairwise_sum(const float (&v)[E]) {
+    if constexpr (E == 4) {
+        return __fadd_rn(__fadd_rn(v[0], v[1]), __fadd_rn(v[2], v[3]));
+    } else {
+        return __fadd_rn(__fadd_rn(__fadd_rn(v[0], v[1]), __fadd_rn(v[2], v[3])),
+                         __fadd_rn(__fadd_rn(v[4], v[5]), __fadd_rn(v[6], v[7])));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wave / workgroup reductions (wave64)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele).
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double n = __shfl_up(v, o, 64);
+        if (lane >= o) v += n;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float block_max(float v, float* lds /* [kWaves] */) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[w] = v;
+    __syncthreads();
+    float r = lds[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, lds[i]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ double block_sum(double v, double* lds /* [kWaves] */) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[w] = v;
+    __syncthreads();
+    double r = lds[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r += lds[i];
+    __syncthreads();
+    return r;
+}
+
+// Exclusive prefix sum over the workgroup in thread order; also returns the
+// total.
+__device__ __forceinline__ double block_exclusive_scan(double v, double* lds /* [kWaves] */,
+                                                       double* total) {
+    const double incl = wave_inclusive_scan(v);
+    const int lane = threadIdx.x & 63;
+    const double up = __shfl_up(incl, 1, 64);
+    const double excl = (lane == 0) ? 0.0 : up;
+    const int w = threadIdx.x >> 6;
+    if (lane == 63) lds[w] = incl;
+    __syncthreads();
+    double before = 0.0, all = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        if (i < w) before += lds[i];
+        all += lds[i];
+    }
+    __syncthreads();
+    *total = all;
+    return before + excl;
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics of one tile: (max m, sum of exp2(x * c - fp32(m * c))) over
+// the tile's vectors [tile * kTileVec, (tile + 1) * kTileVec) of one row.
+// Per thread: max over its vectors, then exponentials relative to that
+// thread's offset, summed in fp32 per vector (pairwise) and in fp64 across
+// vectors; the thread sums are rescaled to the workgroup offset and added in
+// fp64.  The result is valid in thread 0 only.
+// ---------------------------------------------------------------------------
+template <int DT, bool VEC>
+__device__ __forceinline__ void tile_stats(const void* row, int V, int NV, int tile, const Scale& sc,
+                                           float& m_out, double& s_out, float* lds_f,
+                                           double* lds_d) {
+    constexpr int E = Elem<DT>::E;
+    const int v0 = tile * kTileVec + threadIdx.x;
+    u32x4 raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) raw[u] = load_raw<DT, VEC, true>(row, V, NV, v0 + u * kThreads);
+    float mt = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        float x[E];
+        decode<DT>(raw[u], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) mt = fmaxf(mt, x[e]);
+    }
+    const bool empty = (mt == -INFINITY);
+    const float Mt = offset_of(empty ? 0.0f : mt, sc);
+    double s = 0.0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        float x[E], ev[E];
+        decode<DT>(raw[u], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) ev[e] = fast_exp2(exponent2(x[e], Mt, sc));
+        s += (double)pairwise_sum<E>(ev);
+    }
+    const float mb = block_max(mt, lds_f);
+    const float Mb = offset_of(mb, sc);
+    const double scaled = empty ? 0.0 : s * (double)fast_exp2((float)((double)Mt - (double)Mb));
+    const double sb = block_sum(scaled, lds_d);
+    m_out = mb;
+    s_out = sb;
+}
+
+// Merge per-tile partials (m_c, s_c) of one row into (max, sum relative to
+// the row offset fp32(max * c)), rescaling in fp64.  Loads go out 16 tiles
+// at a time.
+__device__ __forceinline__ void merge_partials(const float* pm, const double* ps, int C,
+                                               const Scale& sc, float* m_out, double* z_out) {
+    constexpr int G = 16;
+    float m = -INFINITY;
+    double z = 0.0;
+    for (int g0 = 0; g0 < C; g0 += G) {
+        float lm[G];
+        double ls[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const bool ok = g0 + i < C;
+            lm[i] = ok ? pm[g0 + i] : -INFINITY;
+            ls[i] = ok ? ps[g0 + i] : 0.0;
+        }
+        float gm = m;
+#pragma unroll
+        for (int i = 0; i < G; ++i) gm = fmaxf(gm, lm[i]);
+        if (gm != -INFINITY) {
+            const double Mg = (double)offset_of(gm, sc);
+            if (m != -INFINITY && gm > m) z *= exp2((double)offset_of(m, sc) - Mg);
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+                if (lm[i] != -INFINITY) z += ls[i] * exp2((double)offset_of(lm[i], sc) - Mg);
+            m = gm;
+        }
+    }
+    *m_out = m;
+    *z_out = z;
+}
+
+}  // namespace specdec

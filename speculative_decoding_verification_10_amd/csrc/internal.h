@@ -1,0 +1,85 @@
+// Host/device shared definitions of the specdec library (not part of the
+// public ABI): kernel parameter blocks, the workspace layout and the
+// launchers each kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace specdec {
+
+// How the final draw of one request is made.
+enum FinalMode : int {
+    kBonus = 0,       // every draft accepted: draw from p_{k_b}
+    kResidual = 1,    // rejection at j with draft logits: max(0, p_j - q_j)
+    kResidualOneHot = 2,  // rejection at j with a point-mass draft: p_j without x_j
+};
+
+// Decision of one request, computed from the row statistics.
+struct Decision {
+    int32_t j;        // position of the first rejection (k_b if none)
+    int32_t mode;     // FinalMode
+    int32_t tok;      // rejected draft token (one-hot residual), else -1
+    float Mp;         // offset fp32(max * c) of target row j
+    float Mq;         // offset of draft row j (residual with draft logits)
+    float rho;        // Z_p / Z_q of row j (residual with draft logits)
+    int32_t pad0, pad1;
+};
+
+struct VerifyParams {
+    const void* target;
+    const void* draft;          // null: one-hot drafts
+    const int32_t* tokens;
+    const int32_t* kpr;         // null: every k_b = K
+    const float* unif;
+    int32_t* out;
+    int32_t* nacc;
+    float* aprob;               // may be null
+    int B, K, V;
+    int NV;                     // vectors per row
+    int C;                      // tiles per row
+    int R;                      // row slots per request: K+1 target (+K draft)
+    int NS;                     // slabs per row
+    int kinds;                  // 2 with draft logits, 1 for one-hot drafts
+    int NA;                     // row-statistics workgroups: (K+1) * B * kinds * C
+    int NB;                     // final-tile workgroups: B * C
+    Scale sc;
+    uint32_t* err;              // workspace header: error bits
+    uint32_t* row_done;         // [B * R] tiles of each row written so far
+    uint32_t* req_done;         // [B] final-row tiles of each request written so far
+    uint32_t* slot_m;           // [B * R * C] tile max (self-validating)
+    uint64_t* slot_s;           // [B * R * C] tile sum (self-validating)
+    uint64_t* slot_slab;        // [B * C * 8] slab sums of the final draw (self-validating)
+};
+
+struct GreedyParams {
+    const void* target;
+    const int32_t* tokens;
+    const int32_t* kpr;
+    int32_t* out;
+    int32_t* nacc;
+    int32_t* amax;              // may be null
+    int B, K, V, NV, C;
+    float* part_v;              // [B * (K+1) * C]
+    int32_t* part_i;            // [B * (K+1) * C]
+};
+
+struct StatsParams {
+    const void* logits;
+    int64_t rows;
+    int V, NV, C;
+    Scale sc;
+    float* row_max;
+    float* row_sumexp;
+    float* part_m;              // [rows * C]
+    double* part_s;             // [rows * C]
+};
+
+hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s);
+hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s);
+hipError_t launch_stats(const StatsParams& p, int dtype, bool vec, hipStream_t s);
+
+}  // namespace specdec
