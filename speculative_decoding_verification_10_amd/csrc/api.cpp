@@ -13,7 +13,6 @@
 namespace specdec {
 namespace {
 
-constexpr int32_t kMaxK = 4096;
 constexpr int32_t kMaxV = 1 << 28;
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxBlocks = (size_t)1 << 24;   // gridDim.x * 256 threads < 2^32
@@ -53,7 +52,7 @@ bool make_scale(float temperature, Scale* s) {
 }
 
 struct VerifyLayout {
-    size_t err, row_done, req_done, slot_m, slot_s, slot_slab, total;
+    size_t err, req_done, slot_m, slot_s, slot_slab, total;
 };
 
 // Header (error bits) + self-validating slots: tile max / tile sum of every
@@ -69,7 +68,6 @@ VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, 
     VerifyLayout L;
     size_t off = 0;
     L.err = off;       off = align_up(off + sizeof(uint32_t));
-    L.row_done = off;  off = align_up(off + (size_t)B * R * sizeof(uint32_t));
     L.req_done = off;  off = align_up(off + (size_t)B * sizeof(uint32_t));
     L.slot_m = off;    off = align_up(off + parts * sizeof(uint32_t));
     L.slot_s = off;    off = align_up(off + parts * sizeof(uint64_t));
@@ -229,7 +227,6 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
     p.sc = sc;
     char* ws = static_cast<char*>(workspace);
     p.err = reinterpret_cast<uint32_t*>(ws + L.err);
-    p.row_done = reinterpret_cast<uint32_t*>(ws + L.row_done);
     p.req_done = reinterpret_cast<uint32_t*>(ws + L.req_done);
     p.slot_m = reinterpret_cast<uint32_t*>(ws + L.slot_m);
     p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);

@@ -11,6 +11,10 @@
 
 namespace specdec {
 
+// Largest number of drafted positions per request: the accept test keeps one
+// position per thread of a workgroup and every row's statistics in LDS.
+constexpr int32_t kMaxK = kThreads - 1;
+
 // How the final draw of one request is made.
 enum FinalMode : int {
     kBonus = 0,       // every draft accepted: draw from p_{k_b}
@@ -48,11 +52,10 @@ struct VerifyParams {
     int NB;                     // final-tile workgroups: B * C
     Scale sc;
     uint32_t* err;              // workspace header: error bits
-    uint32_t* row_done;         // [B * R] tiles of each row written so far
     uint32_t* req_done;         // [B] final-row tiles of each request written so far
     uint32_t* slot_m;           // [B * R * C] tile max (self-validating)
     uint64_t* slot_s;           // [B * R * C] tile sum (self-validating)
-    uint64_t* slot_slab;        // [B * C * 8] slab sums of the final draw (self-validating)
+    uint64_t* slot_slab;        // [B * C * kUnroll] slab sums of the final draw (self-validating)
 };
 
 struct GreedyParams {

@@ -1,32 +1,35 @@
-// Stochastic verify step on gfx950: two stream-ordered kernels over three
-// kinds of work.  verify_rows runs every A item in its own workgroup;
-// verify_final is persistent (each workgroup takes items blockIdx.x,
-// blockIdx.x + gridDim.x, ...; the grid is sized so that every workgroup is
-// resident at once) and runs the B items, the last of each request also
-// doing its L step:
+// Stochastic verify step on gfx950: two stream-ordered kernels.
 //
-//  A  (position p, request b, target|draft, tile c), position-major: tile max
-//     and sum of exponentials of target row p <= k_b or draft row p < k_b
-//     ("3.5 Speculative Decoding", "Notation": p and q are the
-//     temperature-processed distributions).  Rows past k_b are skipped.
-//  B  (request b, tile c): the accept test of request b -- u_i < min(1,
-//     p_i(x_i)/q_i(x_i)) left to right, first rejection j by a wavefront
-//     ballot ("The algorithm (one step)", step 3) -- then tile c of the
-//     final row (pair): slab sums of the unnormalised replacement masses
-//     max(0, p_j - q_j), or of p_{k_b} when every draft was accepted (step 4).
-//  L  (request b, by the workgroup that completes its last B item): the slab
-//     that holds u * S (prefix over slab sums), a re-read of that one slab,
-//     the smallest token t with u * S < C_t; then the outputs, and the reset
-//     of the request's slots.
+//  verify_rows   one workgroup per A item (position p, request b,
+//                target|draft, tile c), position-major: tile max and sum of
+//                exponentials of target row p <= k_b or draft row p < k_b
+//                ("3.5 Speculative Decoding", "Notation": p and q are the
+//                temperature-processed distributions).  Rows past k_b are
+//                skipped.
+//  verify_final  persistent (each workgroup takes items blockIdx.x,
+//                blockIdx.x + gridDim.x, ...; the grid is sized so that every
+//                workgroup is resident at once) over B items (request b,
+//                tile c): the accept test of request b -- u_i < min(1,
+//                p_i(x_i)/q_i(x_i)) left to right, first rejection j by a
+//                ballot ("The algorithm (one step)", step 3) -- then tile c of
+//                the final row (pair): slab sums of the unnormalised
+//                replacement masses max(0, p_j - q_j), or of p_{k_b} when
+//                every draft was accepted (step 4).  The workgroup that
+//                completes a request's last tile then locates the token: the
+//                slab that holds u * S (prefix over slab sums), a re-read of
+//                that one slab, the smallest token t with u * S < C_t.
 //
-// A -> B -> L hand-offs go through self-validating slots and a per-request
-// completion counter (slots.h).  The kernel boundary separates A from B; the
+// Tile results travel through self-validating slots and a per-request
+// completion counter (slots.h).  The kernel boundary orders A before B; the
 // only wait inside verify_final is for slab slots of tiles whose workgroups
-// have already counted themselves done, so it always ends.
+// have already counted themselves done, so it always ends.  The workgroup
+// that locates a request's token also zeroes its slots, so the workspace is
+// all zero again when the call ends.
 //
 // Masses are kept unnormalised: the replacement is Z_p * max(0, p - q) =
-// max(0, e_p - (Z_p/Z_q) e_q) with e = exp2((x - max) * c), the bonus is e_p.
-// An inverse CDF only needs the masses up to a common factor.
+// max(0, e_p - (Z_p/Z_q) e_q) with e = exp2(x * c - M) against each row's
+// offset M, the bonus is e_p.  An inverse CDF only needs the masses up to a
+// common factor.
 #include "internal.h"
 #include "slots.h"
 
@@ -107,134 +110,133 @@ __device__ void a_item(const VerifyParams& a, int item, float* lds_f, double* ld
     }
 }
 
-// Row statistics from the tile slots of one row, read once.  Returns false
-// when a tile has not been written yet (the values are then meaningless).
-__device__ bool row_from_slots(const VerifyParams& a, size_t rid, float* m_out, double* z_out) {
-    constexpr int G = 8;
-    const uint32_t* sm = a.slot_m + rid * a.C;
-    const uint64_t* ss = a.slot_s + rid * a.C;
-    bool ok = true;
-    float m = -INFINITY;
-    double z = 0.0;
-    for (int g0 = 0; g0 < a.C; g0 += G) {
-        uint32_t um[G];
-        uint64_t us[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const bool in = g0 + i < a.C;
-            um[i] = in ? slot_peek(sm + g0 + i) : enc_f32(-INFINITY);
-            us[i] = in ? slot_peek(ss + g0 + i) : enc_f64(0.0);
-        }
-        float gm = m;
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            ok = ok && um[i] != 0u && us[i] != 0ull;
-            gm = fmaxf(gm, dec_f32(um[i]));
-        }
-        if (!ok) break;
-        if (gm != -INFINITY) {
-            const double Mg = (double)offset_of(gm, a.sc);
-            if (m != -INFINITY && gm > m) z *= exp2((double)offset_of(m, a.sc) - Mg);
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                const float mi = dec_f32(um[i]);
-                if (mi != -INFINITY) z += dec_f64(us[i]) * exp2((double)offset_of(mi, a.sc) - Mg);
-            }
-            m = gm;
-        }
-    }
-    *m_out = m;
-    *z_out = z;
-    return ok;
+// ---------------------------------------------------------------------------
+// The accept test of request b by the whole workgroup, once every row of the
+// request is complete.
+//
+// Wave w merges the tile partials of row slots w, w+4, ... (lane l takes the
+// tiles l, l+64, ...): row max, row offset M = fp32(max * c), and the row sum
+// relative to M, rescaling each tile by exp2(M_tile - M) -- the difference
+// exact in fp64, the power in fp32 (relative error ~1e-7 per tile, exactly 1
+// for the tile that holds the max).  Thread i < k_b gathers p_i and q_i at
+// the draft token in fp64 and tests u_i < min(1, p_i/q_i); the first
+// rejection j comes from a ballot.  Every load is issued before any is
+// consumed except the gathers, which need the token: two memory round trips.
+// ---------------------------------------------------------------------------
+constexpr int kMaxRows = 2 * kMaxK + 1;
+constexpr int kRowBatch = 4;    // row slots per wave per batch of loads
+
+struct DecideShared {
+    float m[kMaxRows];          // row max
+    double z[kMaxRows];         // row sum relative to offset_of(max)
+    float ratio[kMaxK];         // min(1, p_i/q_i) per drafted position
+    unsigned long long rej[kWaves];
+    Decision dec;
+};
+
+// Row slot of the rs-th row in use: target rows 0..kb, then draft rows 0..kb-1.
+__device__ __forceinline__ int slot_of_rs(int rs, int kb, int K) {
+    return rs <= kb ? rs : (K + 1) + (rs - kb - 1);
 }
 
-// ---------------------------------------------------------------------------
-// The accept test of request b, by wave 0 of a workgroup.  Lane i handles
-// draft position i (lane k_b the bonus row).  The gathers at the draft
-// tokens are issued before any wait; then the tile slots are polled until
-// the positions up to the first rejection (or all of them) are known.  With
-// need_all (accept_prob requested) every drafted position is waited for and
-// its ratio written to accept_prob.  Writes the decision to *dec.
-// ---------------------------------------------------------------------------
 template <int DT>
-__device__ void decide(const VerifyParams& a, int b, bool need_all, Decision* dec) {
+__device__ void decide_block(const VerifyParams& a, int b, DecideShared* sh) {
     constexpr int S = Elem<DT>::S;
-    const int lane = threadIdx.x;
     const int K = a.K;
+    const int C = a.C;
     const int kb = k_of(a, b);
     const bool one_hot = (a.draft == nullptr);
-    const double c = a.sc.c;
-    int j = -1;
-    float fmp = 0.0f, fmq = 0.0f;
-    double fzp = 1.0, fzq = 1.0;
-    for (int base = 0; base <= kb; base += 64) {
-        const int i = min(base + lane, K);
-        const bool pos = (base + lane < kb);
-        const bool need = (base + lane <= kb);
-        const int x = (i < K) ? token_of(a, b, i) : 0;
-        const float u = a.unif[(size_t)b * (K + 1) + i];
-        const float l = load_one<DT>(row_ptr(a.target, (size_t)b * (K + 1) + i, a.V, S), x);
-        float dl = 0.0f;
-        if (!one_hot && K > 0)
-            dl = load_one<DT>(row_ptr(a.draft, (size_t)b * K + min(i, K - 1), a.V, S), x);
-        bool ready = !need, rej = false;
-        double ratio = -1.0;
-        float mp = 0.0f, mq = 0.0f;
-        double zp = 1.0, zq = 1.0;
-        int spins = 0;
-        for (;;) {
-            if (!ready) {
-                bool ok = row_from_slots(a, (size_t)b * a.R + i, &mp, &zp);
-                if (ok && pos && !one_hot) ok = row_from_slots(a, (size_t)b * a.R + K + 1 + i, &mq, &zq);
-                if (ok) {
-                    ready = true;
-                    if (pos) {
-                        const double p = exp2((double)l * c - (double)offset_of(mp, a.sc)) / zp;
-                        const double q = one_hot ? 1.0
-                                                 : exp2((double)dl * c - (double)offset_of(mq, a.sc)) / zq;
-                        ratio = (q == 0.0) ? 1.0 : fmin(1.0, p / q);
-                        rej = !((double)u < ratio);
+    const int nrs = kb + 1 + (one_hot ? 0 : kb);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = threadIdx.x;
+
+    // Position t < kb: token and uniform now, the gathers once the token is in.
+    int x = 0;
+    float u = 0.0f;
+    if (t < kb) {
+        x = token_of(a, b, t);
+        u = a.unif[(size_t)b * (K + 1) + t];
+    }
+    for (int base = 0; base < nrs; base += kWaves * kRowBatch) {
+        float lm[kRowBatch];
+        double ls[kRowBatch];
+#pragma unroll
+        for (int q = 0; q < kRowBatch; ++q) {
+            lm[q] = -INFINITY;
+            ls[q] = 0.0;
+        }
+        // Tiles lane, lane+64, ... of each row; rows with more than 64 tiles
+        // are folded into (max, sum) per lane with an online rescale.
+#pragma unroll
+        for (int q = 0; q < kRowBatch; ++q) {
+            const int rs = base + w + q * kWaves;
+            if (rs < nrs) {
+                const size_t idx = ((size_t)b * a.R + slot_of_rs(rs, kb, K)) * C;
+                for (int c = lane; c < C; c += 64) {
+                    const float mc = dec_f32(a.slot_m[idx + c]);
+                    const double sc = dec_f64(a.slot_s[idx + c]);
+                    if (mc == -INFINITY) continue;
+                    if (mc > lm[q]) {
+                        if (lm[q] != -INFINITY)
+                            ls[q] *= (double)fast_exp2(
+                                (float)((double)offset_of(lm[q], a.sc) - (double)offset_of(mc, a.sc)));
+                        lm[q] = mc;
                     }
+                    ls[q] += sc * (double)fast_exp2(
+                        (float)((double)offset_of(mc, a.sc) - (double)offset_of(lm[q], a.sc)));
                 }
             }
-            const unsigned long long rmask = __ballot(ready);
-            const unsigned long long jmask = __ballot(ready && rej);
-            const bool all_ready = (rmask == ~0ull);
-            const int prefix = all_ready ? 64 : __ffsll((long long)~rmask) - 1;
-            const int first = jmask ? __ffsll((long long)jmask) - 1 : 64;
-            int src = -1;
-            if (j < 0) {
-                if (first < prefix) {
-                    j = base + first;
-                    src = first;
-                } else if (all_ready && kb < base + 64) {
-                    j = kb;
-                    src = kb - base;
-                }
+        }
+#pragma unroll
+        for (int q = 0; q < kRowBatch; ++q) {
+            const int rs = base + w + q * kWaves;
+            const float rmax = wave_max(lm[q]);
+            double scaled = 0.0;
+            if (lm[q] != -INFINITY)
+                scaled = ls[q] * (double)fast_exp2(
+                    (float)((double)offset_of(lm[q], a.sc) - (double)offset_of(rmax, a.sc)));
+            const double zsum = __shfl(wave_sum(scaled), 0, 64);
+            if (rs < nrs && lane == 0) {
+                const int slot = slot_of_rs(rs, kb, K);
+                sh->m[slot] = rmax;
+                sh->z[slot] = zsum;
             }
-            if (src >= 0) {
-                fmp = __shfl(mp, src, 64);
-                fzp = __shfl(zp, src, 64);
-                fmq = __shfl(mq, src, 64);
-                fzq = __shfl(zq, src, 64);
-            }
-            if (need_all ? all_ready : (j >= 0 || all_ready)) break;
-            if (++spins > kSpinLimit) {
-                if (lane == 0) atomicOr(a.err, 1u);
-                if (j < 0) j = kb;
+        }
+    }
+    float l = 0.0f, dl = 0.0f;
+    if (t < kb) {
+        l = load_one<DT>(row_ptr(a.target, (size_t)b * (K + 1) + t, a.V, S), x);
+        if (!one_hot) dl = load_one<DT>(row_ptr(a.draft, (size_t)b * K + t, a.V, S), x);
+    }
+    __syncthreads();
+    bool rej = false;
+    if (t < kb) {
+        const double c = a.sc.c;
+        const double p = exp2((double)l * c - (double)offset_of(sh->m[t], a.sc)) / sh->z[t];
+        double q = 1.0;
+        if (!one_hot) {
+            const int qs = K + 1 + t;
+            q = exp2((double)dl * c - (double)offset_of(sh->m[qs], a.sc)) / sh->z[qs];
+        }
+        const double ratio = (q == 0.0) ? 1.0 : fmin(1.0, p / q);
+        sh->ratio[t] = (float)ratio;
+        rej = !((double)u < ratio);
+    }
+    const unsigned long long mask = __ballot(rej);
+    if (lane == 0) sh->rej[w] = mask;
+    __syncthreads();
+    if (t == 0) {
+        int j = kb;
+        for (int i = 0; i < kWaves; ++i) {
+            if (sh->rej[i]) {
+                j = i * 64 + __ffsll((long long)sh->rej[i]) - 1;
                 break;
             }
-            poll_pause();
         }
-        if (need_all && pos && a.aprob) a.aprob[(size_t)b * K + i] = (float)ratio;
-        if (j >= 0 && !need_all) break;
-    }
-    if (j < 0) j = kb;
-    if (lane == 0) {
         Decision d;
         d.j = j;
         d.tok = -1;
-        d.Mp = offset_of(fmp, a.sc);
+        d.Mp = offset_of(sh->m[j], a.sc);
         d.Mq = 0.0f;
         d.rho = 0.0f;
         d.pad0 = d.pad1 = 0;
@@ -245,21 +247,20 @@ __device__ void decide(const VerifyParams& a, int b, bool need_all, Decision* de
             d.tok = a.tokens[(size_t)b * K + j];
         } else {
             d.mode = kResidual;
-            d.Mq = offset_of(fmq, a.sc);
-            d.rho = (float)(fzp / fzq);
+            d.Mq = offset_of(sh->m[K + 1 + j], a.sc);
+            d.rho = (float)(sh->z[j] / sh->z[K + 1 + j]);
         }
-        *dec = d;
+        sh->dec = d;
     }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// B: one tile of the final row (pair) of request b.  Writes the tile's 8 slab
-// sums; the workgroup that completes the request's last tile then locates the
-// token (L below).
+// B: one tile of the final row (pair), then (last tile only) the locate.
 // ---------------------------------------------------------------------------
 struct BShared {
-    Decision dec;
-    double slab[kWaves][8];
+    DecideShared dsh;
+    double slab[kWaves][kUnroll];
     int last;
     int g, found, lastpos;
     double base, w, total;
@@ -314,21 +315,29 @@ __device__ void find_slab(const VerifyParams& a, const uint64_t* slabs, double u
     }
 }
 
-// L: the smallest token t with u * S < C_t, the outputs, and the reset of the
-// request's slots.  Run by the workgroup that wrote the request's last tile;
-// every other tile of the request has been written (its slab slots are
-// awaited) and has finished reading the row slots.
+// The smallest token t with u * S < C_t, the outputs, and the reset of the
+// request's slots.  Run by the workgroup that wrote the request's last tile:
+// every other tile has counted itself done (its slab slots are awaited) and
+// has finished reading the row slots.
 template <int DT, bool VEC>
 __device__ void locate(const VerifyParams& a, int b, Decision d, BShared* sh) {
     constexpr int E = Elem<DT>::E;
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
     const int kb = k_of(a, b);
-    uint64_t* slabs = a.slot_slab + (size_t)b * a.C * kUnroll;
+    const int nslab = a.C * kUnroll;
+    uint64_t* slabs = a.slot_slab + (size_t)b * nslab;
     const double u = (double)a.unif[(size_t)b * (K + 1) + kb];
     const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
-    if (threadIdx.x < 64) find_slab(a, slabs, u, &sh->g, &sh->base, &sh->w, &sh->total);
+    if (threadIdx.x < 64) {
+        find_slab(a, slabs, u, &sh->g, &sh->base, &sh->w, &sh->total);
+    } else {
+        // Slab slots past the last slab of the row (zeros) must be in before
+        // they are reset.
+        for (int t = a.NS + threadIdx.x - 64; t < nslab; t += kThreads - 64)
+            slot_wait(slabs + t, a.err, (uint64_t)1);
+    }
     if (threadIdx.x == 0) {
         sh->found = 0x7FFFFFFF;
         sh->lastpos = -1;
@@ -386,27 +395,20 @@ __device__ void locate(const VerifyParams& a, int b, Decision d, BShared* sh) {
         if (i < j) o = a.tokens[(size_t)b * K + i];
         else if (i == j) o = tok;
         a.out[(size_t)b * (K + 1) + i] = o;
-        if (a.aprob && i < K && i >= kb) a.aprob[(size_t)b * K + i] = -1.0f;
+        if (a.aprob && i < K) a.aprob[(size_t)b * K + i] = (i < kb) ? sh->dsh.ratio[i] : -1.0f;
     }
     if (threadIdx.x == 0) a.nacc[b] = j;
-    // accept_prob needs every drafted position (also past the rejection).
-    if (a.aprob && threadIdx.x < 64) decide<DT>(a, b, true, &sh->dec);
-    __syncthreads();
 
     // Reset the request's slots and counter for the next call.
-    const int nrow_slots = kb + 1 + (a.draft ? kb : 0);
-    const int nrow = nrow_slots * a.C;
+    const int nrs = kb + 1 + (a.draft ? kb : 0);
+    const int nrow = nrs * a.C;
     for (int t = threadIdx.x; t < nrow; t += kThreads) {
         const int rs = t / a.C, c = t % a.C;
-        const int slot = rs <= kb ? rs : (K + 1) + (rs - kb - 1);
-        const size_t idx = ((size_t)b * a.R + slot) * a.C + c;
+        const size_t idx = ((size_t)b * a.R + slot_of_rs(rs, kb, K)) * a.C + c;
         slot_put(a.slot_m + idx, 0u);
         slot_put(a.slot_s + idx, (uint64_t)0);
     }
-    for (int t = threadIdx.x; t < a.C * kUnroll; t += kThreads) {
-        slot_wait(slabs + t, a.err, (uint64_t)1);
-        slot_put(slabs + t, (uint64_t)0);
-    }
+    for (int t = threadIdx.x; t < nslab; t += kThreads) slot_put(slabs + t, (uint64_t)0);
     if (threadIdx.x == 0) slot_put(a.req_done + b, 0u);
 }
 
@@ -416,9 +418,8 @@ __device__ void b_item(const VerifyParams& a, int item, BShared* sh) {
     constexpr int S = Elem<DT>::S;
     const int b = item / a.C;
     const int tile = item % a.C;
-    if (threadIdx.x < 64) decide<DT>(a, b, false, &sh->dec);
-    __syncthreads();
-    const Decision d = sh->dec;
+    decide_block<DT>(a, b, &sh->dsh);
+    const Decision d = sh->dsh.dec;
     const void* rowp = row_ptr(a.target, (size_t)b * (a.K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * a.K + d.j, a.V, S) : nullptr;
     const int v0 = tile * kTileVec + threadIdx.x;
@@ -463,8 +464,7 @@ __global__ __launch_bounds__(kThreads) void verify_rows(VerifyParams a) {
 }
 
 // Kernel 2 (persistent): the B items; the one completing a request's tiles
-// also locates its token.  Nothing waits except for slab slots that are
-// already written.
+// also locates its token.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
     __shared__ BShared sh;
