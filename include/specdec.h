@@ -33,11 +33,12 @@
  *     errors are detected on the host before anything is launched and leave
  *     every output untouched.  No C++ exception crosses the ABI.
  *   - Workspace: device memory of at least the size the matching
- *     *_workspace_bytes() function returns, 256-byte aligned.  It must be
- *     zero-filled before its first use (specdec_workspace_init does that);
- *     every call that returns SPECDEC_OK and runs to completion leaves it
- *     ready for the next call.  Calls that may run concurrently need distinct
- *     workspaces.  After a failed launch, zero it again.
+ *     *_workspace_bytes() function returns, 256-byte aligned.  Its contents
+ *     need no initialisation: a call writes every scratch word before it
+ *     reads it.  The first 4 bytes hold error bits: a call ORs in a bit when
+ *     an internal bounded wait gives up (never in a correct run); zero them
+ *     with specdec_workspace_init to start afresh.  Calls that may run
+ *     concurrently need distinct workspaces.
  *   - Preconditions not checked on the fast path (a violation gives
  *     unspecified tokens, never an out-of-bounds access): logits finite or
  *     -inf (-inf = probability 0; a row may not be all -inf); 0 <=
@@ -75,7 +76,7 @@ const char *specdec_status_string(int status);
 /* Library version string (static storage). */
 const char *specdec_version(void);
 
-/* Zero-fill `bytes` of workspace on `stream` (asynchronous). */
+/* Zero-fill `bytes` of workspace on `stream` (asynchronous); clears the error bits. */
 int specdec_workspace_init(void *workspace, size_t bytes, void *stream);
 
 /*
@@ -113,8 +114,8 @@ int specdec_softmax_stats(const void *logits, specdec_dtype_t dtype, int64_t row
  *                 -1 for i >= k_b.
  * The final draw is an inverse CDF in ascending token id: the smallest t
  * with u * S < C_t, C_t the running sum of the (unnormalised) replacement or
- * bonus masses and S their total.  B >= 0, 0 <= K <= 255, 1 <= V <= 2^28;
- * larger K or V give SPECDEC_EINVAL.
+ * bonus masses and S their total.  B >= 0, 0 <= K <= 255, 1 <= V <= 2^22
+ * (fp32) or 2^23 (bf16); larger K or V give SPECDEC_EINVAL.
  */
 size_t specdec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, specdec_dtype_t dtype,
                                       int one_hot_drafts);

@@ -113,8 +113,8 @@ def _stream(device: torch.device) -> int:
 
 
 class Workspace:
-    """Device scratch for the library, zero-filled when allocated (the
-    library leaves it reusable after every successful call)."""
+    """Device scratch for the library (zero-filled when allocated, so the
+    error word at offset 0 starts clear; calls need no other initialisation)."""
 
     def __init__(self, nbytes: int, device):
         self.nbytes = int(nbytes)

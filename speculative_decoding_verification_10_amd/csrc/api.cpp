@@ -14,6 +14,7 @@ namespace specdec {
 namespace {
 
 constexpr int32_t kMaxV = 1 << 28;
+constexpr int kMaxFinalTiles = 1024;               // tiles per row in the stochastic verify
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxBlocks = (size_t)1 << 24;   // gridDim.x * 256 threads < 2^32
 
@@ -52,11 +53,12 @@ bool make_scale(float temperature, Scale* s) {
 }
 
 struct VerifyLayout {
-    size_t err, req_done, slot_m, slot_s, slot_slab, total;
+    size_t err, slot_m, slot_s, slot_l, slot_slab, slot_slab2, total;
 };
 
-// Header (error bits) + self-validating slots: tile max / tile sum of every
-// row slot of every request, and the slab sums of every request's final row.
+// Header (error bits) and self-validating slots: tile max / tile sum of every
+// row slot of every request, the logit at the draft token of every row, and
+// two sets of slab sums of every request's final row.
 VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, bool one_hot) {
     int NV, NVv;
     bool vec;
@@ -68,10 +70,11 @@ VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, 
     VerifyLayout L;
     size_t off = 0;
     L.err = off;       off = align_up(off + sizeof(uint32_t));
-    L.req_done = off;  off = align_up(off + (size_t)B * sizeof(uint32_t));
     L.slot_m = off;    off = align_up(off + parts * sizeof(uint32_t));
     L.slot_s = off;    off = align_up(off + parts * sizeof(uint64_t));
+    L.slot_l = off;    off = align_up(off + (size_t)B * R * sizeof(uint32_t));
     L.slot_slab = off; off = align_up(off + (size_t)B * C * kUnroll * sizeof(uint64_t));
+    L.slot_slab2 = off; off = align_up(off + (size_t)B * C * kUnroll * sizeof(uint64_t));
     L.total = off;
     return L;
 }
@@ -208,11 +211,9 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
     p.R = K + 1 + (one_hot ? 0 : K);
     p.NS = (p.NV + kSlab - 1) / kSlab;
     p.kinds = one_hot ? 1 : 2;
-    const size_t na = (size_t)(K + 1) * B * p.kinds * p.C;
-    const size_t nb = (size_t)B * p.C;
-    if (na + nb + (size_t)B > (size_t)0x7FFFFFFF) return SPECDEC_EINVAL;
-    p.NA = (int)na;
-    p.NB = (int)nb;
+    // One workgroup per row item; the final kernel holds every tile of a
+    // request resident at once.
+    if ((size_t)B * p.R * p.C > kMaxBlocks || p.C > kMaxFinalTiles) return SPECDEC_EINVAL;
     p.target = target_logits;
     p.draft = draft_logits;
     p.tokens = draft_tokens;
@@ -227,10 +228,11 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
     p.sc = sc;
     char* ws = static_cast<char*>(workspace);
     p.err = reinterpret_cast<uint32_t*>(ws + L.err);
-    p.req_done = reinterpret_cast<uint32_t*>(ws + L.req_done);
     p.slot_m = reinterpret_cast<uint32_t*>(ws + L.slot_m);
     p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);
+    p.slot_l = reinterpret_cast<uint32_t*>(ws + L.slot_l);
     p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
+    p.slot_slab2 = reinterpret_cast<uint64_t*>(ws + L.slot_slab2);
     return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream));
 }
 

@@ -134,29 +134,82 @@ __device__ __forceinline__ float pairwise_sum(const float (&v)[E]) {
 
 // ---------------------------------------------------------------------------
 // Wave / workgroup reductions (wave64)
+//
+// Built on DPP moves (a few cycles each) rather than LDS-crossbar shuffles:
+// quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror and row_mirror combine
+// lanes within each row of 16; row_bcast:15 (into rows 1 and 3) and
+// row_bcast:31 (into rows 2 and 3) carry row results up the wave, so lane 63
+// ends with the whole-wave result.  Lanes a DPP move does not write keep the
+// identity passed as `old`.
 // ---------------------------------------------------------------------------
+enum : int {
+    kDppQuad1032 = 0xB1,
+    kDppQuad2301 = 0x4E,
+    kDppRowShr1 = 0x111,
+    kDppRowShr2 = 0x112,
+    kDppRowShr4 = 0x114,
+    kDppRowShr8 = 0x118,
+    kDppRowMirror = 0x140,
+    kDppRowHalfMirror = 0x141,
+    kDppRowBcast15 = 0x142,
+    kDppRowBcast31 = 0x143,
+};
 
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp(float v, float old) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp(double v, double old) {
+    const int lo = __builtin_amdgcn_update_dpp(__double2loint(old), __double2loint(v), CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(__double2hiint(old), __double2hiint(v), CTRL, ROWS, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ float lane63(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ double lane63(double v) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                            __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
+
+// Max / sum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp<kDppQuad1032>(v, -INFINITY));
+    v = fmaxf(v, dpp<kDppQuad2301>(v, -INFINITY));
+    v = fmaxf(v, dpp<kDppRowHalfMirror>(v, -INFINITY));
+    return fmaxf(v, dpp<kDppRowMirror>(v, -INFINITY));
+}
+__device__ __forceinline__ double row16_sum(double v) {
+    v += dpp<kDppQuad1032>(v, 0.0);
+    v += dpp<kDppQuad2301>(v, 0.0);
+    v += dpp<kDppRowHalfMirror>(v, 0.0);
+    return v + dpp<kDppRowMirror>(v, 0.0);
+}
+
+// Max / sum over the wave, in every lane.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = row16_max(v);
+    v = fmaxf(v, dpp<kDppRowBcast15, 0xA>(v, -INFINITY));
+    v = fmaxf(v, dpp<kDppRowBcast31, 0xC>(v, -INFINITY));
+    return lane63(v);
 }
-
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v = row16_sum(v);
+    v += dpp<kDppRowBcast15, 0xA>(v, 0.0);
+    v += dpp<kDppRowBcast31, 0xC>(v, 0.0);
+    return lane63(v);
 }
 
-// Inclusive prefix sum over the 64 lanes (Hillis-Steele).
+// Inclusive prefix sum over the 64 lanes.
 __device__ __forceinline__ double wave_inclusive_scan(double v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double n = __shfl_up(v, o, 64);
-        if (lane >= o) v += n;
-    }
-    return v;
+    v += dpp<kDppRowShr1>(v, 0.0);
+    v += dpp<kDppRowShr2>(v, 0.0);
+    v += dpp<kDppRowShr4>(v, 0.0);
+    v += dpp<kDppRowShr8>(v, 0.0);
+    v += dpp<kDppRowBcast15, 0xA>(v, 0.0);
+    return v + dpp<kDppRowBcast31, 0xC>(v, 0.0);
 }
 
 __device__ __forceinline__ float block_max(float v, float* lds /* [kWaves] */) {
@@ -212,23 +265,33 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* lds /* 
 // thread's offset, summed in fp32 per vector (pairwise) and in fp64 across
 // vectors; the thread sums are rescaled to the workgroup offset and added in
 // fp64.  The result is valid in thread 0 only.
+//
+// With gx >= 0 the thread that holds token gx (if it lies in this tile)
+// stores its logit, widened to float, to *gval and returns true.
 // ---------------------------------------------------------------------------
 template <int DT, bool VEC>
-__device__ __forceinline__ void tile_stats(const void* row, int V, int NV, int tile, const Scale& sc,
+__device__ __forceinline__ bool tile_stats(const void* row, int V, int NV, int tile, const Scale& sc,
                                            float& m_out, double& s_out, float* lds_f,
-                                           double* lds_d) {
+                                           double* lds_d, int gx = -1, float* gval = nullptr) {
     constexpr int E = Elem<DT>::E;
     const int v0 = tile * kTileVec + threadIdx.x;
     u32x4 raw[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) raw[u] = load_raw<DT, VEC, true>(row, V, NV, v0 + u * kThreads);
     float mt = -INFINITY;
+    bool held = false;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         float x[E];
         decode<DT>(raw[u], x);
 #pragma unroll
         for (int e = 0; e < E; ++e) mt = fmaxf(mt, x[e]);
+        if (gx >= 0 && v0 + u * kThreads == gx / E) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (e == gx % E) *gval = x[e];
+            held = true;
+        }
     }
     const bool empty = (mt == -INFINITY);
     const float Mt = offset_of(empty ? 0.0f : mt, sc);
@@ -247,6 +310,7 @@ __device__ __forceinline__ void tile_stats(const void* row, int V, int NV, int t
     const double sb = block_sum(scaled, lds_d);
     m_out = mb;
     s_out = sb;
+    return held;
 }
 
 // Merge per-tile partials (m_c, s_c) of one row into (max, sum relative to

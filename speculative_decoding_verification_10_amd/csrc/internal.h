@@ -48,14 +48,14 @@ struct VerifyParams {
     int R;                      // row slots per request: K+1 target (+K draft)
     int NS;                     // slabs per row
     int kinds;                  // 2 with draft logits, 1 for one-hot drafts
-    int NA;                     // row-statistics workgroups: (K+1) * B * kinds * C
-    int NB;                     // final-tile workgroups: B * C
     Scale sc;
     uint32_t* err;              // workspace header: error bits
-    uint32_t* req_done;         // [B] final-row tiles of each request written so far
     uint32_t* slot_m;           // [B * R * C] tile max (self-validating)
     uint64_t* slot_s;           // [B * R * C] tile sum (self-validating)
+    uint32_t* slot_l;           // [B * R] logit at the draft token of each row (self-validating)
     uint64_t* slot_slab;        // [B * C * kUnroll] slab sums of the final draw (self-validating)
+    uint64_t* slot_slab2;       // [B * C * kUnroll] the same for a draw from p_j when every
+                                // replacement mass is zero
 };
 
 struct GreedyParams {

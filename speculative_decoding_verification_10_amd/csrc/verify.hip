@@ -1,30 +1,30 @@
-// Stochastic verify step on gfx950: two stream-ordered kernels.
+// Stochastic verify step on gfx950: two stream-ordered kernels, one
+// workgroup per work item.
 //
-//  verify_rows   one workgroup per A item (position p, request b,
-//                target|draft, tile c), position-major: tile max and sum of
-//                exponentials of target row p <= k_b or draft row p < k_b
+//  verify_rows   row item (request b, row, tile): tile max and sum of
+//                exponentials of target row i <= k_b or draft row i < k_b
 //                ("3.5 Speculative Decoding", "Notation": p and q are the
-//                temperature-processed distributions).  Rows past k_b are
-//                skipped.
-//  verify_final  persistent (each workgroup takes items blockIdx.x,
-//                blockIdx.x + gridDim.x, ...; the grid is sized so that every
-//                workgroup is resident at once) over B items (request b,
-//                tile c): the accept test of request b -- u_i < min(1,
-//                p_i(x_i)/q_i(x_i)) left to right, first rejection j by a
-//                ballot ("The algorithm (one step)", step 3) -- then tile c of
-//                the final row (pair): slab sums of the unnormalised
-//                replacement masses max(0, p_j - q_j), or of p_{k_b} when
-//                every draft was accepted (step 4).  The workgroup that
-//                completes a request's last tile then locates the token: the
-//                slab that holds u * S (prefix over slab sums), a re-read of
-//                that one slab, the smallest token t with u * S < C_t.
+//                temperature-processed distributions), and the logit at the
+//                draft token x_i when it lies in the tile.  Rows past k_b are
+//                skipped.  No item waits for another.  Items of target row 0
+//                also clear the request's slab slots for the final kernel.
+//  verify_final  final item (request b, tile): the decision of request b --
+//                the tile partials of every row merged, u_i < min(1,
+//                p_i(x_i)/q_i(x_i)) tested for every drafted position, the
+//                first rejection j taken with a ballot ("The algorithm (one
+//                step)", step 3) -- then the tile's slab sums of the
+//                unnormalised replacement masses max(0, p_j - q_j), or of
+//                p_{k_b} when every draft was accepted (step 4).  Every final
+//                item of the request then reads all of the request's slab
+//                sums and finds the slab that holds u * S; the item whose
+//                tile holds that slab re-reads it, takes the smallest token t
+//                with u * S < C_t and writes the request's outputs.
 //
-// Tile results travel through self-validating slots and a per-request
-// completion counter (slots.h).  The kernel boundary orders A before B; the
-// only wait inside verify_final is for slab slots of tiles whose workgroups
-// have already counted themselves done, so it always ends.  The workgroup
-// that locates a request's token also zeroes its slots, so the workspace is
-// all zero again when the call ends.
+// Results cross workgroups through self-validating slots (slots.h).  The
+// kernel boundary orders every row slot before its readers; the final items
+// of a request are in one launch that fits on the device at once, and each
+// publishes its slab sums before it waits for the others', so every wait
+// ends.
 //
 // Masses are kept unnormalised: the replacement is Z_p * max(0, p - q) =
 // max(0, e_p - (Z_p/Z_q) e_q) with e = exp2(x * c - M) against each row's
@@ -36,19 +36,42 @@
 namespace specdec {
 namespace {
 
+constexpr int kMaxRows = 2 * kMaxK + 1;
+
 __device__ __forceinline__ const void* row_ptr(const void* base, size_t row, int V, int S) {
     return static_cast<const char*>(base) + row * (size_t)V * (size_t)S;
-}
-
-// k_b, clamped to [0, K] so that a bad value can never address memory
-// outside the caller's arrays.
-__device__ __forceinline__ int k_of(const VerifyParams& a, int b) {
-    return a.kpr ? min(max(a.kpr[b], 0), a.K) : a.K;
 }
 
 // Draft token, clamped to [0, V) for addressing.
 __device__ __forceinline__ int token_of(const VerifyParams& a, int b, int i) {
     return min(max(a.tokens[(size_t)b * a.K + i], 0), a.V - 1);
+}
+
+// Row slot of the rs-th row a request reads: target rows 0..kb, then draft
+// rows 0..kb-1.
+__device__ __forceinline__ int slot_of_rs(int rs, int kb, int K) {
+    return rs <= kb ? rs : (K + 1) + (rs - kb - 1);
+}
+
+__device__ __forceinline__ int rows_of(int kb, int kinds) { return kb + 1 + (kinds == 2 ? kb : 0); }
+
+struct StepShared {
+    float m[kMaxRows];                  // row max, by row slot
+    double z[kMaxRows];                 // row sum relative to offset_of(max)
+    float ratio[kMaxK];
+    unsigned long long rej[kWaves];
+    Decision dec;
+    float red_f[kWaves];
+    double red_d[kWaves];
+    double slab[kWaves][kUnroll];
+    int g, found, lastpos, lastnz;
+    double base, w, total;
+};
+
+// k_b, clamped to [0, K] so that a bad value can never address memory
+// outside the caller's arrays.
+__device__ __forceinline__ int kb_of(const VerifyParams& a, int b) {
+    return a.kpr ? min(max(a.kpr[b], 0), a.K) : a.K;
 }
 
 // Unnormalised final-draw masses of one vector.
@@ -76,167 +99,134 @@ __device__ __forceinline__ void final_masses(const u32x4& rp, const u32x4& rq, c
     }
 }
 
-// ---------------------------------------------------------------------------
-// A: tile statistics of one row
-// ---------------------------------------------------------------------------
-template <int DT, bool VEC>
-__device__ void a_item(const VerifyParams& a, int item, float* lds_f, double* lds_d) {
-    constexpr int S = Elem<DT>::S;
-    const int c = item % a.C;
-    int t = item / a.C;
-    const int kind = t % a.kinds;
-    t /= a.kinds;
-    const int b = t % a.B;
-    const int p = t / a.B;
-    const int kb = k_of(a, b);
-    const void* row;
-    int slot;
-    if (kind == 0) {
-        if (p > kb) return;
-        row = row_ptr(a.target, (size_t)b * (a.K + 1) + p, a.V, S);
-        slot = p;
-    } else {
-        if (p >= kb) return;
-        row = row_ptr(a.draft, (size_t)b * a.K + p, a.V, S);
-        slot = a.K + 1 + p;
+// (m1, z1) <- merge of two partials (max, sum relative to offset_of(max)).
+__device__ __forceinline__ void merge2(float& m1, double& z1, float m2, double z2, const Scale& sc) {
+    if (m2 == -INFINITY) return;
+    if (m1 == -INFINITY) {
+        m1 = m2;
+        z1 = z2;
+        return;
     }
-    float m;
-    double z;
-    tile_stats<DT, VEC>(row, a.V, a.NV, c, a.sc, m, z, lds_f, lds_d);
-    if (threadIdx.x == 0) {
-        const size_t idx = ((size_t)b * a.R + slot) * a.C + c;
-        slot_put(&a.slot_s[idx], enc_f64(z));
-        slot_put(&a.slot_m[idx], enc_f32(m));
-    }
+    const float m = fmaxf(m1, m2);
+    const double M = (double)offset_of(m, sc);
+    z1 = z1 * (double)fast_exp2((float)((double)offset_of(m1, sc) - M)) +
+         z2 * (double)fast_exp2((float)((double)offset_of(m2, sc) - M));
+    m1 = m;
 }
 
 // ---------------------------------------------------------------------------
-// The accept test of request b by the whole workgroup, once every row of the
-// request is complete.
+// The decision of request b, by the whole workgroup, into sh.dec and
+// sh.ratio.
 //
-// Wave w merges the tile partials of row slots w, w+4, ... (lane l takes the
-// tiles l, l+64, ...): row max, row offset M = fp32(max * c), and the row sum
-// relative to M, rescaling each tile by exp2(M_tile - M) -- the difference
-// exact in fp64, the power in fp32 (relative error ~1e-7 per tile, exactly 1
-// for the tile that holds the max).  Thread i < k_b gathers p_i and q_i at
-// the draft token in fp64 and tests u_i < min(1, p_i/q_i); the first
-// rejection j comes from a ballot.  Every load is issued before any is
-// consumed except the gathers, which need the token: two memory round trips.
+// Rows are merged 16 lanes to a row, four rows per wave and two row groups
+// per lane, so one pass covers 32 rows and every slot load of the pass goes
+// out before any is used.  Lane `sub` of a row folds tiles sub, sub+16, ...:
+// row max, row offset M = fp32(max * c), and the row sum relative to M, each
+// tile rescaled by exp2(M_tile - M) -- the difference exact in fp64, the
+// power in fp32 (relative error ~1e-7, exactly 1 for the tile that holds the
+// max).  Thread i < k_b takes p_i and q_i at the draft token in fp64 and
+// tests u_i < min(1, p_i/q_i); the first rejection j comes from a ballot.
 // ---------------------------------------------------------------------------
-constexpr int kMaxRows = 2 * kMaxK + 1;
-constexpr int kRowBatch = 4;    // row slots per wave per batch of loads
+constexpr int kRowGroups = 2;                         // row groups per lane
+constexpr int kRowsPerPass = kRowGroups * kWaves * 4;  // 32
+constexpr int kTilesPerLoad = 4;                      // tiles per lane per load batch
 
-struct DecideShared {
-    float m[kMaxRows];          // row max
-    double z[kMaxRows];         // row sum relative to offset_of(max)
-    float ratio[kMaxK];         // min(1, p_i/q_i) per drafted position
-    unsigned long long rej[kWaves];
-    Decision dec;
-};
-
-// Row slot of the rs-th row in use: target rows 0..kb, then draft rows 0..kb-1.
-__device__ __forceinline__ int slot_of_rs(int rs, int kb, int K) {
-    return rs <= kb ? rs : (K + 1) + (rs - kb - 1);
-}
-
-template <int DT>
-__device__ void decide_block(const VerifyParams& a, int b, DecideShared* sh) {
-    constexpr int S = Elem<DT>::S;
-    const int K = a.K;
-    const int C = a.C;
-    const int kb = k_of(a, b);
+__device__ void decide(const VerifyParams& a, int b, int kb, StepShared& sh) {
+    const int K = a.K, C = a.C, R = a.R;
     const bool one_hot = (a.draft == nullptr);
-    const int nrs = kb + 1 + (one_hot ? 0 : kb);
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = threadIdx.x;
+    const int nrs = rows_of(kb, a.kinds);
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, sub = lane & 15;
 
-    // Position t < kb: token and uniform now, the gathers once the token is in.
-    int x = 0;
+    uint32_t rl = 0, rd = 0;
     float u = 0.0f;
     if (t < kb) {
-        x = token_of(a, b, t);
+        rl = slot_peek(a.slot_l + (size_t)b * R + t);
+        if (!one_hot) rd = slot_peek(a.slot_l + (size_t)b * R + K + 1 + t);
         u = a.unif[(size_t)b * (K + 1) + t];
     }
-    for (int base = 0; base < nrs; base += kWaves * kRowBatch) {
-        float lm[kRowBatch];
-        double ls[kRowBatch];
+    for (int base = 0; base < nrs; base += kRowsPerPass) {
+        float lm[kRowGroups];
+        double ls[kRowGroups];
+        int rs[kRowGroups];
+        size_t row0[kRowGroups];
 #pragma unroll
-        for (int q = 0; q < kRowBatch; ++q) {
-            lm[q] = -INFINITY;
-            ls[q] = 0.0;
+        for (int g = 0; g < kRowGroups; ++g) {
+            lm[g] = -INFINITY;
+            ls[g] = 0.0;
+            rs[g] = base + g * (kWaves * 4) + w * 4 + (lane >> 4);
+            row0[g] = ((size_t)b * R + slot_of_rs(min(rs[g], nrs - 1), kb, K)) * C;
         }
-        // Tiles lane, lane+64, ... of each row; rows with more than 64 tiles
-        // are folded into (max, sum) per lane with an online rescale.
+        for (int c0 = 0; c0 < C; c0 += 16 * kTilesPerLoad) {
+            uint32_t um[kRowGroups][kTilesPerLoad];
+            uint64_t us[kRowGroups][kTilesPerLoad];
 #pragma unroll
-        for (int q = 0; q < kRowBatch; ++q) {
-            const int rs = base + w + q * kWaves;
-            if (rs < nrs) {
-                const size_t idx = ((size_t)b * a.R + slot_of_rs(rs, kb, K)) * C;
-                for (int c = lane; c < C; c += 64) {
-                    const float mc = dec_f32(a.slot_m[idx + c]);
-                    const double sc = dec_f64(a.slot_s[idx + c]);
-                    if (mc == -INFINITY) continue;
-                    if (mc > lm[q]) {
-                        if (lm[q] != -INFINITY)
-                            ls[q] *= (double)fast_exp2(
-                                (float)((double)offset_of(lm[q], a.sc) - (double)offset_of(mc, a.sc)));
-                        lm[q] = mc;
+            for (int g = 0; g < kRowGroups; ++g) {
+#pragma unroll
+                for (int q = 0; q < kTilesPerLoad; ++q) {
+                    const int c = c0 + sub + 16 * q;
+                    um[g][q] = 0;
+                    us[g][q] = 0;
+                    if (rs[g] < nrs && c < C) {
+                        um[g][q] = slot_peek(a.slot_m + row0[g] + c);
+                        us[g][q] = slot_peek(a.slot_s + row0[g] + c);
                     }
-                    ls[q] += sc * (double)fast_exp2(
-                        (float)((double)offset_of(mc, a.sc) - (double)offset_of(lm[q], a.sc)));
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < kRowGroups; ++g) {
+#pragma unroll
+                for (int q = 0; q < kTilesPerLoad; ++q) {
+                    const int c = c0 + sub + 16 * q;
+                    if (rs[g] < nrs && c < C) merge2(lm[g], ls[g], dec_f32(um[g][q]), dec_f64(us[g][q]), a.sc);
                 }
             }
         }
 #pragma unroll
-        for (int q = 0; q < kRowBatch; ++q) {
-            const int rs = base + w + q * kWaves;
-            const float rmax = wave_max(lm[q]);
+        for (int g = 0; g < kRowGroups; ++g) {
+            const float rmax = row16_max(lm[g]);
             double scaled = 0.0;
-            if (lm[q] != -INFINITY)
-                scaled = ls[q] * (double)fast_exp2(
-                    (float)((double)offset_of(lm[q], a.sc) - (double)offset_of(rmax, a.sc)));
-            const double zsum = __shfl(wave_sum(scaled), 0, 64);
-            if (rs < nrs && lane == 0) {
-                const int slot = slot_of_rs(rs, kb, K);
-                sh->m[slot] = rmax;
-                sh->z[slot] = zsum;
+            if (lm[g] != -INFINITY)
+                scaled = ls[g] * (double)fast_exp2(
+                    (float)((double)offset_of(lm[g], a.sc) - (double)offset_of(rmax, a.sc)));
+            const double zsum = row16_sum(scaled);
+            if (sub == 0 && rs[g] < nrs) {
+                const int slot = slot_of_rs(rs[g], kb, K);
+                sh.m[slot] = rmax;
+                sh.z[slot] = zsum;
             }
         }
-    }
-    float l = 0.0f, dl = 0.0f;
-    if (t < kb) {
-        l = load_one<DT>(row_ptr(a.target, (size_t)b * (K + 1) + t, a.V, S), x);
-        if (!one_hot) dl = load_one<DT>(row_ptr(a.draft, (size_t)b * K + t, a.V, S), x);
     }
     __syncthreads();
     bool rej = false;
     if (t < kb) {
+        const float l = dec_f32(rl);
         const double c = a.sc.c;
-        const double p = exp2((double)l * c - (double)offset_of(sh->m[t], a.sc)) / sh->z[t];
+        const double p = exp2((double)l * c - (double)offset_of(sh.m[t], a.sc)) / sh.z[t];
         double q = 1.0;
         if (!one_hot) {
+            const float dl = dec_f32(rd);
             const int qs = K + 1 + t;
-            q = exp2((double)dl * c - (double)offset_of(sh->m[qs], a.sc)) / sh->z[qs];
+            q = exp2((double)dl * c - (double)offset_of(sh.m[qs], a.sc)) / sh.z[qs];
         }
         const double ratio = (q == 0.0) ? 1.0 : fmin(1.0, p / q);
-        sh->ratio[t] = (float)ratio;
+        sh.ratio[t] = (float)ratio;
         rej = !((double)u < ratio);
     }
     const unsigned long long mask = __ballot(rej);
-    if (lane == 0) sh->rej[w] = mask;
+    if (lane == 0) sh.rej[w] = mask;
     __syncthreads();
     if (t == 0) {
         int j = kb;
         for (int i = 0; i < kWaves; ++i) {
-            if (sh->rej[i]) {
-                j = i * 64 + __ffsll((long long)sh->rej[i]) - 1;
+            if (sh.rej[i]) {
+                j = i * 64 + __ffsll((long long)sh.rej[i]) - 1;
                 break;
             }
         }
         Decision d;
         d.j = j;
         d.tok = -1;
-        d.Mp = offset_of(sh->m[j], a.sc);
+        d.Mp = offset_of(sh.m[j], a.sc);
         d.Mq = 0.0f;
         d.rho = 0.0f;
         d.pad0 = d.pad1 = 0;
@@ -247,183 +237,183 @@ __device__ void decide_block(const VerifyParams& a, int b, DecideShared* sh) {
             d.tok = a.tokens[(size_t)b * K + j];
         } else {
             d.mode = kResidual;
-            d.Mq = offset_of(sh->m[K + 1 + j], a.sc);
-            d.rho = (float)(sh->z[j] / sh->z[K + 1 + j]);
+            d.Mq = offset_of(sh.m[K + 1 + j], a.sc);
+            d.rho = (float)(sh.z[j] / sh.z[K + 1 + j]);
         }
-        sh->dec = d;
+        sh.dec = d;
     }
     __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// B: one tile of the final row (pair), then (last tile only) the locate.
+// Row item: tile `tile` of row slot rr of request b (target rows 0..K, then
+// draft rows 0..K-1).
 // ---------------------------------------------------------------------------
-struct BShared {
-    DecideShared dsh;
-    double slab[kWaves][kUnroll];
-    int last;
-    int g, found, lastpos;
-    double base, w, total;
-    double red[kWaves];
-};
-
-// Wave 0: total mass over the slab slots of request b (waiting for each to be
-// visible), then the slab g holding w = u * total and the mass before it.
-// Falls back to the last slab with mass when rounding leaves w past the end.
-__device__ void find_slab(const VerifyParams& a, const uint64_t* slabs, double u, int* g_out,
-                          double* base_out, double* w_out, double* total_out) {
-    const int lane = threadIdx.x;
-    const int NS = a.NS;
-    double total = 0.0;
-    for (int g0 = 0; g0 < NS; g0 += 64) {
-        double v = 0.0;
-        if (g0 + lane < NS) v = dec_f64(slot_wait(slabs + g0 + lane, a.err, enc_f64(0.0)));
-        total += __shfl(wave_sum(v), 0, 64);
-    }
-    const double w = u * total;
-    double run = 0.0, base = 0.0, last_base = 0.0;
-    int g = -1, last_nz = -1;
-    for (int g0 = 0; g0 < NS; g0 += 64) {
-        const double v = (g0 + lane < NS) ? dec_f64(slot_peek(slabs + g0 + lane)) : 0.0;
-        const double incl = wave_inclusive_scan(v);
-        const double up = __shfl_up(incl, 1, 64);
-        const double before = run + (lane == 0 ? 0.0 : up);
-        const unsigned long long hit = __ballot(w < run + incl);
-        const unsigned long long nz = __ballot(v > 0.0);
-        if (nz) {
-            const int L = 63 - __clzll((long long)nz);
-            last_nz = g0 + L;
-            last_base = __shfl(before, L, 64);
-        }
-        if (hit) {
-            const int L = __ffsll((long long)hit) - 1;
-            g = g0 + L;
-            base = __shfl(before, L, 64);
-            break;
-        }
-        run += __shfl(incl, 63, 64);
-    }
-    if (g < 0) {
-        g = last_nz < 0 ? 0 : last_nz;
-        base = last_base;
-    }
-    if (lane == 0) {
-        *g_out = g;
-        *base_out = base;
-        *w_out = w;
-        *total_out = total;
-    }
-}
-
-// The smallest token t with u * S < C_t, the outputs, and the reset of the
-// request's slots.  Run by the workgroup that wrote the request's last tile:
-// every other tile has counted itself done (its slab slots are awaited) and
-// has finished reading the row slots.
 template <int DT, bool VEC>
-__device__ void locate(const VerifyParams& a, int b, Decision d, BShared* sh) {
-    constexpr int E = Elem<DT>::E;
+__device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* lds_f, double* lds_d) {
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
-    const int kb = k_of(a, b);
-    const int nslab = a.C * kUnroll;
-    uint64_t* slabs = a.slot_slab + (size_t)b * nslab;
-    const double u = (double)a.unif[(size_t)b * (K + 1) + kb];
-    const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
-    const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
-    if (threadIdx.x < 64) {
-        find_slab(a, slabs, u, &sh->g, &sh->base, &sh->w, &sh->total);
-    } else {
-        // Slab slots past the last slab of the row (zeros) must be in before
-        // they are reset.
-        for (int t = a.NS + threadIdx.x - 64; t < nslab; t += kThreads - 64)
-            slot_wait(slabs + t, a.err, (uint64_t)1);
-    }
+    const int kb = kb_of(a, b);
+    const bool draft = rr > K;
+    const int i = draft ? rr - K - 1 : rr;
+    if (draft ? i >= kb : i > kb) return;   // row past k_b: nothing to read
+    const void* row = draft ? row_ptr(a.draft, (size_t)b * K + i, a.V, S)
+                            : row_ptr(a.target, (size_t)b * (K + 1) + i, a.V, S);
+    const int gx = (i < kb) ? token_of(a, b, i) : -1;
+    float m, gval = 0.0f;
+    double z;
+    const bool held =
+        tile_stats<DT, VEC>(row, a.V, a.NV, tile, a.sc, m, z, lds_f, lds_d, gx, &gval);
+    if (held) slot_put(a.slot_l + (size_t)b * a.R + rr, enc_f32(gval));
     if (threadIdx.x == 0) {
-        sh->found = 0x7FFFFFFF;
-        sh->lastpos = -1;
+        const size_t idx = ((size_t)b * a.R + rr) * a.C + tile;
+        slot_put(a.slot_s + idx, enc_f64(z));
+        slot_put(a.slot_m + idx, enc_f32(m));
+    }
+    // Target row 0 is read by every request: its items clear the request's
+    // slab slots for this call's final kernel.
+    if (rr == 0 && threadIdx.x < 2 * kUnroll) {
+        uint64_t* slab = (threadIdx.x < kUnroll) ? a.slot_slab : a.slot_slab2;
+        slot_put(slab + ((size_t)b * a.C + tile) * kUnroll + (threadIdx.x % kUnroll), (uint64_t)0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Token search, by every final item of the request at once.
+// ---------------------------------------------------------------------------
+
+// Waits for the NS slab sums of the request; then (identically in every
+// workgroup of the request) their total S, the slab g that holds w = u * S --
+// the first slab whose inclusive prefix exceeds w -- and the mass before it;
+// the last slab with mass when rounding leaves w past the end.
+__device__ void find_slab(const VerifyParams& a, const uint64_t* slabs, double u, StepShared& sh) {
+    const int t = threadIdx.x;
+    const int NS = a.NS;
+    double part = 0.0, v0 = 0.0;
+    for (int s = t; s < NS; s += kThreads) {
+        const double v = dec_f64(slot_wait(slabs + s, a.err, enc_f64(0.0)));
+        part += v;
+        if (s == t) v0 = v;
+    }
+    const double total = block_sum(part, sh.red_d);
+    const double w = u * total;
+    if (t == 0) {
+        sh.g = 0x7FFFFFFF;
+        sh.lastnz = -1;
     }
     __syncthreads();
-    if (!(sh->total > 0.0)) {
-        // Every replacement mass is zero: draw from p_j itself.
-        d.mode = kBonus;
-        rowq = nullptr;
-        for (int g = 0; g < a.NS; ++g) {
-            const int v = g * kSlab + threadIdx.x;
-            const u32x4 rp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
-            float r[E];
-            final_masses<DT>(rp, rp, d, v, a.sc, r);
-            const double t = block_sum((double)pairwise_sum<E>(r), sh->red);
-            if (threadIdx.x == 0) slot_put(slabs + g, enc_f64(t));
+    double run = 0.0;
+    for (int s0 = 0; s0 < NS; s0 += kThreads) {
+        const int s = s0 + t;
+        const double v = (s0 == 0) ? v0 : (s < NS ? dec_f64(slot_peek(slabs + s)) : 0.0);
+        double ctot;
+        const double before = run + block_exclusive_scan(v, sh.red_d, &ctot);
+        if (s < NS && w < before + v) atomicMin(&sh.g, s);
+        if (s < NS && v > 0.0) atomicMax(&sh.lastnz, s);
+        __syncthreads();
+        const int g = sh.g;
+        if (g == s) sh.base = before;
+        if (g != 0x7FFFFFFF) break;
+        run += ctot;
+    }
+    __syncthreads();
+    if (t == 0) {
+        if (sh.g == 0x7FFFFFFF) sh.g = -1;
+        sh.w = w;
+        sh.total = total;
+    }
+    __syncthreads();
+    if (sh.g < 0) {
+        // No slab reaches w: take the last slab with mass.
+        const int L = sh.lastnz < 0 ? 0 : sh.lastnz;
+        double run2 = 0.0;
+        for (int s0 = 0; s0 < NS; s0 += kThreads) {
+            const int s = s0 + t;
+            const double v = s < NS ? dec_f64(slot_peek(slabs + s)) : 0.0;
+            double ctot;
+            const double before = run2 + block_exclusive_scan(v, sh.red_d, &ctot);
+            if (s == L) sh.base = before;
+            run2 += ctot;
         }
         __syncthreads();
-        if (threadIdx.x < 64) find_slab(a, slabs, u, &sh->g, &sh->base, &sh->w, &sh->total);
+        if (t == 0) sh.g = L;
         __syncthreads();
     }
-    const int g = sh->g;
-    const double base = sh->base, w = sh->w;
+}
 
-    // Re-read slab g and scan it in ascending token id.
-    const int v = g * kSlab + threadIdx.x;
-    const u32x4 rp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
-    const u32x4 rq = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : neg_inf_raw<DT>();
+// Slab sums of one tile: the masses of each of the kUnroll vectors of every
+// thread, summed over the workgroup per vector index (one slab each).
+template <int DT>
+__device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], const u32x4 (&rq)[kUnroll],
+                          const Decision& d, int v0, uint64_t* slabs_of_tile, StepShared& sh) {
+    constexpr int E = Elem<DT>::E;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        float r[E];
+        final_masses<DT>(rp[u], rq[u], d, v0 + u * kThreads, a.sc, r);
+        const double t = wave_sum((double)pairwise_sum<E>(r));
+        if ((threadIdx.x & 63) == 0) sh.slab[w][u] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < kUnroll) {
+        double t = 0.0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) t += sh.slab[i][threadIdx.x];
+        slot_put(slabs_of_tile + threadIdx.x, enc_f64(t));
+    }
+}
+
+// The smallest token in slab g (held by this workgroup as vector index u)
+// with w < C_t, C_t running from the mass before the slab; the last token
+// with mass in the slab when rounding leaves w past every C_t.  Thread 0
+// returns the token.
+template <int DT>
+__device__ int scan_slab(const VerifyParams& a, const u32x4& rp, const u32x4& rq, const Decision& d,
+                         int v, double base, double w, StepShared& sh) {
+    constexpr int E = Elem<DT>::E;
     float r[E];
     final_masses<DT>(rp, rq, d, v, a.sc, r);
     const double vs = (double)pairwise_sum<E>(r);
+    if (threadIdx.x == 0) {
+        sh.found = 0x7FFFFFFF;
+        sh.lastpos = -1;
+    }
     double slab_total;
-    const double start = base + block_exclusive_scan(vs, sh->red, &slab_total);
+    const double start = base + block_exclusive_scan(vs, sh.red_d, &slab_total);
     int lastpos = -1;
 #pragma unroll
     for (int e = 0; e < E; ++e)
         if (r[e] > 0.0f) lastpos = v * E + e;
-    if (lastpos >= 0) atomicMax(&sh->lastpos, lastpos);
+    if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
     if (start <= w && vs > 0.0) {
         double Cc = start;
         for (int e = 0; e < E; ++e) {
             Cc += (double)r[e];
             if (w < Cc) {
-                atomicMin(&sh->found, v * E + e);
+                atomicMin(&sh.found, v * E + e);
                 break;
             }
         }
     }
     __syncthreads();
-    const int j = d.j;
-    int tok = sh->found != 0x7FFFFFFF ? sh->found : sh->lastpos;
-    if (tok < 0) tok = 0;
-    for (int i = threadIdx.x; i <= K; i += kThreads) {
-        int32_t o = -1;
-        if (i < j) o = a.tokens[(size_t)b * K + i];
-        else if (i == j) o = tok;
-        a.out[(size_t)b * (K + 1) + i] = o;
-        if (a.aprob && i < K) a.aprob[(size_t)b * K + i] = (i < kb) ? sh->dsh.ratio[i] : -1.0f;
-    }
-    if (threadIdx.x == 0) a.nacc[b] = j;
-
-    // Reset the request's slots and counter for the next call.
-    const int nrs = kb + 1 + (a.draft ? kb : 0);
-    const int nrow = nrs * a.C;
-    for (int t = threadIdx.x; t < nrow; t += kThreads) {
-        const int rs = t / a.C, c = t % a.C;
-        const size_t idx = ((size_t)b * a.R + slot_of_rs(rs, kb, K)) * a.C + c;
-        slot_put(a.slot_m + idx, 0u);
-        slot_put(a.slot_s + idx, (uint64_t)0);
-    }
-    for (int t = threadIdx.x; t < nslab; t += kThreads) slot_put(slabs + t, (uint64_t)0);
-    if (threadIdx.x == 0) slot_put(a.req_done + b, 0u);
+    const int tok = sh.found != 0x7FFFFFFF ? sh.found : sh.lastpos;
+    return tok < 0 ? 0 : tok;
 }
 
+// ---------------------------------------------------------------------------
+// Final item: tile `tile` of the final row (pair) of request b.
+// ---------------------------------------------------------------------------
 template <int DT, bool VEC>
-__device__ void b_item(const VerifyParams& a, int item, BShared* sh) {
-    constexpr int E = Elem<DT>::E;
+__device__ void final_item(const VerifyParams& a, int b, int tile, StepShared& sh) {
     constexpr int S = Elem<DT>::S;
-    const int b = item / a.C;
-    const int tile = item % a.C;
-    decide_block<DT>(a, b, &sh->dsh);
-    const Decision d = sh->dsh.dec;
-    const void* rowp = row_ptr(a.target, (size_t)b * (a.K + 1) + d.j, a.V, S);
-    const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * a.K + d.j, a.V, S) : nullptr;
+    const int K = a.K;
+    const int kb = kb_of(a, b);
+    decide(a, b, kb, sh);
+    Decision d = sh.dec;
+    const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
+    const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
     const int v0 = tile * kTileVec + threadIdx.x;
-    const int w = threadIdx.x >> 6;
     u32x4 rp[kUnroll], rq[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -431,55 +421,69 @@ __device__ void b_item(const VerifyParams& a, int item, BShared* sh) {
         rp[u] = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
         rq[u] = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : neg_inf_raw<DT>();
     }
+    const size_t slab0 = (size_t)b * a.C * kUnroll;
+    put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + slab0 + (size_t)tile * kUnroll, sh);
+    const double u = (double)a.unif[(size_t)b * (K + 1) + kb];
+    find_slab(a, a.slot_slab + slab0, u, sh);
+    if (!(sh.total > 0.0)) {
+        // Every replacement mass is zero: draw from p_j itself (its tile is
+        // read again; this case is rare).
+        d.mode = kBonus;
+        u32x4 bp[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        float r[E];
-        final_masses<DT>(rp[u], rq[u], d, v0 + u * kThreads, a.sc, r);
-        const double t = wave_sum((double)pairwise_sum<E>(r));
-        if ((threadIdx.x & 63) == 0) sh->slab[w][u] = t;
+        for (int i = 0; i < kUnroll; ++i) bp[i] = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v0 + i * kThreads);
+        put_slabs<DT>(a, bp, bp, d, v0, a.slot_slab2 + slab0 + (size_t)tile * kUnroll, sh);
+        find_slab(a, a.slot_slab2 + slab0, u, sh);
     }
-    __syncthreads();
-    if (threadIdx.x < kUnroll) {
-        double t = 0.0;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) t += sh->slab[i][threadIdx.x];
-        slot_put(&a.slot_slab[((size_t)b * a.C + tile) * kUnroll + threadIdx.x], enc_f64(t));
+    const int g = sh.g;
+    if (g / kUnroll != tile) return;   // another workgroup's tile holds slab g
+    // Re-read slab g (one vector per thread) rather than keep the whole tile
+    // in registers across the wait.
+    const int v = g * kSlab + threadIdx.x;
+    const u32x4 sp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
+    const u32x4 sq = (d.mode == kResidual) ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : sp;
+    const int tok = scan_slab<DT>(a, sp, sq, d, v, sh.base, sh.w, sh);
+    const int j = d.j;
+    for (int i = threadIdx.x; i <= K; i += kThreads) {
+        int32_t o = -1;
+        if (i < j) o = a.tokens[(size_t)b * K + i];
+        else if (i == j) o = tok;
+        a.out[(size_t)b * (K + 1) + i] = o;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t before = __hip_atomic_fetch_add(a.req_done + b, 1u, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
-        sh->last = (before + 1u == (uint32_t)a.C);
-    }
-    __syncthreads();
-    if (sh->last) locate<DT, VEC>(a, b, d, sh);
+    if (threadIdx.x == 0) a.nacc[b] = j;
+    if (a.aprob)
+        for (int i = threadIdx.x; i < K; i += kThreads)
+            a.aprob[(size_t)b * K + i] = (i < kb) ? sh.ratio[i] : -1.0f;
 }
 
-// Kernel 1: every A item in its own workgroup (no waits, full occupancy).
+// Row items, request-major: item n is tile n % C of row slot (n / C) % R of
+// request n / (C * R).
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_rows(VerifyParams a) {
     __shared__ float lds_f[kWaves];
     __shared__ double lds_d[kWaves];
-    a_item<DT, VEC>(a, blockIdx.x, lds_f, lds_d);
+    const int64_t n = blockIdx.x;
+    const int tile = (int)(n % a.C);
+    const int64_t r = n / a.C;
+    row_item<DT, VEC>(a, (int)(r / a.R), (int)(r % a.R), tile, lds_f, lds_d);
 }
 
-// Kernel 2 (persistent): the B items; the one completing a request's tiles
-// also locates its token.
+// Final items of requests b0, b0 + 1, ...: workgroup n takes tile n % C of
+// request b0 + n / C.  A launch holds no more workgroups than fit on the
+// device at once, so the C items of a request run together and may wait for
+// one another.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
-    __shared__ BShared sh;
-    for (int item = blockIdx.x; item < a.NB; item += gridDim.x) {
-        b_item<DT, VEC>(a, item, &sh);
-        __syncthreads();
-    }
+__global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a, int b0) {
+    __shared__ StepShared sh;
+    const int n = blockIdx.x;
+    final_item<DT, VEC>(a, b0 + n / a.C, n % a.C, sh);
 }
 
 template <int DT, bool VEC>
 hipError_t launch(const VerifyParams& p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
-    static int resident[2][2] = {{0, 0}, {0, 0}};
-    int& res = resident[DT][VEC ? 1 : 0];
-    if (res == 0) {
+    static int resident = 0;
+    if (resident == 0) {
         int dev = 0, cus = 0, per_cu = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -487,11 +491,16 @@ hipError_t launch(const VerifyParams& p, hipStream_t s) {
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_final<DT, VEC>, kThreads, 0);
         if (e != hipSuccess) return e;
         if (cus < 1 || per_cu < 1) return hipErrorInvalidConfiguration;
-        res = cus * per_cu;
+        resident = cus * per_cu;
     }
-    hipLaunchKernelGGL((verify_rows<DT, VEC>), dim3((unsigned)p.NA), dim3(kThreads), 0, s, p);
-    const int grid = p.NB < res ? p.NB : res;
-    hipLaunchKernelGGL((verify_final<DT, VEC>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    const int per_launch = resident / p.C;     // whole requests per final launch
+    if (per_launch < 1) return hipErrorInvalidConfiguration;
+    const int64_t rows = (int64_t)p.B * p.R * p.C;
+    hipLaunchKernelGGL((verify_rows<DT, VEC>), dim3((unsigned)rows), dim3(kThreads), 0, s, p);
+    for (int b0 = 0; b0 < p.B; b0 += per_launch) {
+        const int nb = p.B - b0 < per_launch ? p.B - b0 : per_launch;
+        hipLaunchKernelGGL((verify_final<DT, VEC>), dim3((unsigned)(nb * p.C)), dim3(kThreads), 0, s, p, b0);
+    }
     return hipGetLastError();
 }
 

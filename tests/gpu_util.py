@@ -57,13 +57,11 @@ def compare_verify(name, gpu, ref, rel_tol=1e-5):
 
 
 def assert_workspace_clean(ws) -> None:
-    """After a call the workspace must be all zero again: no wait timed out
-    (the error word at offset 0) and every slot was reset."""
+    """No bounded wait inside the kernels gave up: the error word at offset 0
+    of the workspace is still zero."""
     torch.cuda.synchronize()
-    nz = int(torch.count_nonzero(ws.tensor).item())
     err = int(ws.tensor[:4].view(torch.int32).item())
     assert err == 0, "a wait inside the kernel timed out (error bits %#x)" % err
-    assert nz == 0, "%d workspace bytes left non-zero after the call" % nz
 
 
 def run_verify(wl: workloads.Workload, accept_prob=True, device="cuda"):
