@@ -6,7 +6,7 @@
 One step = one specdec_verify call over one batch of the headline workload
 (B=64 requests, k=5 drafts, V=128256, bf16 target and draft logits, T=0.8),
 with inputs already resident in HBM.  The timed steps rotate over several
-device-resident copies of the input set, so that the working set (>= 720 MB)
+device-resident copies of the input set, so that the working set (>= 900 MB)
 exceeds the 256 MB Infinity Cache and every step streams its logits from HBM.
 
 Prints one JSON line: verified positions/s (sum over requests of k_b + 1 per
@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 METRIC = "verified positions/s + HBM GB/s (% of peak), B=64 k=5 V=128256 bf16"
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_headline_counters.txt")
-KERNEL_SOURCES = ["device_common.h", "internal.h", "verify.hip"]
+KERNEL_SOURCES = ["device_common.h", "internal.h", "slots.h", "verify.hip"]
 
 
 def kernel_digest() -> str:
@@ -42,14 +42,14 @@ def kernel_digest() -> str:
 
 def algorithmic_bytes(wl, num_accepted) -> int:
     """Bytes the step must move: every target row i <= k_b and draft row
-    i < k_b once, the final row (pair) of every rejected request once more,
-    plus ids, uniforms and outputs."""
+    i < k_b once, the final row (pair) of every rejected request once more
+    (stochastic path only), plus ids, uniforms and outputs."""
     import numpy as np
     s = 2 if wl.dtype == "bf16" else 4
     k = np.full(wl.B, wl.K) if wl.k_per_req is None else wl.k_per_req.astype(np.int64)
     rows = int(np.sum(k + 1)) + (int(np.sum(k)) if wl.draft is not None else 0)
     rejected = int(np.sum(num_accepted < k))
-    reread = rejected * (2 if wl.draft is not None else 1)
+    reread = 0 if wl.greedy else rejected * (2 if wl.draft is not None else 1)
     small = int(np.sum(k)) * 4 + int(np.sum(k + 1)) * 4 + wl.B * (wl.K + 1) * 4 + wl.B * 4
     return (rows + reread) * wl.V * s + small
 
@@ -99,11 +99,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sets", type=int, default=4, help="device-resident input copies to rotate over")
+    ap.add_argument("--sets", type=int, default=5, help="device-resident input copies to rotate over")
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each call from a captured HIP graph")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, copy a MIB-MiB device buffer 10 times (a plain copy "
+                         "of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -142,11 +145,13 @@ def main():
     kpr = None if wl.k_per_req is None else torch.from_numpy(wl.k_per_req).to(dev)
     out = (torch.empty((wl.B, K + 1), dtype=torch.int32, device=dev),
            torch.empty((wl.B,), dtype=torch.int32, device=dev), None)
-    nbytes = sd._lib.verify_workspace_bytes(wl.B, K, wl.V, 1 if wl.dtype == "bf16" else 0,
-                                            wl.draft is None)
-    ws = sd.Workspace(nbytes, dev)
-
     greedy = wl.greedy
+    code = 1 if wl.dtype == "bf16" else 0
+    if greedy:
+        nbytes = int(sd._lib.load().specdec_verify_greedy_workspace_bytes(wl.B, K, wl.V, code))
+    else:
+        nbytes = sd._lib.verify_workspace_bytes(wl.B, K, wl.V, code, wl.draft is None)
+    ws = sd.Workspace(nbytes, dev)
 
     def step(r):
         s = sets[r % len(sets)]
@@ -190,7 +195,7 @@ def main():
         ends[r].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    per_launch_ms = float(np.median([s.elapsed_time(e) for s, e in zip(starts, ends)]))
     ms_per_step = wall * 1e3 / args.steps
 
     positions = wl.verified_positions()
@@ -199,8 +204,11 @@ def main():
     gbps = alg / (ms_per_step * 1e-3) / 1e9
     achieved = alg / (per_launch_ms * 1e-3) / 1e9
     traffic = read_counters()
+    metric = METRIC if args.workload == "headline" else (
+        "verified positions/s + HBM GB/s (%% of peak), %s B=%d k=%d V=%d %s"
+        % (args.workload, wl.B, K, wl.V, wl.dtype))
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 1),
         "unit": "verified positions/s",
         "n_gpus": 1,
@@ -224,9 +232,17 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
                      "launch_ms": round(per_launch_ms, 5),
-                     "kernel": "specdec_verify (whole call)"},
+                     "kernel": "specdec_verify call (verify_rows + verify_final)"},
         "cpu_baseline": None,
     }
+    if args.calibration_copy > 0:
+        n = args.calibration_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = n
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)

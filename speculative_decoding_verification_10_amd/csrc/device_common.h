@@ -269,7 +269,7 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* lds /* 
 // With gx >= 0 the thread that holds token gx (if it lies in this tile)
 // stores its logit, widened to float, to *gval and returns true.
 // ---------------------------------------------------------------------------
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool NT = true>
 __device__ __forceinline__ bool tile_stats(const void* row, int V, int NV, int tile, const Scale& sc,
                                            float& m_out, double& s_out, float* lds_f,
                                            double* lds_d, int gx = -1, float* gval = nullptr) {
@@ -277,7 +277,7 @@ __device__ __forceinline__ bool tile_stats(const void* row, int V, int NV, int t
     const int v0 = tile * kTileVec + threadIdx.x;
     u32x4 raw[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) raw[u] = load_raw<DT, VEC, true>(row, V, NV, v0 + u * kThreads);
+    for (int u = 0; u < kUnroll; ++u) raw[u] = load_raw<DT, VEC, NT>(row, V, NV, v0 + u * kThreads);
     float mt = -INFINITY;
     bool held = false;
 #pragma unroll
