@@ -13,7 +13,7 @@
 // Waiting is safe because a producer writes its slots before it waits for
 // anything, and every producer is a workgroup that is running: producer and
 // consumer belong to one launch that holds no more workgroups than fit on
-// the device at once.  A poll gives up after kSpinLimit rounds (far
+// the device at once.  A poll gives up after kWaitTicks (far
 // beyond any legitimate wait), raises an error bit in the workspace header
 // and continues with a harmless value, so every wave always exits.
 //
@@ -26,7 +26,9 @@
 
 namespace specdec {
 
-constexpr int kSpinLimit = 1 << 20;
+// A wait gives up after 50 ms of wall-clock time (100 MHz counter), far
+// beyond any legitimate wait.
+constexpr uint64_t kWaitTicks = 5000000;
 
 __device__ __forceinline__ uint32_t enc_f32(float f) {
     return ~(f != f ? 0x7FC00000u : __float_as_uint(f));
@@ -54,9 +56,10 @@ __device__ __forceinline__ uint64_t slot_peek(const uint64_t* p) {
 // the slot is written; on time-out flag the error and return `fallback`.
 template <typename T>
 __device__ __forceinline__ T settle(const T* p, T v, uint32_t* err, T fallback) {
-    int n = 0;
+    if (v != 0) return v;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     while (v == 0) {
-        if (++n > kSpinLimit) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
             atomicOr(err, 1u);
             return fallback;
         }
