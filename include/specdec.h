@@ -114,8 +114,9 @@ int specdec_softmax_stats(const void *logits, specdec_dtype_t dtype, int64_t row
  *                 -1 for i >= k_b.
  * The final draw is an inverse CDF in ascending token id: the smallest t
  * with u * S < C_t, C_t the running sum of the (unnormalised) replacement or
- * bonus masses and S their total.  B >= 0, 0 <= K <= 255, 1 <= V <= 2^22
- * (fp32) or 2^23 (bf16); larger K or V give SPECDEC_EINVAL.
+ * bonus masses and S their total.  B >= 0, 0 <= K <= 255, 1 <= V <= 2^28;
+ * larger K or V, or more than 2^24 row tiles (B * (2K+1) rows of 16 KB
+ * tiles), give SPECDEC_EINVAL.
  */
 size_t specdec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, specdec_dtype_t dtype,
                                       int one_hot_drafts);

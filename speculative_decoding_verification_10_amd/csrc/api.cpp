@@ -14,7 +14,6 @@ namespace specdec {
 namespace {
 
 constexpr int32_t kMaxV = 1 << 28;
-constexpr int kMaxFinalTiles = 1024;               // tiles per row in the stochastic verify
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxBlocks = (size_t)1 << 24;   // gridDim.x * 256 threads < 2^32
 
@@ -53,12 +52,12 @@ bool make_scale(float temperature, Scale* s) {
 }
 
 struct VerifyLayout {
-    size_t err, slot_m, slot_s, slot_l, slot_slab, slot_slab2, total;
+    size_t err, slot_m, slot_s, slot_l, slot_slab, total;
 };
 
 // Header (error bits) and self-validating slots: tile max / tile sum of every
 // row slot of every request, the logit at the draft token of every row, and
-// two sets of slab sums of every request's final row.
+// the slab sums of every request's final row.
 VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, bool one_hot) {
     int NV, NVv;
     bool vec;
@@ -74,7 +73,6 @@ VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, 
     L.slot_s = off;    off = align_up(off + parts * sizeof(uint64_t));
     L.slot_l = off;    off = align_up(off + (size_t)B * R * sizeof(uint32_t));
     L.slot_slab = off; off = align_up(off + (size_t)B * C * kUnroll * sizeof(uint64_t));
-    L.slot_slab2 = off; off = align_up(off + (size_t)B * C * kUnroll * sizeof(uint64_t));
     L.total = off;
     return L;
 }
@@ -211,9 +209,8 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
     p.R = K + 1 + (one_hot ? 0 : K);
     p.NS = (p.NV + kSlab - 1) / kSlab;
     p.kinds = one_hot ? 1 : 2;
-    // One workgroup per row item; the final kernel holds every tile of a
-    // request resident at once.
-    if ((size_t)B * p.R * p.C > kMaxBlocks || p.C > kMaxFinalTiles) return SPECDEC_EINVAL;
+    // One workgroup per row item and per final item.
+    if ((size_t)B * p.R * p.C > kMaxBlocks) return SPECDEC_EINVAL;
     p.target = target_logits;
     p.draft = draft_logits;
     p.tokens = draft_tokens;
@@ -232,7 +229,6 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
     p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);
     p.slot_l = reinterpret_cast<uint32_t*>(ws + L.slot_l);
     p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
-    p.slot_slab2 = reinterpret_cast<uint64_t*>(ws + L.slot_slab2);
     return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream));
 }
 

@@ -10,12 +10,12 @@
 // agent-scope release (an L2 writeback on this multi-XCD part) per workgroup
 // would cost far more than the work.
 //
-// Waiting is safe because a producer writes its slots before it waits for
-// anything, and every producer is a workgroup that is running: producer and
-// consumer belong to one launch that holds no more workgroups than fit on
-// the device at once.  A poll gives up after kWaitTicks (far
-// beyond any legitimate wait), raises an error bit in the workspace header
-// and continues with a harmless value, so every wave always exits.
+// Waiting is safe because a consumer only waits for workgroups with a lower
+// index in the same grid: the hardware dispatches those no later than the
+// consumer, and they never wait themselves, so they finish.  A poll gives up
+// after kWaitTicks (far beyond any legitimate wait), raises an error bit in
+// the workspace header and continues with a harmless value, so every wave
+// always exits.
 //
 // A slot must read zero before its producer runs: the kernel that precedes
 // the producers in stream order clears it.

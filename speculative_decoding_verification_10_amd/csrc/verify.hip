@@ -14,17 +14,17 @@
 //                first rejection j taken with a ballot ("The algorithm (one
 //                step)", step 3) -- then the tile's slab sums of the
 //                unnormalised replacement masses max(0, p_j - q_j), or of
-//                p_{k_b} when every draft was accepted (step 4).  Every final
-//                item of the request then reads all of the request's slab
-//                sums and finds the slab that holds u * S; the item whose
-//                tile holds that slab re-reads it, takes the smallest token t
-//                with u * S < C_t and writes the request's outputs.
+//                p_{k_b} when every draft was accepted (step 4).  The
+//                request's last tile then reads all of the request's slab
+//                sums, finds the slab that holds u * S, re-reads that one
+//                slab, takes the smallest token t with u * S < C_t and writes
+//                the request's outputs.
 //
 // Results cross workgroups through self-validating slots (slots.h).  The
-// kernel boundary orders every row slot before its readers; the final items
-// of a request are in one launch that fits on the device at once, and each
-// publishes its slab sums before it waits for the others', so every wait
-// ends.
+// kernel boundary orders every row slot before its readers.  The only wait
+// is the last tile's, for the slab sums of its request's other tiles: those
+// have lower workgroup indices, which the hardware dispatches no later, and
+// they never wait themselves, so the wait ends.
 //
 // Masses are kept unnormalised: the replacement is Z_p * max(0, p - q) =
 // max(0, e_p - (Z_p/Z_q) e_q) with e = exp2(x * c - M) against each row's
@@ -272,10 +272,8 @@ __device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* 
     }
     // Target row 0 is read by every request: its items clear the request's
     // slab slots for this call's final kernel.
-    if (rr == 0 && threadIdx.x < 2 * kUnroll) {
-        uint64_t* slab = (threadIdx.x < kUnroll) ? a.slot_slab : a.slot_slab2;
-        slot_put(slab + ((size_t)b * a.C + tile) * kUnroll + (threadIdx.x % kUnroll), (uint64_t)0);
-    }
+    if (rr == 0 && threadIdx.x < kUnroll)
+        slot_put(a.slot_slab + ((size_t)b * a.C + tile) * kUnroll + threadIdx.x, (uint64_t)0);
 }
 
 // ---------------------------------------------------------------------------
@@ -406,6 +404,7 @@ __device__ int scan_slab(const VerifyParams& a, const u32x4& rp, const u32x4& rq
 // ---------------------------------------------------------------------------
 template <int DT, bool VEC>
 __device__ void final_item(const VerifyParams& a, int b, int tile, StepShared& sh) {
+    constexpr int E = Elem<DT>::E;
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
     const int kb = kb_of(a, b);
@@ -423,23 +422,30 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, StepShared& s
     }
     const size_t slab0 = (size_t)b * a.C * kUnroll;
     put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + slab0 + (size_t)tile * kUnroll, sh);
+    if (tile != a.C - 1) return;
+
+    // The request's last tile: every other tile of the request has a lower
+    // workgroup index.
     const double u = (double)a.unif[(size_t)b * (K + 1) + kb];
-    find_slab(a, a.slot_slab + slab0, u, sh);
+    uint64_t* slabs = a.slot_slab + slab0;
+    find_slab(a, slabs, u, sh);
     if (!(sh.total > 0.0)) {
-        // Every replacement mass is zero: draw from p_j itself (its tile is
-        // read again; this case is rare).
+        // Every replacement mass is zero: draw from p_j itself.  Its slab
+        // sums replace the residual ones (rare; one workgroup streams the row).
         d.mode = kBonus;
-        u32x4 bp[kUnroll];
-#pragma unroll
-        for (int i = 0; i < kUnroll; ++i) bp[i] = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v0 + i * kThreads);
-        put_slabs<DT>(a, bp, bp, d, v0, a.slot_slab2 + slab0 + (size_t)tile * kUnroll, sh);
-        find_slab(a, a.slot_slab2 + slab0, u, sh);
+        for (int g = 0; g < a.NS; ++g) {
+            const int v = g * kSlab + threadIdx.x;
+            const u32x4 bp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
+            float r[E];
+            final_masses<DT>(bp, bp, d, v, a.sc, r);
+            const double t = block_sum((double)pairwise_sum<E>(r), sh.red_d);
+            if (threadIdx.x == 0) slot_put(slabs + g, enc_f64(t));
+        }
+        __syncthreads();
+        find_slab(a, slabs, u, sh);
     }
-    const int g = sh.g;
-    if (g / kUnroll != tile) return;   // another workgroup's tile holds slab g
-    // Re-read slab g (one vector per thread) rather than keep the whole tile
-    // in registers across the wait.
-    const int v = g * kSlab + threadIdx.x;
+    // Re-read slab g (one vector per thread) and search it.
+    const int v = sh.g * kSlab + threadIdx.x;
     const u32x4 sp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
     const u32x4 sq = (d.mode == kResidual) ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : sp;
     const int tok = scan_slab<DT>(a, sp, sq, d, v, sh.base, sh.w, sh);
@@ -468,39 +474,21 @@ __global__ __launch_bounds__(kThreads) void verify_rows(VerifyParams a) {
     row_item<DT, VEC>(a, (int)(r / a.R), (int)(r % a.R), tile, lds_f, lds_d);
 }
 
-// Final items of requests b0, b0 + 1, ...: workgroup n takes tile n % C of
-// request b0 + n / C.  A launch holds no more workgroups than fit on the
-// device at once, so the C items of a request run together and may wait for
-// one another.
+// Final items: workgroup n takes tile n % C of request n / C.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a, int b0) {
+__global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
     __shared__ StepShared sh;
     const int n = blockIdx.x;
-    final_item<DT, VEC>(a, b0 + n / a.C, n % a.C, sh);
+    final_item<DT, VEC>(a, n / a.C, n % a.C, sh);
 }
 
 template <int DT, bool VEC>
 hipError_t launch(const VerifyParams& p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
-    static int resident = 0;
-    if (resident == 0) {
-        int dev = 0, cus = 0, per_cu = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_final<DT, VEC>, kThreads, 0);
-        if (e != hipSuccess) return e;
-        if (cus < 1 || per_cu < 1) return hipErrorInvalidConfiguration;
-        resident = cus * per_cu;
-    }
-    const int per_launch = resident / p.C;     // whole requests per final launch
-    if (per_launch < 1) return hipErrorInvalidConfiguration;
     const int64_t rows = (int64_t)p.B * p.R * p.C;
+    const int64_t fins = (int64_t)p.B * p.C;
     hipLaunchKernelGGL((verify_rows<DT, VEC>), dim3((unsigned)rows), dim3(kThreads), 0, s, p);
-    for (int b0 = 0; b0 < p.B; b0 += per_launch) {
-        const int nb = p.B - b0 < per_launch ? p.B - b0 : per_launch;
-        hipLaunchKernelGGL((verify_final<DT, VEC>), dim3((unsigned)(nb * p.C)), dim3(kThreads), 0, s, p, b0);
-    }
+    hipLaunchKernelGGL((verify_final<DT, VEC>), dim3((unsigned)fins), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
