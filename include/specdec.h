@@ -114,9 +114,9 @@ int specdec_softmax_stats(const void *logits, specdec_dtype_t dtype, int64_t row
  *                 -1 for i >= k_b.
  * The final draw is an inverse CDF in ascending token id: the smallest t
  * with u * S < C_t, C_t the running sum of the (unnormalised) replacement or
- * bonus masses and S their total.  B >= 0, 0 <= K <= 255, 1 <= V <= 2^28;
- * larger K or V, or more than 2^24 row tiles (B * (2K+1) rows of 16 KB
- * tiles), give SPECDEC_EINVAL.
+ * bonus masses and S their total.  0 <= B <= 65535, 0 <= K <= 255,
+ * 1 <= V <= 2^28; larger values, or more than 2^24 row tiles (B * (2K+1)
+ * rows of 16 KB tiles), give SPECDEC_EINVAL.
  */
 size_t specdec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, specdec_dtype_t dtype,
                                       int one_hot_drafts);
@@ -133,7 +133,8 @@ int specdec_verify(const void *target_logits, const void *draft_logits, specdec_
  * No temperature (argmax does not depend on T > 0).
  *   target_logits [B, K+1, V]; draft_tokens [B, K]; k_per_req [B] or NULL.
  *   argmax_out    [B, K+1] int32, or NULL: a_i for i <= k_b, -1 beyond.
- * B >= 0, 0 <= K <= 255, 1 <= V <= 2^28; larger K or V give SPECDEC_EINVAL.
+ * 0 <= B <= 65535, 0 <= K <= 255, 1 <= V <= 2^28; larger values, or more than
+ * 2^24 row tiles, give SPECDEC_EINVAL.
  */
 size_t specdec_verify_greedy_workspace_bytes(int32_t B, int32_t K, int32_t V,
                                              specdec_dtype_t dtype);

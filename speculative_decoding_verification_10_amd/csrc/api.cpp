@@ -16,6 +16,7 @@ namespace {
 constexpr int32_t kMaxV = 1 << 28;
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxBlocks = (size_t)1 << 24;   // gridDim.x * 256 threads < 2^32
+constexpr int32_t kMaxBatch = 65535;              // requests: a grid dimension other than x
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -210,7 +211,7 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
     p.NS = (p.NV + kSlab - 1) / kSlab;
     p.kinds = one_hot ? 1 : 2;
     // One workgroup per row item and per final item.
-    if ((size_t)B * p.R * p.C > kMaxBlocks) return SPECDEC_EINVAL;
+    if ((size_t)B * p.R * p.C > kMaxBlocks || B > kMaxBatch) return SPECDEC_EINVAL;
     p.target = target_logits;
     p.draft = draft_logits;
     p.tokens = draft_tokens;
@@ -254,7 +255,7 @@ int specdec_verify_greedy(const void* target_logits, specdec_dtype_t dtype,
     bool vec;
     row_geometry(V, dtype, aligned16(target_logits), &p.NV, &vec);
     p.C = tiles_of(p.NV);
-    if ((size_t)B * (K + 1) * p.C > kMaxBlocks) return SPECDEC_EINVAL;
+    if ((size_t)B * (K + 1) * p.C > kMaxBlocks || B > kMaxBatch) return SPECDEC_EINVAL;
     p.target = target_logits;
     p.tokens = draft_tokens;
     p.kpr = k_per_req;

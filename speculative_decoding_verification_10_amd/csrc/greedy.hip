@@ -31,11 +31,11 @@ __global__ __launch_bounds__(kThreads) void greedy_partial(GreedyParams a) {
     constexpr int S = Elem<DT>::S;
     __shared__ float lv[kWaves];
     __shared__ int li[kWaves];
-    const int item = blockIdx.x;
-    const int tile = item % a.C;
-    const int rid = item / a.C;
-    const int b = rid / (a.K + 1);
-    const int i = rid % (a.K + 1);
+    const int tile = blockIdx.x;
+    const int i = blockIdx.y;
+    const int b = blockIdx.z;
+    const size_t rid = (size_t)b * (a.K + 1) + i;
+    const size_t item = rid * a.C + tile;
     if (i > greedy_k(a, b)) return;
     const void* row = static_cast<const char*>(a.target) + (size_t)rid * a.V * S;
     const int v0 = tile * kTileVec + threadIdx.x;
@@ -124,8 +124,8 @@ __global__ __launch_bounds__(64) void greedy_decide(GreedyParams a) {
 template <int DT, bool VEC>
 hipError_t launch(const GreedyParams& p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
-    const unsigned g1 = (unsigned)((size_t)p.B * (p.K + 1) * p.C);
-    hipLaunchKernelGGL((greedy_partial<DT, VEC>), dim3(g1), dim3(kThreads), 0, s, p);
+    // Workgroup (x, y, z): tile x of row y of request z.
+    hipLaunchKernelGGL((greedy_partial<DT, VEC>), dim3(p.C, p.K + 1, p.B), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL(greedy_decide, dim3((unsigned)p.B), dim3(64), 0, s, p);
     return hipGetLastError();
 }

@@ -9,14 +9,18 @@
 namespace specdec {
 namespace {
 
+constexpr int64_t kRowsPerZ = 32768;   // rows per grid z-slice (grid y and z stay below 2^16)
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void stats_partial(StatsParams a) {
     __shared__ float lds_f[kWaves];
     __shared__ double lds_d[kWaves];
     constexpr int S = Elem<DT>::S;
-    const size_t item = blockIdx.x;
-    const int tile = (int)(item % a.C);
-    const size_t row = item / a.C;
+    // Workgroup (x, y, z): tile x of row z * kRowsPerZ + y.
+    const int tile = blockIdx.x;
+    const size_t row = (size_t)blockIdx.z * kRowsPerZ + blockIdx.y;
+    if (row >= (size_t)a.rows) return;
+    const size_t item = row * a.C + tile;
     const void* p = static_cast<const char*>(a.logits) + row * (size_t)a.V * S;
     float m;
     double z;
@@ -41,8 +45,9 @@ __global__ __launch_bounds__(kThreads) void stats_merge(StatsParams a) {
 template <int DT, bool VEC>
 hipError_t launch(const StatsParams& p, hipStream_t s) {
     if (p.rows == 0) return hipSuccess;
-    const unsigned g1 = (unsigned)(p.rows * p.C);
-    hipLaunchKernelGGL((stats_partial<DT, VEC>), dim3(g1), dim3(kThreads), 0, s, p);
+    const int64_t ny = p.rows < kRowsPerZ ? p.rows : kRowsPerZ;
+    const int64_t nz = (p.rows + kRowsPerZ - 1) / kRowsPerZ;
+    hipLaunchKernelGGL((stats_partial<DT, VEC>), dim3(p.C, (unsigned)ny, (unsigned)nz), dim3(kThreads), 0, s, p);
     const unsigned g2 = (unsigned)((p.rows + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(stats_merge, dim3(g2), dim3(kThreads), 0, s, p);
     return hipGetLastError();

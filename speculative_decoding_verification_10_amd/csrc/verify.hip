@@ -462,33 +462,28 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, StepShared& s
             a.aprob[(size_t)b * K + i] = (i < kb) ? sh.ratio[i] : -1.0f;
 }
 
-// Row items, request-major: item n is tile n % C of row slot (n / C) % R of
-// request n / (C * R).
+// Row items: workgroup (x, y, z) takes tile x of row slot y of request z
+// (the grid is dispatched x fastest, so request-major).
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_rows(VerifyParams a) {
     __shared__ float lds_f[kWaves];
     __shared__ double lds_d[kWaves];
-    const int64_t n = blockIdx.x;
-    const int tile = (int)(n % a.C);
-    const int64_t r = n / a.C;
-    row_item<DT, VEC>(a, (int)(r / a.R), (int)(r % a.R), tile, lds_f, lds_d);
+    row_item<DT, VEC>(a, blockIdx.z, blockIdx.y, blockIdx.x, lds_f, lds_d);
 }
 
-// Final items: workgroup n takes tile n % C of request n / C.
+// Final items: workgroup (x, y) takes tile x of request y; the request's last
+// tile has the highest index of its row of the grid.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
     __shared__ StepShared sh;
-    const int n = blockIdx.x;
-    final_item<DT, VEC>(a, n / a.C, n % a.C, sh);
+    final_item<DT, VEC>(a, blockIdx.y, blockIdx.x, sh);
 }
 
 template <int DT, bool VEC>
 hipError_t launch(const VerifyParams& p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
-    const int64_t rows = (int64_t)p.B * p.R * p.C;
-    const int64_t fins = (int64_t)p.B * p.C;
-    hipLaunchKernelGGL((verify_rows<DT, VEC>), dim3((unsigned)rows), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL((verify_final<DT, VEC>), dim3((unsigned)fins), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((verify_rows<DT, VEC>), dim3(p.C, p.R, p.B), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((verify_final<DT, VEC>), dim3(p.C, p.B), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -69,6 +69,8 @@ def call_verify(lib, **kw):
     (dict(B=-1), EINVAL),
     (dict(K=-1), EINVAL),
     (dict(K=5000), EINVAL),
+    (dict(K=256), EINVAL),
+    (dict(B=65536, wsb=1 << 40), EINVAL),
     (dict(V=0), EINVAL),
     (dict(T=0.0), EINVAL),
     (dict(T=-1.0), EINVAL),
@@ -102,6 +104,7 @@ def call_greedy(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=2), EDTYPE), (dict(B=-3), EINVAL), (dict(V=-1), EINVAL),
+    (dict(K=256), EINVAL), (dict(B=65536, wsb=1 << 40), EINVAL),
     (dict(target=None), EINVAL), (dict(tokens=None), EINVAL), (dict(out=None), EINVAL),
     (dict(ws=None), EWORKSPACE), (dict(wsb=0), EWORKSPACE),
 ])
