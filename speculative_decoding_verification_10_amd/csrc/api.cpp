@@ -79,7 +79,7 @@ VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, 
 }
 
 struct GreedyLayout {
-    size_t part_v, part_i, total;
+    size_t err, slot, total;
 };
 
 GreedyLayout greedy_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt) {
@@ -91,9 +91,9 @@ GreedyLayout greedy_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt) 
     const size_t parts = (size_t)B * ((size_t)K + 1) * C;
     GreedyLayout L;
     size_t off = 0;
-    L.part_v = off; off = align_up(off + parts * sizeof(float));
-    L.part_i = off; off = align_up(off + parts * sizeof(int32_t));
-    L.total = off < kAlign ? kAlign : off;
+    L.err = off;  off = align_up(off + sizeof(uint32_t));
+    L.slot = off; off = align_up(off + parts * sizeof(uint64_t));
+    L.total = off;
     return L;
 }
 
@@ -266,8 +266,8 @@ int specdec_verify_greedy(const void* target_logits, specdec_dtype_t dtype,
     p.K = K;
     p.V = V;
     char* ws = static_cast<char*>(workspace);
-    p.part_v = reinterpret_cast<float*>(ws + L.part_v);
-    p.part_i = reinterpret_cast<int32_t*>(ws + L.part_i);
+    p.err = reinterpret_cast<uint32_t*>(ws + L.err);
+    p.slot = reinterpret_cast<uint64_t*>(ws + L.slot);
     return map_launch(launch_greedy(p, dtype, vec, (hipStream_t)stream));
 }
 

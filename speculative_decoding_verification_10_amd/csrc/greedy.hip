@@ -5,13 +5,15 @@
 // target argmax at the first mismatch, or the argmax after the last draft
 // when every draft matches.  No exponentials: one pass over the target rows.
 //
-//  1. greedy_partial  one workgroup per (target row i <= k_b, tile): the
-//                     tile's (max, lowest index of the max).
-//  2. greedy_decide   one wave per request: merges the tiles of each row in
-//                     ascending order (the first tile holding the max wins,
-//                     so ties resolve to the lowest id), compares with the
-//                     drafts with a ballot and writes the outputs.
+// One kernel, one workgroup per (target row i <= k_b, tile): the tile's
+// (max, lowest index of the max) goes to a self-validating slot.  The
+// request's last workgroup -- last tile of row k_b, the highest index of the
+// request's workgroups -- waits for the other slots of its request (lower
+// indices, dispatched no later, and they never wait), merges each row's
+// tiles, compares the argmaxes with the drafts with a ballot, writes the
+// outputs and zeroes the slots for the next call.
 #include "internal.h"
+#include "slots.h"
 
 namespace specdec {
 namespace {
@@ -25,19 +27,93 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return (v > bv) || (v == bv && i < bi);
 }
 
+// A (value, index) pair as one self-validating word: never all ones, since
+// NaN values are stored canonically and indices are below 2^31.
+__device__ __forceinline__ uint64_t enc_pair(float v, int i) {
+    const uint32_t vb = (v != v) ? 0x7FC00000u : __float_as_uint(v);
+    return ~(((uint64_t)vb << 32) | (uint32_t)i);
+}
+__device__ __forceinline__ void dec_pair(uint64_t s, float& v, int& i) {
+    const uint64_t w = ~s;
+    v = __uint_as_float((uint32_t)(w >> 32));
+    i = (int)(uint32_t)w;
+}
+
+// Best pair over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ void row16_best(float& v, int& i) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(v, o, 16);
+        const int oi = __shfl_xor(i, o, 16);
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+}
+
+struct GreedyShared {
+    float lv[kWaves];
+    int li[kWaves];
+    int am[kMaxK + 1];
+    unsigned long long miss[kWaves];
+};
+
+// The request's decision, by its last workgroup.
+__device__ void greedy_decide(const GreedyParams& a, int b, int kb, GreedyShared& sh) {
+    const int K = a.K, C = a.C;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, sub = lane & 15;
+    uint64_t* slots = a.slot + (size_t)b * (K + 1) * C;
+    // Rows 16 lanes at a time, four rows per wave.
+    for (int base = 0; base <= kb; base += kWaves * 4) {
+        const int r = base + w * 4 + (lane >> 4);
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+        if (r <= kb) {
+            for (int c = sub; c < C; c += 16) {
+                const uint64_t* p = slots + (size_t)r * C + c;
+                float v;
+                int i;
+                dec_pair(slot_wait(p, a.err, enc_pair(-INFINITY, 0)), v, i);
+                if (better(v, i, bv, bi)) { bv = v; bi = i; }
+            }
+        }
+        row16_best(bv, bi);
+        if (sub == 0 && r <= kb) sh.am[r] = min(max(bi, 0), a.V - 1);
+    }
+    __syncthreads();
+    const bool miss = (t < kb) && (a.tokens[(size_t)b * K + t] != sh.am[t]);
+    const unsigned long long mask = __ballot(miss);
+    if (lane == 0) sh.miss[w] = mask;
+    __syncthreads();
+    int j = kb;
+    for (int k = 0; k < kWaves; ++k)
+        if (sh.miss[k]) {
+            j = k * 64 + __ffsll((long long)sh.miss[k]) - 1;
+            break;
+        }
+    for (int i = t; i <= K; i += kThreads) {
+        int32_t v = -1;
+        if (i < j) v = a.tokens[(size_t)b * K + i];
+        else if (i == j) v = sh.am[j];
+        a.out[(size_t)b * (K + 1) + i] = v;
+        if (a.amax) a.amax[(size_t)b * (K + 1) + i] = (i <= kb) ? sh.am[i] : -1;
+    }
+    if (t == 0) a.nacc[b] = j;
+    // Every slot of the request was awaited above.
+    for (int s = t; s < (kb + 1) * C; s += kThreads) slot_put(slots + s, (uint64_t)0);
+}
+
+// Workgroup (x, y, z): tile x of target row y of request z.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void greedy_partial(GreedyParams a) {
+__global__ __launch_bounds__(kThreads) void greedy_rows(GreedyParams a) {
     constexpr int E = Elem<DT>::E;
     constexpr int S = Elem<DT>::S;
-    __shared__ float lv[kWaves];
-    __shared__ int li[kWaves];
+    __shared__ GreedyShared sh;
     const int tile = blockIdx.x;
     const int i = blockIdx.y;
     const int b = blockIdx.z;
+    const int kb = greedy_k(a, b);
+    if (i > kb) return;
     const size_t rid = (size_t)b * (a.K + 1) + i;
-    const size_t item = rid * a.C + tile;
-    if (i > greedy_k(a, b)) return;
-    const void* row = static_cast<const char*>(a.target) + (size_t)rid * a.V * S;
+    const void* row = static_cast<const char*>(a.target) + rid * a.V * S;
     const int v0 = tile * kTileVec + threadIdx.x;
     u32x4 raw[kUnroll];
 #pragma unroll
@@ -70,63 +146,22 @@ __global__ __launch_bounds__(kThreads) void greedy_partial(GreedyParams a) {
         if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
     }
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { lv[w] = bv; li[w] = bi; }
+    if ((threadIdx.x & 63) == 0) { sh.lv[w] = bv; sh.li[w] = bi; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        float rv = lv[0];
-        int ri = li[0];
+        float rv = sh.lv[0];
+        int ri = sh.li[0];
         for (int k = 1; k < kWaves; ++k)
-            if (better(lv[k], li[k], rv, ri)) { rv = lv[k]; ri = li[k]; }
-        a.part_v[item] = rv;
-        a.part_i[item] = ri;
+            if (better(sh.lv[k], sh.li[k], rv, ri)) { rv = sh.lv[k]; ri = sh.li[k]; }
+        slot_put(a.slot + rid * a.C + tile, enc_pair(rv, ri));
     }
-}
-
-__global__ __launch_bounds__(64) void greedy_decide(GreedyParams a) {
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int K = a.K;
-    const int kb = greedy_k(a, b);
-    int j = kb;
-    int aj = 0;
-    for (int base = 0; base <= kb; base += 64) {
-        const int i = base + lane;
-        int am = -1;
-        bool miss = false;
-        if (i <= kb) {
-            const size_t rid = (size_t)b * (K + 1) + i;
-            float bv = a.part_v[rid * a.C];
-            int bi = a.part_i[rid * a.C];
-            for (int t = 1; t < a.C; ++t) {
-                const float v = a.part_v[rid * a.C + t];
-                if (v > bv) { bv = v; bi = a.part_i[rid * a.C + t]; }
-            }
-            am = min(bi, a.V - 1);
-            if (a.amax) a.amax[rid] = am;
-            if (i < kb) miss = (a.tokens[(size_t)b * K + i] != am);
-        }
-        const unsigned long long mask = __ballot(miss);
-        if (j == kb) {
-            if (mask) j = base + __ffsll((long long)mask) - 1;
-            if (j - base >= 0 && j - base < 64) aj = __shfl(am, j - base, 64);
-        }
-    }
-    for (int i = lane; i <= K; i += 64) {
-        int32_t v = -1;
-        if (i < j) v = a.tokens[(size_t)b * K + i];
-        else if (i == j) v = aj;
-        a.out[(size_t)b * (K + 1) + i] = v;
-        if (a.amax && i > kb) a.amax[(size_t)b * (K + 1) + i] = -1;
-    }
-    if (lane == 0) a.nacc[b] = j;
+    if (i == kb && tile == a.C - 1) greedy_decide(a, b, kb, sh);
 }
 
 template <int DT, bool VEC>
 hipError_t launch(const GreedyParams& p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
-    // Workgroup (x, y, z): tile x of row y of request z.
-    hipLaunchKernelGGL((greedy_partial<DT, VEC>), dim3(p.C, p.K + 1, p.B), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(greedy_decide, dim3((unsigned)p.B), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((greedy_rows<DT, VEC>), dim3(p.C, p.K + 1, p.B), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

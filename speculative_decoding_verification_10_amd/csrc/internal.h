@@ -64,8 +64,8 @@ struct GreedyParams {
     int32_t* nacc;
     int32_t* amax;              // may be null
     int B, K, V, NV, C;
-    float* part_v;              // [B * (K+1) * C]
-    int32_t* part_i;            // [B * (K+1) * C]
+    uint32_t* err;              // workspace header: error bits
+    uint64_t* slot;             // [B * (K+1) * C] tile (max, index) (self-validating)
 };
 
 struct StatsParams {
