@@ -53,12 +53,12 @@ bool make_scale(float temperature, Scale* s) {
 }
 
 struct VerifyLayout {
-    size_t err, slot_m, slot_s, slot_l, slot_slab, total;
+    size_t err, slot_m, slot_s, slot_l, slot_slab, dec, total;
 };
 
-// Header (error bits) and self-validating slots: tile max / tile sum of every
-// row slot of every request, the logit at the draft token of every row, and
-// the slab sums of every request's final row.
+// Header (error bits), self-validating slots -- tile max / tile sum of every
+// row slot of every request, the logit at the draft token of every row, the
+// slab sums of every request's final row -- and each request's decision.
 VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, bool one_hot) {
     int NV, NVv;
     bool vec;
@@ -74,6 +74,7 @@ VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, 
     L.slot_s = off;    off = align_up(off + parts * sizeof(uint64_t));
     L.slot_l = off;    off = align_up(off + (size_t)B * R * sizeof(uint32_t));
     L.slot_slab = off; off = align_up(off + (size_t)B * C * kUnroll * sizeof(uint64_t));
+    L.dec = off;       off = align_up(off + (size_t)B * sizeof(Decision));
     L.total = off;
     return L;
 }
@@ -230,6 +231,7 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
     p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);
     p.slot_l = reinterpret_cast<uint32_t*>(ws + L.slot_l);
     p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
+    p.dec = reinterpret_cast<Decision*>(ws + L.dec);
     return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream));
 }
 

@@ -1,30 +1,26 @@
-// Stochastic verify step on gfx950: two stream-ordered kernels, one
-// workgroup per work item.
+// Stochastic verify step on gfx950: three stream-ordered kernels, one
+// workgroup per work item, and no waits inside any of them.
 //
-//  verify_rows   row item (request b, row, tile): tile max and sum of
-//                exponentials of target row i <= k_b or draft row i < k_b
-//                ("3.5 Speculative Decoding", "Notation": p and q are the
-//                temperature-processed distributions), and the logit at the
-//                draft token x_i when it lies in the tile.  Rows past k_b are
-//                skipped.  No item waits for another.  Items of target row 0
-//                also clear the request's slab slots for the final kernel.
-//  verify_final  final item (request b, tile): the decision of request b --
-//                the tile partials of every row merged, u_i < min(1,
-//                p_i(x_i)/q_i(x_i)) tested for every drafted position, the
-//                first rejection j taken with a ballot ("The algorithm (one
-//                step)", step 3) -- then the tile's slab sums of the
-//                unnormalised replacement masses max(0, p_j - q_j), or of
-//                p_{k_b} when every draft was accepted (step 4).  The
-//                request's last tile then reads all of the request's slab
-//                sums, finds the slab that holds u * S, re-reads that one
-//                slab, takes the smallest token t with u * S < C_t and writes
-//                the request's outputs.
+//  verify_rows    row item (request b, row, tile): tile max and sum of
+//                 exponentials of target row i <= k_b or draft row i < k_b
+//                 ("3.5 Speculative Decoding", "Notation": p and q are the
+//                 temperature-processed distributions), and the logit at the
+//                 draft token x_i when it lies in the tile.  Rows past k_b are
+//                 skipped.
+//  verify_final   final item (request b, tile): the decision of request b --
+//                 the tile partials of every row merged, u_i < min(1,
+//                 p_i(x_i)/q_i(x_i)) tested for every drafted position, the
+//                 first rejection j taken with a ballot ("The algorithm (one
+//                 step)", step 3) -- then the tile's slab sums of the
+//                 unnormalised replacement masses max(0, p_j - q_j), or of
+//                 p_{k_b} when every draft was accepted (step 4).  Tile 0
+//                 stores the decision and the accept probabilities.
+//  verify_search  one wave per request: the slab that holds u * S, a re-read
+//                 of that one slab, the smallest token t with u * S < C_t,
+//                 and the outputs.
 //
-// Results cross workgroups through self-validating slots (slots.h).  The
-// kernel boundary orders every row slot before its readers.  The only wait
-// is the last tile's, for the slab sums of its request's other tiles: those
-// have lower workgroup indices, which the hardware dispatches no later, and
-// they never wait themselves, so the wait ends.
+// Each kernel reads only what the kernels before it wrote; the slots keep
+// their self-validating encoding (slots.h) as a guard.
 //
 // Masses are kept unnormalised: the replacement is Z_p * max(0, p - q) =
 // max(0, e_p - (Z_p/Z_q) e_q) with e = exp2(x * c - M) against each row's
@@ -64,8 +60,6 @@ struct StepShared {
     float red_f[kWaves];
     double red_d[kWaves];
     double slab[kWaves][kUnroll];
-    int g, found, lastpos, lastnz;
-    double base, w, total;
 };
 
 // k_b, clamped to [0, K] so that a bad value can never address memory
@@ -270,73 +264,6 @@ __device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* 
         slot_put(a.slot_s + idx, enc_f64(z));
         slot_put(a.slot_m + idx, enc_f32(m));
     }
-    // Target row 0 is read by every request: its items clear the request's
-    // slab slots for this call's final kernel.
-    if (rr == 0 && threadIdx.x < kUnroll)
-        slot_put(a.slot_slab + ((size_t)b * a.C + tile) * kUnroll + threadIdx.x, (uint64_t)0);
-}
-
-// ---------------------------------------------------------------------------
-// Token search, by every final item of the request at once.
-// ---------------------------------------------------------------------------
-
-// Waits for the NS slab sums of the request; then (identically in every
-// workgroup of the request) their total S, the slab g that holds w = u * S --
-// the first slab whose inclusive prefix exceeds w -- and the mass before it;
-// the last slab with mass when rounding leaves w past the end.
-__device__ void find_slab(const VerifyParams& a, const uint64_t* slabs, double u, StepShared& sh) {
-    const int t = threadIdx.x;
-    const int NS = a.NS;
-    double part = 0.0, v0 = 0.0;
-    for (int s = t; s < NS; s += kThreads) {
-        const double v = dec_f64(slot_wait(slabs + s, a.err, enc_f64(0.0)));
-        part += v;
-        if (s == t) v0 = v;
-    }
-    const double total = block_sum(part, sh.red_d);
-    const double w = u * total;
-    if (t == 0) {
-        sh.g = 0x7FFFFFFF;
-        sh.lastnz = -1;
-    }
-    __syncthreads();
-    double run = 0.0;
-    for (int s0 = 0; s0 < NS; s0 += kThreads) {
-        const int s = s0 + t;
-        const double v = (s0 == 0) ? v0 : (s < NS ? dec_f64(slot_peek(slabs + s)) : 0.0);
-        double ctot;
-        const double before = run + block_exclusive_scan(v, sh.red_d, &ctot);
-        if (s < NS && w < before + v) atomicMin(&sh.g, s);
-        if (s < NS && v > 0.0) atomicMax(&sh.lastnz, s);
-        __syncthreads();
-        const int g = sh.g;
-        if (g == s) sh.base = before;
-        if (g != 0x7FFFFFFF) break;
-        run += ctot;
-    }
-    __syncthreads();
-    if (t == 0) {
-        if (sh.g == 0x7FFFFFFF) sh.g = -1;
-        sh.w = w;
-        sh.total = total;
-    }
-    __syncthreads();
-    if (sh.g < 0) {
-        // No slab reaches w: take the last slab with mass.
-        const int L = sh.lastnz < 0 ? 0 : sh.lastnz;
-        double run2 = 0.0;
-        for (int s0 = 0; s0 < NS; s0 += kThreads) {
-            const int s = s0 + t;
-            const double v = s < NS ? dec_f64(slot_peek(slabs + s)) : 0.0;
-            double ctot;
-            const double before = run2 + block_exclusive_scan(v, sh.red_d, &ctot);
-            if (s == L) sh.base = before;
-            run2 += ctot;
-        }
-        __syncthreads();
-        if (t == 0) sh.g = L;
-        __syncthreads();
-    }
 }
 
 // Slab sums of one tile: the masses of each of the kUnroll vectors of every
@@ -362,43 +289,6 @@ __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], con
     }
 }
 
-// The smallest token in slab g (held by this workgroup as vector index u)
-// with w < C_t, C_t running from the mass before the slab; the last token
-// with mass in the slab when rounding leaves w past every C_t.  Thread 0
-// returns the token.
-template <int DT>
-__device__ int scan_slab(const VerifyParams& a, const u32x4& rp, const u32x4& rq, const Decision& d,
-                         int v, double base, double w, StepShared& sh) {
-    constexpr int E = Elem<DT>::E;
-    float r[E];
-    final_masses<DT>(rp, rq, d, v, a.sc, r);
-    const double vs = (double)pairwise_sum<E>(r);
-    if (threadIdx.x == 0) {
-        sh.found = 0x7FFFFFFF;
-        sh.lastpos = -1;
-    }
-    double slab_total;
-    const double start = base + block_exclusive_scan(vs, sh.red_d, &slab_total);
-    int lastpos = -1;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-        if (r[e] > 0.0f) lastpos = v * E + e;
-    if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
-    if (start <= w && vs > 0.0) {
-        double Cc = start;
-        for (int e = 0; e < E; ++e) {
-            Cc += (double)r[e];
-            if (w < Cc) {
-                atomicMin(&sh.found, v * E + e);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-    const int tok = sh.found != 0x7FFFFFFF ? sh.found : sh.lastpos;
-    return tok < 0 ? 0 : tok;
-}
-
 // ---------------------------------------------------------------------------
 // Final item: tile `tile` of the final row (pair) of request b.
 // ---------------------------------------------------------------------------
@@ -422,44 +312,154 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, StepShared& s
     }
     const size_t slab0 = (size_t)b * a.C * kUnroll;
     put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + slab0 + (size_t)tile * kUnroll, sh);
-    if (tile != a.C - 1) return;
-
-    // The request's last tile: every other tile of the request has a lower
-    // workgroup index.
-    const double u = (double)a.unif[(size_t)b * (K + 1) + kb];
-    uint64_t* slabs = a.slot_slab + slab0;
-    find_slab(a, slabs, u, sh);
-    if (!(sh.total > 0.0)) {
-        // Every replacement mass is zero: draw from p_j itself.  Its slab
-        // sums replace the residual ones (rare; one workgroup streams the row).
-        d.mode = kBonus;
-        for (int g = 0; g < a.NS; ++g) {
-            const int v = g * kSlab + threadIdx.x;
-            const u32x4 bp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
-            float r[E];
-            final_masses<DT>(bp, bp, d, v, a.sc, r);
-            const double t = block_sum((double)pairwise_sum<E>(r), sh.red_d);
-            if (threadIdx.x == 0) slot_put(slabs + g, enc_f64(t));
-        }
-        __syncthreads();
-        find_slab(a, slabs, u, sh);
+    if (tile == 0) {
+        if (threadIdx.x == 0) a.dec[b] = d;
+        if (a.aprob)
+            for (int i = threadIdx.x; i < K; i += kThreads)
+                a.aprob[(size_t)b * K + i] = (i < kb) ? sh.ratio[i] : -1.0f;
     }
-    // Re-read slab g (one vector per thread) and search it.
-    const int v = sh.g * kSlab + threadIdx.x;
-    const u32x4 sp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
-    const u32x4 sq = (d.mode == kResidual) ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : sp;
-    const int tok = scan_slab<DT>(a, sp, sq, d, v, sh.base, sh.w, sh);
+}
+
+// ---------------------------------------------------------------------------
+// Token search of request b, by one wave (no workgroup barriers).
+//
+// The slab sums give S and the slab g that holds w = u * S: the first slab
+// whose inclusive prefix exceeds w (the last slab with mass when rounding
+// leaves w past the end).  Slab g is re-read, four vectors per lane in
+// ascending token order, and the smallest token t with w < C_t is taken, C_t
+// running from the mass before the slab (the last token with mass in the
+// slab when rounding leaves w past every C_t).
+// ---------------------------------------------------------------------------
+constexpr int kSearchLanes = 64;
+constexpr int kSlabPerLane = kSlab / kSearchLanes;   // vectors of a slab per lane
+
+// Wave: first index in [0, n) of values v (read by get(i)) whose inclusive
+// prefix exceeds w, and the mass before it; else the last index with mass.
+template <class Get>
+__device__ __forceinline__ int wave_locate(int n, double w, Get get, double* before_out) {
+    const int lane = threadIdx.x & 63;
+    double run = 0.0, last_before = 0.0;
+    int last_nz = -1;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        const double v = (i0 + lane < n) ? get(i0 + lane) : 0.0;
+        const double incl = run + wave_inclusive_scan(v);
+        const double before = incl - v;
+        const unsigned long long hit = __ballot(w < incl && i0 + lane < n);
+        const unsigned long long nz = __ballot(v > 0.0);
+        if (nz) {
+            const int L = 63 - __clzll((long long)nz);
+            last_nz = i0 + L;
+            last_before = __shfl(before, L, 64);
+        }
+        if (hit) {
+            const int L = __ffsll((long long)hit) - 1;
+            *before_out = __shfl(before, L, 64);
+            return i0 + L;
+        }
+        run = __shfl(incl, 63, 64);
+    }
+    *before_out = last_before;
+    return last_nz < 0 ? 0 : last_nz;
+}
+
+template <int DT, bool VEC>
+__device__ void search(const VerifyParams& a, int b) {
+    constexpr int E = Elem<DT>::E;
+    constexpr int S = Elem<DT>::S;
+    const int K = a.K;
+    const int lane = threadIdx.x;
+    const int kb = kb_of(a, b);
+    Decision d = a.dec[b];
+    const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
+    const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
+    const double u = (double)a.unif[(size_t)b * (K + 1) + kb];
+    uint64_t* slabs = a.slot_slab + (size_t)b * a.C * kUnroll;
+    const int NS = a.NS;
+
+    double total = 0.0;
+    for (int g0 = 0; g0 < NS; g0 += 64)
+        if (g0 + lane < NS) total += dec_f64(slot_wait(slabs + g0 + lane, a.err, enc_f64(0.0)));
+    total = wave_sum(total);
+    if (!(total > 0.0)) {
+        // Every replacement mass is zero: draw from p_j itself.  Its slab
+        // sums replace the residual ones (rare; one wave streams the row).
+        d.mode = kBonus;
+        rowq = nullptr;
+        for (int g = 0; g < NS; ++g) {
+            double t = 0.0;
+            for (int k = 0; k < kSlabPerLane; ++k) {
+                const int v = g * kSlab + k * 64 + lane;
+                const u32x4 bp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
+                float r[E];
+                final_masses<DT>(bp, bp, d, v, a.sc, r);
+                t += (double)pairwise_sum<E>(r);
+            }
+            t = wave_sum(t);
+            if (lane == 0) slot_put(slabs + g, enc_f64(t));
+        }
+        total = 0.0;
+        for (int g0 = 0; g0 < NS; g0 += 64)
+            if (g0 + lane < NS) total += dec_f64(slot_wait(slabs + g0 + lane, a.err, enc_f64(0.0)));
+        total = wave_sum(total);
+    }
+    const double w = u * total;
+    double base;
+    const int g = wave_locate(NS, w, [&](int i) { return dec_f64(slot_peek(slabs + i)); }, &base);
+
+    // Slab g: vector g * kSlab + k * 64 + lane for k = 0..3, in ascending order.
+    float r[kSlabPerLane][E];
+    double vs[kSlabPerLane];
+#pragma unroll
+    for (int k = 0; k < kSlabPerLane; ++k) {
+        const int v = g * kSlab + k * 64 + lane;
+        const u32x4 sp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
+        const u32x4 sq = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : sp;
+        final_masses<DT>(sp, sq, d, v, a.sc, r[k]);
+        vs[k] = (double)pairwise_sum<E>(r[k]);
+    }
+    double vbase;
+    const int vi = wave_locate(kSlabPerLane * 64, w - base,
+                               [&](int i) {
+                                   double x = 0.0;
+#pragma unroll
+                                   for (int k = 0; k < kSlabPerLane; ++k)
+                                       if ((i >> 6) == k) x = vs[k];
+                                   return x;
+                               },
+                               &vbase);
+    // Lane vi & 63 holds vector vi (k = vi >> 6); scan its elements.
+    int tok = -1;
+    if (lane == (vi & 63)) {
+        const int k = vi >> 6;
+        float rr[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float x = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < kSlabPerLane; ++kk)
+                if (kk == k) x = r[kk][e];
+            rr[e] = x;
+        }
+        const int v = g * kSlab + vi;
+        double Cc = base + vbase;
+        int lastpos = -1;
+        for (int e = 0; e < E; ++e) {
+            if (rr[e] > 0.0f) lastpos = v * E + e;
+            Cc += (double)rr[e];
+            if (tok < 0 && w < Cc) tok = v * E + e;
+        }
+        if (tok < 0) tok = lastpos;
+    }
+    tok = __shfl(tok, vi & 63, 64);
+    if (tok < 0) tok = 0;
     const int j = d.j;
-    for (int i = threadIdx.x; i <= K; i += kThreads) {
+    for (int i = lane; i <= K; i += 64) {
         int32_t o = -1;
         if (i < j) o = a.tokens[(size_t)b * K + i];
         else if (i == j) o = tok;
         a.out[(size_t)b * (K + 1) + i] = o;
     }
-    if (threadIdx.x == 0) a.nacc[b] = j;
-    if (a.aprob)
-        for (int i = threadIdx.x; i < K; i += kThreads)
-            a.aprob[(size_t)b * K + i] = (i < kb) ? sh.ratio[i] : -1.0f;
+    if (lane == 0) a.nacc[b] = j;
 }
 
 // Row items: workgroup (x, y, z) takes tile x of row slot y of request z
@@ -471,12 +471,17 @@ __global__ __launch_bounds__(kThreads) void verify_rows(VerifyParams a) {
     row_item<DT, VEC>(a, blockIdx.z, blockIdx.y, blockIdx.x, lds_f, lds_d);
 }
 
-// Final items: workgroup (x, y) takes tile x of request y; the request's last
-// tile has the highest index of its row of the grid.
+// Final items: workgroup (x, y) takes tile x of request y.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
     __shared__ StepShared sh;
     final_item<DT, VEC>(a, blockIdx.y, blockIdx.x, sh);
+}
+
+// Token search: one wave per request.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kSearchLanes) void verify_search(VerifyParams a) {
+    search<DT, VEC>(a, blockIdx.x);
 }
 
 template <int DT, bool VEC>
@@ -484,6 +489,7 @@ hipError_t launch(const VerifyParams& p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
     hipLaunchKernelGGL((verify_rows<DT, VEC>), dim3(p.C, p.R, p.B), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL((verify_final<DT, VEC>), dim3(p.C, p.B), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((verify_search<DT, VEC>), dim3(p.B), dim3(kSearchLanes), 0, s, p);
     return hipGetLastError();
 }
 
