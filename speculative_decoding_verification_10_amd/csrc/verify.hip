@@ -376,8 +376,18 @@ __device__ void search(const VerifyParams& a, int b) {
     uint64_t* slabs = a.slot_slab + (size_t)b * a.C * kUnroll;
     const int NS = a.NS;
 
+    // The slab sums, kept in registers for up to kHeld * 64 slabs (read
+    // again from the slots beyond that).
+    constexpr int kHeld = 4;
+    double held[kHeld];
     double total = 0.0;
-    for (int g0 = 0; g0 < NS; g0 += 64)
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) {
+        held[k] = 0.0;
+        if (k * 64 + lane < NS) held[k] = dec_f64(slot_wait(slabs + k * 64 + lane, a.err, enc_f64(0.0)));
+        total += held[k];
+    }
+    for (int g0 = kHeld * 64; g0 < NS; g0 += 64)
         if (g0 + lane < NS) total += dec_f64(slot_wait(slabs + g0 + lane, a.err, enc_f64(0.0)));
     total = wave_sum(total);
     if (!(total > 0.0)) {
@@ -398,13 +408,27 @@ __device__ void search(const VerifyParams& a, int b) {
             if (lane == 0) slot_put(slabs + g, enc_f64(t));
         }
         total = 0.0;
-        for (int g0 = 0; g0 < NS; g0 += 64)
+#pragma unroll
+        for (int k = 0; k < kHeld; ++k) {
+            held[k] = 0.0;
+            if (k * 64 + lane < NS) held[k] = dec_f64(slot_wait(slabs + k * 64 + lane, a.err, enc_f64(0.0)));
+            total += held[k];
+        }
+        for (int g0 = kHeld * 64; g0 < NS; g0 += 64)
             if (g0 + lane < NS) total += dec_f64(slot_wait(slabs + g0 + lane, a.err, enc_f64(0.0)));
         total = wave_sum(total);
     }
     const double w = u * total;
     double base;
-    const int g = wave_locate(NS, w, [&](int i) { return dec_f64(slot_peek(slabs + i)); }, &base);
+    const int g = wave_locate(NS, w,
+                              [&](int i) {
+                                  double x = 0.0;
+#pragma unroll
+                                  for (int k = 0; k < kHeld; ++k)
+                                      if ((i >> 6) == k) x = held[k];
+                                  return i < kHeld * 64 ? x : dec_f64(slot_peek(slabs + i));
+                              },
+                              &base);
 
     // Slab g: vector g * kSlab + k * 64 + lane for k = 0..3, in ascending order.
     float r[kSlabPerLane][E];
