@@ -14,7 +14,9 @@
 //                 step)", step 3) -- then the tile's slab sums of the
 //                 unnormalised replacement masses max(0, p_j - q_j), or of
 //                 p_{k_b} when every draft was accepted (step 4).  Tile 0
-//                 stores the decision and the accept probabilities.
+//                 stores the decision and the accept probabilities.  For
+//                 long rows of many positions the decision is instead taken
+//                 once per request by verify_decide, launched before it.
 //  verify_search  one wave per request: the slab that holds u * S, a re-read
 //                 of that one slab, the smallest token t with u * S < C_t,
 //                 and the outputs.
@@ -33,6 +35,9 @@ namespace specdec {
 namespace {
 
 constexpr int kMaxRows = 2 * kMaxK + 1;
+// Above this many partial loads per request (C tiles x R rows x C tiles), the
+// decision is taken once per request by its own kernel.
+constexpr int64_t kDecideOnceAbove = 8192;
 
 __device__ __forceinline__ const void* row_ptr(const void* base, size_t row, int V, int S) {
     return static_cast<const char*>(base) + row * (size_t)V * (size_t)S;
@@ -289,17 +294,31 @@ __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], con
     }
 }
 
+// The decision of request b for the search kernel, and the accept
+// probabilities.
+__device__ void publish_decision(const VerifyParams& a, int b, int kb, const StepShared& sh) {
+    if (threadIdx.x == 0) a.dec[b] = sh.dec;
+    if (a.aprob)
+        for (int i = threadIdx.x; i < a.K; i += kThreads)
+            a.aprob[(size_t)b * a.K + i] = (i < kb) ? sh.ratio[i] : -1.0f;
+}
+
 // ---------------------------------------------------------------------------
 // Final item: tile `tile` of the final row (pair) of request b.
 // ---------------------------------------------------------------------------
 template <int DT, bool VEC>
-__device__ void final_item(const VerifyParams& a, int b, int tile, StepShared& sh) {
+__device__ void final_item(const VerifyParams& a, int b, int tile, bool decided, StepShared& sh) {
     constexpr int E = Elem<DT>::E;
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
     const int kb = kb_of(a, b);
-    decide(a, b, kb, sh);
-    Decision d = sh.dec;
+    if (decided) {
+        if (threadIdx.x == 0) sh.dec = a.dec[b];
+        __syncthreads();
+    } else {
+        decide(a, b, kb, sh);
+    }
+    const Decision d = sh.dec;
     const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
     const int v0 = tile * kTileVec + threadIdx.x;
@@ -312,13 +331,9 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, StepShared& s
     }
     const size_t slab0 = (size_t)b * a.C * kUnroll;
     put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + slab0 + (size_t)tile * kUnroll, sh);
-    if (tile == 0) {
-        if (threadIdx.x == 0) a.dec[b] = d;
-        if (a.aprob)
-            for (int i = threadIdx.x; i < K; i += kThreads)
-                a.aprob[(size_t)b * K + i] = (i < kb) ? sh.ratio[i] : -1.0f;
-    }
+    if (tile == 0 && !decided) publish_decision(a, b, kb, sh);
 }
+
 
 // ---------------------------------------------------------------------------
 // Token search of request b, by one wave (no workgroup barriers).
@@ -495,11 +510,20 @@ __global__ __launch_bounds__(kThreads) void verify_rows(VerifyParams a) {
     row_item<DT, VEC>(a, blockIdx.z, blockIdx.y, blockIdx.x, lds_f, lds_d);
 }
 
+// Decisions, when taken once per request: workgroup x takes request x.
+__global__ __launch_bounds__(kThreads) void verify_decide(VerifyParams a) {
+    __shared__ StepShared sh;
+    const int b = blockIdx.x;
+    const int kb = kb_of(a, b);
+    decide(a, b, kb, sh);
+    publish_decision(a, b, kb, sh);
+}
+
 // Final items: workgroup (x, y) takes tile x of request y.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool DECIDED>
 __global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
     __shared__ StepShared sh;
-    final_item<DT, VEC>(a, blockIdx.y, blockIdx.x, sh);
+    final_item<DT, VEC>(a, blockIdx.y, blockIdx.x, DECIDED, sh);
 }
 
 // Token search: one wave per request.
@@ -512,7 +536,14 @@ template <int DT, bool VEC>
 hipError_t launch(const VerifyParams& p, hipStream_t s) {
     if (p.B == 0) return hipSuccess;
     hipLaunchKernelGGL((verify_rows<DT, VEC>), dim3(p.C, p.R, p.B), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL((verify_final<DT, VEC>), dim3(p.C, p.B), dim3(kThreads), 0, s, p);
+    // Every final tile takes the decision itself (no extra launch) unless
+    // that repeats much work: C tiles each merging R * C row-tile partials.
+    if ((int64_t)p.C * p.R * p.C > kDecideOnceAbove) {
+        hipLaunchKernelGGL(verify_decide, dim3(p.B), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((verify_final<DT, VEC, true>), dim3(p.C, p.B), dim3(kThreads), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((verify_final<DT, VEC, false>), dim3(p.C, p.B), dim3(kThreads), 0, s, p);
+    }
     hipLaunchKernelGGL((verify_search<DT, VEC>), dim3(p.B), dim3(kSearchLanes), 0, s, p);
     return hipGetLastError();
 }

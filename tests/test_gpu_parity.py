@@ -101,6 +101,20 @@ def test_verify_ragged_full_size():
     assert nd == 0
 
 
+@pytest.mark.parametrize("name,B,V,K", [
+    ("peaked", 2, 4096, 255),     # the largest K; the final tiles take the decision
+    ("headline", 2, 40000, 255),  # the largest K; the decision taken once per request
+    ("ragged", 3, 40000, 60),     # ragged k_b, decision once per request
+])
+def test_verify_long_drafts(name, B, V, K):
+    say("verify long drafts", name, B, V, K)
+    wl = workloads.make(name, set_index=1, B=B, V=V, K=K)
+    ref = oracle_verify(wl)
+    nf, nd = compare_verify("%s-K%d" % (name, K), run_verify(wl), ref)
+    say("flagged", nf, "differ", nd, "of", wl.B)
+    assert nd == 0
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("V", [5, 777, 1001, 8192, 40001])
 @pytest.mark.parametrize("one_hot", [False, True])
