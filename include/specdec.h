@@ -33,12 +33,17 @@
  *     errors are detected on the host before anything is launched and leave
  *     every output untouched.  No C++ exception crosses the ABI.
  *   - Workspace: device memory of at least the size the matching
- *     *_workspace_bytes() function returns, 256-byte aligned.  Its contents
- *     need no initialisation: a call writes every scratch word before it
- *     reads it.  The first 4 bytes hold error bits: a call ORs in a bit when
- *     an internal bounded wait gives up (never in a correct run); zero them
- *     with specdec_workspace_init to start afresh.  Calls that may run
- *     concurrently need distinct workspaces.
+ *     *_workspace_bytes() function returns, 256-byte aligned.  The first 4
+ *     bytes hold error bits: a call ORs in a bit when an internal bounded
+ *     wait gives up (never in a correct run).  specdec_verify and
+ *     specdec_softmax_stats write every other scratch word before they read
+ *     it, so their workspace needs no initialisation.  specdec_verify_greedy
+ *     hands partial results between workgroups of one kernel through slots
+ *     that must read zero when the call starts: zero-fill its workspace once
+ *     with specdec_workspace_init before the first call; every call leaves
+ *     the slots it used at zero again.  specdec_workspace_init also clears
+ *     the error bits.  Calls that may run concurrently need distinct
+ *     workspaces.
  *   - Preconditions not checked on the fast path (a violation gives
  *     unspecified tokens, never an out-of-bounds access): logits finite or
  *     -inf (-inf = probability 0; a row may not be all -inf); 0 <=

@@ -113,8 +113,9 @@ def _stream(device: torch.device) -> int:
 
 
 class Workspace:
-    """Device scratch for the library (zero-filled when allocated, so the
-    error word at offset 0 starts clear; calls need no other initialisation)."""
+    """Device scratch for the library, zero-filled when allocated: the error
+    word at offset 0 starts clear and the greedy path's slots start empty
+    (each greedy call leaves them empty again)."""
 
     def __init__(self, nbytes: int, device):
         self.nbytes = int(nbytes)
