@@ -73,7 +73,7 @@ VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, 
     L.slot_m = off;    off = align_up(off + parts * sizeof(uint32_t));
     L.slot_s = off;    off = align_up(off + parts * sizeof(uint64_t));
     L.slot_l = off;    off = align_up(off + (size_t)B * R * sizeof(uint32_t));
-    L.slot_slab = off; off = align_up(off + (size_t)B * C * kUnroll * sizeof(uint64_t));
+    L.slot_slab = off; off = align_up(off + (size_t)B * C * kSlabsPerTile * sizeof(uint64_t));
     L.dec = off;       off = align_up(off + (size_t)B * sizeof(Decision));
     L.total = off;
     return L;

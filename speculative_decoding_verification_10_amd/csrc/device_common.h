@@ -27,8 +27,9 @@ namespace specdec {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;                       // vectors per thread per tile
-constexpr int kSlab = kThreads;                  // vectors per slab
 constexpr int kTileVec = kThreads * kUnroll;     // vectors per tile (16 KB)
+constexpr int kSlab = 64;                        // vectors per slab: one wave's vectors of one unroll step
+constexpr int kSlabsPerTile = kTileVec / kSlab;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

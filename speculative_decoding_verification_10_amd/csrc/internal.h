@@ -53,7 +53,7 @@ struct VerifyParams {
     uint32_t* slot_m;           // [B * R * C] tile max (self-validating)
     uint64_t* slot_s;           // [B * R * C] tile sum (self-validating)
     uint32_t* slot_l;           // [B * R] logit at the draft token of each row (self-validating)
-    uint64_t* slot_slab;        // [B * C * kUnroll] slab sums of the final draw (self-validating)
+    uint64_t* slot_slab;        // [B * C * kSlabsPerTile] slab sums of the final draw (self-validating)
     Decision* dec;              // [B] decision of each request
 };
 

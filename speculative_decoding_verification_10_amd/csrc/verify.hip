@@ -61,10 +61,9 @@ struct StepShared {
     double z[kMaxRows];                 // row sum relative to offset_of(max)
     float ratio[kMaxK];
     unsigned long long rej[kWaves];
-    Decision dec;
     float red_f[kWaves];
     double red_d[kWaves];
-    double slab[kWaves][kUnroll];
+    double slab[kSlabsPerTile];
 };
 
 // k_b, clamped to [0, K] so that a bad value can never address memory
@@ -114,8 +113,8 @@ __device__ __forceinline__ void merge2(float& m1, double& z1, float m2, double z
 }
 
 // ---------------------------------------------------------------------------
-// The decision of request b, by the whole workgroup, into sh.dec and
-// sh.ratio.
+// The decision of request b, by the whole workgroup: returned to every
+// thread, the accept probabilities left in sh.ratio.
 //
 // Rows are merged 16 lanes to a row, four rows per wave and two row groups
 // per lane, so one pass covers 32 rows and every slot load of the pass goes
@@ -123,14 +122,14 @@ __device__ __forceinline__ void merge2(float& m1, double& z1, float m2, double z
 // row max, row offset M = fp32(max * c), and the row sum relative to M, each
 // tile rescaled by exp2(M_tile - M) -- the difference exact in fp64, the
 // power in fp32 (relative error ~1e-7, exactly 1 for the tile that holds the
-// max).  Thread i < k_b takes p_i and q_i at the draft token in fp64 and
-// tests u_i < min(1, p_i/q_i); the first rejection j comes from a ballot.
+// max).  Thread i < k_b forms p_i/q_i at the draft token in fp64 and tests
+// u_i < min(1, p_i/q_i); the first rejection j comes from a ballot.
 // ---------------------------------------------------------------------------
 constexpr int kRowGroups = 2;                         // row groups per lane
 constexpr int kRowsPerPass = kRowGroups * kWaves * 4;  // 32
 constexpr int kTilesPerLoad = 4;                      // tiles per lane per load batch
 
-__device__ void decide(const VerifyParams& a, int b, int kb, StepShared& sh) {
+__device__ Decision decide(const VerifyParams& a, int b, int kb, StepShared& sh) {
     const int K = a.K, C = a.C, R = a.R;
     const bool one_hot = (a.draft == nullptr);
     const int nrs = rows_of(kb, a.kinds);
@@ -198,50 +197,55 @@ __device__ void decide(const VerifyParams& a, int b, int kb, StepShared& sh) {
     __syncthreads();
     bool rej = false;
     if (t < kb) {
+        // p_i/q_i = exp2((l - l_q) c - M_p + M_q) * Z_q / Z_p: one power of
+        // two, the logit difference exact in fp64.  q_i = 0 (draft logit
+        // -inf) counts as ratio 1.
         const float l = dec_f32(rl);
         const double c = a.sc.c;
-        const double p = exp2((double)l * c - (double)offset_of(sh.m[t], a.sc)) / sh.z[t];
-        double q = 1.0;
-        if (!one_hot) {
+        const double Mp = (double)offset_of(sh.m[t], a.sc);
+        double ratio;
+        if (one_hot) {
+            ratio = fmin(1.0, exp2((double)l * c - Mp) / sh.z[t]);
+        } else {
             const float dl = dec_f32(rd);
             const int qs = K + 1 + t;
-            q = exp2((double)dl * c - (double)offset_of(sh.m[qs], a.sc)) / sh.z[qs];
+            const double Mq = (double)offset_of(sh.m[qs], a.sc);
+            ratio = (dl == -INFINITY)
+                        ? 1.0
+                        : fmin(1.0, exp2(((double)l - (double)dl) * c + (Mq - Mp)) * (sh.z[qs] / sh.z[t]));
         }
-        const double ratio = (q == 0.0) ? 1.0 : fmin(1.0, p / q);
         sh.ratio[t] = (float)ratio;
         rej = !((double)u < ratio);
     }
     const unsigned long long mask = __ballot(rej);
     if (lane == 0) sh.rej[w] = mask;
     __syncthreads();
-    if (t == 0) {
-        int j = kb;
-        for (int i = 0; i < kWaves; ++i) {
-            if (sh.rej[i]) {
-                j = i * 64 + __ffsll((long long)sh.rej[i]) - 1;
-                break;
-            }
+    // Every thread reads the first rejection and builds the same decision.
+    int j = kb;
+    for (int i = 0; i < kWaves; ++i) {
+        if (sh.rej[i]) {
+            j = i * 64 + __ffsll((long long)sh.rej[i]) - 1;
+            break;
         }
-        Decision d;
-        d.j = j;
-        d.tok = -1;
-        d.Mp = offset_of(sh.m[j], a.sc);
-        d.Mq = 0.0f;
-        d.rho = 0.0f;
-        d.pad0 = d.pad1 = 0;
-        if (j == kb) {
-            d.mode = kBonus;
-        } else if (one_hot) {
-            d.mode = kResidualOneHot;
-            d.tok = a.tokens[(size_t)b * K + j];
-        } else {
-            d.mode = kResidual;
-            d.Mq = offset_of(sh.m[K + 1 + j], a.sc);
-            d.rho = (float)(sh.z[j] / sh.z[K + 1 + j]);
-        }
-        sh.dec = d;
     }
-    __syncthreads();
+    Decision d;
+    d.j = j;
+    d.tok = -1;
+    d.Mp = offset_of(sh.m[j], a.sc);
+    d.Mq = 0.0f;
+    d.rho = 0.0f;
+    d.pad0 = d.pad1 = 0;
+    if (j == kb) {
+        d.mode = kBonus;
+    } else if (one_hot) {
+        d.mode = kResidualOneHot;
+        d.tok = a.tokens[(size_t)b * K + j];
+    } else {
+        d.mode = kResidual;
+        d.Mq = offset_of(sh.m[K + 1 + j], a.sc);
+        d.rho = (float)(sh.z[j] / sh.z[K + 1 + j]);
+    }
+    return d;
 }
 
 // ---------------------------------------------------------------------------
@@ -271,8 +275,9 @@ __device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* 
     }
 }
 
-// Slab sums of one tile: the masses of each of the kUnroll vectors of every
-// thread, summed over the workgroup per vector index (one slab each).
+// Slab sums of one tile: slab u * kWaves + w of the tile holds the 64
+// vectors that wave w loaded in unroll step u, summed by that wave; the
+// tile's sums leave in one batch of stores.
 template <int DT>
 __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], const u32x4 (&rq)[kUnroll],
                           const Decision& d, int v0, uint64_t* slabs_of_tile, StepShared& sh) {
@@ -283,21 +288,17 @@ __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], con
         float r[E];
         final_masses<DT>(rp[u], rq[u], d, v0 + u * kThreads, a.sc, r);
         const double t = wave_sum((double)pairwise_sum<E>(r));
-        if ((threadIdx.x & 63) == 0) sh.slab[w][u] = t;
+        if ((threadIdx.x & 63) == 0) sh.slab[u * kWaves + w] = t;
     }
     __syncthreads();
-    if (threadIdx.x < kUnroll) {
-        double t = 0.0;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) t += sh.slab[i][threadIdx.x];
-        slot_put(slabs_of_tile + threadIdx.x, enc_f64(t));
-    }
+    if (threadIdx.x < kSlabsPerTile) slot_put(slabs_of_tile + threadIdx.x, enc_f64(sh.slab[threadIdx.x]));
 }
 
 // The decision of request b for the search kernel, and the accept
 // probabilities.
-__device__ void publish_decision(const VerifyParams& a, int b, int kb, const StepShared& sh) {
-    if (threadIdx.x == 0) a.dec[b] = sh.dec;
+__device__ void publish_decision(const VerifyParams& a, int b, int kb, const Decision& d,
+                                 const StepShared& sh) {
+    if (threadIdx.x == 0) a.dec[b] = d;
     if (a.aprob)
         for (int i = threadIdx.x; i < a.K; i += kThreads)
             a.aprob[(size_t)b * a.K + i] = (i < kb) ? sh.ratio[i] : -1.0f;
@@ -312,13 +313,7 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
     const int kb = kb_of(a, b);
-    if (decided) {
-        if (threadIdx.x == 0) sh.dec = a.dec[b];
-        __syncthreads();
-    } else {
-        decide(a, b, kb, sh);
-    }
-    const Decision d = sh.dec;
+    const Decision d = decided ? a.dec[b] : decide(a, b, kb, sh);
     const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
     const int v0 = tile * kTileVec + threadIdx.x;
@@ -329,52 +324,41 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
         rp[u] = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
         rq[u] = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : neg_inf_raw<DT>();
     }
-    const size_t slab0 = (size_t)b * a.C * kUnroll;
-    put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + slab0 + (size_t)tile * kUnroll, sh);
-    if (tile == 0 && !decided) publish_decision(a, b, kb, sh);
+    put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile, sh);
+    if (tile == 0 && !decided) publish_decision(a, b, kb, d, sh);
 }
 
 
 // ---------------------------------------------------------------------------
 // Token search of request b, by one wave (no workgroup barriers).
 //
-// The slab sums give S and the slab g that holds w = u * S: the first slab
-// whose inclusive prefix exceeds w (the last slab with mass when rounding
-// leaves w past the end).  Slab g is re-read, four vectors per lane in
-// ascending token order, and the smallest token t with w < C_t is taken, C_t
-// running from the mass before the slab (the last token with mass in the
-// slab when rounding leaves w past every C_t).
+// Slab g covers vectors [64 g, 64 g + 64).  Lane L owns the P = ceil(NS/64)
+// consecutive slabs from L * P: one inclusive scan of the lanes' sums gives S
+// (lane 63) and the lane whose range holds w = u * S; that lane walks its
+// slabs to the first one whose running prefix exceeds w (the last slab with
+// mass when rounding leaves w past the end).  Slab g is re-read, one vector
+// per lane, a second scan finds the vector, and the smallest token t of it
+// with w < C_t is taken (the last token with mass when rounding leaves w past
+// every C_t).  Only entries with mass can be taken at any level, so a token
+// of zero probability is never drawn, however the sums round.
 // ---------------------------------------------------------------------------
 constexpr int kSearchLanes = 64;
-constexpr int kSlabPerLane = kSlab / kSearchLanes;   // vectors of a slab per lane
+constexpr int kHeld = 16;   // slab sums per lane kept in registers
 
-// Wave: first index in [0, n) of values v (read by get(i)) whose inclusive
-// prefix exceeds w, and the mass before it; else the last index with mass.
-template <class Get>
-__device__ __forceinline__ int wave_locate(int n, double w, Get get, double* before_out) {
-    const int lane = threadIdx.x & 63;
-    double run = 0.0, last_before = 0.0;
-    int last_nz = -1;
-    for (int i0 = 0; i0 < n; i0 += 64) {
-        const double v = (i0 + lane < n) ? get(i0 + lane) : 0.0;
-        const double incl = run + wave_inclusive_scan(v);
-        const double before = incl - v;
-        const unsigned long long hit = __ballot(w < incl && i0 + lane < n);
-        const unsigned long long nz = __ballot(v > 0.0);
-        if (nz) {
-            const int L = 63 - __clzll((long long)nz);
-            last_nz = i0 + L;
-            last_before = __shfl(before, L, 64);
-        }
-        if (hit) {
-            const int L = __ffsll((long long)hit) - 1;
-            *before_out = __shfl(before, L, 64);
-            return i0 + L;
-        }
-        run = __shfl(incl, 63, 64);
+// Unnormalised mass of slab g of the final row, summed by one lane alone
+// (the fallback draw from p_j when every replacement mass is zero).
+template <int DT, bool VEC>
+__device__ double lane_slab_mass(const VerifyParams& a, const void* rowp, const Decision& d, int g) {
+    constexpr int E = Elem<DT>::E;
+    double t = 0.0;
+    for (int k = 0; k < kSlab; ++k) {
+        const int v = g * kSlab + k;
+        const u32x4 bp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
+        float r[E];
+        final_masses<DT>(bp, bp, d, v, a.sc, r);
+        t += (double)pairwise_sum<E>(r);
     }
-    *before_out = last_before;
-    return last_nz < 0 ? 0 : last_nz;
+    return t;
 }
 
 template <int DT, bool VEC>
@@ -384,112 +368,119 @@ __device__ void search(const VerifyParams& a, int b) {
     const int K = a.K;
     const int lane = threadIdx.x;
     const int kb = kb_of(a, b);
+    const int NS = a.NS;
+    const int P = (NS + 63) >> 6;             // slabs per lane
+    const int g0 = lane * P;                  // this lane's first slab
+    uint64_t* slabs = a.slot_slab + (size_t)b * a.C * kSlabsPerTile;
+
+    // This lane's slab sums (the first kHeld kept in registers) and their
+    // sum in slab order.
+    double held[kHeld];
+    double mine = 0.0;
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) {
+        held[k] = 0.0;
+        if (k < P && g0 + k < NS) held[k] = dec_f64(slot_wait(slabs + g0 + k, a.err, enc_f64(0.0)));
+        mine += held[k];
+    }
+    for (int k = kHeld; k < P; ++k)
+        if (g0 + k < NS) mine += dec_f64(slot_wait(slabs + g0 + k, a.err, enc_f64(0.0)));
+
     Decision d = a.dec[b];
     const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
     const double u = (double)a.unif[(size_t)b * (K + 1) + kb];
-    uint64_t* slabs = a.slot_slab + (size_t)b * a.C * kUnroll;
-    const int NS = a.NS;
 
-    // The slab sums, kept in registers for up to kHeld * 64 slabs (read
-    // again from the slots beyond that).
-    constexpr int kHeld = 4;
-    double held[kHeld];
-    double total = 0.0;
-#pragma unroll
-    for (int k = 0; k < kHeld; ++k) {
-        held[k] = 0.0;
-        if (k * 64 + lane < NS) held[k] = dec_f64(slot_wait(slabs + k * 64 + lane, a.err, enc_f64(0.0)));
-        total += held[k];
-    }
-    for (int g0 = kHeld * 64; g0 < NS; g0 += 64)
-        if (g0 + lane < NS) total += dec_f64(slot_wait(slabs + g0 + lane, a.err, enc_f64(0.0)));
-    total = wave_sum(total);
+    double incl = wave_inclusive_scan(mine);
+    double total = __shfl(incl, 63, 64);
     if (!(total > 0.0)) {
-        // Every replacement mass is zero: draw from p_j itself.  Its slab
-        // sums replace the residual ones (rare; one wave streams the row).
+        // Every replacement mass is zero: draw from p_j itself, its slab sums
+        // taking the place of the residual ones (rare; each lane sums its
+        // own slabs).
         d.mode = kBonus;
         rowq = nullptr;
-        for (int g = 0; g < NS; ++g) {
-            double t = 0.0;
-            for (int k = 0; k < kSlabPerLane; ++k) {
-                const int v = g * kSlab + k * 64 + lane;
-                const u32x4 bp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
-                float r[E];
-                final_masses<DT>(bp, bp, d, v, a.sc, r);
-                t += (double)pairwise_sum<E>(r);
-            }
-            t = wave_sum(t);
-            if (lane == 0) slot_put(slabs + g, enc_f64(t));
-        }
-        total = 0.0;
+        mine = 0.0;
 #pragma unroll
         for (int k = 0; k < kHeld; ++k) {
             held[k] = 0.0;
-            if (k * 64 + lane < NS) held[k] = dec_f64(slot_wait(slabs + k * 64 + lane, a.err, enc_f64(0.0)));
-            total += held[k];
+            if (k < P && g0 + k < NS) held[k] = lane_slab_mass<DT, VEC>(a, rowp, d, g0 + k);
+            mine += held[k];
         }
-        for (int g0 = kHeld * 64; g0 < NS; g0 += 64)
-            if (g0 + lane < NS) total += dec_f64(slot_wait(slabs + g0 + lane, a.err, enc_f64(0.0)));
-        total = wave_sum(total);
+        for (int k = kHeld; k < P; ++k)
+            if (g0 + k < NS) {
+                const double t = lane_slab_mass<DT, VEC>(a, rowp, d, g0 + k);
+                slot_put(slabs + g0 + k, enc_f64(t));
+                mine += t;
+            }
+        incl = wave_inclusive_scan(mine);
+        total = __shfl(incl, 63, 64);
     }
     const double w = u * total;
-    double base;
-    const int g = wave_locate(NS, w,
-                              [&](int i) {
-                                  double x = 0.0;
-#pragma unroll
-                                  for (int k = 0; k < kHeld; ++k)
-                                      if ((i >> 6) == k) x = held[k];
-                                  return i < kHeld * 64 ? x : dec_f64(slot_peek(slabs + i));
-                              },
-                              &base);
 
-    // Slab g: vector g * kSlab + k * 64 + lane for k = 0..3, in ascending order.
-    float r[kSlabPerLane][E];
-    double vs[kSlabPerLane];
+    // The lane whose slabs hold w, else the last lane with mass.
+    int L;
+    {
+        const unsigned long long hit = __ballot(w < incl && mine > 0.0);
+        const unsigned long long nz = __ballot(mine > 0.0);
+        L = hit ? __ffsll((long long)hit) - 1 : (nz ? 63 - __clzll((long long)nz) : 0);
+    }
+    // Every lane walks its own slabs; lane L's answer is the one kept.
+    int kk = -1, klast = -1;
+    double kbefore = 0.0, klast_before = 0.0;
+    {
+        double c = incl - mine;
+        auto visit = [&](int k, double x) {
+            if (x > 0.0) {
+                klast = k;
+                klast_before = c;
+            }
+            if (kk < 0 && x > 0.0 && w < c + x) {
+                kk = k;
+                kbefore = c;
+            }
+            c += x;
+        };
 #pragma unroll
-    for (int k = 0; k < kSlabPerLane; ++k) {
-        const int v = g * kSlab + k * 64 + lane;
+        for (int k = 0; k < kHeld; ++k) visit(k, held[k]);
+        for (int k = kHeld; k < P; ++k)
+            if (g0 + k < NS) visit(k, dec_f64(slot_peek(slabs + g0 + k)));
+        if (kk < 0) {
+            kk = max(klast, 0);
+            kbefore = klast_before;
+        }
+    }
+    const int g = __shfl(g0 + kk, L, 64);
+    const double base = __shfl(kbefore, L, 64);
+
+    // Slab g, one vector per lane in ascending order.
+    const int v = g * kSlab + lane;
+    float r[E];
+    {
         const u32x4 sp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
         const u32x4 sq = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : sp;
-        final_masses<DT>(sp, sq, d, v, a.sc, r[k]);
-        vs[k] = (double)pairwise_sum<E>(r[k]);
+        final_masses<DT>(sp, sq, d, v, a.sc, r);
     }
-    double vbase;
-    const int vi = wave_locate(kSlabPerLane * 64, w - base,
-                               [&](int i) {
-                                   double x = 0.0;
-#pragma unroll
-                                   for (int k = 0; k < kSlabPerLane; ++k)
-                                       if ((i >> 6) == k) x = vs[k];
-                                   return x;
-                               },
-                               &vbase);
-    // Lane vi & 63 holds vector vi (k = vi >> 6); scan its elements.
-    int tok = -1;
-    if (lane == (vi & 63)) {
-        const int k = vi >> 6;
-        float rr[E];
+    const double vs = (double)pairwise_sum<E>(r);
+    const double vincl = base + wave_inclusive_scan(vs);
+    int L2;
+    {
+        const unsigned long long hit = __ballot(w < vincl && vs > 0.0);
+        const unsigned long long nz = __ballot(vs > 0.0);
+        L2 = hit ? __ffsll((long long)hit) - 1 : (nz ? 63 - __clzll((long long)nz) : 0);
+    }
+    // Every lane scans its own elements; lane L2's answer is the one kept.
+    int tok = -1, last = -1;
+    {
+        double Cc = vincl - vs;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            float x = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < kSlabPerLane; ++kk)
-                if (kk == k) x = r[kk][e];
-            rr[e] = x;
+            if (r[e] > 0.0f) last = v * E + e;
+            Cc += (double)r[e];
+            if (tok < 0 && r[e] > 0.0f && w < Cc) tok = v * E + e;
         }
-        const int v = g * kSlab + vi;
-        double Cc = base + vbase;
-        int lastpos = -1;
-        for (int e = 0; e < E; ++e) {
-            if (rr[e] > 0.0f) lastpos = v * E + e;
-            Cc += (double)rr[e];
-            if (tok < 0 && w < Cc) tok = v * E + e;
-        }
-        if (tok < 0) tok = lastpos;
+        if (tok < 0) tok = last;
     }
-    tok = __shfl(tok, vi & 63, 64);
+    tok = __shfl(tok, L2, 64);
     if (tok < 0) tok = 0;
     const int j = d.j;
     for (int i = lane; i <= K; i += 64) {
@@ -515,8 +506,8 @@ __global__ __launch_bounds__(kThreads) void verify_decide(VerifyParams a) {
     __shared__ StepShared sh;
     const int b = blockIdx.x;
     const int kb = kb_of(a, b);
-    decide(a, b, kb, sh);
-    publish_decision(a, b, kb, sh);
+    const Decision d = decide(a, b, kb, sh);
+    publish_decision(a, b, kb, d, sh);
 }
 
 // Final items: workgroup (x, y) takes tile x of request y.

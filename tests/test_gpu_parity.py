@@ -133,6 +133,27 @@ def test_verify_ragged_vocab(dtype, V, one_hot):
     compare_verify("V=%d" % V, run_verify(wl), oracle_verify(wl))
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("one_hot", [False, True])
+def test_verify_large_vocab(dtype, one_hot):
+    """A vocabulary of 300007 tokens: in fp32 more than 1024 slabs of 64
+    vectors per row, so the search lanes read part of their slab sums back
+    from the workspace instead of holding them."""
+    rng = np.random.default_rng(300007 + one_hot)
+    B, K, V, T = 8, 3, 300007, 0.8
+    lt = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    ld = (lt[:, :K] + rng.standard_normal((B, K, V)) * 0.5).astype(np.float32)
+    if dtype == "bf16":
+        lt, ld = workloads.bf16_bits(lt), workloads.bf16_bits(ld)
+    vals = workloads.stored_as_f32(ld)
+    toks = np.stack([workloads.gumbel_draw(vals[:, i], T, rng) for i in range(K)], axis=1)
+    uni = rng.random((B, K + 1), dtype=np.float32)
+    wl = workloads.Workload("adhoc", B, K, V, dtype, T, False, lt, None if one_hot else ld,
+                            toks.astype(np.int32), uni)
+    nf, nd = compare_verify("V=%d" % V, run_verify(wl), oracle_verify(wl))
+    assert nd == 0
+
+
 def test_verify_misaligned_pointers():
     """Rows that do not start on a 16-byte boundary take the element-wise
     load path."""
