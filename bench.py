@@ -232,7 +232,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
                      "launch_ms": round(per_launch_ms, 5),
-                     "kernel": "specdec_verify call (all its kernels: verify_rows, [verify_decide,] verify_final, verify_search)"},
+                     "kernel": "specdec_verify call (all its kernels: verify_rows, [verify_decide,] verify_final)"},
         "cpu_baseline": None,
     }
     if args.calibration_copy > 0:

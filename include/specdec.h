@@ -36,13 +36,15 @@
  *     *_workspace_bytes() function returns, 256-byte aligned.  The first 4
  *     bytes hold error bits: a call ORs in a bit when an internal bounded
  *     wait gives up (never in a correct run).  specdec_verify and
- *     specdec_softmax_stats write every other scratch word before they read
- *     it, so their workspace needs no initialisation.  specdec_verify_greedy
- *     hands partial results between workgroups of one kernel through slots
- *     that must read zero when the call starts: zero-fill its workspace once
- *     with specdec_workspace_init before the first call; every call leaves
- *     the slots it used at zero again.  specdec_workspace_init also clears
- *     the error bits.  Calls that may run concurrently need distinct
+ *     specdec_softmax_stats set every other scratch word they read earlier
+ *     in the same call, so their workspace needs no initialisation and may
+ *     hold anything.  specdec_verify_greedy hands partial results between
+ *     workgroups of one kernel through slots that must read zero when the
+ *     call starts: zero-fill its workspace with specdec_workspace_init before
+ *     the first call, and again after any other entry point has used it
+ *     (those leave non-zero scratch behind); every greedy call leaves the
+ *     slots it used at zero again.  specdec_workspace_init also clears the
+ *     error bits.  Calls that may run concurrently need distinct
  *     workspaces.
  *   - Preconditions not checked on the fast path (a violation gives
  *     unspecified tokens, never an out-of-bounds access): logits finite or

@@ -115,7 +115,10 @@ def _stream(device: torch.device) -> int:
 class Workspace:
     """Device scratch for the library, zero-filled when allocated: the error
     word at offset 0 starts clear and the greedy path's slots start empty
-    (each greedy call leaves them empty again)."""
+    (each greedy call leaves them empty again).  A workspace handed to
+    verify_greedy must not be used by the other entry points in between:
+    they leave non-zero scratch behind.  The workspaces this module caches
+    are kept per device, stream and entry point for that reason."""
 
     def __init__(self, nbytes: int, device):
         self.nbytes = int(nbytes)
@@ -126,12 +129,12 @@ class Workspace:
         return self.tensor.data_ptr()
 
 
-def _workspace(nbytes: int, device: torch.device, ws: Optional[Workspace]) -> Workspace:
+def _workspace(nbytes: int, device: torch.device, ws: Optional[Workspace], kind: str) -> Workspace:
     if ws is not None:
         if ws.nbytes < nbytes or ws.device != device:
             raise ValueError("workspace too small (%d < %d) or on the wrong device" % (ws.nbytes, nbytes))
         return ws
-    key = (device.index, _stream(device))
+    key = (device.index, _stream(device), kind)
     cur = _workspaces.get(key)
     if cur is None or cur.nbytes < nbytes:
         cur = Workspace(nbytes, device)
@@ -179,7 +182,7 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
         if ap is not None:
             _check(ap, "accept_prob", torch.float32, (B, K), dev)
     nbytes = verify_workspace_bytes(B, K, V, code, draft is None)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, "verify")
     rc = lib.specdec_verify(_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(k_per_req),
                             _ptr(uniforms), float(temperature), B, K, V, _ptr(out_tokens),
                             _ptr(nacc), _ptr(ap), ws.ptr(), ws.nbytes, _stream(dev))
@@ -211,7 +214,7 @@ def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
     else:
         out_tokens, nacc, am = out
     nbytes = int(lib.specdec_verify_greedy_workspace_bytes(B, K, V, code))
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, "greedy")
     rc = lib.specdec_verify_greedy(_ptr(target), code, _ptr(draft_tokens), _ptr(k_per_req), B, K, V,
                                    _ptr(out_tokens), _ptr(nacc), _ptr(am), ws.ptr(), ws.nbytes,
                                    _stream(dev))
@@ -235,7 +238,7 @@ def softmax_stats(logits: torch.Tensor, temperature: float, workspace: Optional[
     rmax = torch.empty(logits.shape[:-1], dtype=torch.float32, device=dev)
     rsum = torch.empty(logits.shape[:-1], dtype=torch.float32, device=dev)
     nbytes = int(lib.specdec_softmax_stats_workspace_bytes(rows, V, code))
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, "stats")
     rc = lib.specdec_softmax_stats(_ptr(logits), code, rows, V, float(temperature), _ptr(rmax),
                                    _ptr(rsum), ws.ptr(), ws.nbytes, _stream(dev))
     if rc != 0:

@@ -1,12 +1,12 @@
-// Stochastic verify step on gfx950: three stream-ordered kernels, one
-// workgroup per work item, and no waits inside any of them.
+// Stochastic verify step on gfx950: two stream-ordered kernels (three for
+// long rows of many positions), one workgroup per work item.
 //
 //  verify_rows    row item (request b, row, tile): tile max and sum of
 //                 exponentials of target row i <= k_b or draft row i < k_b
 //                 ("3.5 Speculative Decoding", "Notation": p and q are the
 //                 temperature-processed distributions), and the logit at the
 //                 draft token x_i when it lies in the tile.  Rows past k_b are
-//                 skipped.
+//                 skipped.  Row 0 also empties the slab slots of the call.
 //  verify_final   final item (request b, tile): the decision of request b --
 //                 the tile partials of every row merged, u_i < min(1,
 //                 p_i(x_i)/q_i(x_i)) tested for every drafted position, the
@@ -14,15 +14,17 @@
 //                 step)", step 3) -- then the tile's slab sums of the
 //                 unnormalised replacement masses max(0, p_j - q_j), or of
 //                 p_{k_b} when every draft was accepted (step 4).  Tile 0
-//                 stores the decision and the accept probabilities.  For
-//                 long rows of many positions the decision is instead taken
-//                 once per request by verify_decide, launched before it.
-//  verify_search  one wave per request: the slab that holds u * S, a re-read
-//                 of that one slab, the smallest token t with u * S < C_t,
-//                 and the outputs.
+//                 stores the accept probabilities.  The request's last tile
+//                 then searches with one wave: the slab that holds u * S, a
+//                 re-read of that one slab, the smallest token t with
+//                 u * S < C_t, and the outputs; it empties the slab slots
+//                 again.  For long rows of many positions the decision is
+//                 instead taken once per request by verify_decide, launched
+//                 before it.
 //
-// Each kernel reads only what the kernels before it wrote; the slots keep
-// their self-validating encoding (slots.h) as a guard.
+// Only the search waits inside a kernel, on the slab slots of its own
+// request's other tiles (self-validating, slots.h); everything else reads
+// what earlier kernels wrote.
 //
 // Masses are kept unnormalised: the replacement is Z_p * max(0, p - q) =
 // max(0, e_p - (Z_p/Z_q) e_q) with e = exp2(x * c - M) against each row's
@@ -273,14 +275,18 @@ __device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* 
         slot_put(a.slot_s + idx, enc_f64(z));
         slot_put(a.slot_m + idx, enc_f32(m));
     }
+    // Row 0 (always read) empties the tile's slab slots for the final kernel.
+    if (rr == 0 && threadIdx.x < kSlabsPerTile)
+        slot_put(a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile + threadIdx.x, (uint64_t)0);
 }
 
 // Slab sums of one tile: slab u * kWaves + w of the tile holds the 64
 // vectors that wave w loaded in unroll step u, summed by that wave; the
-// tile's sums leave in one batch of stores.
+// tile's first nslabs sums (the slabs that start inside the row) leave in
+// one batch of stores.
 template <int DT>
 __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], const u32x4 (&rq)[kUnroll],
-                          const Decision& d, int v0, uint64_t* slabs_of_tile, StepShared& sh) {
+                          const Decision& d, int v0, uint64_t* slabs_of_tile, int nslabs, StepShared& sh) {
     constexpr int E = Elem<DT>::E;
     const int w = threadIdx.x >> 6;
 #pragma unroll
@@ -291,18 +297,20 @@ __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], con
         if ((threadIdx.x & 63) == 0) sh.slab[u * kWaves + w] = t;
     }
     __syncthreads();
-    if (threadIdx.x < kSlabsPerTile) slot_put(slabs_of_tile + threadIdx.x, enc_f64(sh.slab[threadIdx.x]));
+    if (threadIdx.x < nslabs) slot_put(slabs_of_tile + threadIdx.x, enc_f64(sh.slab[threadIdx.x]));
 }
 
-// The decision of request b for the search kernel, and the accept
-// probabilities.
-__device__ void publish_decision(const VerifyParams& a, int b, int kb, const Decision& d,
-                                 const StepShared& sh) {
-    if (threadIdx.x == 0) a.dec[b] = d;
+// The accept probabilities of request b.
+__device__ void publish_aprob(const VerifyParams& a, int b, int kb, const StepShared& sh) {
     if (a.aprob)
         for (int i = threadIdx.x; i < a.K; i += kThreads)
             a.aprob[(size_t)b * a.K + i] = (i < kb) ? sh.ratio[i] : -1.0f;
 }
+
+constexpr int kSearchLanes = 64;
+
+template <int DT, bool VEC>
+__device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d);
 
 // ---------------------------------------------------------------------------
 // Final item: tile `tile` of the final row (pair) of request b.
@@ -324,13 +332,19 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
         rp[u] = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
         rq[u] = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : neg_inf_raw<DT>();
     }
-    put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile, sh);
-    if (tile == 0 && !decided) publish_decision(a, b, kb, d, sh);
+    put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile,
+                  min(kSlabsPerTile, a.NS - tile * kSlabsPerTile), sh);
+    if (tile == 0 && !decided) publish_aprob(a, b, kb, sh);
+    // The request's last tile -- dispatched after its other tiles, which
+    // never wait -- searches, with its first wave, once every slab sum of
+    // the request is in.
+    if (tile == a.C - 1 && threadIdx.x < kSearchLanes) search_wave<DT, VEC>(a, b, kb, d);
 }
 
 
 // ---------------------------------------------------------------------------
-// Token search of request b, by one wave (no workgroup barriers).
+// Token search of request b, by the first wave of its last final tile (no
+// workgroup barriers; the other waves have left).
 //
 // Slab g covers vectors [64 g, 64 g + 64).  Lane L owns the P = ceil(NS/64)
 // consecutive slabs from L * P: one inclusive scan of the lanes' sums gives S
@@ -342,7 +356,6 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
 // every C_t).  Only entries with mass can be taken at any level, so a token
 // of zero probability is never drawn, however the sums round.
 // ---------------------------------------------------------------------------
-constexpr int kSearchLanes = 64;
 constexpr int kHeld = 16;   // slab sums per lane kept in registers
 
 // Unnormalised mass of slab g of the final row, summed by one lane alone
@@ -362,12 +375,11 @@ __device__ double lane_slab_mass(const VerifyParams& a, const void* rowp, const 
 }
 
 template <int DT, bool VEC>
-__device__ void search(const VerifyParams& a, int b) {
+__device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     constexpr int E = Elem<DT>::E;
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
-    const int lane = threadIdx.x;
-    const int kb = kb_of(a, b);
+    const int lane = threadIdx.x & 63;
     const int NS = a.NS;
     const int P = (NS + 63) >> 6;             // slabs per lane
     const int g0 = lane * P;                  // this lane's first slab
@@ -386,7 +398,6 @@ __device__ void search(const VerifyParams& a, int b) {
     for (int k = kHeld; k < P; ++k)
         if (g0 + k < NS) mine += dec_f64(slot_wait(slabs + g0 + k, a.err, enc_f64(0.0)));
 
-    Decision d = a.dec[b];
     const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
     const double u = (double)a.unif[(size_t)b * (K + 1) + kb];
@@ -451,6 +462,8 @@ __device__ void search(const VerifyParams& a, int b) {
     }
     const int g = __shfl(g0 + kk, L, 64);
     const double base = __shfl(kbefore, L, 64);
+    // Every slab sum has been read: empty this lane's slots for the next call.
+    for (int k = 0; k < P && g0 + k < NS; ++k) slot_put(slabs + g0 + k, (uint64_t)0);
 
     // Slab g, one vector per lane in ascending order.
     const int v = g * kSlab + lane;
@@ -507,7 +520,8 @@ __global__ __launch_bounds__(kThreads) void verify_decide(VerifyParams a) {
     const int b = blockIdx.x;
     const int kb = kb_of(a, b);
     const Decision d = decide(a, b, kb, sh);
-    publish_decision(a, b, kb, d, sh);
+    if (threadIdx.x == 0) a.dec[b] = d;
+    publish_aprob(a, b, kb, sh);
 }
 
 // Final items: workgroup (x, y) takes tile x of request y.
@@ -515,12 +529,6 @@ template <int DT, bool VEC, bool DECIDED>
 __global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
     __shared__ StepShared sh;
     final_item<DT, VEC>(a, blockIdx.y, blockIdx.x, DECIDED, sh);
-}
-
-// Token search: one wave per request.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kSearchLanes) void verify_search(VerifyParams a) {
-    search<DT, VEC>(a, blockIdx.x);
 }
 
 template <int DT, bool VEC>
@@ -535,7 +543,6 @@ hipError_t launch(const VerifyParams& p, hipStream_t s) {
     } else {
         hipLaunchKernelGGL((verify_final<DT, VEC, false>), dim3(p.C, p.B), dim3(kThreads), 0, s, p);
     }
-    hipLaunchKernelGGL((verify_search<DT, VEC>), dim3(p.B), dim3(kSearchLanes), 0, s, p);
     return hipGetLastError();
 }
 

@@ -243,6 +243,49 @@ def test_verify_deterministic_and_reusable_workspace():
         compare_verify("small", call(small), ref_small)
 
 
+def test_verify_workspace_needs_no_initialisation():
+    """A workspace full of random bytes (error word aside) gives the same
+    results: every scratch word is set before it is read in the same call."""
+    import speculative_decoding_verification_10_amd as sd
+    from tests.gpu_util import to_device
+    wl = workloads.make("peaked", set_index=2, B=6, V=9000)
+    ref = oracle_verify(wl)
+    ws = sd.Workspace(sd._lib.verify_workspace_bytes(wl.B, wl.K, wl.V, 1, False), "cuda")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    for _ in range(3):
+        ws.tensor.random_(0, 256, generator=g)
+        ws.tensor[:4] = 0
+        d = to_device(wl)
+        res = sd.verify(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], wl.temperature,
+                        accept_prob=True, workspace=ws)
+        assert_workspace_clean(ws)
+        nf, nd = compare_verify("garbage workspace", res, ref)
+        assert nd == 0
+
+
+def test_default_workspaces_across_entry_points():
+    """verify, softmax_stats and verify_greedy called in turn on one stream
+    with the module's cached workspaces."""
+    import speculative_decoding_verification_10_amd as sd
+    from tests.gpu_util import to_device
+    wl = workloads.make("peaked", set_index=0, B=5, V=7000)
+    gw = workloads.make("greedy", set_index=0, B=7, V=7000)
+    ref = oracle_verify(wl)
+    gref = oracle.verify_greedy(gw.target, gw.draft_tokens)
+    d = to_device(wl)
+    t = dev_logits(gw.target)
+    for _ in range(3):
+        res = sd.verify(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], wl.temperature,
+                        accept_prob=True)
+        torch.cuda.synchronize()
+        assert compare_verify("cached", res, ref)[1] == 0
+        sd.softmax_stats(d["target"].view(-1, wl.V), wl.temperature)
+        out, nacc, _ = sd.verify_greedy(t, torch.from_numpy(gw.draft_tokens).cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), gref["out_tokens"])
+        assert np.array_equal(nacc.cpu().numpy(), gref["num_accepted"])
+
+
 # ---------------------------------------------------------------------------
 # Greedy verify
 # ---------------------------------------------------------------------------
