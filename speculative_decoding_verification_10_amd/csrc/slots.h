@@ -17,8 +17,9 @@
 // the workspace header and continues with a harmless value, so every wave
 // always exits.
 //
-// A slot must read zero before its producer runs: the kernel that precedes
-// the producers in stream order clears it.
+// A slot must read zero before its producer runs: an earlier kernel of the
+// same call empties it, or the consumer of the previous call did, after its
+// wait.
 #pragma once
 
 #include <hip/hip_runtime.h>
