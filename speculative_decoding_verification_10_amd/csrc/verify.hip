@@ -140,8 +140,8 @@ __device__ Decision decide(const VerifyParams& a, int b, int kb, StepShared& sh)
     uint32_t rl = 0, rd = 0;
     float u = 0.0f;
     if (t < kb) {
-        rl = slot_peek(a.slot_l + (size_t)b * R + t);
-        if (!one_hot) rd = slot_peek(a.slot_l + (size_t)b * R + K + 1 + t);
+        rl = a.slot_l[(size_t)b * R + t];
+        if (!one_hot) rd = a.slot_l[(size_t)b * R + K + 1 + t];
         u = a.unif[(size_t)b * (K + 1) + t];
     }
     for (int base = 0; base < nrs; base += kRowsPerPass) {
@@ -156,6 +156,8 @@ __device__ Decision decide(const VerifyParams& a, int b, int kb, StepShared& sh)
             rs[g] = base + g * (kWaves * 4) + w * 4 + (lane >> 4);
             row0[g] = ((size_t)b * R + slot_of_rs(min(rs[g], nrs - 1), kb, K)) * C;
         }
+        // Groups and tile batches wholly past the end are skipped by the
+        // whole workgroup (the conditions are uniform).
         for (int c0 = 0; c0 < C; c0 += 16 * kTilesPerLoad) {
             uint32_t um[kRowGroups][kTilesPerLoad];
             uint64_t us[kRowGroups][kTilesPerLoad];
@@ -166,16 +168,18 @@ __device__ Decision decide(const VerifyParams& a, int b, int kb, StepShared& sh)
                     const int c = c0 + sub + 16 * q;
                     um[g][q] = 0;
                     us[g][q] = 0;
-                    if (rs[g] < nrs && c < C) {
-                        um[g][q] = slot_peek(a.slot_m + row0[g] + c);
-                        us[g][q] = slot_peek(a.slot_s + row0[g] + c);
+                    if (base + g * (kWaves * 4) < nrs && c0 + 16 * q < C && rs[g] < nrs && c < C) {
+                        um[g][q] = a.slot_m[row0[g] + c];
+                        us[g][q] = a.slot_s[row0[g] + c];
                     }
                 }
             }
 #pragma unroll
             for (int g = 0; g < kRowGroups; ++g) {
+                if (base + g * (kWaves * 4) >= nrs) continue;
 #pragma unroll
                 for (int q = 0; q < kTilesPerLoad; ++q) {
+                    if (c0 + 16 * q >= C) continue;
                     const int c = c0 + sub + 16 * q;
                     if (rs[g] < nrs && c < C) merge2(lm[g], ls[g], dec_f32(um[g][q]), dec_f64(us[g][q]), a.sc);
                 }
@@ -183,6 +187,7 @@ __device__ Decision decide(const VerifyParams& a, int b, int kb, StepShared& sh)
         }
 #pragma unroll
         for (int g = 0; g < kRowGroups; ++g) {
+            if (base + g * (kWaves * 4) >= nrs) continue;
             const float rmax = row16_max(lm[g]);
             double scaled = 0.0;
             if (lm[g] != -INFINITY)
