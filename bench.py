@@ -11,8 +11,10 @@ exceeds the 256 MB Infinity Cache and every step streams its logits from HBM.
 
 Prints one JSON line: verified positions/s (sum over requests of k_b + 1 per
 step), the algorithmic HBM bytes per step and their rate against the MI355X
-peak (8 TB/s), the dominant kernel's roofline, and the fp64 CPU oracle timed
-on the host cores on a bounded sample of the same workload.
+peak (8 TB/s), the roofline of the dominant kernel (the row pass,
+verify_rows, timed with events the library records around it inside each
+call), the same for the whole call (call_roofline), and the fp64 CPU oracle
+timed on the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -28,8 +30,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "verified positions/s + HBM GB/s (% of peak), B=64 k=5 V=128256 bf16"
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "verify_headline_counters.txt")
-KERNEL_SOURCES = ["device_common.h", "internal.h", "slots.h", "verify.hip"]
+PROFILE_COUNTERS = {"headline": os.path.join(ROOT, "profiles", "verify_headline_counters.txt"),
+                    "greedy": os.path.join(ROOT, "profiles", "verify_greedy_counters.txt")}
+KERNEL_SOURCES = ["device_common.h", "internal.h", "slots.h", "verify.hip", "greedy.hip"]
 
 
 def kernel_digest() -> str:
@@ -54,14 +57,26 @@ def algorithmic_bytes(wl, num_accepted) -> int:
     return (rows + reread) * wl.V * s + small
 
 
-def read_counters():
+def row_pass_bytes(wl) -> int:
+    """Bytes the row pass (verify_rows) must move: every target row i <= k_b
+    and draft row i < k_b once (V elements each), plus the draft ids it
+    gathers at."""
+    import numpy as np
+    s = 2 if wl.dtype == "bf16" else 4
+    k = np.full(wl.B, wl.K) if wl.k_per_req is None else wl.k_per_req.astype(np.int64)
+    rows = int(np.sum(k + 1)) + (int(np.sum(k)) if wl.draft is not None else 0)
+    return rows * wl.V * s + int(np.sum(k)) * 4
+
+
+def read_counters(workload, key):
     """Per-launch HBM bytes measured with rocprofv3 (FETCH_SIZE + WRITE_SIZE,
-    scaled by a copy-kernel calibration), if the stored summary was taken on
-    the current kernel sources."""
-    if not os.path.exists(PROFILE_COUNTERS):
+    scaled by a copy-kernel calibration) for the workloads whose counters are
+    stored, if the stored summary was taken on the current kernel sources."""
+    path = PROFILE_COUNTERS.get(workload)
+    if path is None or not os.path.exists(path):
         return None
     vals = {}
-    with open(PROFILE_COUNTERS) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -69,7 +84,7 @@ def read_counters():
     if vals.get("kernel_digest") != kernel_digest():
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -104,6 +119,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each call from a captured HIP graph")
+    ap.add_argument("--no-phase-events", action="store_true",
+                    help="time whole calls only (no events recorded inside specdec_verify)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a MIB-MiB device buffer 10 times (a plain copy "
                          "of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -153,24 +170,58 @@ def main():
         nbytes = sd._lib.verify_workspace_bytes(wl.B, K, wl.V, code, wl.draft is None)
     ws = sd.Workspace(nbytes, dev)
 
-    def step(r):
-        s = sets[r % len(sets)]
+    # The row pass is timed inside each stochastic call by events that its
+    # kernel dispatches take themselves (specdec_verify_timed).
+    phase = not args.graph and not args.no_phase_events
+    phase_ev = None
+    handles = None
+
+    # The timed steps call the C ABI directly with argument lists built once
+    # (the binding's per-call checks cost more host time than the GPU work of
+    # small calls); the first warm-up call goes through the checked binding.
+    import ctypes
+    lib = sd._lib.load()
+    stream = torch.cuda.current_stream(dev)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    cargs = []
+    for st in sets:
         if greedy:
-            sd.verify_greedy(s["target"], tokens, k_per_req=kpr, workspace=ws, out=out)
+            cargs.append((st["target"].data_ptr(), code, tokens.data_ptr(), ptr(kpr), wl.B, K, wl.V,
+                          out[0].data_ptr(), out[1].data_ptr(), None, ws.ptr(), ws.nbytes,
+                          stream.cuda_stream))
         else:
-            sd.verify(s["target"], s["draft"], tokens, unif, wl.temperature, k_per_req=kpr,
+            cargs.append((st["target"].data_ptr(), ptr(st["draft"]), code, tokens.data_ptr(), ptr(kpr),
+                          unif.data_ptr(), float(wl.temperature), wl.B, K, wl.V, out[0].data_ptr(),
+                          out[1].data_ptr(), None, ws.ptr(), ws.nbytes, stream.cuda_stream))
+
+    def step(r):
+        a = cargs[r % len(cargs)]
+        if handles is not None:
+            rc = (lib.specdec_verify_greedy_timed if greedy else lib.specdec_verify_timed)(*a, handles[r])
+        else:
+            rc = (lib.specdec_verify_greedy if greedy else lib.specdec_verify)(*a)
+        if rc != 0:
+            raise sd.SpecdecError(rc, "bench step")
+
+    def checked_step(r):
+        st = sets[r % len(sets)]
+        if greedy:
+            sd.verify_greedy(st["target"], tokens, k_per_req=kpr, workspace=ws, out=out)
+        else:
+            sd.verify(st["target"], st["draft"], tokens, unif, wl.temperature, k_per_req=kpr,
                       workspace=ws, out=out)
 
-    stream = torch.cuda.current_stream(dev)
+    checked_step(0)
     graphs = None
     if args.graph:
+        # Captured through the binding, which launches on the capture stream.
         graphs = []
         for r in range(len(sets)):
-            step(r)
+            checked_step(r)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(r)
+                checked_step(r)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -185,25 +236,65 @@ def main():
     torch.cuda.synchronize()
     nacc = out[1].cpu().numpy()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    if phase:
+        nev = 2 if greedy else 3
+        phase_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+        for evs in phase_ev:          # torch creates an event at its first record
+            for e in evs:
+                e.record(stream)
+        handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in evs]) for evs in phase_ev]
+        starts = ends = None
+    else:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in range(args.steps):
-        starts[r].record(stream)
+        if starts is not None:
+            starts[r].record(stream)
         run(r)
-        ends[r].record(stream)
+        if ends is not None:
+            ends[r].record(stream)
+    host = time.perf_counter() - t0       # time to enqueue the steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = float(np.median([s.elapsed_time(e) for s, e in zip(starts, ends)]))
     ms_per_step = wall * 1e3 / args.steps
+    rows_ms = None
+    if phase:
+        rows_ms = float(np.median([e[0].elapsed_time(e[1]) for e in phase_ev]))
+        call_ms = float(np.median([e[0].elapsed_time(e[-1]) for e in phase_ev]))
+        per_launch_ms = call_ms
+    else:
+        per_launch_ms = float(np.median([s.elapsed_time(e) for s, e in zip(starts, ends)]))
 
     positions = wl.verified_positions()
     alg = algorithmic_bytes(wl, nacc)
     value = positions / (ms_per_step * 1e-3)
     gbps = alg / (ms_per_step * 1e-3) / 1e9
     achieved = alg / (per_launch_ms * 1e-3) / 1e9
-    traffic = read_counters()
+    if phase and not greedy:
+        # The dominant kernel: the row pass, which moves ~85% of the bytes.
+        rb = row_pass_bytes(wl)
+        rows_gbps = rb / (rows_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(rows_gbps, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(rows_gbps / PEAK_HBM_GBPS, 4),
+                    "traffic": read_counters(args.workload, "verify_rows_hbm_bytes_per_launch"),
+                    "kernel": "verify_rows", "algorithmic_bytes": rb,
+                    "launch_ms": round(rows_ms, 5)}
+        call = {"achieved": round(alg / (call_ms * 1e-3) / 1e9, 1),
+                "frac": round(alg / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                "traffic": read_counters(args.workload, "hbm_bytes_per_launch"), "algorithmic_bytes": alg,
+                "launch_ms": round(call_ms, 5),
+                "kernels": "verify_rows, [verify_decide,] verify_final"}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                    "traffic": read_counters(args.workload, "greedy_rows_hbm_bytes_per_launch" if greedy
+                                             else "hbm_bytes_per_launch"),
+                    "kernel": ("greedy_rows" if greedy else
+                               "specdec_verify call (verify_rows, [verify_decide,] verify_final)"),
+                    "algorithmic_bytes": alg, "launch_ms": round(per_launch_ms, 5)}
+        call = None
     metric = METRIC if args.workload == "headline" else (
         "verified positions/s + HBM GB/s (%% of peak), %s B=%d k=%d V=%d %s"
         % (args.workload, wl.B, K, wl.V, wl.dtype))
@@ -215,6 +306,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "host_enqueue_ms_per_step": round(host * 1e3 / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -228,13 +320,11 @@ def main():
         "hbm_pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "algorithmic_bytes_per_step": alg,
         "rejected_requests": int(np.sum(nacc < (wl.K if wl.k_per_req is None else wl.k_per_req))),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic,
-                     "launch_ms": round(per_launch_ms, 5),
-                     "kernel": "specdec_verify call (all its kernels: verify_rows, [verify_decide,] verify_final)"},
+        "roofline": roofline,
         "cpu_baseline": None,
     }
+    if call is not None:
+        line["call_roofline"] = call
     if args.calibration_copy > 0:
         n = args.calibration_copy << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -134,6 +134,26 @@ int specdec_verify(const void *target_logits, const void *draft_logits, specdec_
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * specdec_verify with per-phase timing, for telemetry and benchmarks: the
+ * same operation, arguments and results, and in addition the caller's HIP
+ * events (hipEvent_t, created by the caller, owned by the caller), taken by
+ * the kernel dispatches themselves on `stream` (no separate marker):
+ *   events[0]  the start of the row-statistics kernel (the pass that reads
+ *              every target and draft row once),
+ *   events[1]  its end,
+ *   events[2]  the end of the call's last kernel.
+ * `events` may be NULL and any entry may be NULL (not recorded).
+ * hipEventElapsedTime(events[0], events[1]) is then the row kernel's own
+ * duration.  Nothing is recorded when B = 0 or the arguments are rejected.
+ */
+int specdec_verify_timed(const void *target_logits, const void *draft_logits,
+                         specdec_dtype_t dtype, const int32_t *draft_tokens,
+                         const int32_t *k_per_req, const float *uniforms, float temperature,
+                         int32_t B, int32_t K, int32_t V, int32_t *out_tokens,
+                         int32_t *num_accepted, float *accept_prob, void *workspace,
+                         size_t workspace_bytes, void *stream, void *const *events);
+
+/*
  * Greedy verify step: a_i = argmax_t target_logits[b, i, t] (lowest id on
  * ties); j = first i < k_b with draft_tokens[b, i] != a_i, else k_b;
  * out_tokens[b] = drafts 0..j-1, then a_j, then -1; num_accepted[b] = j.
@@ -150,6 +170,20 @@ int specdec_verify_greedy(const void *target_logits, specdec_dtype_t dtype,
                           int32_t B, int32_t K, int32_t V,
                           int32_t *out_tokens, int32_t *num_accepted, int32_t *argmax_out,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * specdec_verify_greedy with the duration of its one kernel, for telemetry
+ * and benchmarks: the same operation, arguments and results; events[0] and
+ * events[1] (hipEvent_t, caller-created and caller-owned; `events` or either
+ * entry may be NULL) are taken by the kernel's dispatch at its start and
+ * end on `stream`.  Nothing is recorded when B = 0 or the arguments are
+ * rejected.
+ */
+int specdec_verify_greedy_timed(const void *target_logits, specdec_dtype_t dtype,
+                                const int32_t *draft_tokens, const int32_t *k_per_req,
+                                int32_t B, int32_t K, int32_t V, int32_t *out_tokens,
+                                int32_t *num_accepted, int32_t *argmax_out, void *workspace,
+                                size_t workspace_bytes, void *stream, void *const *events);
 
 #ifdef __cplusplus
 }

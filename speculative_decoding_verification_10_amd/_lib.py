@@ -65,11 +65,17 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.specdec_verify.argtypes = [vp, vp, ci, vp, vp, vp, f32, i32, i32, i32,
                                        vp, vp, vp, vp, sz, vp]
         lib.specdec_verify.restype = ci
+        lib.specdec_verify_timed.argtypes = [vp, vp, ci, vp, vp, vp, f32, i32, i32, i32,
+                                             vp, vp, vp, vp, sz, vp, vp]
+        lib.specdec_verify_timed.restype = ci
         lib.specdec_verify_greedy_workspace_bytes.argtypes = [i32, i32, i32, ci]
         lib.specdec_verify_greedy_workspace_bytes.restype = sz
         lib.specdec_verify_greedy.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, vp,
                                               vp, sz, vp]
         lib.specdec_verify_greedy.restype = ci
+        lib.specdec_verify_greedy_timed.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, vp,
+                                                    vp, sz, vp, vp]
+        lib.specdec_verify_greedy_timed.restype = ci
         _lib = lib
         return lib
 
@@ -148,14 +154,18 @@ def verify_workspace_bytes(B, K, V, dtype_code, one_hot) -> int:
 
 def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
            uniforms: torch.Tensor, temperature: float, k_per_req: Optional[torch.Tensor] = None,
-           accept_prob: bool = False, workspace: Optional[Workspace] = None, out=None):
+           accept_prob: bool = False, workspace: Optional[Workspace] = None, out=None,
+           events=None):
     """Stochastic verify step (specdec_verify).
 
     target [B, K+1, V], draft [B, K, V] or None (one-hot drafts), both fp32 or
     bf16; draft_tokens [B, K] int32; uniforms [B, K+1] fp32; k_per_req [B]
     int32 or None.  Returns (out_tokens [B, K+1], num_accepted [B],
     accept_prob [B, K] or None).  ``out`` may hold preallocated
-    (out_tokens, num_accepted, accept_prob) tensors.
+    (out_tokens, num_accepted, accept_prob) tensors.  ``events``: three
+    torch.cuda.Event (enable_timing=True) or None entries, taken at the row
+    kernel's start, its end and the end of the call's last kernel
+    (specdec_verify_timed).
     """
     lib = load()
     if target.dim() != 3:
@@ -183,19 +193,48 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
             _check(ap, "accept_prob", torch.float32, (B, K), dev)
     nbytes = verify_workspace_bytes(B, K, V, code, draft is None)
     ws = _workspace(nbytes, dev, workspace, "verify")
-    rc = lib.specdec_verify(_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(k_per_req),
-                            _ptr(uniforms), float(temperature), B, K, V, _ptr(out_tokens),
-                            _ptr(nacc), _ptr(ap), ws.ptr(), ws.nbytes, _stream(dev))
+    if events is None:
+        rc = lib.specdec_verify(_ptr(target), _ptr(draft), code, _ptr(draft_tokens),
+                                _ptr(k_per_req), _ptr(uniforms), float(temperature), B, K, V,
+                                _ptr(out_tokens), _ptr(nacc), _ptr(ap), ws.ptr(), ws.nbytes,
+                                _stream(dev))
+        what = "specdec_verify"
+    else:
+        if len(events) != 3:
+            raise ValueError("events must hold three entries")
+        handles = (ctypes.c_void_p * 3)(*[_event_handle(e, dev) for e in events])
+        rc = lib.specdec_verify_timed(_ptr(target), _ptr(draft), code, _ptr(draft_tokens),
+                                      _ptr(k_per_req), _ptr(uniforms), float(temperature), B, K,
+                                      V, _ptr(out_tokens), _ptr(nacc), _ptr(ap), ws.ptr(),
+                                      ws.nbytes, _stream(dev), handles)
+        what = "specdec_verify_timed"
     if rc != 0:
-        raise SpecdecError(rc, "specdec_verify")
+        raise SpecdecError(rc, what)
     return out_tokens, nacc, ap
+
+
+def _event_handle(ev, device: torch.device):
+    """The hipEvent_t of a torch.cuda.Event (None -> NULL).  torch creates the
+    event lazily at its first record, so an event never recorded is recorded
+    once on the current stream first."""
+    if ev is None:
+        return None
+    h = int(ev.cuda_event)
+    if h == 0:
+        ev.record(torch.cuda.current_stream(device))
+        h = int(ev.cuda_event)
+    if h == 0:
+        raise ValueError("could not obtain the event's handle")
+    return h
 
 
 def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
                   k_per_req: Optional[torch.Tensor] = None, argmax: bool = False,
-                  workspace: Optional[Workspace] = None, out=None):
+                  workspace: Optional[Workspace] = None, out=None, events=None):
     """Greedy verify step (specdec_verify_greedy).  Returns (out_tokens,
-    num_accepted, argmax [B, K+1] or None)."""
+    num_accepted, argmax [B, K+1] or None).  ``events``: two
+    torch.cuda.Event (enable_timing=True) or None entries, taken at the
+    kernel's start and end (specdec_verify_greedy_timed)."""
     lib = load()
     if target.dim() != 3:
         raise ValueError("target must be [B, K+1, V]")
@@ -213,13 +252,25 @@ def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
         am = torch.empty((B, K + 1), dtype=torch.int32, device=dev) if argmax else None
     else:
         out_tokens, nacc, am = out
+        _check(out_tokens, "out_tokens", torch.int32, (B, K + 1), dev)
+        _check(nacc, "num_accepted", torch.int32, (B,), dev)
+        if am is not None:
+            _check(am, "argmax", torch.int32, (B, K + 1), dev)
     nbytes = int(lib.specdec_verify_greedy_workspace_bytes(B, K, V, code))
     ws = _workspace(nbytes, dev, workspace, "greedy")
-    rc = lib.specdec_verify_greedy(_ptr(target), code, _ptr(draft_tokens), _ptr(k_per_req), B, K, V,
-                                   _ptr(out_tokens), _ptr(nacc), _ptr(am), ws.ptr(), ws.nbytes,
-                                   _stream(dev))
+    args = (_ptr(target), code, _ptr(draft_tokens), _ptr(k_per_req), B, K, V, _ptr(out_tokens),
+            _ptr(nacc), _ptr(am), ws.ptr(), ws.nbytes, _stream(dev))
+    if events is None:
+        rc = lib.specdec_verify_greedy(*args)
+        what = "specdec_verify_greedy"
+    else:
+        if len(events) != 2:
+            raise ValueError("events must hold two entries")
+        rc = lib.specdec_verify_greedy_timed(
+            *args, (ctypes.c_void_p * 2)(*[_event_handle(e, dev) for e in events]))
+        what = "specdec_verify_greedy_timed"
     if rc != 0:
-        raise SpecdecError(rc, "specdec_verify_greedy")
+        raise SpecdecError(rc, what)
     return out_tokens, nacc, am
 
 

@@ -194,6 +194,16 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
                    float temperature, int32_t B, int32_t K, int32_t V, int32_t* out_tokens,
                    int32_t* num_accepted, float* accept_prob, void* workspace,
                    size_t workspace_bytes, void* stream) {
+    return specdec_verify_timed(target_logits, draft_logits, dtype, draft_tokens, k_per_req,
+                                uniforms, temperature, B, K, V, out_tokens, num_accepted,
+                                accept_prob, workspace, workspace_bytes, stream, nullptr);
+}
+
+int specdec_verify_timed(const void* target_logits, const void* draft_logits, specdec_dtype_t dtype,
+                         const int32_t* draft_tokens, const int32_t* k_per_req, const float* uniforms,
+                         float temperature, int32_t B, int32_t K, int32_t V, int32_t* out_tokens,
+                         int32_t* num_accepted, float* accept_prob, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events) {
     if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
     if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
     Scale sc;
@@ -232,7 +242,8 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
     p.slot_l = reinterpret_cast<uint32_t*>(ws + L.slot_l);
     p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
     p.dec = reinterpret_cast<Decision*>(ws + L.dec);
-    return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream));
+    return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream,
+                                    reinterpret_cast<hipEvent_t const*>(events)));
 }
 
 size_t specdec_verify_greedy_workspace_bytes(int32_t B, int32_t K, int32_t V,
@@ -246,6 +257,16 @@ int specdec_verify_greedy(const void* target_logits, specdec_dtype_t dtype,
                           int32_t K, int32_t V, int32_t* out_tokens, int32_t* num_accepted,
                           int32_t* argmax_out, void* workspace, size_t workspace_bytes,
                           void* stream) {
+    return specdec_verify_greedy_timed(target_logits, dtype, draft_tokens, k_per_req, B, K, V,
+                                       out_tokens, num_accepted, argmax_out, workspace,
+                                       workspace_bytes, stream, nullptr);
+}
+
+int specdec_verify_greedy_timed(const void* target_logits, specdec_dtype_t dtype,
+                                const int32_t* draft_tokens, const int32_t* k_per_req, int32_t B,
+                                int32_t K, int32_t V, int32_t* out_tokens, int32_t* num_accepted,
+                                int32_t* argmax_out, void* workspace, size_t workspace_bytes,
+                                void* stream, void* const* events) {
     if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
     if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
     if (B == 0) return SPECDEC_OK;
@@ -270,7 +291,8 @@ int specdec_verify_greedy(const void* target_logits, specdec_dtype_t dtype,
     char* ws = static_cast<char*>(workspace);
     p.err = reinterpret_cast<uint32_t*>(ws + L.err);
     p.slot = reinterpret_cast<uint64_t*>(ws + L.slot);
-    return map_launch(launch_greedy(p, dtype, vec, (hipStream_t)stream));
+    return map_launch(launch_greedy(p, dtype, vec, (hipStream_t)stream,
+                                    reinterpret_cast<hipEvent_t const*>(events)));
 }
 
 }  // extern "C"

@@ -213,6 +213,9 @@ __device__ __forceinline__ double wave_inclusive_scan(double v) {
     return v + dpp<kDppRowBcast31, 0xC>(v, 0.0);
 }
 
+// Max / sum over the workgroup, in every thread.  Each call needs an LDS
+// array of its own that nothing else writes afterwards (one barrier, no
+// second one to guard the array's reuse).
 __device__ __forceinline__ float block_max(float v, float* lds /* [kWaves] */) {
     v = wave_max(v);
     const int w = threadIdx.x >> 6;
@@ -221,7 +224,6 @@ __device__ __forceinline__ float block_max(float v, float* lds /* [kWaves] */) {
     float r = lds[0];
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) r = fmaxf(r, lds[i]);
-    __syncthreads();
     return r;
 }
 
@@ -233,30 +235,7 @@ __device__ __forceinline__ double block_sum(double v, double* lds /* [kWaves] */
     double r = lds[0];
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) r += lds[i];
-    __syncthreads();
     return r;
-}
-
-// Exclusive prefix sum over the workgroup in thread order; also returns the
-// total.
-__device__ __forceinline__ double block_exclusive_scan(double v, double* lds /* [kWaves] */,
-                                                       double* total) {
-    const double incl = wave_inclusive_scan(v);
-    const int lane = threadIdx.x & 63;
-    const double up = __shfl_up(incl, 1, 64);
-    const double excl = (lane == 0) ? 0.0 : up;
-    const int w = threadIdx.x >> 6;
-    if (lane == 63) lds[w] = incl;
-    __syncthreads();
-    double before = 0.0, all = 0.0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        if (i < w) before += lds[i];
-        all += lds[i];
-    }
-    __syncthreads();
-    *total = all;
-    return before + excl;
 }
 
 // ---------------------------------------------------------------------------

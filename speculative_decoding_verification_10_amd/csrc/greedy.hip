@@ -12,6 +12,8 @@
 // indices, dispatched no later, and they never wait), merges each row's
 // tiles, compares the argmaxes with the drafts with a ballot, writes the
 // outputs and zeroes the slots for the next call.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 #include "slots.h"
 
@@ -159,17 +161,19 @@ __global__ __launch_bounds__(kThreads) void greedy_rows(GreedyParams a) {
 }
 
 template <int DT, bool VEC>
-hipError_t launch(const GreedyParams& p, hipStream_t s) {
+hipError_t launch(const GreedyParams& p, hipStream_t s, hipEvent_t const* events) {
     if (p.B == 0) return hipSuccess;
-    hipLaunchKernelGGL((greedy_rows<DT, VEC>), dim3(p.C, p.K + 1, p.B), dim3(kThreads), 0, s, p);
+    hipExtLaunchKernelGGL((greedy_rows<DT, VEC>), dim3(p.C, p.K + 1, p.B), dim3(kThreads), 0, s,
+                          events ? events[0] : nullptr, events ? events[1] : nullptr, 0, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s) {
-    if (dtype == kBF16) return vec ? launch<kBF16, true>(p, s) : launch<kBF16, false>(p, s);
-    return vec ? launch<kFP32, true>(p, s) : launch<kFP32, false>(p, s);
+hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
+                         hipEvent_t const* events) {
+    if (dtype == kBF16) return vec ? launch<kBF16, true>(p, s, events) : launch<kBF16, false>(p, s, events);
+    return vec ? launch<kFP32, true>(p, s, events) : launch<kFP32, false>(p, s, events);
 }
 
 }  // namespace specdec

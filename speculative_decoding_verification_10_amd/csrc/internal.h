@@ -80,8 +80,14 @@ struct StatsParams {
     double* part_s;             // [rows * C]
 };
 
-hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s);
-hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s);
+// events: null, or three events (each may be null) recorded on s before the
+// row kernel, after it, and after the call's last kernel.
+hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s,
+                         hipEvent_t const* events = nullptr);
+// events: null, or two events (each may be null) taken by the kernel's
+// dispatch at its start and end.
+hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
+                         hipEvent_t const* events = nullptr);
 hipError_t launch_stats(const StatsParams& p, int dtype, bool vec, hipStream_t s);
 
 }  // namespace specdec

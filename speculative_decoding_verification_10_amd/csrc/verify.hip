@@ -30,6 +30,8 @@
 // max(0, e_p - (Z_p/Z_q) e_q) with e = exp2(x * c - M) against each row's
 // offset M, the bonus is e_p.  An inverse CDF only needs the masses up to a
 // common factor.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 #include "slots.h"
 
@@ -537,25 +539,34 @@ __global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
 }
 
 template <int DT, bool VEC>
-hipError_t launch(const VerifyParams& p, hipStream_t s) {
+hipError_t launch(const VerifyParams& p, hipStream_t s, hipEvent_t const* events) {
     if (p.B == 0) return hipSuccess;
-    hipLaunchKernelGGL((verify_rows<DT, VEC>), dim3(p.C, p.R, p.B), dim3(kThreads), 0, s, p);
+    // Events, when given, are taken by the dispatches themselves (the
+    // kernels' own start and end times), so no marker sits between kernels.
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    if (events)
+        for (int k = 0; k < 3; ++k) ev[k] = events[k];
+    hipExtLaunchKernelGGL((verify_rows<DT, VEC>), dim3(p.C, p.R, p.B), dim3(kThreads), 0, s, ev[0],
+                          ev[1], 0, p);
     // Every final tile takes the decision itself (no extra launch) unless
     // that repeats much work: C tiles each merging R * C row-tile partials.
     if ((int64_t)p.C * p.R * p.C > kDecideOnceAbove) {
         hipLaunchKernelGGL(verify_decide, dim3(p.B), dim3(kThreads), 0, s, p);
-        hipLaunchKernelGGL((verify_final<DT, VEC, true>), dim3(p.C, p.B), dim3(kThreads), 0, s, p);
+        hipExtLaunchKernelGGL((verify_final<DT, VEC, true>), dim3(p.C, p.B), dim3(kThreads), 0, s,
+                              nullptr, ev[2], 0, p);
     } else {
-        hipLaunchKernelGGL((verify_final<DT, VEC, false>), dim3(p.C, p.B), dim3(kThreads), 0, s, p);
+        hipExtLaunchKernelGGL((verify_final<DT, VEC, false>), dim3(p.C, p.B), dim3(kThreads), 0, s,
+                              nullptr, ev[2], 0, p);
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s) {
-    if (dtype == kBF16) return vec ? launch<kBF16, true>(p, s) : launch<kBF16, false>(p, s);
-    return vec ? launch<kFP32, true>(p, s) : launch<kFP32, false>(p, s);
+hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s,
+                         hipEvent_t const* events) {
+    if (dtype == kBF16) return vec ? launch<kBF16, true>(p, s, events) : launch<kBF16, false>(p, s, events);
+    return vec ? launch<kFP32, true>(p, s, events) : launch<kFP32, false>(p, s, events);
 }
 
 }  // namespace specdec

@@ -58,10 +58,13 @@ FAKE = ctypes.c_void_p(0x10000)     # never dereferenced: every call below fails
 def call_verify(lib, **kw):
     a = dict(target=FAKE, draft=FAKE, dtype=1, tokens=FAKE, kpr=None, unif=FAKE, T=1.0,
              B=4, K=3, V=1000, out=FAKE, nacc=FAKE, ap=None, ws=FAKE, wsb=1 << 20, stream=None)
+    timed = kw.pop("timed", False)
     a.update(kw)
-    return lib.specdec_verify(a["target"], a["draft"], a["dtype"], a["tokens"], a["kpr"], a["unif"],
-                              a["T"], a["B"], a["K"], a["V"], a["out"], a["nacc"], a["ap"],
-                              a["ws"], a["wsb"], a["stream"])
+    args = (a["target"], a["draft"], a["dtype"], a["tokens"], a["kpr"], a["unif"], a["T"], a["B"],
+            a["K"], a["V"], a["out"], a["nacc"], a["ap"], a["ws"], a["wsb"], a["stream"])
+    if timed:
+        return lib.specdec_verify_timed(*args, (ctypes.c_void_p * 3)(None, None, None))
+    return lib.specdec_verify(*args)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -87,19 +90,28 @@ def call_verify(lib, **kw):
 ])
 def test_verify_rejects(lib, kw, status):
     assert call_verify(lib, **kw) == status
+    # The timed entry point checks its arguments the same way, before it
+    # records any event (the entries here are NULL, so none would be).
+    assert call_verify(lib, timed=True, **kw) == status
 
 
 def test_verify_empty_batch_is_ok(lib):
     assert call_verify(lib, B=0, target=None, ws=None) == OK
+    assert call_verify(lib, B=0, target=None, ws=None, timed=True) == OK
+    assert lib.specdec_verify_timed(None, None, 1, None, None, None, 1.0, 0, 3, 100, None, None,
+                                    None, None, 0, None, None) == OK
 
 
 def call_greedy(lib, **kw):
     a = dict(target=FAKE, dtype=1, tokens=FAKE, kpr=None, B=4, K=3, V=1000, out=FAKE, nacc=FAKE,
              am=None, ws=FAKE, wsb=1 << 20, stream=None)
+    timed = kw.pop("timed", False)
     a.update(kw)
-    return lib.specdec_verify_greedy(a["target"], a["dtype"], a["tokens"], a["kpr"], a["B"], a["K"],
-                                     a["V"], a["out"], a["nacc"], a["am"], a["ws"], a["wsb"],
-                                     a["stream"])
+    args = (a["target"], a["dtype"], a["tokens"], a["kpr"], a["B"], a["K"], a["V"], a["out"],
+            a["nacc"], a["am"], a["ws"], a["wsb"], a["stream"])
+    if timed:
+        return lib.specdec_verify_greedy_timed(*args, (ctypes.c_void_p * 2)(None, None))
+    return lib.specdec_verify_greedy(*args)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -110,6 +122,7 @@ def call_greedy(lib, **kw):
 ])
 def test_greedy_rejects(lib, kw, status):
     assert call_greedy(lib, **kw) == status
+    assert call_greedy(lib, timed=True, **kw) == status
 
 
 def test_stats_rejects(lib):

@@ -154,6 +154,30 @@ def test_verify_large_vocab(dtype, one_hot):
     assert nd == 0
 
 
+def test_verify_timed_matches_and_records():
+    """specdec_verify_timed gives the bits of specdec_verify and has the
+    dispatches take the caller's events (row kernel start and end, call
+    end)."""
+    import speculative_decoding_verification_10_amd as sd
+    from tests.gpu_util import to_device
+    wl = workloads.make("peaked", set_index=1)
+    d = to_device(wl)
+    args = (d["target"], d["draft"], d["draft_tokens"], d["uniforms"], wl.temperature)
+    ref = sd.verify(*args, accept_prob=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    got = sd.verify(*args, accept_prob=True, events=ev)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    rows_ms, call_ms = ev[0].elapsed_time(ev[1]), ev[0].elapsed_time(ev[2])
+    assert 0.0 < rows_ms < call_ms < 100.0, (rows_ms, call_ms)
+    # Partial event lists: only the given events are recorded.
+    e2 = torch.cuda.Event(enable_timing=True)
+    got2 = sd.verify(*args, accept_prob=True, events=(None, None, e2))
+    e2.synchronize()
+    assert torch.equal(got2[0], ref[0])
+
+
 def test_verify_misaligned_pointers():
     """Rows that do not start on a 16-byte boundary take the element-wise
     load path."""
@@ -301,6 +325,22 @@ def _greedy(wl, kp=None):
                                      argmax=True, workspace=ws)
     assert_workspace_clean(ws)
     return out.cpu().numpy(), nacc.cpu().numpy(), am.cpu().numpy()
+
+
+def test_greedy_timed_matches_and_records():
+    """specdec_verify_greedy_timed gives the bits of specdec_verify_greedy
+    and has the dispatch take the caller's two events."""
+    import speculative_decoding_verification_10_amd as sd
+    wl = workloads.make("greedy", set_index=1, B=16)
+    t = dev_logits(wl.target)
+    toks = torch.from_numpy(wl.draft_tokens).cuda()
+    ref = sd.verify_greedy(t, toks, argmax=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    got = sd.verify_greedy(t, toks, argmax=True, events=ev)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    assert 0.0 < ev[0].elapsed_time(ev[1]) < 100.0
 
 
 def test_greedy_full_size():
