@@ -72,6 +72,18 @@ template <int DT> __device__ __forceinline__ u32x4 neg_inf_raw() {
 // whole vector when v >= NV) read as -inf.  NT selects nontemporal loads.
 template <int DT, bool VEC, bool NT>
 __device__ __forceinline__ u32x4 load_raw(const void* row, int V, int NV, int v) {
+    if (VEC && NT) {
+        // Streaming passes, branch-free: a vector past the end re-reads the
+        // last one and is then replaced, so a tile's loads issue back to
+        // back.  (The re-read passes keep the branch: fewer registers.)
+        const u32x4* p = reinterpret_cast<const u32x4*>(row) + min(v, NV - 1);
+        u32x4 r = __builtin_nontemporal_load(p);
+        const u32x4 ninf = neg_inf_raw<DT>();
+        const bool past = v >= NV;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r[k] = past ? ninf[k] : r[k];
+        return r;
+    }
     if (v >= NV) return neg_inf_raw<DT>();
     if (VEC) {
         const u32x4* p = reinterpret_cast<const u32x4*>(row) + v;
@@ -245,33 +257,23 @@ __device__ __forceinline__ double block_sum(double v, double* lds /* [kWaves] */
 // thread's offset, summed in fp32 per vector (pairwise) and in fp64 across
 // vectors; the thread sums are rescaled to the workgroup offset and added in
 // fp64.  The result is valid in thread 0 only.
-//
-// With gx >= 0 the thread that holds token gx (if it lies in this tile)
-// stores its logit, widened to float, to *gval and returns true.
 // ---------------------------------------------------------------------------
 template <int DT, bool VEC, bool NT = true>
-__device__ __forceinline__ bool tile_stats(const void* row, int V, int NV, int tile, const Scale& sc,
+__device__ __forceinline__ void tile_stats(const void* row, int V, int NV, int tile, const Scale& sc,
                                            float& m_out, double& s_out, float* lds_f,
-                                           double* lds_d, int gx = -1, float* gval = nullptr) {
+                                           double* lds_d) {
     constexpr int E = Elem<DT>::E;
     const int v0 = tile * kTileVec + threadIdx.x;
     u32x4 raw[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) raw[u] = load_raw<DT, VEC, NT>(row, V, NV, v0 + u * kThreads);
     float mt = -INFINITY;
-    bool held = false;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         float x[E];
         decode<DT>(raw[u], x);
 #pragma unroll
         for (int e = 0; e < E; ++e) mt = fmaxf(mt, x[e]);
-        if (gx >= 0 && v0 + u * kThreads == gx / E) {
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                if (e == gx % E) *gval = x[e];
-            held = true;
-        }
     }
     const bool empty = (mt == -INFINITY);
     const float Mt = offset_of(empty ? 0.0f : mt, sc);
@@ -290,7 +292,6 @@ __device__ __forceinline__ bool tile_stats(const void* row, int V, int NV, int t
     const double sb = block_sum(scaled, lds_d);
     m_out = mb;
     s_out = sb;
-    return held;
 }
 
 // Merge per-tile partials (m_c, s_c) of one row into (max, sum relative to

@@ -271,12 +271,16 @@ __device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* 
     if (draft ? i >= kb : i > kb) return;   // row past k_b: nothing to read
     const void* row = draft ? row_ptr(a.draft, (size_t)b * K + i, a.V, S)
                             : row_ptr(a.target, (size_t)b * (K + 1) + i, a.V, S);
+    // Thread 0 of the tile that holds the draft token x_i reads its logit
+    // (issued before the tile's loads, stored after them).
     const int gx = (i < kb) ? token_of(a, b, i) : -1;
-    float m, gval = 0.0f;
+    const bool holder = gx >= 0 && threadIdx.x == 0 && gx / (kTileVec * Elem<DT>::E) == tile;
+    float gval = 0.0f;
+    if (holder) gval = load_one<DT>(row, gx);
+    float m;
     double z;
-    const bool held =
-        tile_stats<DT, VEC>(row, a.V, a.NV, tile, a.sc, m, z, lds_f, lds_d, gx, &gval);
-    if (held) slot_put(a.slot_l + (size_t)b * a.R + rr, enc_f32(gval));
+    tile_stats<DT, VEC>(row, a.V, a.NV, tile, a.sc, m, z, lds_f, lds_d);
+    if (holder) slot_put(a.slot_l + (size_t)b * a.R + rr, enc_f32(gval));
     if (threadIdx.x == 0) {
         const size_t idx = ((size_t)b * a.R + rr) * a.C + tile;
         slot_put(a.slot_s + idx, enc_f64(z));
