@@ -179,6 +179,11 @@ __device__ __forceinline__ double dpp(double v, double old) {
     return __hiloint2double(hi, lo);
 }
 
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp(int v, int old) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+
 __device__ __forceinline__ float lane63(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
@@ -259,14 +264,18 @@ __device__ __forceinline__ double block_sum(double v, double* lds /* [kWaves] */
 // fp64.  The result is valid in thread 0 only.
 // ---------------------------------------------------------------------------
 template <int DT, bool VEC, bool NT = true>
-__device__ __forceinline__ void tile_stats(const void* row, int V, int NV, int tile, const Scale& sc,
-                                           float& m_out, double& s_out, float* lds_f,
-                                           double* lds_d) {
-    constexpr int E = Elem<DT>::E;
+__device__ __forceinline__ void tile_load(const void* row, int V, int NV, int tile,
+                                          u32x4 (&raw)[kUnroll]) {
     const int v0 = tile * kTileVec + threadIdx.x;
-    u32x4 raw[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) raw[u] = load_raw<DT, VEC, NT>(row, V, NV, v0 + u * kThreads);
+}
+
+template <int DT>
+__device__ __forceinline__ void tile_reduce(const u32x4 (&raw)[kUnroll], const Scale& sc,
+                                            float& m_out, double& s_out, float* lds_f,
+                                            double* lds_d) {
+    constexpr int E = Elem<DT>::E;
     float mt = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -292,6 +301,15 @@ __device__ __forceinline__ void tile_stats(const void* row, int V, int NV, int t
     const double sb = block_sum(scaled, lds_d);
     m_out = mb;
     s_out = sb;
+}
+
+template <int DT, bool VEC, bool NT = true>
+__device__ __forceinline__ void tile_stats(const void* row, int V, int NV, int tile, const Scale& sc,
+                                           float& m_out, double& s_out, float* lds_f,
+                                           double* lds_d) {
+    u32x4 raw[kUnroll];
+    tile_load<DT, VEC, NT>(row, V, NV, tile, raw);
+    tile_reduce<DT>(raw, sc, m_out, s_out, lds_f, lds_d);
 }
 
 // Merge per-tile partials (m_c, s_c) of one row into (max, sum relative to

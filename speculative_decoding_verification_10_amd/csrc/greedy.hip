@@ -41,14 +41,32 @@ __device__ __forceinline__ void dec_pair(uint64_t s, float& v, int& i) {
     i = (int)(uint32_t)w;
 }
 
+// One DPP step of a (value, index) reduction: the pair a DPP move brings in
+// replaces this lane's if it is better (lanes the move skips see the
+// identity (-inf, INT_MAX)).
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+    const float ov = dpp<CTRL, ROWS>(v, -INFINITY);
+    const int oi = dpp<CTRL, ROWS>(i, 0x7FFFFFFF);
+    if (better(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
 // Best pair over each row of 16 lanes, in every lane of the row.
 __device__ __forceinline__ void row16_best(float& v, int& i) {
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(v, o, 16);
-        const int oi = __shfl_xor(i, o, 16);
-        if (better(ov, oi, v, i)) { v = ov; i = oi; }
-    }
+    best_step<kDppQuad1032>(v, i);
+    best_step<kDppQuad2301>(v, i);
+    best_step<kDppRowHalfMirror>(v, i);
+    best_step<kDppRowMirror>(v, i);
+}
+
+// Best pair over the wave, in lane 63.
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+    row16_best(v, i);
+    best_step<kDppRowBcast15, 0xA>(v, i);
+    best_step<kDppRowBcast31, 0xC>(v, i);
 }
 
 struct GreedyShared {
@@ -141,14 +159,9 @@ __global__ __launch_bounds__(kThreads) void greedy_rows(GreedyParams a) {
         for (int e = 0; e < E; ++e)
             if (x[e] > bv) { bv = x[e]; bi = t0 + e; }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
+    wave_best(bv, bi);
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { sh.lv[w] = bv; sh.li[w] = bi; }
+    if ((threadIdx.x & 63) == 63) { sh.lv[w] = bv; sh.li[w] = bi; }
     __syncthreads();
     if (threadIdx.x == 0) {
         float rv = sh.lv[0];
