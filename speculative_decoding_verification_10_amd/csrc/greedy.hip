@@ -6,12 +6,12 @@
 // when every draft matches.  No exponentials: one pass over the target rows.
 //
 // One kernel, one workgroup per (target row i <= k_b, tile): the tile's
-// (max, lowest index of the max) goes to a self-validating slot.  The
-// request's last workgroup -- last tile of row k_b, the highest index of the
-// request's workgroups -- waits for the other slots of its request (lower
-// indices, dispatched no later, and they never wait), merges each row's
-// tiles, compares the argmaxes with the drafts with a ballot, writes the
-// outputs and zeroes the slots for the next call.
+// (max, lowest index of the max) goes to a self-validating slot.  The first
+// wave of the request's last workgroup -- last tile of row k_b, the highest
+// index of the request's workgroups -- waits for the other slots of its
+// request (lower indices, dispatched no later, and they never wait), merges
+// each row's tiles, compares the argmaxes with the drafts with a ballot,
+// writes the outputs and zeroes the slots for the next call.
 #include <hip/hip_ext.h>
 
 #include "internal.h"
@@ -73,17 +73,17 @@ struct GreedyShared {
     float lv[kWaves];
     int li[kWaves];
     int am[kMaxK + 1];
-    unsigned long long miss[kWaves];
 };
 
-// The request's decision, by its last workgroup.
+// The request's decision, by one wave of its last workgroup (the other waves
+// have left, so a waiting decider holds one wave slot, not four).
 __device__ void greedy_decide(const GreedyParams& a, int b, int kb, GreedyShared& sh) {
     const int K = a.K, C = a.C;
-    const int t = threadIdx.x, w = t >> 6, lane = t & 63, sub = lane & 15;
+    const int lane = threadIdx.x & 63, sub = lane & 15;
     uint64_t* slots = a.slot + (size_t)b * (K + 1) * C;
-    // Rows 16 lanes at a time, four rows per wave.
-    for (int base = 0; base <= kb; base += kWaves * 4) {
-        const int r = base + w * 4 + (lane >> 4);
+    // Rows 16 lanes at a time, four rows per pass.
+    for (int base = 0; base <= kb; base += 4) {
+        const int r = base + (lane >> 4);
         float bv = -INFINITY;
         int bi = 0x7FFFFFFF;
         if (r <= kb) {
@@ -98,27 +98,29 @@ __device__ void greedy_decide(const GreedyParams& a, int b, int kb, GreedyShared
         row16_best(bv, bi);
         if (sub == 0 && r <= kb) sh.am[r] = min(max(bi, 0), a.V - 1);
     }
-    __syncthreads();
-    const bool miss = (t < kb) && (a.tokens[(size_t)b * K + t] != sh.am[t]);
-    const unsigned long long mask = __ballot(miss);
-    if (lane == 0) sh.miss[w] = mask;
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // First mismatch, 64 positions at a time.
     int j = kb;
-    for (int k = 0; k < kWaves; ++k)
-        if (sh.miss[k]) {
-            j = k * 64 + __ffsll((long long)sh.miss[k]) - 1;
+    for (int t0 = 0; t0 < kb; t0 += 64) {
+        const int t = t0 + lane;
+        const unsigned long long m = __ballot(t < kb && a.tokens[(size_t)b * K + t] != sh.am[t]);
+        if (m) {
+            j = t0 + __ffsll((long long)m) - 1;
             break;
         }
-    for (int i = t; i <= K; i += kThreads) {
+    }
+    for (int i = lane; i <= K; i += 64) {
         int32_t v = -1;
         if (i < j) v = a.tokens[(size_t)b * K + i];
         else if (i == j) v = sh.am[j];
         a.out[(size_t)b * (K + 1) + i] = v;
         if (a.amax) a.amax[(size_t)b * (K + 1) + i] = (i <= kb) ? sh.am[i] : -1;
     }
-    if (t == 0) a.nacc[b] = j;
-    // Every slot of the request was awaited above.
-    for (int s = t; s < (kb + 1) * C; s += kThreads) slot_put(slots + s, (uint64_t)0);
+    if (lane == 0) a.nacc[b] = j;
+    // Every slot of the request was awaited above, by this wave.
+    for (int s = lane; s < (kb + 1) * C; s += 64) slot_put(slots + s, (uint64_t)0);
 }
 
 // Workgroup (x, y, z): tile x of target row y of request z.
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void greedy_rows(GreedyParams a) {
             if (better(sh.lv[k], sh.li[k], rv, ri)) { rv = sh.lv[k]; ri = sh.li[k]; }
         slot_put(a.slot + rid * a.C + tile, enc_pair(rv, ri));
     }
-    if (i == kb && tile == a.C - 1) greedy_decide(a, b, kb, sh);
+    if (i == kb && tile == a.C - 1 && threadIdx.x < 64) greedy_decide(a, b, kb, sh);
 }
 
 template <int DT, bool VEC>
