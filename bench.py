@@ -58,14 +58,14 @@ def algorithmic_bytes(wl, num_accepted) -> int:
 
 
 def row_pass_bytes(wl) -> int:
-    """Bytes the row pass (verify_rows) must move: every target row i <= k_b
-    and draft row i < k_b once (V elements each), plus the draft ids it
-    gathers at."""
+    """Bytes the pass over the rows (verify_rows, greedy_rows) must move:
+    every target row i <= k_b and draft row i < k_b once (V elements each),
+    plus the draft ids the stochastic pass gathers at."""
     import numpy as np
     s = 2 if wl.dtype == "bf16" else 4
     k = np.full(wl.B, wl.K) if wl.k_per_req is None else wl.k_per_req.astype(np.int64)
     rows = int(np.sum(k + 1)) + (int(np.sum(k)) if wl.draft is not None else 0)
-    return rows * wl.V * s + int(np.sum(k)) * 4
+    return rows * wl.V * s + (0 if wl.greedy else int(np.sum(k)) * 4)
 
 
 def read_counters(workload, key):
@@ -237,7 +237,7 @@ def main():
     nacc = out[1].cpu().numpy()
 
     if phase:
-        nev = 2 if greedy else 3
+        nev = 3
         phase_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
         for evs in phase_ev:          # torch creates an event at its first record
             for e in evs:
@@ -272,20 +272,23 @@ def main():
     value = positions / (ms_per_step * 1e-3)
     gbps = alg / (ms_per_step * 1e-3) / 1e9
     achieved = alg / (per_launch_ms * 1e-3) / 1e9
-    if phase and not greedy:
-        # The dominant kernel: the row pass, which moves ~85% of the bytes.
+    if phase:
+        # The dominant kernel: the pass over the rows (all of the greedy
+        # path's bytes, ~85% of the stochastic path's).
         rb = row_pass_bytes(wl)
         rows_gbps = rb / (rows_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(rows_gbps, 1), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(rows_gbps / PEAK_HBM_GBPS, 4),
-                    "traffic": read_counters(args.workload, "verify_rows_hbm_bytes_per_launch"),
-                    "kernel": "verify_rows", "algorithmic_bytes": rb,
+                    "traffic": read_counters(args.workload, "greedy_rows_hbm_bytes_per_launch" if greedy
+                                             else "verify_rows_hbm_bytes_per_launch"),
+                    "kernel": "greedy_rows" if greedy else "verify_rows", "algorithmic_bytes": rb,
                     "launch_ms": round(rows_ms, 5)}
         call = {"achieved": round(alg / (call_ms * 1e-3) / 1e9, 1),
                 "frac": round(alg / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                 "traffic": read_counters(args.workload, "hbm_bytes_per_launch"), "algorithmic_bytes": alg,
                 "launch_ms": round(call_ms, 5),
-                "kernels": "verify_rows, [verify_decide,] verify_final"}
+                "kernels": ("greedy_rows, greedy_decisions" if greedy
+                            else "verify_rows, [verify_decide,] verify_final")}
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),

@@ -35,17 +35,12 @@
  *   - Workspace: device memory of at least the size the matching
  *     *_workspace_bytes() function returns, 256-byte aligned.  The first 4
  *     bytes hold error bits: a call ORs in a bit when an internal bounded
- *     wait gives up (never in a correct run).  specdec_verify and
- *     specdec_softmax_stats set every other scratch word they read earlier
- *     in the same call, so their workspace needs no initialisation and may
- *     hold anything.  specdec_verify_greedy hands partial results between
- *     workgroups of one kernel through slots that must read zero when the
- *     call starts: zero-fill its workspace with specdec_workspace_init before
- *     the first call, and again after any other entry point has used it
- *     (those leave non-zero scratch behind); every greedy call leaves the
- *     slots it used at zero again.  specdec_workspace_init also clears the
- *     error bits.  Calls that may run concurrently need distinct
- *     workspaces.
+ *     wait gives up (never in a correct run); specdec_workspace_init clears
+ *     them.  Every call sets each other scratch word it reads earlier in the
+ *     same call, so a workspace needs no initialisation beyond a clear error
+ *     word, may hold anything else, and may be shared by calls of different
+ *     entry points and shapes that do not run concurrently.  Calls that may
+ *     run concurrently need distinct workspaces.
  *   - Preconditions not checked on the fast path (a violation gives
  *     unspecified tokens, never an out-of-bounds access): logits finite or
  *     -inf (-inf = probability 0; a row may not be all -inf); 0 <=
@@ -172,12 +167,13 @@ int specdec_verify_greedy(const void *target_logits, specdec_dtype_t dtype,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * specdec_verify_greedy with the duration of its one kernel, for telemetry
- * and benchmarks: the same operation, arguments and results; events[0] and
- * events[1] (hipEvent_t, caller-created and caller-owned; `events` or either
- * entry may be NULL) are taken by the kernel's dispatch at its start and
- * end on `stream`.  Nothing is recorded when B = 0 or the arguments are
- * rejected.
+ * specdec_verify_greedy with per-phase timing, for telemetry and
+ * benchmarks: the same operation, arguments and results; the caller's HIP
+ * events (hipEvent_t, caller-created and caller-owned; `events` or any
+ * entry may be NULL) are taken by the kernel dispatches on `stream`:
+ * events[0] the start of the argmax pass over the target rows, events[1]
+ * its end, events[2] the end of the call's last kernel.  Nothing is
+ * recorded when B = 0 or the arguments are rejected.
  */
 int specdec_verify_greedy_timed(const void *target_logits, specdec_dtype_t dtype,
                                 const int32_t *draft_tokens, const int32_t *k_per_req,

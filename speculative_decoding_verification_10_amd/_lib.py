@@ -119,12 +119,10 @@ def _stream(device: torch.device) -> int:
 
 
 class Workspace:
-    """Device scratch for the library, zero-filled when allocated: the error
-    word at offset 0 starts clear and the greedy path's slots start empty
-    (each greedy call leaves them empty again).  A workspace handed to
-    verify_greedy must not be used by the other entry points in between:
-    they leave non-zero scratch behind.  The workspaces this module caches
-    are kept per device, stream and entry point for that reason."""
+    """Device scratch for the library, zero-filled when allocated so that the
+    error word at offset 0 starts clear (no other initialisation is needed).
+    The workspaces this module caches are kept per device, stream and entry
+    point."""
 
     def __init__(self, nbytes: int, device):
         self.nbytes = int(nbytes)
@@ -232,9 +230,10 @@ def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
                   k_per_req: Optional[torch.Tensor] = None, argmax: bool = False,
                   workspace: Optional[Workspace] = None, out=None, events=None):
     """Greedy verify step (specdec_verify_greedy).  Returns (out_tokens,
-    num_accepted, argmax [B, K+1] or None).  ``events``: two
+    num_accepted, argmax [B, K+1] or None).  ``events``: three
     torch.cuda.Event (enable_timing=True) or None entries, taken at the
-    kernel's start and end (specdec_verify_greedy_timed)."""
+    argmax pass's start and end and the end of the call
+    (specdec_verify_greedy_timed)."""
     lib = load()
     if target.dim() != 3:
         raise ValueError("target must be [B, K+1, V]")
@@ -264,10 +263,10 @@ def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
         rc = lib.specdec_verify_greedy(*args)
         what = "specdec_verify_greedy"
     else:
-        if len(events) != 2:
-            raise ValueError("events must hold two entries")
+        if len(events) != 3:
+            raise ValueError("events must hold three entries")
         rc = lib.specdec_verify_greedy_timed(
-            *args, (ctypes.c_void_p * 2)(*[_event_handle(e, dev) for e in events]))
+            *args, (ctypes.c_void_p * 3)(*[_event_handle(e, dev) for e in events]))
         what = "specdec_verify_greedy_timed"
     if rc != 0:
         raise SpecdecError(rc, what)

@@ -5,17 +5,15 @@
 // target argmax at the first mismatch, or the argmax after the last draft
 // when every draft matches.  No exponentials: one pass over the target rows.
 //
-// One kernel, one workgroup per (target row i <= k_b, tile): the tile's
-// (max, lowest index of the max) goes to a self-validating slot.  The first
-// wave of the request's last workgroup -- last tile of row k_b, the highest
-// index of the request's workgroups -- waits for the other slots of its
-// request (lower indices, dispatched no later, and they never wait), merges
-// each row's tiles, compares the argmaxes with the drafts with a ballot,
-// writes the outputs and zeroes the slots for the next call.
+// Two stream-ordered kernels, no waits inside either:
+//  greedy_rows       one workgroup per (target row i <= k_b, tile): the
+//                    tile's (max, lowest index of the max), one word per tile;
+//  greedy_decisions  one wave per request: merges each row's tiles, compares
+//                    the argmaxes with the drafts by ballot, writes the
+//                    outputs.
 #include <hip/hip_ext.h>
 
 #include "internal.h"
-#include "slots.h"
 
 namespace specdec {
 namespace {
@@ -29,14 +27,11 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return (v > bv) || (v == bv && i < bi);
 }
 
-// A (value, index) pair as one self-validating word: never all ones, since
-// NaN values are stored canonically and indices are below 2^31.
+// A (value, index) pair as one 8-byte word.
 __device__ __forceinline__ uint64_t enc_pair(float v, int i) {
-    const uint32_t vb = (v != v) ? 0x7FC00000u : __float_as_uint(v);
-    return ~(((uint64_t)vb << 32) | (uint32_t)i);
+    return ((uint64_t)__float_as_uint(v) << 32) | (uint32_t)i;
 }
-__device__ __forceinline__ void dec_pair(uint64_t s, float& v, int& i) {
-    const uint64_t w = ~s;
+__device__ __forceinline__ void dec_pair(uint64_t w, float& v, int& i) {
     v = __uint_as_float((uint32_t)(w >> 32));
     i = (int)(uint32_t)w;
 }
@@ -69,34 +64,39 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
     best_step<kDppRowBcast31, 0xC>(v, i);
 }
 
-struct GreedyShared {
-    float lv[kWaves];
-    int li[kWaves];
-    int am[kMaxK + 1];
-};
-
-// The request's decision, by one wave of its last workgroup (the other waves
-// have left, so a waiting decider holds one wave slot, not four).
-__device__ void greedy_decide(const GreedyParams& a, int b, int kb, GreedyShared& sh) {
+// The decision of request b, by one wave (its own workgroup): the row
+// maxima come from the tile slots the previous kernel wrote.
+__device__ void greedy_decide(const GreedyParams& a, int b, int* am) {
     const int K = a.K, C = a.C;
+    const int kb = greedy_k(a, b);
     const int lane = threadIdx.x & 63, sub = lane & 15;
-    uint64_t* slots = a.slot + (size_t)b * (K + 1) * C;
-    // Rows 16 lanes at a time, four rows per pass.
+    const uint64_t* slots = a.slot + (size_t)b * (K + 1) * C;
+    // Rows 16 lanes at a time, four rows per pass; every load of a pass is
+    // issued before any is used.
     for (int base = 0; base <= kb; base += 4) {
         const int r = base + (lane >> 4);
         float bv = -INFINITY;
         int bi = 0x7FFFFFFF;
         if (r <= kb) {
-            for (int c = sub; c < C; c += 16) {
-                const uint64_t* p = slots + (size_t)r * C + c;
-                float v;
-                int i;
-                dec_pair(slot_wait(p, a.err, enc_pair(-INFINITY, 0)), v, i);
-                if (better(v, i, bv, bi)) { bv = v; bi = i; }
+            for (int c0 = sub; c0 < C; c0 += 64) {
+                uint64_t got[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = c0 + 16 * q;
+                    got[q] = (c < C) ? slots[(size_t)r * C + c] : 0;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (c0 + 16 * q >= C) break;
+                    float v;
+                    int i;
+                    dec_pair(got[q], v, i);
+                    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+                }
             }
         }
         row16_best(bv, bi);
-        if (sub == 0 && r <= kb) sh.am[r] = min(max(bi, 0), a.V - 1);
+        if (sub == 0 && r <= kb) am[r] = min(max(bi, 0), a.V - 1);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -105,7 +105,7 @@ __device__ void greedy_decide(const GreedyParams& a, int b, int kb, GreedyShared
     int j = kb;
     for (int t0 = 0; t0 < kb; t0 += 64) {
         const int t = t0 + lane;
-        const unsigned long long m = __ballot(t < kb && a.tokens[(size_t)b * K + t] != sh.am[t]);
+        const unsigned long long m = __ballot(t < kb && a.tokens[(size_t)b * K + t] != am[t]);
         if (m) {
             j = t0 + __ffsll((long long)m) - 1;
             break;
@@ -114,13 +114,11 @@ __device__ void greedy_decide(const GreedyParams& a, int b, int kb, GreedyShared
     for (int i = lane; i <= K; i += 64) {
         int32_t v = -1;
         if (i < j) v = a.tokens[(size_t)b * K + i];
-        else if (i == j) v = sh.am[j];
+        else if (i == j) v = am[j];
         a.out[(size_t)b * (K + 1) + i] = v;
-        if (a.amax) a.amax[(size_t)b * (K + 1) + i] = (i <= kb) ? sh.am[i] : -1;
+        if (a.amax) a.amax[(size_t)b * (K + 1) + i] = (i <= kb) ? am[i] : -1;
     }
     if (lane == 0) a.nacc[b] = j;
-    // Every slot of the request was awaited above, by this wave.
-    for (int s = lane; s < (kb + 1) * C; s += 64) slot_put(slots + s, (uint64_t)0);
 }
 
 // Workgroup (x, y, z): tile x of target row y of request z.
@@ -128,7 +126,8 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void greedy_rows(GreedyParams a) {
     constexpr int E = Elem<DT>::E;
     constexpr int S = Elem<DT>::S;
-    __shared__ GreedyShared sh;
+    __shared__ float lv[kWaves];
+    __shared__ int li[kWaves];
     const int tile = blockIdx.x;
     const int i = blockIdx.y;
     const int b = blockIdx.z;
@@ -163,16 +162,21 @@ __global__ __launch_bounds__(kThreads) void greedy_rows(GreedyParams a) {
     }
     wave_best(bv, bi);
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 63) { sh.lv[w] = bv; sh.li[w] = bi; }
+    if ((threadIdx.x & 63) == 63) { lv[w] = bv; li[w] = bi; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        float rv = sh.lv[0];
-        int ri = sh.li[0];
+        float rv = lv[0];
+        int ri = li[0];
         for (int k = 1; k < kWaves; ++k)
-            if (better(sh.lv[k], sh.li[k], rv, ri)) { rv = sh.lv[k]; ri = sh.li[k]; }
-        slot_put(a.slot + rid * a.C + tile, enc_pair(rv, ri));
+            if (better(lv[k], li[k], rv, ri)) { rv = lv[k]; ri = li[k]; }
+        a.slot[rid * a.C + tile] = enc_pair(rv, ri);
     }
-    if (i == kb && tile == a.C - 1 && threadIdx.x < 64) greedy_decide(a, b, kb, sh);
+}
+
+// Decisions: workgroup x (one wave) takes request x.
+__global__ __launch_bounds__(64) void greedy_decisions(GreedyParams a) {
+    __shared__ int am[kMaxK + 1];
+    greedy_decide(a, blockIdx.x, am);
 }
 
 template <int DT, bool VEC>
@@ -180,6 +184,8 @@ hipError_t launch(const GreedyParams& p, hipStream_t s, hipEvent_t const* events
     if (p.B == 0) return hipSuccess;
     hipExtLaunchKernelGGL((greedy_rows<DT, VEC>), dim3(p.C, p.K + 1, p.B), dim3(kThreads), 0, s,
                           events ? events[0] : nullptr, events ? events[1] : nullptr, 0, p);
+    hipExtLaunchKernelGGL(greedy_decisions, dim3(p.B), dim3(64), 0, s, nullptr,
+                          events ? events[2] : nullptr, 0, p);
     return hipGetLastError();
 }
 

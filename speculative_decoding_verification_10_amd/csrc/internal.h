@@ -66,7 +66,7 @@ struct GreedyParams {
     int32_t* amax;              // may be null
     int B, K, V, NV, C;
     uint32_t* err;              // workspace header: error bits
-    uint64_t* slot;             // [B * (K+1) * C] tile (max, index) (self-validating)
+    uint64_t* slot;             // [B * (K+1) * C] tile (max, index) words
 };
 
 struct StatsParams {
@@ -84,8 +84,8 @@ struct StatsParams {
 // row kernel, after it, and after the call's last kernel.
 hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s,
                          hipEvent_t const* events = nullptr);
-// events: null, or two events (each may be null) taken by the kernel's
-// dispatch at its start and end.
+// events: null, or three events (each may be null) taken by the dispatches:
+// the row kernel's start and end, and the end of the call's last kernel.
 hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
                          hipEvent_t const* events = nullptr);
 hipError_t launch_stats(const StatsParams& p, int dtype, bool vec, hipStream_t s);

@@ -18,8 +18,7 @@
 // always exits.
 //
 // A slot must read zero before its producer runs: an earlier kernel of the
-// same call empties it, or the consumer of the previous call did, after its
-// wait.
+// same call empties it.
 #pragma once
 
 #include <hip/hip_runtime.h>

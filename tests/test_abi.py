@@ -110,7 +110,7 @@ def call_greedy(lib, **kw):
     args = (a["target"], a["dtype"], a["tokens"], a["kpr"], a["B"], a["K"], a["V"], a["out"],
             a["nacc"], a["am"], a["ws"], a["wsb"], a["stream"])
     if timed:
-        return lib.specdec_verify_greedy_timed(*args, (ctypes.c_void_p * 2)(None, None))
+        return lib.specdec_verify_greedy_timed(*args, (ctypes.c_void_p * 3)(None, None, None))
     return lib.specdec_verify_greedy(*args)
 
 
