@@ -36,10 +36,16 @@ KERNEL_SOURCES = ["device_common.h", "internal.h", "slots.h", "verify.hip", "gre
 
 
 def kernel_digest() -> str:
+    """Hash of the kernel sources with comments and blank space removed, so
+    that stored counter figures stay valid across comment-only edits."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "speculative_decoding_verification_10_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "speculative_decoding_verification_10_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
