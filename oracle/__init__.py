@@ -87,6 +87,10 @@ class Oracle:
         lib.oracle_verify.restype = ci
         lib.oracle_verify_greedy.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, vp]
         lib.oracle_verify_greedy.restype = ci
+        lib.oracle_acceptance_counts.argtypes = [vp, vp, i32, i32, vp]
+        lib.oracle_acceptance_counts.restype = ci
+        lib.oracle_choose_k.argtypes = [vp, i32, dbl, i32, i32, vp, vp, vp, vp]
+        lib.oracle_choose_k.restype = ci
         self.lib = lib
         self.path = path
 
@@ -153,6 +157,36 @@ class Oracle:
         return {"out_tokens": out, "num_accepted": nacc, "argmax": am}
 
 
+    def acceptance_counts(self, num_accepted, K, k_per_req=None, counters=None):
+        """Per-position (drafted, tested, accepted) counts of one step, added
+        to ``counters`` ([3, K] uint64, zeros if None); returns the array."""
+        nacc = _c(num_accepted, np.int32)
+        B = nacc.size
+        kp = None if k_per_req is None else _c(k_per_req, np.int32).reshape(B)
+        cnt = np.zeros((3, K), np.uint64) if counters is None else counters
+        if cnt.dtype != np.uint64 or cnt.shape != (3, K) or not cnt.flags.c_contiguous:
+            raise ValueError("counters must be a contiguous uint64 [3, K] array")
+        rc = self.lib.oracle_acceptance_counts(_ptr(nacc), _ptr(kp), B, K, _ptr(cnt))
+        if rc != 0:
+            raise ValueError("oracle_acceptance_counts rejected its arguments")
+        return cnt
+
+    def choose_k(self, counters, c, k_min, k_max):
+        """(k, alpha_test, alpha_draft, speedup at k) from [3, K] counters."""
+        cnt = _c(counters, np.uint64)
+        K = cnt.shape[-1]
+        at = ctypes.c_double()
+        ad = ctypes.c_double()
+        sp = ctypes.c_double()
+        k = ctypes.c_int32()
+        rc = self.lib.oracle_choose_k(_ptr(cnt), K, float(c), int(k_min), int(k_max),
+                                      ctypes.byref(at), ctypes.byref(ad), ctypes.byref(k),
+                                      ctypes.byref(sp))
+        if rc != 0:
+            raise ValueError("oracle_choose_k rejected its arguments")
+        return k.value, at.value, ad.value, sp.value
+
+
 def default() -> Oracle:
     global _default
     with _lock:
@@ -171,3 +205,11 @@ def verify(target, draft, draft_tokens, uniforms, temperature, k_per_req=None):
 
 def verify_greedy(target, draft_tokens, k_per_req=None):
     return default().verify_greedy(target, draft_tokens, k_per_req)
+
+
+def acceptance_counts(num_accepted, K, k_per_req=None, counters=None):
+    return default().acceptance_counts(num_accepted, K, k_per_req, counters)
+
+
+def choose_k(counters, c, k_min, k_max):
+    return default().choose_k(counters, c, k_min, k_max)

@@ -267,3 +267,76 @@ int oracle_verify_greedy(const void *target, int dtype,
     }
     return err ? -1 : 0;
 }
+
+/*
+ * Acceptance telemetry per drafted position i (0-based), over the requests
+ * of one verify step, added to counters[3][K]:
+ *   counters[0][i] (drafted)  += #{b : i < k_b}
+ *   counters[1][i] (tested)   += #{b : i < k_b and i <= n_b}
+ *   counters[2][i] (accepted) += #{b : i < n_b}
+ * with n_b = num_accepted[b].  Position i is tested exactly when every
+ * earlier draft was accepted.  The serving engine's counters of drafted and
+ * accepted tokens ([SS] "What the numbers say", per-position acceptance
+ * falling along the draft) and the acceptance rate measured over the tests
+ * performed ([AIA] 3.4).
+ */
+int oracle_acceptance_counts(const int32_t *num_accepted, const int32_t *k_per_req,
+                             int32_t B, int32_t K, uint64_t *counters) {
+    if (!num_accepted || !counters || B < 0 || K < 0) return -1;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t k = k_per_req ? k_per_req[b] : K;
+        const int32_t n = num_accepted[b];
+        if (k < 0 || k > K || n < 0 || n > k) return -1;
+        for (int32_t i = 0; i < K; ++i) {
+            if (i < k) counters[i] += 1;
+            if (i < k && i <= n) counters[(size_t)K + i] += 1;
+            if (i < n) counters[2 * (size_t)K + i] += 1;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Draft length from the counters.  alpha_test = sum accepted / sum tested
+ * (the per-draft acceptance probability of the independent-acceptance
+ * model); alpha_draft = sum accepted / sum drafted (the engine counter
+ * ratio).  Under independent acceptance with probability alpha a step emits
+ * sum_{i=0..k} alpha^i tokens on average and costs 1 + c k target passes (c
+ * = draft-to-target cost ratio), so the speedup over plain decoding is their
+ * quotient ([LP] "Expected tokens per step", "Speedup" and the worked
+ * example's table for choosing k; [AIA] 2.4, 3.5).  Returns the k in
+ * [k_min, k_max] with the largest speedup at alpha = alpha_test (the
+ * smallest such k on ties) and that speedup.  With no tested position
+ * alpha_test is 0 (and k_min is chosen).
+ */
+int oracle_choose_k(const uint64_t *counters, int32_t K, double c, int32_t k_min,
+                    int32_t k_max, double *alpha_test, double *alpha_draft, int32_t *k_out,
+                    double *speedup_out) {
+    if (!counters || !k_out || K < 0 || k_min < 0 || k_max < k_min || !(c >= 0.0)) return -1;
+    double drafted = 0.0, tested = 0.0, accepted = 0.0;
+    for (int32_t i = 0; i < K; ++i) {
+        drafted += (double)counters[i];
+        tested += (double)counters[(size_t)K + i];
+        accepted += (double)counters[2 * (size_t)K + i];
+    }
+    const double a = tested > 0.0 ? accepted / tested : 0.0;
+    if (alpha_test) *alpha_test = a;
+    if (alpha_draft) *alpha_draft = drafted > 0.0 ? accepted / drafted : 0.0;
+    int32_t best_k = k_min;
+    double best = -1.0;
+    for (int32_t k = k_min; k <= k_max; ++k) {
+        double tokens = 0.0, power = 1.0;
+        for (int32_t i = 0; i <= k; ++i) {
+            tokens += power;
+            power *= a;
+        }
+        const double speedup = tokens / (1.0 + c * (double)k);
+        if (speedup > best) {
+            best = speedup;
+            best_k = k;
+        }
+    }
+    *k_out = best_k;
+    if (speedup_out) *speedup_out = best;
+    return 0;
+}

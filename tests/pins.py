@@ -575,6 +575,84 @@ def pin_markov_chain_third_token(o):
     assert stats.chisquare(counts, N * exact).pvalue > 1e-3, (counts / N, exact)
 
 
+def _counters_for_alpha(num, den):
+    """One-position counters whose tested/accepted ratio is num/den."""
+    return np.array([[den], [den], [num]], np.uint64)
+
+
+def pin_speedup_table_and_choice(o):
+    """3.5 Speculative Decoding, 'Worked example' (alpha = 0.8, c = 0.05):
+    the speedup of every k the table prints, to its two decimals, and the
+    table's best k (8) chosen over k = 1..10."""
+    g = golden("speedup_choosing_k.json")
+    cnt = _counters_for_alpha(4, 5)
+    for case in g["cases"]:
+        k, at, ad, sp = o.choose_k(cnt, g["c"], case["k"], case["k"])
+        assert k == case["k"] and abs(at - g["alpha"]) < 1e-15
+        assert round(sp, case["decimals"]) == case["speedup"], (case, sp)
+    k, _, _, sp = o.choose_k(cnt, g["c"], 1, 10)
+    assert k == g["best_printed_k"], k
+    # 'Speedup: each step costs T(1 + 4 x 0.05) = 1.2 T, so speedup = 3.36 / 1.2 = 2.8'
+    assert abs(o.choose_k(cnt, g["c"], 4, 4)[3] - 3.3616 / 1.2) < 1e-12
+    # A dearer draft shifts the optimum to a smaller k ('with a separate 1B
+    # draft model (c perhaps 0.1-0.2) the optimum shifts to smaller k').
+    assert o.choose_k(cnt, 0.15, 1, 10)[0] < k
+    # alpha = 0: one token per step whatever k, so the cheapest k; alpha = 1:
+    # k + 1 tokens per step, so the largest k while c < 1.
+    assert o.choose_k(_counters_for_alpha(0, 7), 0.05, 1, 10)[0] == 1
+    assert o.choose_k(_counters_for_alpha(7, 7), 0.05, 1, 10)[0] == 10
+    # Reading: on equal speedups the smaller k (fewer draft passes).  With
+    # alpha = 0 and free drafts every k gives exactly one token per pass.
+    assert o.choose_k(_counters_for_alpha(0, 7), 0.0, 2, 9)[0] == 2
+
+
+def pin_acceptance_count_identities(o):
+    """Per-position counters against identities that hold for any step:
+    sum_i drafted_i = sum_b k_b; sum_i accepted_i = sum_b n_b; every
+    request tests its accepted positions plus the one it rejects, so
+    sum_i tested_i = sum_b (n_b + [n_b < k_b]); accepted_i <= tested_i <=
+    drafted_i; position 0 is tested by every request that drafts; position
+    i+1 is tested by the requests that accepted i and drafted i+1.  Counters
+    accumulate across calls."""
+    rng = np.random.default_rng(31)
+    K = 7
+    for trial in range(20):
+        B = int(rng.integers(1, 40))
+        kp = rng.integers(0, K + 1, size=B).astype(np.int32)
+        n = np.array([rng.integers(0, k + 1) for k in kp], np.int32)
+        c = o.acceptance_counts(n, K, kp)
+        d, t, a = (c[r].astype(np.int64) for r in range(3))
+        assert d.sum() == kp.sum() and a.sum() == n.sum()
+        assert t.sum() == (n + (n < kp)).sum()
+        assert np.all(a <= t) and np.all(t <= d)
+        assert t[0] == np.count_nonzero(kp > 0)
+        for i in range(K - 1):
+            assert t[i + 1] == np.count_nonzero((n > i) & (kp > i + 1))
+        c2 = o.acceptance_counts(n, K, kp, c.copy())
+        assert np.array_equal(c2, 2 * c)
+    # k_per_req omitted means k_b = K for every request.
+    n = np.array([0, K, 3], np.int32)
+    assert np.array_equal(o.acceptance_counts(n, K), o.acceptance_counts(n, K, np.full(3, K, np.int32)))
+
+
+def pin_alpha_test_estimates_alpha(o):
+    """Draws from the pages' simplifying model -- each draft accepted
+    independently with probability alpha, the step stopping at the first
+    rejection -- give alpha_test = accepted / tested within sampling error
+    of alpha, while the engine ratio accepted / drafted stays below it (the
+    positions after a rejection are drafted but never tested)."""
+    rng = np.random.default_rng(47)
+    K, B = 6, 20000
+    for alpha in (0.3, 0.6, 0.85):
+        acc = rng.random((B, K)) < alpha
+        n = np.where(acc.all(axis=1), K, np.argmin(acc, axis=1)).astype(np.int32)
+        c = o.acceptance_counts(n, K)
+        _, at, ad, _ = o.choose_k(c, 0.0, 1, 1)
+        tested = float(c[1].sum())
+        assert abs(at - alpha) < 4.0 * np.sqrt(alpha * (1 - alpha) / tested), (alpha, at)
+        assert ad < alpha - 0.01, (alpha, ad)
+
+
 ALL_PINS = [
     pin_stats_logsumexp, pin_stats_closed_forms,
     pin_check_your_understanding, pin_single_position_experiment,
@@ -585,4 +663,6 @@ ALL_PINS = [
     pin_closed_form_through_oracle, pin_ragged_equals_truncated,
     pin_invariants, pin_greedy_worked_trace, pin_greedy_ties_and_bonus,
     pin_greedy_equals_argmax_decoding, pin_markov_chain_third_token,
+    pin_speedup_table_and_choice, pin_acceptance_count_identities,
+    pin_alpha_test_estimates_alpha,
 ]

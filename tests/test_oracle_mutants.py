@@ -42,6 +42,17 @@ MUTANTS = {
     "does_not_stop_at_first_rejection": ("if (j == k) { /* still on the path */", "if (1) {"),
     "rejected_draft_emitted": ("out[j] = tok;", "out[j] = (j < k) ? xt[j] : tok;"),
     "max_not_subtracted_in_prob": ("return exp((l - m) / T) / z;", "return exp(l / T) / z;"),
+    "tested_excludes_rejected": ("if (i < k && i <= n) counters[(size_t)K + i] += 1;",
+                                 "if (i < k && i < n) counters[(size_t)K + i] += 1;"),
+    "accepted_counts_reached": ("if (i < n) counters[2 * (size_t)K + i] += 1;",
+                                "if (i <= n && i < k) counters[2 * (size_t)K + i] += 1;"),
+    "alpha_over_drafted": ("const double a = tested > 0.0 ? accepted / tested : 0.0;",
+                           "const double a = drafted > 0.0 ? accepted / drafted : 0.0;"),
+    "cost_counts_target_pass_twice": ("const double speedup = tokens / (1.0 + c * (double)k);",
+                                      "const double speedup = tokens / (1.0 + c * (double)(k + 1));"),
+    "tokens_without_extra_token": ("for (int32_t i = 0; i <= k; ++i) {\n            tokens += power;",
+                                   "for (int32_t i = 1; i <= k; ++i) {\n            tokens += power;"),
+    "ties_pick_larger_k": ("if (speedup > best) {", "if (speedup >= best) {"),
 }
 
 RUNNER = r"""
