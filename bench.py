@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each call from a captured HIP graph")
+    ap.add_argument("--telemetry", action="store_true",
+                    help="each step also adds the step's per-position acceptance counts "
+                         "(specdec_acceptance_counts) to device counters")
     ap.add_argument("--no-phase-events", action="store_true",
                     help="time whole calls only (no events recorded inside specdec_verify)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
@@ -200,12 +203,18 @@ def main():
                           unif.data_ptr(), float(wl.temperature), wl.B, K, wl.V, out[0].data_ptr(),
                           out[1].data_ptr(), None, ws.ptr(), ws.nbytes, stream.cuda_stream))
 
+    counters = torch.zeros((3, max(K, 1)), dtype=torch.int64, device=dev) if args.telemetry else None
+    kpr_ptr = ptr(kpr)
+
     def step(r):
         a = cargs[r % len(cargs)]
         if handles is not None:
             rc = (lib.specdec_verify_greedy_timed if greedy else lib.specdec_verify_timed)(*a, handles[r])
         else:
             rc = (lib.specdec_verify_greedy if greedy else lib.specdec_verify)(*a)
+        if rc == 0 and counters is not None:
+            rc = lib.specdec_acceptance_counts(out[1].data_ptr(), kpr_ptr, wl.B, K, counters.data_ptr(),
+                                               stream.cuda_stream)
         if rc != 0:
             raise sd.SpecdecError(rc, "bench step")
 
@@ -334,6 +343,13 @@ def main():
     }
     if call is not None:
         line["call_roofline"] = call
+    if counters is not None:
+        # The draft length the step's own acceptance counters suggest at the
+        # worked example's draft cost ratio (c = 0.05).
+        k_next, a_test, a_draft, sp = sd.choose_k(counters, 0.05, 1, max(K, 1))
+        line["telemetry"] = {"kernel": "acceptance_counts", "alpha_test": round(a_test, 4),
+                             "alpha_draft": round(a_draft, 4), "chosen_k_at_c_0.05": k_next,
+                             "predicted_speedup": round(sp, 3)}
     if args.calibration_copy > 0:
         n = args.calibration_copy << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

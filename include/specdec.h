@@ -181,6 +181,49 @@ int specdec_verify_greedy_timed(const void *target_logits, specdec_dtype_t dtype
                                 int32_t *num_accepted, int32_t *argmax_out, void *workspace,
                                 size_t workspace_bytes, void *stream, void *const *events);
 
+/*
+ * Acceptance telemetry of one verify step ("Speculative Decoding from First
+ * Principles", "What the numbers say": the engine's counters of drafted and
+ * accepted tokens, acceptance per drafted position; "246 Speculative
+ * Decoding", 3.4: acceptance measured over the tests performed).  For each
+ * drafted position i < K it adds, on `stream`:
+ *   counters[i]       += #{b : i < k_b}                    (drafted)
+ *   counters[K + i]   += #{b : i < k_b and i <= n_b}       (tested: every
+ *                                                          earlier draft kept)
+ *   counters[2K + i]  += #{b : i < n_b}                    (accepted)
+ * with n_b = num_accepted[b] and k_b = k_per_req[b] (K when NULL).
+ *   num_accepted [B] int32, device (e.g. specdec_verify's output)
+ *   k_per_req    [B] int32, device, or NULL
+ *   counters     [3 * K] uint64, device, owned by the caller, zeroed by the
+ *                caller once and accumulated across calls (atomic adds).
+ * Preconditions not checked on the device: 0 <= n_b <= k_b <= K (values
+ * outside are clamped, never used as addresses).  0 <= B <= 65535 and
+ * 0 <= K <= 255, else SPECDEC_EINVAL.  No workspace.
+ */
+int specdec_acceptance_counts(const int32_t *num_accepted, const int32_t *k_per_req, int32_t B,
+                              int32_t K, uint64_t *counters, void *stream);
+
+/*
+ * Draft length from the counters (host function, synchronous; `counters`
+ * is HOST memory, [3 * K] as above).  alpha_test = sum accepted / sum
+ * tested, the per-draft acceptance probability of the independent-
+ * acceptance model; alpha_draft = sum accepted / sum drafted, the engine
+ * ratio (0 when the denominator is 0).  Under independent acceptance a step
+ * of block length k emits 1 + a + ... + a^k tokens on average and costs
+ * 1 + c k target passes (c = draft-to-target cost ratio, >= 0), so its
+ * speedup over plain decoding is their quotient ("3.5 Speculative
+ * Decoding", "Expected tokens per step", "Speedup" and the worked example's
+ * table for choosing k; "246 Speculative Decoding", 2.4 and 3.5).  *k_out is
+ * the k in [k_min, k_max] with the largest speedup at a = alpha_test (the
+ * smallest such k on ties), *speedup_out that speedup.  alpha_test,
+ * alpha_draft and speedup_out may be NULL.  SPECDEC_EINVAL for a NULL
+ * counters / k_out, K < 0, k_min < 0, k_max < k_min, or c negative or not
+ * finite.
+ */
+int specdec_choose_k(const uint64_t *counters, int32_t K, double c, int32_t k_min, int32_t k_max,
+                     double *alpha_test, double *alpha_draft, int32_t *k_out,
+                     double *speedup_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,8 +4,8 @@ The work runs in hand-written HIP kernels behind a C ABI (include/specdec.h);
 this package holds the thin ctypes binding over it, the in-tree build and the
 seeded synthetic workloads used by the tests and the benchmark.
 """
-from ._lib import (SpecdecError, Workspace, load, softmax_stats, verify,  # noqa: F401
-                   verify_greedy, version)
+from ._lib import (SpecdecError, Workspace, acceptance_counts, choose_k, load,  # noqa: F401
+                   softmax_stats, verify, verify_greedy, version)
 
-__all__ = ["SpecdecError", "Workspace", "load", "softmax_stats", "verify", "verify_greedy",
-           "version"]
+__all__ = ["SpecdecError", "Workspace", "acceptance_counts", "choose_k", "load", "softmax_stats",
+           "verify", "verify_greedy", "version"]

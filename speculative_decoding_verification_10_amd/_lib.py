@@ -76,6 +76,11 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.specdec_verify_greedy_timed.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, vp,
                                                     vp, sz, vp, vp]
         lib.specdec_verify_greedy_timed.restype = ci
+        lib.specdec_acceptance_counts.argtypes = [vp, vp, i32, i32, vp, vp]
+        lib.specdec_acceptance_counts.restype = ci
+        dbl = ctypes.c_double
+        lib.specdec_choose_k.argtypes = [vp, i32, dbl, i32, i32, vp, vp, vp, vp]
+        lib.specdec_choose_k.restype = ci
         _lib = lib
         return lib
 
@@ -294,3 +299,46 @@ def softmax_stats(logits: torch.Tensor, temperature: float, workspace: Optional[
     if rc != 0:
         raise SpecdecError(rc, "specdec_softmax_stats")
     return rmax, rsum
+
+
+def acceptance_counts(num_accepted: torch.Tensor, K: int, k_per_req: Optional[torch.Tensor] = None,
+                      counters: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-position (drafted, tested, accepted) counts of one verify step
+    (specdec_acceptance_counts), added on the device to ``counters``: an
+    int64 [3, K] tensor holding the uint64 counters (zeros when None).
+    Returns the counters."""
+    lib = load()
+    dev = num_accepted.device
+    B = num_accepted.numel()
+    _check(num_accepted, "num_accepted", torch.int32, (B,), dev)
+    if k_per_req is not None:
+        _check(k_per_req, "k_per_req", torch.int32, (B,), dev)
+    if counters is None:
+        counters = torch.zeros((3, K), dtype=torch.int64, device=dev)
+    _check(counters, "counters", torch.int64, (3, K), dev)
+    rc = lib.specdec_acceptance_counts(_ptr(num_accepted), _ptr(k_per_req), B, int(K),
+                                       _ptr(counters), _stream(dev))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_acceptance_counts")
+    return counters
+
+
+def choose_k(counters, c: float, k_min: int, k_max: int):
+    """Draft length from [3, K] counters (specdec_choose_k, on the host):
+    returns (k, alpha_test, alpha_draft, speedup at k)."""
+    import numpy as np
+    lib = load()
+    if isinstance(counters, torch.Tensor):
+        counters = counters.detach().cpu().numpy()
+    cnt = np.ascontiguousarray(counters).view(np.uint64) if counters.dtype == np.int64 else \
+        np.ascontiguousarray(counters, dtype=np.uint64)
+    if cnt.ndim != 2 or cnt.shape[0] != 3:
+        raise ValueError("counters must be [3, K]")
+    K = cnt.shape[1]
+    at, ad, sp = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    k = ctypes.c_int32()
+    rc = lib.specdec_choose_k(cnt.ctypes.data, K, float(c), int(k_min), int(k_max),
+                              ctypes.byref(at), ctypes.byref(ad), ctypes.byref(k), ctypes.byref(sp))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_choose_k")
+    return k.value, at.value, ad.value, sp.value

@@ -295,4 +295,52 @@ int specdec_verify_greedy_timed(const void* target_logits, specdec_dtype_t dtype
                                     reinterpret_cast<hipEvent_t const*>(events)));
 }
 
+int specdec_acceptance_counts(const int32_t* num_accepted, const int32_t* k_per_req, int32_t B,
+                              int32_t K, uint64_t* counters, void* stream) {
+    if (B < 0 || B > kMaxBatch || K < 0 || K > kMaxK) return SPECDEC_EINVAL;
+    if (B == 0 || K == 0) return SPECDEC_OK;
+    if (!num_accepted || !counters) return SPECDEC_EINVAL;
+    TelemetryParams p{};
+    p.nacc = num_accepted;
+    p.kpr = k_per_req;
+    p.B = B;
+    p.K = K;
+    p.counters = counters;
+    return map_launch(launch_acceptance_counts(p, (hipStream_t)stream));
+}
+
+int specdec_choose_k(const uint64_t* counters, int32_t K, double c, int32_t k_min, int32_t k_max,
+                     double* alpha_test, double* alpha_draft, int32_t* k_out,
+                     double* speedup_out) {
+    if (!counters || !k_out || K < 0 || k_min < 0 || k_max < k_min || !(c >= 0.0) ||
+        !std::isfinite(c))
+        return SPECDEC_EINVAL;
+    double n_drafted = 0.0, n_tested = 0.0, n_accepted = 0.0;
+    for (int32_t i = 0; i < K; ++i) {
+        n_drafted += (double)counters[i];
+        n_tested += (double)counters[(size_t)K + i];
+        n_accepted += (double)counters[2 * (size_t)K + i];
+    }
+    const double a = (n_tested > 0.0) ? n_accepted / n_tested : 0.0;
+    if (alpha_test) *alpha_test = a;
+    if (alpha_draft) *alpha_draft = (n_drafted > 0.0) ? n_accepted / n_drafted : 0.0;
+    // Expected tokens for block length k: 1 + a + ... + a^k, grown one term
+    // at a time; cost 1 + c k target passes.
+    double tokens = 0.0, term = 1.0, best = -1.0;
+    int32_t best_k = k_min;
+    for (int32_t k = 0; k <= k_max; ++k) {
+        tokens += term;
+        term *= a;
+        if (k < k_min) continue;
+        const double speedup = tokens / (1.0 + c * (double)k);
+        if (speedup > best) {
+            best = speedup;
+            best_k = k;
+        }
+    }
+    *k_out = best_k;
+    if (speedup_out) *speedup_out = best;
+    return SPECDEC_OK;
+}
+
 }  // extern "C"

@@ -82,6 +82,13 @@ struct StatsParams {
 
 // events: null, or three events (each may be null) recorded on s before the
 // row kernel, after it, and after the call's last kernel.
+struct TelemetryParams {
+    const int32_t* nacc;        // [B] accepted drafts per request
+    const int32_t* kpr;         // [B] drafted positions per request, or null (K)
+    int B, K;
+    uint64_t* counters;         // [3 * K]: drafted, tested, accepted per position
+};
+
 hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s,
                          hipEvent_t const* events = nullptr);
 // events: null, or three events (each may be null) taken by the dispatches:
@@ -89,5 +96,6 @@ hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t
 hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
                          hipEvent_t const* events = nullptr);
 hipError_t launch_stats(const StatsParams& p, int dtype, bool vec, hipStream_t s);
+hipError_t launch_acceptance_counts(const TelemetryParams& p, hipStream_t s);
 
 }  // namespace specdec

@@ -147,3 +147,32 @@ def test_binding_rejects_bad_tensors():
         _lib.verify(t, None, torch.zeros((2, 2), dtype=torch.int32), torch.zeros((2, 4)), 1.0)
     with pytest.raises(TypeError):
         _lib.verify(t, None, torch.zeros((2, 3), dtype=torch.int64), torch.zeros((2, 4)), 1.0)
+
+
+def test_acceptance_counts_rejects(lib):
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.specdec_acceptance_counts(fake, None, -1, 3, fake, None) == EINVAL
+    assert lib.specdec_acceptance_counts(fake, None, 4, 256, fake, None) == EINVAL
+    assert lib.specdec_acceptance_counts(fake, None, 65536, 3, fake, None) == EINVAL
+    assert lib.specdec_acceptance_counts(None, None, 4, 3, fake, None) == EINVAL
+    assert lib.specdec_acceptance_counts(fake, None, 4, 3, None, None) == EINVAL
+    # Nothing to count: no launch, no pointer touched.
+    assert lib.specdec_acceptance_counts(None, None, 0, 3, None, None) == OK
+    assert lib.specdec_acceptance_counts(None, None, 5, 0, None, None) == OK
+
+
+def test_choose_k_rejects(lib):
+    import numpy as np
+    cnt = np.zeros(6, np.uint64)
+    k = ctypes.c_int32()
+    p = cnt.ctypes.data
+    assert lib.specdec_choose_k(None, 2, 0.1, 1, 4, None, None, ctypes.byref(k), None) == EINVAL
+    assert lib.specdec_choose_k(p, 2, 0.1, 1, 4, None, None, None, None) == EINVAL
+    assert lib.specdec_choose_k(p, -1, 0.1, 1, 4, None, None, ctypes.byref(k), None) == EINVAL
+    assert lib.specdec_choose_k(p, 2, 0.1, -1, 4, None, None, ctypes.byref(k), None) == EINVAL
+    assert lib.specdec_choose_k(p, 2, 0.1, 5, 4, None, None, ctypes.byref(k), None) == EINVAL
+    assert lib.specdec_choose_k(p, 2, -0.1, 1, 4, None, None, ctypes.byref(k), None) == EINVAL
+    assert lib.specdec_choose_k(p, 2, float("nan"), 1, 4, None, None, ctypes.byref(k), None) == EINVAL
+    assert lib.specdec_choose_k(p, 2, float("inf"), 1, 4, None, None, ctypes.byref(k), None) == EINVAL
+    assert lib.specdec_choose_k(p, 2, 0.1, 1, 4, None, None, ctypes.byref(k), None) == OK
+    assert k.value == 1      # no test performed: alpha_test = 0, the cheapest k
