@@ -91,6 +91,8 @@ class Oracle:
         lib.oracle_acceptance_counts.restype = ci
         lib.oracle_choose_k.argtypes = [vp, i32, dbl, i32, i32, vp, vp, vp, vp]
         lib.oracle_choose_k.restype = ci
+        lib.oracle_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
+        lib.oracle_ngram_propose.restype = ci
         self.lib = lib
         self.path = path
 
@@ -187,6 +189,23 @@ class Oracle:
         return k.value, at.value, ad.value, sp.value
 
 
+    def ngram_propose(self, context, context_len, n_min, n_max, K):
+        """n-gram drafter: context [B, L_stride] int32, context_len [B] int32.
+        Returns (draft_tokens [B, K] int32, k_per_req [B] int32)."""
+        ctx = _c(context, np.int32)
+        if ctx.ndim != 2:
+            raise ValueError("context must be [B, L]")
+        B, Ls = ctx.shape
+        ln = _c(context_len, np.int32).reshape(B)
+        drafts = np.empty((B, K), np.int32)
+        kp = np.empty(B, np.int32)
+        rc = self.lib.oracle_ngram_propose(_ptr(ctx), _ptr(ln), B, Ls, int(n_min), int(n_max), int(K),
+                                           _ptr(drafts), _ptr(kp))
+        if rc != 0:
+            raise ValueError("oracle_ngram_propose rejected its arguments")
+        return drafts, kp
+
+
 def default() -> Oracle:
     global _default
     with _lock:
@@ -213,3 +232,7 @@ def acceptance_counts(num_accepted, K, k_per_req=None, counters=None):
 
 def choose_k(counters, c, k_min, k_max):
     return default().choose_k(counters, c, k_min, k_max)
+
+
+def ngram_propose(context, context_len, n_min, n_max, K):
+    return default().ngram_propose(context, context_len, n_min, n_max, K)

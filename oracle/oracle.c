@@ -340,3 +340,51 @@ int oracle_choose_k(const uint64_t *counters, int32_t K, double c, int32_t k_min
     if (speedup_out) *speedup_out = best;
     return 0;
 }
+
+/*
+ * n-gram (prompt-lookup) drafter: find the last few tokens earlier in the
+ * context and propose what followed them there ([LP] "Choosing a draft",
+ * n-gram / prompt lookup row; [MF] "Non-Parametric Drafters": match n-grams
+ * in the prompt and speculate the tokens that followed; [SS] "Four kinds of
+ * drafter", n-gram lookup).  Readings where the pages are silent:
+ *   - the context is every token so far (prompt and output), c[0..L-1];
+ *   - longer suffixes first: n from n_max down to n_min;
+ *   - for a given n, the latest earlier occurrence: the largest end e < L-1
+ *     with c[e-n+1..e] == c[L-n..L-1];
+ *   - the proposal is c[e+1 .. e+K], cut at the end of the context (it may
+ *     run into the suffix itself); k_b is its length;
+ *   - no occurrence for any n: k_b = 0.
+ * draft_tokens[b, i] = -1 for i >= k_b.
+ */
+int oracle_ngram_propose(const int32_t *context, const int32_t *context_len, int32_t B,
+                         int32_t L_stride, int32_t n_min, int32_t n_max, int32_t K,
+                         int32_t *draft_tokens, int32_t *k_per_req) {
+    if (!context || !context_len || !draft_tokens || !k_per_req) return -1;
+    if (B < 0 || K < 0 || n_min < 1 || n_max < n_min || L_stride < 0) return -1;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t L = context_len[b];
+        if (L < 0 || L > L_stride) return -1;
+        const int32_t *c = context + (size_t)b * L_stride;
+        int32_t found_e = -1;
+        for (int32_t n = n_max; n >= n_min && found_e < 0; --n) {
+            if (n > L - 1) continue;   /* the suffix needs an earlier occurrence */
+            for (int32_t e = L - 2; e >= n - 1; --e) {
+                int32_t m = 0;
+                while (m < n && c[e - m] == c[L - 1 - m]) ++m;
+                if (m == n) {
+                    found_e = e;
+                    break;
+                }
+            }
+        }
+        int32_t kb = 0;
+        if (found_e >= 0) {
+            kb = L - 1 - found_e;
+            if (kb > K) kb = K;
+        }
+        for (int32_t i = 0; i < K; ++i)
+            draft_tokens[(size_t)b * K + i] = (i < kb) ? c[found_e + 1 + i] : -1;
+        k_per_req[b] = kb;
+    }
+    return 0;
+}

@@ -653,6 +653,67 @@ def pin_alpha_test_estimates_alpha(o):
         assert ad < alpha - 0.01, (alpha, ad)
 
 
+def _ngram_by_rfind(ctx, n_min, n_max, K):
+    """The drafter's reading restated with str.rfind: one code point per
+    token; the haystack stops one token short of the end, so a match can
+    not be the suffix itself."""
+    s = "".join(chr(0x100 + int(t)) for t in ctx)
+    L = len(ctx)
+    for n in range(n_max, n_min - 1, -1):
+        if n > L - 1:
+            continue
+        idx = s[:L - 1].rfind(s[L - n:])
+        if idx >= 0:
+            e = idx + n - 1
+            prop = [int(t) for t in ctx[e + 1:e + 1 + K]]
+            return prop + [-1] * (K - len(prop)), len(prop)
+    return [-1] * K, 0
+
+
+def pin_ngram_drafter(o):
+    """n-gram / prompt lookup: find the last few tokens earlier in the
+    context and propose what followed them (3.5 Speculative Decoding,
+    'Choosing a draft'; Mathematical Foundations, 'Non-Parametric Drafters';
+    First Principles, 'Four kinds of drafter').  Hand cases for each reading,
+    then random copy-heavy contexts against str.rfind."""
+    def run(tokens, n_min, n_max, K):
+        ctx = np.array([tokens], np.int32)
+        d, k = o.ngram_propose(ctx, np.array([len(tokens)], np.int32), n_min, n_max, K)
+        return list(d[0][:k[0]]), int(k[0]), list(d[0])
+    # 'the cat sat on the mat . the cat' -> 'sat on the'
+    w = "the cat sat on the mat . the cat".split()
+    ids = {t: i for i, t in enumerate(dict.fromkeys(w))}
+    prop, k, _ = run([ids[t] for t in w], 1, 4, 3)
+    assert [list(ids)[i] for i in prop] == ["sat", "on", "the"] and k == 3
+    # No earlier occurrence: no drafts, padding -1.
+    assert run([1, 2, 3, 4], 1, 3, 3) == ([], 0, [-1, -1, -1])
+    # The latest occurrence wins: ... 5 7 | ... 5 8 | 5  -> propose 8.
+    assert run([5, 7, 9, 5, 8, 9, 5], 1, 1, 1)[0] == [8]
+    # A longer match beats a later shorter one: suffix (3, 4); (3, 4) occurs
+    # early (followed by 10), 4 alone occurs late (followed by 11).
+    assert run([3, 4, 10, 4, 11, 3, 4], 1, 2, 1)[0] == [10]
+    # n_min: a length-1 match is ignored when n_min = 2.
+    assert run([7, 1, 2, 9, 7], 2, 3, 2)[1] == 0
+    # Cut at the end of the context, running into the suffix: 6 6 6 -> 6 6.
+    assert run([6, 6, 6], 1, 2, 4)[0] == [6]
+    assert run([1, 6, 6, 6], 1, 1, 4)[0] == [6]
+    rng = np.random.default_rng(77)
+    for _ in range(300):
+        L = int(rng.integers(1, 60))
+        base = rng.integers(0, 6, size=L).astype(np.int32)
+        # Copy a random segment to the end now and then (copy-heavy text).
+        if L > 8 and rng.random() < 0.5:
+            a = int(rng.integers(0, L - 4))
+            m = int(rng.integers(2, 5))
+            base[L - m:] = base[a:a + m]
+        n_min = int(rng.integers(1, 4))
+        n_max = n_min + int(rng.integers(0, 4))
+        K = int(rng.integers(1, 6))
+        _, k, d = run(list(base), n_min, n_max, K)
+        ref, kr = _ngram_by_rfind(base, n_min, n_max, K)
+        assert (d, k) == (ref, kr), (list(base), n_min, n_max, K)
+
+
 ALL_PINS = [
     pin_stats_logsumexp, pin_stats_closed_forms,
     pin_check_your_understanding, pin_single_position_experiment,
@@ -664,5 +725,5 @@ ALL_PINS = [
     pin_invariants, pin_greedy_worked_trace, pin_greedy_ties_and_bonus,
     pin_greedy_equals_argmax_decoding, pin_markov_chain_third_token,
     pin_speedup_table_and_choice, pin_acceptance_count_identities,
-    pin_alpha_test_estimates_alpha,
+    pin_alpha_test_estimates_alpha, pin_ngram_drafter,
 ]

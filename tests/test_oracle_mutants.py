@@ -53,6 +53,14 @@ MUTANTS = {
     "tokens_without_extra_token": ("for (int32_t i = 0; i <= k; ++i) {\n            tokens += power;",
                                    "for (int32_t i = 1; i <= k; ++i) {\n            tokens += power;"),
     "ties_pick_larger_k": ("if (speedup > best) {", "if (speedup >= best) {"),
+    "ngram_earliest_occurrence": ("for (int32_t e = L - 2; e >= n - 1; --e) {",
+                                  "for (int32_t e = n - 1; e <= L - 2; ++e) {"),
+    "ngram_shorter_first": ("for (int32_t n = n_max; n >= n_min && found_e < 0; --n) {",
+                            "for (int32_t n = n_min; n <= n_max && found_e < 0; ++n) {"),
+    "ngram_matches_itself": ("for (int32_t e = L - 2; e >= n - 1; --e) {",
+                             "for (int32_t e = L - 1; e >= n - 1; --e) {"),
+    "ngram_proposes_from_match_end": ("? c[found_e + 1 + i] : -1;", "? c[found_e + i] : -1;"),
+    "ngram_no_run_in": ("kb = L - 1 - found_e;", "kb = L - 1 - found_e - 1;"),
 }
 
 RUNNER = r"""
