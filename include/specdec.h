@@ -204,6 +204,33 @@ int specdec_acceptance_counts(const int32_t *num_accepted, const int32_t *k_per_
                               int32_t K, uint64_t *counters, void *stream);
 
 /*
+ * n-gram (prompt-lookup) drafter: find the last few tokens earlier in the
+ * context and propose what followed them there ("3.5 Speculative
+ * Decoding", "Choosing a draft": n-gram / prompt lookup; "Speculative
+ * Decoding: Mathematical Foundations ...", "Non-Parametric Drafters";
+ * "Speculative Decoding from First Principles", "Four kinds of drafter").
+ * For request b with context c = context[b, 0 .. L-1] (L = context_len[b],
+ * every token so far: prompt and output):
+ *   - for n = n_max down to n_min, the suffix c[L-n .. L-1] is looked for
+ *     earlier in the context; the first n that occurs is used, at its latest
+ *     occurrence: the largest e < L-1 with c[e-n+1 .. e] = c[L-n .. L-1];
+ *   - the proposal is c[e+1 .. e+K], cut at the end of the context;
+ *     k_per_req[b] is its length (0 when no suffix of n_min or more tokens
+ *     occurs earlier) and draft_tokens[b, i] = -1 for i >= k_per_req[b].
+ *   context      [B, L_stride] int32, device, row-major (row stride L_stride)
+ *   context_len  [B] int32, device, 0 <= context_len[b] <= L_stride (values
+ *                outside are clamped)
+ *   draft_tokens [B, K] int32, device (output)
+ *   k_per_req    [B] int32, device (output), ready for
+ *                specdec_verify_greedy's k_per_req
+ * 0 <= B <= 65535, 0 <= K <= 255, 1 <= n_min <= n_max <= 64, L_stride >= 0,
+ * else SPECDEC_EINVAL.  One workgroup per request; no workspace.
+ */
+int specdec_ngram_propose(const int32_t *context, const int32_t *context_len, int32_t B,
+                          int32_t L_stride, int32_t n_min, int32_t n_max, int32_t K,
+                          int32_t *draft_tokens, int32_t *k_per_req, void *stream);
+
+/*
  * Draft length from the counters (host function, synchronous; `counters`
  * is HOST memory, [3 * K] as above).  alpha_test = sum accepted / sum
  * tested, the per-draft acceptance probability of the independent-

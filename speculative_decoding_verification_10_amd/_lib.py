@@ -78,6 +78,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.specdec_verify_greedy_timed.restype = ci
         lib.specdec_acceptance_counts.argtypes = [vp, vp, i32, i32, vp, vp]
         lib.specdec_acceptance_counts.restype = ci
+        lib.specdec_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+        lib.specdec_ngram_propose.restype = ci
         dbl = ctypes.c_double
         lib.specdec_choose_k.argtypes = [vp, i32, dbl, i32, i32, vp, vp, vp, vp]
         lib.specdec_choose_k.restype = ci
@@ -342,3 +344,29 @@ def choose_k(counters, c: float, k_min: int, k_max: int):
     if rc != 0:
         raise SpecdecError(rc, "specdec_choose_k")
     return k.value, at.value, ad.value, sp.value
+
+
+def ngram_propose(context: torch.Tensor, context_len: torch.Tensor, n_min: int, n_max: int,
+                  K: int, out=None):
+    """n-gram (prompt-lookup) drafter (specdec_ngram_propose).  context
+    [B, L] int32, context_len [B] int32, both on the device.  Returns
+    (draft_tokens [B, K] int32, k_per_req [B] int32)."""
+    lib = load()
+    if context.dim() != 2:
+        raise ValueError("context must be [B, L]")
+    B, Ls = context.shape
+    dev = context.device
+    _check(context, "context", torch.int32, (B, Ls), dev)
+    _check(context_len, "context_len", torch.int32, (B,), dev)
+    if out is None:
+        drafts = torch.empty((B, K), dtype=torch.int32, device=dev)
+        kpr = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        drafts, kpr = out
+        _check(drafts, "draft_tokens", torch.int32, (B, K), dev)
+        _check(kpr, "k_per_req", torch.int32, (B,), dev)
+    rc = lib.specdec_ngram_propose(_ptr(context), _ptr(context_len), B, Ls, int(n_min), int(n_max),
+                                   int(K), _ptr(drafts), _ptr(kpr), _stream(dev))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_ngram_propose")
+    return drafts, kpr

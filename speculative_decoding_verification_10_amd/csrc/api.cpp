@@ -309,6 +309,28 @@ int specdec_acceptance_counts(const int32_t* num_accepted, const int32_t* k_per_
     return map_launch(launch_acceptance_counts(p, (hipStream_t)stream));
 }
 
+int specdec_ngram_propose(const int32_t* context, const int32_t* context_len, int32_t B,
+                          int32_t L_stride, int32_t n_min, int32_t n_max, int32_t K,
+                          int32_t* draft_tokens, int32_t* k_per_req, void* stream) {
+    if (B < 0 || B > kMaxBatch || K < 0 || K > kMaxK || L_stride < 0 || n_min < 1 ||
+        n_max < n_min || n_max > kMaxNgram)
+        return SPECDEC_EINVAL;
+    if (B == 0) return SPECDEC_OK;
+    if (!context_len || !k_per_req || (K > 0 && !draft_tokens) || (L_stride > 0 && !context))
+        return SPECDEC_EINVAL;
+    NgramParams p{};
+    p.ctx = context;
+    p.len = context_len;
+    p.B = B;
+    p.Ls = L_stride;
+    p.n_min = n_min;
+    p.n_max = n_max;
+    p.K = K;
+    p.drafts = draft_tokens;
+    p.kpr = k_per_req;
+    return map_launch(launch_ngram(p, (hipStream_t)stream));
+}
+
 int specdec_choose_k(const uint64_t* counters, int32_t K, double c, int32_t k_min, int32_t k_max,
                      double* alpha_test, double* alpha_draft, int32_t* k_out,
                      double* speedup_out) {

@@ -89,6 +89,17 @@ struct TelemetryParams {
     uint64_t* counters;         // [3 * K]: drafted, tested, accepted per position
 };
 
+// Longest n-gram the drafter matches.
+constexpr int32_t kMaxNgram = 64;
+
+struct NgramParams {
+    const int32_t* ctx;         // [B, Ls] context tokens, row stride Ls
+    const int32_t* len;         // [B] context lengths
+    int B, Ls, n_min, n_max, K;
+    int32_t* drafts;            // [B, K] proposals, -1 past k_b
+    int32_t* kpr;               // [B] k_b: proposals per request
+};
+
 hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s,
                          hipEvent_t const* events = nullptr);
 // events: null, or three events (each may be null) taken by the dispatches:
@@ -97,5 +108,6 @@ hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t
                          hipEvent_t const* events = nullptr);
 hipError_t launch_stats(const StatsParams& p, int dtype, bool vec, hipStream_t s);
 hipError_t launch_acceptance_counts(const TelemetryParams& p, hipStream_t s);
+hipError_t launch_ngram(const NgramParams& p, hipStream_t s);
 
 }  // namespace specdec

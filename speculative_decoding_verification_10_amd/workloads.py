@@ -235,3 +235,33 @@ def tiny_steps(n_steps: int, set_index: int = 0) -> Workload:
     return Workload(name="tiny", B=n_steps, K=K, V=V, dtype=base.dtype,
                     temperature=base.temperature, greedy=False, target=target, draft=draft,
                     draft_tokens=tokens, uniforms=uniforms, meta=dict(base.meta, steps=n_steps))
+
+
+def ngram_contexts(B: int = 256, L_max: int = 4096, V: int = 151936, set_index: int = 0,
+                   copy_prob: float = 0.6):
+    """Copy-heavy token contexts for the n-gram drafter (a stand-in for the
+    code-edit / RAG traffic the pages name, where the output quotes its
+    input): each request's context is built from spans of 8..64 tokens,
+    each span either copied from a random earlier position of the same
+    context (probability copy_prob) or drawn uniformly from [0, V).
+    Lengths are uniform on [L_max / 4, L_max].  Returns (context [B, L_max]
+    int32, padded with uniform ids past each length; context_len [B] int32).
+    Seed 1006, stream set_index."""
+    rng = np.random.default_rng(np.random.SeedSequence([1006, set_index]))
+    ctx = rng.integers(0, V, size=(B, L_max), dtype=np.int64).astype(np.int32)
+    lens = rng.integers(max(1, L_max // 4), L_max + 1, size=B).astype(np.int32)
+    for b in range(B):
+        L = int(lens[b])
+        pos = min(L, 64)
+        while pos < L:
+            m = int(rng.integers(8, 65))
+            m = min(m, L - pos)
+            if rng.random() < copy_prob:
+                src = int(rng.integers(0, pos))
+                if src + m <= pos:
+                    ctx[b, pos:pos + m] = ctx[b, src:src + m]
+                else:                # overlaps the span being written
+                    for i in range(m):
+                        ctx[b, pos + i] = ctx[b, src + i]
+            pos += m
+    return ctx, lens

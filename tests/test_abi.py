@@ -176,3 +176,20 @@ def test_choose_k_rejects(lib):
     assert lib.specdec_choose_k(p, 2, float("inf"), 1, 4, None, None, ctypes.byref(k), None) == EINVAL
     assert lib.specdec_choose_k(p, 2, 0.1, 1, 4, None, None, ctypes.byref(k), None) == OK
     assert k.value == 1      # no test performed: alpha_test = 0, the cheapest k
+
+
+def test_ngram_propose_rejects(lib):
+    f = ctypes.c_void_p(0x1000)
+    # context, context_len, B, L_stride, n_min, n_max, K, drafts, k_per_req, stream
+    assert lib.specdec_ngram_propose(f, f, -1, 10, 1, 3, 3, f, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(f, f, 65536, 10, 1, 3, 3, f, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(f, f, 4, -1, 1, 3, 3, f, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(f, f, 4, 10, 0, 3, 3, f, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(f, f, 4, 10, 3, 2, 3, f, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(f, f, 4, 10, 1, 65, 3, f, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(f, f, 4, 10, 1, 3, 256, f, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(None, f, 4, 10, 1, 3, 3, f, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(f, None, 4, 10, 1, 3, 3, f, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(f, f, 4, 10, 1, 3, 3, None, f, None) == EINVAL
+    assert lib.specdec_ngram_propose(f, f, 4, 10, 1, 3, 3, f, None, None) == EINVAL
+    assert lib.specdec_ngram_propose(None, None, 0, 10, 1, 3, 3, None, None, None) == OK
