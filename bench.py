@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+NGRAM_N_MIN, NGRAM_N_MAX = 1, 4     # suffix lengths the n-gram workload's drafter tries
 METRIC = "verified positions/s + HBM GB/s (% of peak), B=64 k=5 V=128256 bf16"
 PROFILE_COUNTERS = {"headline": os.path.join(ROOT, "profiles", "verify_headline_counters.txt"),
                     "greedy": os.path.join(ROOT, "profiles", "verify_greedy_counters.txt")}
@@ -95,24 +96,37 @@ def read_counters(workload, key):
         return None
 
 
-def cpu_baseline(wl, budget_s: float):
+def cpu_baseline(wl, name: str, budget_s: float, ngram=None):
     """The fp64 oracle as it stands, on the host cores, over a bounded
-    number of steps of the same workload."""
+    number of steps of the same workload (for the n-gram workload: the
+    oracle drafter, then the oracle greedy verify)."""
+    import numpy as np
     import oracle
     oracle.default()
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.perf_counter()
     n = 0
+    pos = 0
     while True:
-        oracle.verify(wl.target, wl.draft, wl.draft_tokens, wl.uniforms, wl.temperature, wl.k_per_req)
+        if ngram is not None:
+            ctx, lens, n_min, n_max = ngram
+            drafts, kp = oracle.ngram_propose(ctx, lens, n_min, n_max, wl.K)
+            oracle.verify_greedy(wl.target, drafts, kp)
+            pos += int(np.sum(kp.astype(np.int64) + 1))
+        elif wl.greedy:
+            oracle.verify_greedy(wl.target, wl.draft_tokens, wl.k_per_req)
+            pos += wl.verified_positions()
+        else:
+            oracle.verify(wl.target, wl.draft, wl.draft_tokens, wl.uniforms, wl.temperature,
+                          wl.k_per_req)
+            pos += wl.verified_positions()
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 5000:
             break
-    pos = wl.verified_positions() * n
     return {"value": pos / el, "unit": "verified positions/s", "cores": cores, "kind": "oracle",
-            "sample": "%d full steps of the headline workload (%d verified positions) in %.1f s"
-                      % (n, pos, el)}
+            "sample": "%d full steps of the %s workload (%d verified positions) in %.1f s"
+                      % (n, name, pos, el)}
 
 
 def main():
@@ -121,7 +135,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=5, help="device-resident input copies to rotate over")
-    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--workload", default="headline",
+                    help="headline (default), tiny, peaked, greedy, ragged, or ngram (the n-gram "
+                         "drafter over copy-heavy contexts, then the greedy verify of its drafts)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each call from a captured HIP graph")
@@ -154,8 +170,17 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
-    wl = workloads.make(args.workload)
+    # The n-gram workload: the drafter over seeded copy-heavy contexts, then
+    # the greedy verify of its drafts against the greedy workload's logits.
+    ngram = args.workload == "ngram"
+    wl = workloads.make("greedy" if ngram else args.workload)
     K = wl.K
+    ngram_host = None
+    if ngram:
+        ctx_h, lens_h = workloads.ngram_contexts(B=wl.B, V=wl.V)
+        ngram_host = (ctx_h, lens_h, NGRAM_N_MIN, NGRAM_N_MAX)
+        ctx_d = torch.from_numpy(ctx_h).to(dev)
+        lens_d = torch.from_numpy(lens_h).to(dev)
     sets = []
     base = {
         "target": dev_logits(wl.target, dev),
@@ -169,6 +194,9 @@ def main():
     tokens = torch.from_numpy(wl.draft_tokens).to(dev)
     unif = torch.from_numpy(wl.uniforms).to(dev)
     kpr = None if wl.k_per_req is None else torch.from_numpy(wl.k_per_req).to(dev)
+    if ngram:                      # the drafter writes these every step
+        tokens = torch.zeros_like(tokens)
+        kpr = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
     out = (torch.empty((wl.B, K + 1), dtype=torch.int32, device=dev),
            torch.empty((wl.B,), dtype=torch.int32, device=dev), None)
     greedy = wl.greedy
@@ -208,6 +236,12 @@ def main():
 
     def step(r):
         a = cargs[r % len(cargs)]
+        if ngram:
+            rc = lib.specdec_ngram_propose(ctx_d.data_ptr(), lens_d.data_ptr(), wl.B, ctx_d.shape[1],
+                                           NGRAM_N_MIN, NGRAM_N_MAX, K, tokens.data_ptr(), kpr.data_ptr(),
+                                           stream.cuda_stream)
+            if rc != 0:
+                raise sd.SpecdecError(rc, "bench drafter")
         if handles is not None:
             rc = (lib.specdec_verify_greedy_timed if greedy else lib.specdec_verify_timed)(*a, handles[r])
         else:
@@ -220,6 +254,8 @@ def main():
 
     def checked_step(r):
         st = sets[r % len(sets)]
+        if ngram:
+            sd.ngram_propose(ctx_d, lens_d, NGRAM_N_MIN, NGRAM_N_MAX, K, out=(tokens, kpr))
         if greedy:
             sd.verify_greedy(st["target"], tokens, k_per_req=kpr, workspace=ws, out=out)
         else:
@@ -250,6 +286,8 @@ def main():
         run(r)
     torch.cuda.synchronize()
     nacc = out[1].cpu().numpy()
+    if ngram:                      # the step's drafted positions come from the drafter
+        wl.k_per_req = kpr.cpu().numpy()
 
     if phase:
         nev = 3
@@ -284,6 +322,27 @@ def main():
 
     positions = wl.verified_positions()
     alg = algorithmic_bytes(wl, nacc)
+    drafter = None
+    if ngram:
+        # The drafter reads every context token once and writes the drafts.
+        dbytes = int(np.sum(lens_h.astype(np.int64))) * 4 + wl.B * 4 + wl.B * (K + 1) * 4
+        alg += dbytes
+        n_dr = 200
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_dr):
+            lib.specdec_ngram_propose(ctx_d.data_ptr(), lens_d.data_ptr(), wl.B, ctx_d.shape[1],
+                                      NGRAM_N_MIN, NGRAM_N_MAX, K, tokens.data_ptr(), kpr.data_ptr(),
+                                      stream.cuda_stream)
+        e1.record(stream)
+        e1.synchronize()
+        d_ms = e0.elapsed_time(e1) / n_dr
+        drafter = {"kernel": "ngram_propose", "algorithmic_bytes": dbytes,
+                   "us_per_call": round(d_ms * 1e3, 3),
+                   "achieved_gbps": round(dbytes / (d_ms * 1e-3) / 1e9, 1),
+                   "timing": "%d back-to-back calls between two stream events" % n_dr,
+                   "drafted_requests": int(np.count_nonzero(wl.k_per_req)),
+                   "n_min": NGRAM_N_MIN, "n_max": NGRAM_N_MAX}
     value = positions / (ms_per_step * 1e-3)
     gbps = alg / (ms_per_step * 1e-3) / 1e9
     achieved = alg / (per_launch_ms * 1e-3) / 1e9
@@ -343,6 +402,8 @@ def main():
     }
     if call is not None:
         line["call_roofline"] = call
+    if drafter is not None:
+        line["drafter"] = drafter
     if counters is not None:
         # The draft length the step's own acceptance counters suggest at the
         # worked example's draft cost ratio (c = 0.05).
@@ -359,7 +420,7 @@ def main():
         torch.cuda.synchronize()
         line["calibration_copy_bytes"] = n
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(wl, args.workload, args.cpu_budget, ngram_host)
     print(json.dumps(line), flush=True)
 
 

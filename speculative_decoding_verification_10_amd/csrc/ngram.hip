@@ -9,8 +9,8 @@
 // first) go to LDS; every thread takes end positions e = L-2-t, L-2-t-256,
 // ... and measures how many tokens ending at e match the suffix, capped at
 // n_max.  The occurrence kept is the largest (matched length, e): the longest
-// suffix that occurs earlier, and its latest occurrence.  The proposal is
-// the up to K tokens after e, cut at the end of the context.
+// suffix that occurs earlier, and its latest occurrence.  The proposal is the
+// up to K tokens after e, cut at the end of the context.
 #include "internal.h"
 
 namespace specdec {
@@ -30,11 +30,26 @@ __global__ __launch_bounds__(kThreads) void ngram_propose(NgramParams a) {
     for (int i = threadIdx.x; i < ns; i += kThreads) suf[i] = c[L - 1 - i];
     __syncthreads();
     // Key (matched length << 32 | e + 1); 0 = no occurrence of >= n_min tokens.
+    // Each pass loads the last token of kBatch end positions per thread at
+    // once; only positions whose last token matches read further back.
+    constexpr int kBatch = 8;
     unsigned long long best = 0;
-    for (int e = L - 2 - (int)threadIdx.x; e >= a.n_min - 1; e -= kThreads) {
-        int m = 0;
-        while (m < ns && m <= e && c[e - m] == suf[m]) ++m;
-        if (m >= a.n_min) best = max_u64(best, ((unsigned long long)m << 32) | (unsigned)(e + 1));
+    const int32_t s0 = (ns > 0) ? suf[0] : 0;
+    for (int base = L - 2 - (int)threadIdx.x; base >= a.n_min - 1; base -= kBatch * kThreads) {
+        int32_t tok[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int e = base - j * kThreads;
+            tok[j] = (e >= a.n_min - 1) ? c[e] : ~s0;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (tok[j] != s0) continue;
+            const int e = base - j * kThreads;
+            int m = 1;
+            while (m < ns && m <= e && c[e - m] == suf[m]) ++m;
+            if (m >= a.n_min) best = max_u64(best, ((unsigned long long)m << 32) | (unsigned)(e + 1));
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) best = max_u64(best, __shfl_xor(best, o, 64));
