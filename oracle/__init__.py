@@ -93,6 +93,10 @@ class Oracle:
         lib.oracle_choose_k.restype = ci
         lib.oracle_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
         lib.oracle_ngram_propose.restype = ci
+        lib.oracle_tree_verify_greedy.argtypes = [vp, ci, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+        lib.oracle_tree_verify_greedy.restype = ci
+        lib.oracle_tree_mask.argtypes = [vp, vp, i32, i32, vp, vp]
+        lib.oracle_tree_mask.restype = ci
         self.lib = lib
         self.path = path
 
@@ -206,6 +210,39 @@ class Oracle:
         return drafts, kp
 
 
+    def tree_verify_greedy(self, target, node_tokens, parents, n_nodes=None):
+        """Greedy tree verify: target [B, N+1, V], node_tokens / parents
+        [B, N] int32, n_nodes [B] int32 or None.  Returns out_tokens
+        [B, N+1], path_nodes [B, N], num_accepted [B]."""
+        target = np.ascontiguousarray(target)
+        code = _dtype_code(target)
+        B, N1, V = target.shape
+        N = N1 - 1
+        tok = _c(node_tokens, np.int32).reshape(B, N)
+        par = _c(parents, np.int32).reshape(B, N)
+        nn = None if n_nodes is None else _c(n_nodes, np.int32).reshape(B)
+        out = np.empty((B, N + 1), np.int32)
+        path = np.empty((B, N), np.int32)
+        nacc = np.empty(B, np.int32)
+        rc = self.lib.oracle_tree_verify_greedy(_ptr(target), code, _ptr(tok), _ptr(par), _ptr(nn),
+                                                B, N, V, _ptr(out), _ptr(path), _ptr(nacc))
+        if rc != 0:
+            raise ValueError("oracle_tree_verify_greedy rejected its arguments")
+        return {"out_tokens": out, "path_nodes": path, "num_accepted": nacc}
+
+    def tree_mask(self, parents, n_nodes=None):
+        """Ancestor-or-self attention mask [B, N, N] uint8 and depth [B, N]
+        int32 of flattened draft trees (parents [B, N] int32)."""
+        par = _c(parents, np.int32)
+        B, N = par.shape
+        nn = None if n_nodes is None else _c(n_nodes, np.int32).reshape(B)
+        mask = np.empty((B, N, N), np.uint8)
+        depth = np.empty((B, N), np.int32)
+        if self.lib.oracle_tree_mask(_ptr(par), _ptr(nn), B, N, _ptr(mask), _ptr(depth)) != 0:
+            raise ValueError("oracle_tree_mask rejected its arguments")
+        return mask, depth
+
+
 def default() -> Oracle:
     global _default
     with _lock:
@@ -236,3 +273,11 @@ def choose_k(counters, c, k_min, k_max):
 
 def ngram_propose(context, context_len, n_min, n_max, K):
     return default().ngram_propose(context, context_len, n_min, n_max, K)
+
+
+def tree_verify_greedy(target, node_tokens, parents, n_nodes=None):
+    return default().tree_verify_greedy(target, node_tokens, parents, n_nodes)
+
+
+def tree_mask(parents, n_nodes=None):
+    return default().tree_mask(parents, n_nodes)

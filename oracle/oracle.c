@@ -388,3 +388,105 @@ int oracle_ngram_propose(const int32_t *context, const int32_t *context_len, int
     }
     return 0;
 }
+
+/*
+ * Greedy tree verification ([LP] "Tree verification": a tree of drafted
+ * nodes flattened into one sequence, every node attending to its ancestors
+ * only; one target pass scores all nodes; keep the longest root-to-leaf
+ * path that passes verification; [MF] "Tree-Based Verification and Custom
+ * Attention Masks").  Greedy acceptance (the chain rule applied along each
+ * path, [LP] "Worked example"):
+ *   - node n (flattened order, parent[n] < n, -1 = child of the root) is
+ *     accepted iff its parent is accepted (the root always is) and its token
+ *     equals the argmax of the parent's target row (row 0 = the root's,
+ *     row p + 1 = the row after node p);
+ *   - the kept path ends at the deepest accepted node, the lowest index on
+ *     ties (only when siblings repeat a token);
+ *   - the emitted tokens are the path's tokens, root side first, then the
+ *     argmax of the row after the path's last node (row 0 when no node is
+ *     accepted); num_accepted is the path length.
+ * target [B, N+1, V]; node_tokens, parents [B, N]; n_nodes [B] or NULL (N).
+ * out_tokens [B, N+1] (-1 padded); path_nodes [B, N] (node indices, root
+ * side first, -1 padded); num_accepted [B].
+ */
+int oracle_tree_verify_greedy(const void *target, int dtype, const int32_t *node_tokens,
+                              const int32_t *parents, const int32_t *n_nodes, int32_t B,
+                              int32_t N, int32_t V, int32_t *out_tokens, int32_t *path_nodes,
+                              int32_t *num_accepted) {
+    if (!target || !out_tokens || !num_accepted || B < 0 || N < 0 || V <= 0) return -1;
+    if (N > 0 && (!node_tokens || !parents)) return -1;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t n_b = n_nodes ? n_nodes[b] : N;
+        if (n_b < 0 || n_b > N) { err |= 1; continue; }
+        const int32_t *tok = node_tokens + (size_t)b * N;
+        const int32_t *par = parents + (size_t)b * N;
+        int32_t amax[N + 1], depth[N + 1], acc[N + 1];
+        for (int32_t r = 0; r <= n_b; ++r) {
+            size_t off = ((size_t)b * (N + 1) + r) * (size_t)V;
+            int32_t best = 0;
+            double bv = load_logit(target, dtype, off);
+            for (int32_t t = 1; t < V; ++t) {
+                double l = load_logit(target, dtype, off + (size_t)t);
+                if (l > bv) { bv = l; best = t; }
+            }
+            amax[r] = best;
+        }
+        int32_t end = -1, end_depth = 0;
+        for (int32_t n = 0; n < n_b; ++n) {
+            const int32_t p = par[n];
+            if (p < -1 || p >= n) { err |= 1; break; }
+            const int32_t parent_ok = (p < 0) ? 1 : acc[p];
+            acc[n] = parent_ok && tok[n] == amax[p + 1];
+            depth[n] = (p < 0) ? 1 : depth[p] + 1;
+            if (acc[n] && depth[n] > end_depth) { end = n; end_depth = depth[n]; }
+        }
+        int32_t *out = out_tokens + (size_t)b * (N + 1);
+        int32_t *path = path_nodes ? path_nodes + (size_t)b * N : NULL;
+        for (int32_t i = 0; i <= N; ++i) out[i] = -1;
+        if (path) for (int32_t i = 0; i < N; ++i) path[i] = -1;
+        for (int32_t n = end, d = end_depth - 1; n >= 0; n = par[n], --d) {
+            out[d] = tok[n];
+            if (path) path[d] = n;
+        }
+        out[end_depth] = amax[end + 1];
+        num_accepted[b] = end_depth;
+    }
+    return err ? -1 : 0;
+}
+
+/*
+ * Tree attention metadata ([LP] "Tree verification": each flattened node
+ * attends to the context, its ancestors and itself, never to siblings or
+ * cousins; nodes at equal depth share a position index; [MF] "Tree-Based
+ * Verification and Custom Attention Masks": the mask admits j for i exactly
+ * when j is an ancestor of i).  Reading: the diagonal is admitted, as in the
+ * [LP] mask table.
+ *   mask[b, i, j] = 1 iff j == i or j is an ancestor of i, else 0 (j < n_b);
+ *                   rows and columns at or beyond n_b are 0;
+ *   depth[b, i]   = 1 for a child of the root, depth of the parent + 1
+ *                   otherwise; -1 at or beyond n_b.
+ * parents [B, N] (parent[n] < n, -1 = root); n_nodes [B] or NULL (N).
+ * mask [B, N, N] bytes; depth [B, N].
+ */
+int oracle_tree_mask(const int32_t *parents, const int32_t *n_nodes, int32_t B, int32_t N,
+                     uint8_t *mask, int32_t *depth) {
+    if (B < 0 || N < 0 || !mask || !depth || (N > 0 && !parents)) return -1;
+    int err = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t n_b = n_nodes ? n_nodes[b] : N;
+        const int32_t *par = parents + (size_t)b * N;
+        uint8_t *m = mask + (size_t)b * N * N;
+        int32_t *d = depth + (size_t)b * N;
+        for (size_t i = 0; i < (size_t)N * N; ++i) m[i] = 0;
+        for (int32_t i = 0; i < N; ++i) d[i] = -1;
+        if (n_b < 0 || n_b > N) { err = 1; continue; }
+        for (int32_t i = 0; i < n_b; ++i) {
+            if (par[i] < -1 || par[i] >= i) { err = 1; break; }
+            d[i] = par[i] < 0 ? 1 : d[par[i]] + 1;
+            for (int32_t j = i; j >= 0; j = par[j]) m[(size_t)i * N + j] = 1;
+        }
+    }
+    return err ? -1 : 0;
+}

@@ -714,6 +714,150 @@ def pin_ngram_drafter(o):
         assert (d, k) == (ref, kr), (list(base), n_min, n_max, K)
 
 
+def _tree_logits(B, N, V, argmax_rows, rng=None):
+    """Logits whose row r has its maximum at argmax_rows[b][r] (lower,
+    distinct values elsewhere)."""
+    rng = rng or np.random.default_rng(0)
+    t = rng.random((B, N + 1, V)).astype(np.float32)
+    for b in range(B):
+        for r, a in enumerate(argmax_rows[b]):
+            t[b, r, a] = 2.0
+    return t
+
+
+def pin_tree_verify_page_trees(o):
+    """The pages' trees: 3.5 Speculative Decoding, 'Tree verification'
+    (flattened [a, b, a1, a2, b1, b2]) and Mathematical Foundations,
+    'Tree-Based Verification' (its drawn topology): the longest
+    root-to-leaf path whose tokens match the target's argmax after their
+    parent is kept, then the argmax after its last node."""
+    V = 16
+    a, b, a1, a2, b1, b2 = 1, 2, 3, 4, 5, 6
+    tok = np.array([[a, b, a1, a2, b1, b2]], np.int32)
+    par = np.array([[-1, -1, 0, 0, 1, 1]], np.int32)
+    # rows: 0 root, then after a, b, a1, a2, b1, b2
+    cases = [
+        ([a, a2, 0, 0, 11, 0, 0], [a, a2, 11], [0, 3]),   # a then a2, bonus 11
+        ([b, 0, b1, 0, 0, 12, 0], [b, b1, 12], [1, 4]),   # b then b1, bonus 12
+        ([b, a1, 9, 0, 0, 0, 0], [b, 9], [1]),            # b, then none of b1 / b2
+        ([7, a1, b1, 0, 0, 0, 0], [7], []),                # root argmax drafted nowhere
+    ]
+    for rows, want, path in cases:
+        r = o.tree_verify_greedy(_tree_logits(1, 6, V, [rows]), tok, par)
+        n = int(r["num_accepted"][0])
+        assert list(r["out_tokens"][0][:n + 1]) == want and n == len(want) - 1, (rows, r)
+        assert list(r["path_nodes"][0][:n]) == path and np.all(r["out_tokens"][0][n + 1:] == -1)
+    # The Mathematical Foundations tree (A_1, B_1, C_1 under the root; A_2
+    # and A_3 under A_1, B_2 under B_1, C_2 under C_1), flattened breadth
+    # first as [A1, B1, C1, A2, A3, B2, C2].
+    A1, B1, C1, A2, A3, B2, C2 = 1, 2, 3, 4, 5, 6, 7
+    tok = np.array([[A1, B1, C1, A2, A3, B2, C2]], np.int32)
+    par = np.array([[-1, -1, -1, 0, 0, 1, 2]], np.int32)
+    rows = [C1, 0, 0, C2, 0, 0, 0, 13]                     # root -> C1, after C1 -> C2, after C2 -> 13
+    r = o.tree_verify_greedy(_tree_logits(1, 7, V, [rows]), tok, par)
+    assert list(r["out_tokens"][0][:3]) == [C1, C2, 13] and list(r["path_nodes"][0][:2]) == [2, 6]
+
+
+def pin_tree_chain_is_linear_greedy(o):
+    """A tree that is one chain (parent[n] = n - 1) is the linear greedy
+    verify of the same drafts (pinned by the worked example and by plain
+    argmax decoding)."""
+    rng = np.random.default_rng(8)
+    B, N, V = 30, 6, 7
+    t = rng.standard_normal((B, N + 1, V)).astype(np.float32)
+    am = t.argmax(axis=2)
+    tok = np.where(rng.random((B, N)) < 0.75, am[:, :N], rng.integers(0, V, (B, N))).astype(np.int32)
+    par = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    r = o.tree_verify_greedy(t, tok, par)
+    g = o.verify_greedy(t, tok)
+    assert np.array_equal(r["out_tokens"], g["out_tokens"])
+    assert np.array_equal(r["num_accepted"], g["num_accepted"])
+
+
+def pin_tree_best_of_paths(o):
+    """Brute force on random small trees: the kept length is the longest
+    accepted prefix over all root-to-leaf paths, each path checked as a
+    linear greedy verify of its own rows; on equal lengths the path whose
+    last node comes first in the flattened order (only repeated sibling
+    tokens make several paths pass)."""
+    rng = np.random.default_rng(12)
+    for trial in range(200):
+        N = int(rng.integers(1, 9))
+        V = int(rng.integers(2, 5))          # few ids: many repeated siblings
+        par = np.array([int(rng.integers(-1, n)) for n in range(N)], np.int32)
+        tok = rng.integers(0, V, N).astype(np.int32)
+        t = rng.standard_normal((1, N + 1, V)).astype(np.float32)
+        r = o.tree_verify_greedy(t, tok[None], par[None])
+        best_len, best_end = 0, -1
+        leaves = [n for n in range(N) if n not in set(par.tolist())]
+        for leaf in leaves:
+            chain = []
+            n = leaf
+            while n >= 0:
+                chain.append(n)
+                n = int(par[n])
+            chain = chain[::-1]
+            rows = np.stack([t[0, 0]] + [t[0, n + 1] for n in chain])
+            g = o.verify_greedy(rows[None], tok[chain][None])
+            ln = int(g["num_accepted"][0])
+            end = chain[ln - 1] if ln > 0 else -1
+            if ln > best_len or (ln == best_len and ln > 0 and end < best_end):
+                best_len, best_end = ln, end
+        assert int(r["num_accepted"][0]) == best_len, (trial, par, tok)
+        if best_len:
+            assert int(r["path_nodes"][0][best_len - 1]) == best_end
+        bonus_row = t[0, best_end + 1]
+        assert int(r["out_tokens"][0][best_len]) == int(np.argmax(bonus_row))
+
+
+def pin_tree_mask_page(o):
+    """The mask printed under 3.5 Speculative Decoding, 'Tree verification'
+    for [a, b, a1, a2, b1, b2], and its equal position indices at equal
+    depth (tests/golden/tree_mask_page.json)."""
+    with open(os.path.join(GOLDEN, "tree_mask_page.json")) as f:
+        g = json.load(f)
+    par = np.array([g["parents"]], np.int32)
+    mask, depth = o.tree_mask(par)
+    assert np.array_equal(mask[0], np.array(g["mask"], np.uint8)), mask[0]
+    idx = {n: i for i, n in enumerate(g["nodes"])}
+    for group in g["equal_positions"]:
+        assert len({int(depth[0, idx[n]]) for n in group}) == 1
+    assert depth[0, idx["a"]] < depth[0, idx["a1"]]
+
+
+def pin_tree_mask_properties(o):
+    """Closed forms and invariants: a chain gives the causal lower-triangular
+    mask with positions 1..N; a star (every node under the root) gives the
+    identity; on random trees the attended set of a node is a chain (any two
+    attended nodes are nested), closed under 'attended by what it attends
+    to', contains the node and its parent, and has as many members as the
+    node's depth; padded rows and columns are empty."""
+    N = 9
+    chain = np.arange(-1, N - 1, dtype=np.int32)[None]
+    m, d = o.tree_mask(chain)
+    assert np.array_equal(m[0], np.tril(np.ones((N, N), np.uint8))) and list(d[0]) == list(range(1, N + 1))
+    m, d = o.tree_mask(np.full((1, N), -1, np.int32))
+    assert np.array_equal(m[0], np.eye(N, dtype=np.uint8)) and np.all(d == 1)
+    rng = np.random.default_rng(21)
+    B = 40
+    par = np.array([[int(rng.integers(-1, n)) for n in range(N)] for _ in range(B)], np.int32)
+    nn = rng.integers(0, N + 1, B).astype(np.int32)
+    m, d = o.tree_mask(par, nn)
+    for b in range(B):
+        n = int(nn[b])
+        assert not m[b, n:, :].any() and not m[b, :, n:].any() and np.all(d[b, n:] == -1)
+        mb = m[b, :n, :n].astype(bool)
+        for i in range(n):
+            att = np.flatnonzero(mb[i])
+            assert mb[i, i] and (par[b, i] < 0 or mb[i, par[b, i]])
+            assert len(att) == d[b, i]
+            for j in att:
+                assert np.all(mb[i] >= mb[j])            # closed: what j attends to, i does
+                for k in att:
+                    assert mb[j, k] or mb[k, j]           # nested: one chain
+            assert not mb[i, i + 1:].any()
+
+
 ALL_PINS = [
     pin_stats_logsumexp, pin_stats_closed_forms,
     pin_check_your_understanding, pin_single_position_experiment,
@@ -725,5 +869,7 @@ ALL_PINS = [
     pin_invariants, pin_greedy_worked_trace, pin_greedy_ties_and_bonus,
     pin_greedy_equals_argmax_decoding, pin_markov_chain_third_token,
     pin_speedup_table_and_choice, pin_acceptance_count_identities,
-    pin_alpha_test_estimates_alpha, pin_ngram_drafter,
+    pin_alpha_test_estimates_alpha, pin_ngram_drafter, pin_tree_verify_page_trees,
+    pin_tree_chain_is_linear_greedy, pin_tree_best_of_paths, pin_tree_mask_page,
+    pin_tree_mask_properties,
 ]

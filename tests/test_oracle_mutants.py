@@ -61,6 +61,22 @@ MUTANTS = {
                              "for (int32_t e = L - 1; e >= n - 1; --e) {"),
     "ngram_proposes_from_match_end": ("? c[found_e + 1 + i] : -1;", "? c[found_e + i] : -1;"),
     "ngram_no_run_in": ("kb = L - 1 - found_e;", "kb = L - 1 - found_e - 1;"),
+    "tree_ignores_parent": ("acc[n] = parent_ok && tok[n] == amax[p + 1];",
+                            "acc[n] = (parent_ok || 1) && tok[n] == amax[p + 1];"),
+    "tree_own_row": ("acc[n] = parent_ok && tok[n] == amax[p + 1];",
+                     "acc[n] = parent_ok && tok[n] == amax[n + 1];"),
+    "tree_ties_last": ("if (acc[n] && depth[n] > end_depth) { end = n; end_depth = depth[n]; }",
+                       "if (acc[n] && depth[n] >= end_depth) { end = n; end_depth = depth[n]; }"),
+    "tree_bonus_from_parent": ("out[end_depth] = amax[end + 1];",
+                               "out[end_depth] = amax[end >= 0 && par[end] >= 0 ? par[end] + 1 : 0];"),
+    "mask_excludes_self": ("for (int32_t j = i; j >= 0; j = par[j]) m[",
+                           "for (int32_t j = par[i]; j >= 0; j = par[j]) m["),
+    "mask_parent_only": ("for (int32_t j = i; j >= 0; j = par[j]) m[",
+                         "for (int32_t j = i; j >= 0 && j >= par[i]; j = par[j]) m["),
+    "mask_transposed": ("m[(size_t)i * N + j] = 1;", "m[(size_t)j * N + i] = 1;"),
+    "depth_zero_based": ("d[i] = par[i] < 0 ? 1 : d[par[i]] + 1;", "d[i] = par[i] < 0 ? 0 : d[par[i]] + 1;"),
+    "tree_first_accepted_not_deepest": ("if (acc[n] && depth[n] > end_depth) { end = n; end_depth = depth[n]; }",
+                                        "if (acc[n] && end < 0) { end = n; end_depth = depth[n]; }"),
 }
 
 RUNNER = r"""
