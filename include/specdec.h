@@ -182,6 +182,78 @@ int specdec_verify_greedy_timed(const void *target_logits, specdec_dtype_t dtype
                                 size_t workspace_bytes, void *stream, void *const *events);
 
 /*
+ * Greedy tree verification ("3.5 Speculative Decoding", "Tree verification";
+ * "Speculative Decoding: Mathematical Foundations ...", "Tree-Based
+ * Verification and Custom Attention Masks"): a tree of drafted tokens,
+ * flattened into N nodes, was scored by one target pass; keep the longest
+ * root-to-leaf path that passes greedy verification.  For request b with
+ * n = n_nodes[b] nodes (N when n_nodes is NULL):
+ *   a_r       = argmax_t target_logits[b, r, t] (lowest id on ties), where
+ *               row 0 follows the root (the last accepted token) and row
+ *               i + 1 follows node i;
+ *   node i    (parent p = parents[b, i], -1 = a child of the root) is
+ *               accepted iff p is the root or accepted, and
+ *               node_tokens[b, i] == a_{p+1};
+ *   the path  ends at the deepest accepted node e (lowest index among equal
+ *               depths; none: the empty path, e = -1) with depth D;
+ *   out_tokens[b]   = the path's tokens from the root side, then a_{e+1},
+ *                     then -1 (N + 1 entries);
+ *   path_nodes[b]   = the path's node indices from the root side, then -1
+ *                     (N entries), or NULL (not written);
+ *   num_accepted[b] = D.
+ * A chain (parents[b, i] = i - 1) gives specdec_verify_greedy's result.
+ *   target_logits [B, N+1, V]; node_tokens, parents [B, N] int32;
+ *   n_nodes [B] int32 or NULL.  Target rows past n are never read.
+ * Preconditions not checked on the device: -1 <= parents[b, i] < i for
+ * i < n (a node that breaks it is never accepted and no address comes from
+ * it); 0 <= n_nodes[b] <= N (clamped).  0 <= B <= 65535, 0 <= N <= 255,
+ * 1 <= V <= 2^28, else SPECDEC_EINVAL; more than 2^24 row tiles, likewise.
+ * Workspace: specdec_tree_verify_greedy_workspace_bytes (the same layout as
+ * specdec_verify_greedy with K = N).
+ */
+size_t specdec_tree_verify_greedy_workspace_bytes(int32_t B, int32_t N, int32_t V,
+                                                  specdec_dtype_t dtype);
+int specdec_tree_verify_greedy(const void *target_logits, specdec_dtype_t dtype,
+                               const int32_t *node_tokens, const int32_t *parents,
+                               const int32_t *n_nodes, int32_t B, int32_t N, int32_t V,
+                               int32_t *out_tokens, int32_t *path_nodes, int32_t *num_accepted,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * specdec_tree_verify_greedy with per-phase timing: events[0] / events[1]
+ * are taken at the start / end of the row kernel, events[2] at the end of
+ * the call's last kernel, as for specdec_verify_timed.
+ */
+int specdec_tree_verify_greedy_timed(const void *target_logits, specdec_dtype_t dtype,
+                                     const int32_t *node_tokens, const int32_t *parents,
+                                     const int32_t *n_nodes, int32_t B, int32_t N, int32_t V,
+                                     int32_t *out_tokens, int32_t *path_nodes,
+                                     int32_t *num_accepted, void *workspace,
+                                     size_t workspace_bytes, void *stream, void *const *events);
+
+/*
+ * Tree attention metadata for the target pass that scores a flattened draft
+ * tree ("3.5 Speculative Decoding", "Tree verification": each node attends
+ * to the context, its ancestors and itself, not to siblings; nodes of equal
+ * depth share a position index; "Speculative Decoding: Mathematical
+ * Foundations ...", "Tree-Based Verification and Custom Attention Masks").
+ * For request b with n = n_nodes[b] nodes (N when NULL):
+ *   mask[b, i, j]  = 1 if i, j < n and j is i or an ancestor of i, else 0
+ *                    (uint8; the context columns, always open, are not
+ *                    included);
+ *   depth[b, i]    = 1 for a child of the root, the parent's depth + 1
+ *                    otherwise; -1 for i >= n.  A node's position index is
+ *                    the root's position plus its depth.
+ *   parents [B, N] int32; n_nodes [B] int32 or NULL; mask [B, N, N] uint8;
+ *   depth [B, N] int32 -- all device memory.
+ * Preconditions not checked on the device: -1 <= parents[b, i] < i (a
+ * broken link is read as -1); 0 <= n_nodes[b] <= N (clamped).
+ * 0 <= B <= 65535 and 0 <= N <= 255, else SPECDEC_EINVAL.  No workspace.
+ */
+int specdec_tree_mask(const int32_t *parents, const int32_t *n_nodes, int32_t B, int32_t N,
+                      uint8_t *mask, int32_t *depth, void *stream);
+
+/*
  * Acceptance telemetry of one verify step ("Speculative Decoding from First
  * Principles", "What the numbers say": the engine's counters of drafted and
  * accepted tokens, acceptance per drafted position; "246 Speculative

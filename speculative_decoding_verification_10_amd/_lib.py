@@ -76,6 +76,16 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.specdec_verify_greedy_timed.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, vp,
                                                     vp, sz, vp, vp]
         lib.specdec_verify_greedy_timed.restype = ci
+        lib.specdec_tree_verify_greedy_workspace_bytes.argtypes = [i32, i32, i32, ci]
+        lib.specdec_tree_verify_greedy_workspace_bytes.restype = sz
+        lib.specdec_tree_verify_greedy.argtypes = [vp, ci, vp, vp, vp, i32, i32, i32, vp, vp, vp,
+                                                   vp, sz, vp]
+        lib.specdec_tree_verify_greedy.restype = ci
+        lib.specdec_tree_verify_greedy_timed.argtypes = [vp, ci, vp, vp, vp, i32, i32, i32, vp, vp,
+                                                         vp, vp, sz, vp, vp]
+        lib.specdec_tree_verify_greedy_timed.restype = ci
+        lib.specdec_tree_mask.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+        lib.specdec_tree_mask.restype = ci
         lib.specdec_acceptance_counts.argtypes = [vp, vp, i32, i32, vp, vp]
         lib.specdec_acceptance_counts.restype = ci
         lib.specdec_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
@@ -278,6 +288,74 @@ def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
     if rc != 0:
         raise SpecdecError(rc, what)
     return out_tokens, nacc, am
+
+
+def tree_verify_greedy(target: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,
+                       n_nodes: Optional[torch.Tensor] = None, path: bool = True,
+                       workspace: Optional[Workspace] = None, out=None, events=None):
+    """Greedy verification of flattened draft trees
+    (specdec_tree_verify_greedy): target [B, N+1, V] (row 0 after the root,
+    row i + 1 after node i), node_tokens / parents [B, N] int32, n_nodes [B]
+    int32 or None.  Returns (out_tokens [B, N+1], num_accepted [B],
+    path_nodes [B, N] or None).  ``events`` as for verify_greedy."""
+    lib = load()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, N+1, V]")
+    B, N1, V = target.shape
+    N = N1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    _check(target, "target", target.dtype, (B, N + 1, V), dev)
+    _check(node_tokens, "node_tokens", torch.int32, (B, N), dev)
+    _check(parents, "parents", torch.int32, (B, N), dev)
+    if n_nodes is not None:
+        _check(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    if out is None:
+        out_tokens = torch.empty((B, N + 1), dtype=torch.int32, device=dev)
+        nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+        pn = torch.empty((B, N), dtype=torch.int32, device=dev) if path else None
+    else:
+        out_tokens, nacc, pn = out
+        _check(out_tokens, "out_tokens", torch.int32, (B, N + 1), dev)
+        _check(nacc, "num_accepted", torch.int32, (B,), dev)
+        if pn is not None:
+            _check(pn, "path_nodes", torch.int32, (B, N), dev)
+    nbytes = int(lib.specdec_tree_verify_greedy_workspace_bytes(B, N, V, code))
+    ws = _workspace(nbytes, dev, workspace, "greedy")
+    args = (_ptr(target), code, _ptr(node_tokens), _ptr(parents), _ptr(n_nodes), B, N, V,
+            _ptr(out_tokens), _ptr(pn), _ptr(nacc), ws.ptr(), ws.nbytes, _stream(dev))
+    if events is None:
+        rc = lib.specdec_tree_verify_greedy(*args)
+        what = "specdec_tree_verify_greedy"
+    else:
+        if len(events) != 3:
+            raise ValueError("events must hold three entries")
+        rc = lib.specdec_tree_verify_greedy_timed(
+            *args, (ctypes.c_void_p * 3)(*[_event_handle(e, dev) for e in events]))
+        what = "specdec_tree_verify_greedy_timed"
+    if rc != 0:
+        raise SpecdecError(rc, what)
+    return out_tokens, nacc, pn
+
+
+def tree_mask(parents: torch.Tensor, n_nodes: Optional[torch.Tensor] = None):
+    """Ancestor-or-self attention mask [B, N, N] uint8 and depth [B, N] int32
+    of flattened draft trees (specdec_tree_mask)."""
+    lib = load()
+    if parents.dim() != 2:
+        raise ValueError("parents must be [B, N]")
+    B, N = parents.shape
+    dev = parents.device
+    _check(parents, "parents", torch.int32, (B, N), dev)
+    if n_nodes is not None:
+        _check(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    mask = torch.empty((B, N, N), dtype=torch.uint8, device=dev)
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    rc = lib.specdec_tree_mask(_ptr(parents), _ptr(n_nodes), B, N, _ptr(mask), _ptr(depth),
+                               _stream(dev))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_tree_mask")
+    return mask, depth
 
 
 def softmax_stats(logits: torch.Tensor, temperature: float, workspace: Optional[Workspace] = None):

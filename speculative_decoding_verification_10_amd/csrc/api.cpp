@@ -295,6 +295,71 @@ int specdec_verify_greedy_timed(const void* target_logits, specdec_dtype_t dtype
                                     reinterpret_cast<hipEvent_t const*>(events)));
 }
 
+size_t specdec_tree_verify_greedy_workspace_bytes(int32_t B, int32_t N, int32_t V,
+                                                  specdec_dtype_t dtype) {
+    return specdec_verify_greedy_workspace_bytes(B, N, V, dtype);
+}
+
+int specdec_tree_verify_greedy(const void* target_logits, specdec_dtype_t dtype,
+                               const int32_t* node_tokens, const int32_t* parents,
+                               const int32_t* n_nodes, int32_t B, int32_t N, int32_t V,
+                               int32_t* out_tokens, int32_t* path_nodes, int32_t* num_accepted,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return specdec_tree_verify_greedy_timed(target_logits, dtype, node_tokens, parents, n_nodes, B,
+                                            N, V, out_tokens, path_nodes, num_accepted, workspace,
+                                            workspace_bytes, stream, nullptr);
+}
+
+int specdec_tree_verify_greedy_timed(const void* target_logits, specdec_dtype_t dtype,
+                                     const int32_t* node_tokens, const int32_t* parents,
+                                     const int32_t* n_nodes, int32_t B, int32_t N, int32_t V,
+                                     int32_t* out_tokens, int32_t* path_nodes,
+                                     int32_t* num_accepted, void* workspace,
+                                     size_t workspace_bytes, void* stream, void* const* events) {
+    if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
+    if (B < 0 || N < 0 || N > kMaxK || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
+    if (B == 0) return SPECDEC_OK;
+    if (!target_logits || !out_tokens || !num_accepted) return SPECDEC_EINVAL;
+    if (N > 0 && (!node_tokens || !parents)) return SPECDEC_EINVAL;
+    const GreedyLayout L = greedy_layout(B, N, V, dtype);
+    if (!workspace_ok(workspace, workspace_bytes, L.total)) return SPECDEC_EWORKSPACE;
+    GreedyParams p{};
+    bool vec;
+    row_geometry(V, dtype, aligned16(target_logits), &p.NV, &vec);
+    p.C = tiles_of(p.NV);
+    if ((size_t)B * (N + 1) * p.C > kMaxBlocks || B > kMaxBatch) return SPECDEC_EINVAL;
+    p.target = target_logits;
+    p.tokens = node_tokens;
+    p.kpr = n_nodes;
+    p.parents = parents;
+    p.out = out_tokens;
+    p.nacc = num_accepted;
+    p.path = path_nodes;
+    p.B = B;
+    p.K = N;
+    p.V = V;
+    char* ws = static_cast<char*>(workspace);
+    p.err = reinterpret_cast<uint32_t*>(ws + L.err);
+    p.slot = reinterpret_cast<uint64_t*>(ws + L.slot);
+    return map_launch(launch_tree_greedy(p, dtype, vec, (hipStream_t)stream,
+                                         reinterpret_cast<hipEvent_t const*>(events)));
+}
+
+int specdec_tree_mask(const int32_t* parents, const int32_t* n_nodes, int32_t B, int32_t N,
+                      uint8_t* mask, int32_t* depth, void* stream) {
+    if (B < 0 || B > kMaxBatch || N < 0 || N > kMaxK) return SPECDEC_EINVAL;
+    if (B == 0 || N == 0) return SPECDEC_OK;
+    if (!parents || !mask || !depth) return SPECDEC_EINVAL;
+    TreeMaskParams p{};
+    p.parents = parents;
+    p.nn = n_nodes;
+    p.B = B;
+    p.N = N;
+    p.mask = mask;
+    p.depth = depth;
+    return map_launch(launch_tree_mask(p, (hipStream_t)stream));
+}
+
 int specdec_acceptance_counts(const int32_t* num_accepted, const int32_t* k_per_req, int32_t B,
                               int32_t K, uint64_t* counters, void* stream) {
     if (B < 0 || B > kMaxBatch || K < 0 || K > kMaxK) return SPECDEC_EINVAL;

@@ -11,6 +11,9 @@
 //  greedy_decisions  one wave per request: merges each row's tiles, compares
 //                    the argmaxes with the drafts by ballot, writes the
 //                    outputs.
+// The tree variant runs the same row kernel over the N + 1 rows of a
+// flattened draft tree, then tree_decisions (one wave per request) instead
+// of greedy_decisions.
 #include <hip/hip_ext.h>
 
 #include "internal.h"
@@ -64,11 +67,18 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
     best_step<kDppRowBcast31, 0xC>(v, i);
 }
 
-// The decision of request b, by one wave (its own workgroup): the row
-// maxima come from the tile slots the previous kernel wrote.
-__device__ void greedy_decide(const GreedyParams& a, int b, int* am) {
+// Wave-level memory ordering of LDS between the lanes of one wave.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// am[r] = argmax of target row r of request b, r = 0 .. kb, by one wave,
+// from the tile words the row kernel wrote; visible to the whole wave on
+// return.
+__device__ void row_argmaxes(const GreedyParams& a, int b, int kb, int* am) {
     const int K = a.K, C = a.C;
-    const int kb = greedy_k(a, b);
     const int lane = threadIdx.x & 63, sub = lane & 15;
     const uint64_t* slots = a.slot + (size_t)b * (K + 1) * C;
     // Rows 16 lanes at a time, four rows per pass; every load of a pass is
@@ -98,9 +108,15 @@ __device__ void greedy_decide(const GreedyParams& a, int b, int* am) {
         row16_best(bv, bi);
         if (sub == 0 && r <= kb) am[r] = min(max(bi, 0), a.V - 1);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync();
+}
+
+// The decision of request b, by one wave (its own workgroup).
+__device__ void greedy_decide(const GreedyParams& a, int b, int* am) {
+    const int K = a.K;
+    const int kb = greedy_k(a, b);
+    const int lane = threadIdx.x & 63;
+    row_argmaxes(a, b, kb, am);
     // First mismatch, 64 positions at a time.
     int j = kb;
     for (int t0 = 0; t0 < kb; t0 += 64) {
@@ -119,6 +135,130 @@ __device__ void greedy_decide(const GreedyParams& a, int b, int* am) {
         if (a.amax) a.amax[(size_t)b * (K + 1) + i] = (i <= kb) ? am[i] : -1;
     }
     if (lane == 0) a.nacc[b] = j;
+}
+
+// Greedy tree verification ("3.5 Speculative Decoding", "Tree
+// verification"; "Speculative Decoding: Mathematical Foundations ...",
+// "Tree-Based Verification and Custom Attention Masks"), by one wave for
+// request b with n = kb nodes in flattened order (parent[i] < i, -1 = the
+// root).  Node i passes its own test when its token is the argmax of its
+// parent's row (row 0 for the root, row p + 1 after node p); it is accepted
+// when it and every ancestor pass.  The kept path ends at the deepest
+// accepted node (lowest index on ties) and is followed by the argmax of the
+// row after it.
+//
+// Acceptance and depth by pointer jumping over the parent links
+// (log2 n synchronous rounds over LDS; every lane holds up to 4 nodes), the
+// 2^r-th ancestor of every node kept per round, so that each path slot finds
+// its node by binary lifting from the path's end.  A node whose parent link
+// breaks the precondition (-1 <= parent[i] < i) is never accepted.
+constexpr int kTreeLift = 8;                       // 2^8 > kMaxK ancestors
+constexpr int kTreePerLane = (kMaxK + 64) / 64;    // nodes per lane
+constexpr int kTreeKeyBits = 9;                    // node index field of a path key
+
+__device__ void tree_decide(const GreedyParams& a, int b, int* am) {
+    __shared__ int32_t tok[kMaxK];
+    __shared__ int32_t ok[kMaxK];
+    __shared__ int32_t dep[kMaxK];
+    __shared__ int16_t up[kTreeLift][kMaxK];
+    const int N = a.K;
+    const int n = greedy_k(a, b);
+    const int lane = threadIdx.x & 63;
+    const int32_t* ptok = a.tokens + (size_t)b * N;
+    const int32_t* ppar = a.parents + (size_t)b * N;
+    int par[kTreePerLane];
+#pragma unroll
+    for (int q = 0; q < kTreePerLane; ++q) {
+        const int i = lane + 64 * q;
+        par[q] = -1;
+        if (i < n) {
+            const int p = ppar[i];
+            par[q] = (p >= -1 && p < i) ? p : -2;      // -2: a broken link
+            tok[i] = ptok[i];
+        }
+    }
+    row_argmaxes(a, b, n, am);
+    // Own test, then the links (a broken link becomes "no parent, rejected").
+    int jmp[kTreePerLane];
+#pragma unroll
+    for (int q = 0; q < kTreePerLane; ++q) {
+        const int i = lane + 64 * q;
+        jmp[q] = -1;
+        if (i < n) {
+            const int p = par[q];
+            ok[i] = (p >= -1) && tok[i] == am[p + 1];
+            dep[i] = 1;
+            jmp[q] = max(p, -1);
+            up[0][i] = (int16_t)jmp[q];
+        }
+    }
+    wave_sync();
+    // Round r: ok / dep cover the 2^r nodes from i up (fewer near the root),
+    // jmp is the 2^r-th ancestor; afterwards the 2^(r+1)-th.
+    for (int r = 0; r < kTreeLift; ++r) {
+        bool linked = false;
+#pragma unroll
+        for (int q = 0; q < kTreePerLane; ++q) linked |= jmp[q] >= 0;
+        if (__ballot(linked) == 0) break;
+        int nok[kTreePerLane], ndep[kTreePerLane], njmp[kTreePerLane];
+#pragma unroll
+        for (int q = 0; q < kTreePerLane; ++q) {
+            const int i = lane + 64 * q;
+            const int j = jmp[q];
+            nok[q] = 0;
+            ndep[q] = 0;
+            njmp[q] = j;
+            if (i < n) {
+                nok[q] = ok[i];
+                ndep[q] = dep[i];
+                if (j >= 0) {
+                    nok[q] &= ok[j];
+                    ndep[q] += dep[j];
+                    njmp[q] = up[r][j];
+                }
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int q = 0; q < kTreePerLane; ++q) {
+            const int i = lane + 64 * q;
+            jmp[q] = njmp[q];
+            if (i < n) {
+                ok[i] = nok[q];
+                dep[i] = ndep[q];
+                if (r + 1 < kTreeLift) up[r + 1][i] = (int16_t)njmp[q];
+            }
+        }
+        wave_sync();
+    }
+    // Deepest accepted node, lowest index on ties: the largest key.
+    uint32_t key = 0;
+#pragma unroll
+    for (int q = 0; q < kTreePerLane; ++q) {
+        const int i = lane + 64 * q;
+        if (i < n && ok[i])
+            key = max(key, ((uint32_t)dep[i] << kTreeKeyBits) | (uint32_t)((1 << kTreeKeyBits) - 1 - i));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) key = max(key, (uint32_t)__shfl_xor((int)key, off));
+    const int D = (int)(key >> kTreeKeyBits);
+    const int end = key ? (1 << kTreeKeyBits) - 1 - (int)(key & ((1u << kTreeKeyBits) - 1)) : -1;
+    // Slot d < D holds the ancestor of `end` at distance D - 1 - d.
+    for (int d = lane; d <= N; d += 64) {
+        int32_t v = -1, node = -1;
+        if (d < D) {
+            node = end;
+            const int dist = D - 1 - d;
+            for (int r = 0; r < kTreeLift; ++r)
+                if ((dist >> r) & 1) node = up[r][node];
+            v = tok[node];
+        } else if (d == D) {
+            v = am[end + 1];
+        }
+        a.out[(size_t)b * (N + 1) + d] = v;
+        if (a.path && d < N) a.path[(size_t)b * N + d] = node;
+    }
+    if (lane == 0) a.nacc[b] = D;
 }
 
 // Workgroup (x, y, z): tile x of target row y of request z.
@@ -179,22 +319,43 @@ __global__ __launch_bounds__(64) void greedy_decisions(GreedyParams a) {
     greedy_decide(a, blockIdx.x, am);
 }
 
+// Tree decisions: workgroup x (one wave) takes request x.
+__global__ __launch_bounds__(64) void tree_decisions(GreedyParams a) {
+    __shared__ int am[kMaxK + 1];
+    tree_decide(a, blockIdx.x, am);
+}
+
 template <int DT, bool VEC>
-hipError_t launch(const GreedyParams& p, hipStream_t s, hipEvent_t const* events) {
+hipError_t launch(const GreedyParams& p, hipStream_t s, hipEvent_t const* events, bool tree) {
     if (p.B == 0) return hipSuccess;
     hipExtLaunchKernelGGL((greedy_rows<DT, VEC>), dim3(p.C, p.K + 1, p.B), dim3(kThreads), 0, s,
                           events ? events[0] : nullptr, events ? events[1] : nullptr, 0, p);
-    hipExtLaunchKernelGGL(greedy_decisions, dim3(p.B), dim3(64), 0, s, nullptr,
-                          events ? events[2] : nullptr, 0, p);
+    if (tree)
+        hipExtLaunchKernelGGL(tree_decisions, dim3(p.B), dim3(64), 0, s, nullptr,
+                              events ? events[2] : nullptr, 0, p);
+    else
+        hipExtLaunchKernelGGL(greedy_decisions, dim3(p.B), dim3(64), 0, s, nullptr,
+                              events ? events[2] : nullptr, 0, p);
     return hipGetLastError();
+}
+
+hipError_t dispatch(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
+                    hipEvent_t const* events, bool tree) {
+    if (dtype == kBF16)
+        return vec ? launch<kBF16, true>(p, s, events, tree) : launch<kBF16, false>(p, s, events, tree);
+    return vec ? launch<kFP32, true>(p, s, events, tree) : launch<kFP32, false>(p, s, events, tree);
 }
 
 }  // namespace
 
 hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
                          hipEvent_t const* events) {
-    if (dtype == kBF16) return vec ? launch<kBF16, true>(p, s, events) : launch<kBF16, false>(p, s, events);
-    return vec ? launch<kFP32, true>(p, s, events) : launch<kFP32, false>(p, s, events);
+    return dispatch(p, dtype, vec, s, events, false);
+}
+
+hipError_t launch_tree_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
+                              hipEvent_t const* events) {
+    return dispatch(p, dtype, vec, s, events, true);
 }
 
 }  // namespace specdec

@@ -57,16 +57,30 @@ struct VerifyParams {
     Decision* dec;              // [B] decision of each request
 };
 
+// Linear greedy verify (launch_greedy) or greedy tree verify
+// (launch_tree_greedy): for a tree, K is the node count N, tokens the node
+// tokens, kpr the node count of each request and amax unused.
 struct GreedyParams {
     const void* target;
     const int32_t* tokens;
     const int32_t* kpr;
+    const int32_t* parents;     // [B, K] tree parents (tree only)
     int32_t* out;
     int32_t* nacc;
     int32_t* amax;              // may be null
+    int32_t* path;              // [B, K] tree path node indices, may be null
     int B, K, V, NV, C;
     uint32_t* err;              // workspace header: error bits
     uint64_t* slot;             // [B * (K+1) * C] tile (max, index) words
+};
+
+// Ancestor masks and depths of flattened draft trees.
+struct TreeMaskParams {
+    const int32_t* parents;     // [B, N]
+    const int32_t* nn;          // [B] node counts, or null (N)
+    int B, N;
+    uint8_t* mask;              // [B, N, N]
+    int32_t* depth;             // [B, N]
 };
 
 struct StatsParams {
@@ -106,6 +120,10 @@ hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t
 // the row kernel's start and end, and the end of the call's last kernel.
 hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
                          hipEvent_t const* events = nullptr);
+// Tree variant of launch_greedy (same events).
+hipError_t launch_tree_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
+                              hipEvent_t const* events = nullptr);
+hipError_t launch_tree_mask(const TreeMaskParams& p, hipStream_t s);
 hipError_t launch_stats(const StatsParams& p, int dtype, bool vec, hipStream_t s);
 hipError_t launch_acceptance_counts(const TelemetryParams& p, hipStream_t s);
 hipError_t launch_ngram(const NgramParams& p, hipStream_t s);

@@ -328,7 +328,6 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d);
 // ---------------------------------------------------------------------------
 template <int DT, bool VEC>
 __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided, StepShared& sh) {
-    constexpr int E = Elem<DT>::E;
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
     const int kb = kb_of(a, b);

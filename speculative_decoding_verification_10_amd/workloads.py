@@ -265,3 +265,66 @@ def ngram_contexts(B: int = 256, L_max: int = 4096, V: int = 151936, set_index: 
                         ctx[b, pos + i] = ctx[b, src + i]
             pos += m
     return ctx, lens
+
+
+def tree_parents(branching) -> np.ndarray:
+    """Parent links of a static draft tree flattened breadth first, the
+    order of the pages' example [a, b, a1, a2, b1, b2]: branching[d] children
+    under every node of depth d (the root has depth 0); -1 = the root."""
+    parents, level = [], [-1]
+    for m in branching:
+        nxt = []
+        for p in level:
+            for _ in range(int(m)):
+                parents.append(p)
+                nxt.append(len(parents) - 1)
+        level = nxt
+    return np.array(parents, np.int32)
+
+
+@dataclass
+class TreeWorkload:
+    name: str
+    B: int
+    N: int
+    V: int
+    dtype: str
+    target: np.ndarray              # [B, N+1, V]: row 0 after the root, row i+1 after node i
+    node_tokens: np.ndarray         # [B, N] int32
+    parents: np.ndarray             # [B, N] int32
+    n_nodes: Optional[np.ndarray]   # [B] int32 or None (all N)
+    meta: dict = field(default_factory=dict)
+
+    def rows_read(self) -> int:
+        nn = np.full(self.B, self.N) if self.n_nodes is None else self.n_nodes
+        return int(np.sum(nn.astype(np.int64) + 1))
+
+
+def tree(B: int = 64, V: int = 128256, branching=(3, 2, 2), set_index: int = 0,
+         dtype: str = "bf16", hit: float = 0.7) -> TreeWorkload:
+    """A batch of draft trees scored by one target pass: every request uses
+    the static tree of `branching` (default 3 candidates at depth 1, 2 under
+    each at depths 2 and 3: 21 nodes), target rows as the greedy workload's
+    (N(0, 2^2) + 10 on one id per row).  The first child under each node --
+    the draft's top candidate -- is the target argmax of the parent's stored
+    row with probability `hit`, otherwise a uniform id; the other children
+    (lower-ranked candidates) are uniform ids.  Seed 1007."""
+    par1 = tree_parents(branching)
+    N = len(par1)
+    r_logit, r_noise, r_draft, _ = _rngs(1007, set_index)
+    l = r_logit.standard_normal((B, N + 1, V)) * 2.0
+    peak = r_logit.integers(0, V, size=(B, N + 1))
+    np.add.at(l, (np.arange(B)[:, None], np.arange(N + 1)[None, :], peak), 10.0)
+    target = _store(l, dtype)
+    del l
+    am = np.argmax(stored_as_f32(target), axis=-1).astype(np.int32)
+    first = np.array([i == 0 or par1[i - 1] != par1[i] for i in range(N)], bool)
+    parents = np.tile(par1, (B, 1))
+    above = am[:, par1 + 1]                                  # argmax of each node's parent row
+    take = first[None, :] & (r_draft.random((B, N)) < hit)
+    rnd = r_draft.integers(0, V, size=(B, N)).astype(np.int32)
+    tokens = np.where(take, above, rnd).astype(np.int32)
+    return TreeWorkload(name="tree", B=B, N=N, V=V, dtype=dtype, target=target,
+                        node_tokens=tokens, parents=parents.astype(np.int32), n_nodes=None,
+                        meta={"seed": 1007, "set_index": set_index,
+                              "branching": tuple(int(m) for m in branching)})

@@ -193,3 +193,59 @@ def test_ngram_propose_rejects(lib):
     assert lib.specdec_ngram_propose(f, f, 4, 10, 1, 3, 3, None, f, None) == EINVAL
     assert lib.specdec_ngram_propose(f, f, 4, 10, 1, 3, 3, f, None, None) == EINVAL
     assert lib.specdec_ngram_propose(None, None, 0, 10, 1, 3, 3, None, None, None) == OK
+
+
+def call_tree(lib, timed=False, **kw):
+    a = dict(target=FAKE, dtype=1, tokens=FAKE, parents=FAKE, nn=None, B=4, N=6, V=1000,
+             out=FAKE, path=None, nacc=FAKE, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("target", "dtype", "tokens", "parents", "nn", "B", "N", "V", "out",
+                           "path", "nacc", "ws", "wsb", "stream")]
+    if timed:
+        return lib.specdec_tree_verify_greedy_timed(*args, None)
+    return lib.specdec_tree_verify_greedy(*args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), EDTYPE),
+    (dict(B=-1), EINVAL),
+    (dict(B=65536, wsb=1 << 40), EINVAL),
+    (dict(N=-1), EINVAL),
+    (dict(N=256), EINVAL),
+    (dict(V=0), EINVAL),
+    (dict(V=(1 << 28) + 1), EINVAL),
+    (dict(target=None), EINVAL),
+    (dict(tokens=None), EINVAL),
+    (dict(parents=None), EINVAL),
+    (dict(out=None), EINVAL),
+    (dict(nacc=None), EINVAL),
+    (dict(ws=None), EWORKSPACE),
+    (dict(wsb=16), EWORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x10010)), EWORKSPACE),
+    (dict(B=0, target=None, tokens=None, parents=None, out=None, nacc=None, ws=None), OK),
+])
+def test_tree_verify_rejects(lib, kw, status):
+    assert call_tree(lib, **kw) == status
+    assert call_tree(lib, timed=True, **kw) == status
+
+
+def test_tree_verify_workspace_is_greedy_layout(lib):
+    for B, N, V, dt in ((64, 21, 128256, 1), (1, 0, 10, 0), (3, 255, 1000, 1)):
+        n = lib.specdec_tree_verify_greedy_workspace_bytes(B, N, V, dt)
+        assert n > 0 and n % 256 == 0
+        assert n == lib.specdec_verify_greedy_workspace_bytes(B, N, V, dt)
+    assert lib.specdec_tree_verify_greedy_workspace_bytes(4, 256, 10, 1) == 0
+
+
+def test_tree_mask_rejects(lib):
+    f = ctypes.c_void_p(0x1000)
+    # parents, n_nodes, B, N, mask, depth, stream
+    assert lib.specdec_tree_mask(f, None, -1, 6, f, f, None) == EINVAL
+    assert lib.specdec_tree_mask(f, None, 65536, 6, f, f, None) == EINVAL
+    assert lib.specdec_tree_mask(f, None, 4, -1, f, f, None) == EINVAL
+    assert lib.specdec_tree_mask(f, None, 4, 256, f, f, None) == EINVAL
+    assert lib.specdec_tree_mask(None, None, 4, 6, f, f, None) == EINVAL
+    assert lib.specdec_tree_mask(f, None, 4, 6, None, f, None) == EINVAL
+    assert lib.specdec_tree_mask(f, None, 4, 6, f, None, None) == EINVAL
+    assert lib.specdec_tree_mask(None, None, 0, 6, None, None, None) == OK
+    assert lib.specdec_tree_mask(None, None, 4, 0, None, None, None) == OK
