@@ -96,10 +96,11 @@ def read_counters(workload, key):
         return None
 
 
-def cpu_baseline(wl, name: str, budget_s: float, ngram=None):
+def cpu_baseline(wl, name: str, budget_s: float, ngram=None, parents=None):
     """The fp64 oracle as it stands, on the host cores, over a bounded
     number of steps of the same workload (for the n-gram workload: the
-    oracle drafter, then the oracle greedy verify)."""
+    oracle drafter, then the oracle greedy verify; for the tree workload
+    the oracle tree verify)."""
     import numpy as np
     import oracle
     oracle.default()
@@ -113,6 +114,9 @@ def cpu_baseline(wl, name: str, budget_s: float, ngram=None):
             drafts, kp = oracle.ngram_propose(ctx, lens, n_min, n_max, wl.K)
             oracle.verify_greedy(wl.target, drafts, kp)
             pos += int(np.sum(kp.astype(np.int64) + 1))
+        elif parents is not None:
+            oracle.tree_verify_greedy(wl.target, wl.draft_tokens, parents)
+            pos += wl.verified_positions()
         elif wl.greedy:
             oracle.verify_greedy(wl.target, wl.draft_tokens, wl.k_per_req)
             pos += wl.verified_positions()
@@ -136,8 +140,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=5, help="device-resident input copies to rotate over")
     ap.add_argument("--workload", default="headline",
-                    help="headline (default), tiny, peaked, greedy, ragged, or ngram (the n-gram "
-                         "drafter over copy-heavy contexts, then the greedy verify of its drafts)")
+                    help="headline (default), tiny, peaked, greedy, ragged, ngram (the n-gram "
+                         "drafter over copy-heavy contexts, then the greedy verify of its drafts), "
+                         "or tree (greedy verification of 21-node draft trees)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each call from a captured HIP graph")
@@ -173,7 +178,18 @@ def main():
     # The n-gram workload: the drafter over seeded copy-heavy contexts, then
     # the greedy verify of its drafts against the greedy workload's logits.
     ngram = args.workload == "ngram"
-    wl = workloads.make("greedy" if ngram else args.workload)
+    tree = args.workload == "tree"
+    parents_h = None
+    if tree:
+        # Node i's token is "draft position" i; row i + 1 follows node i.
+        tw = workloads.tree()
+        parents_h = tw.parents
+        wl = workloads.Workload("tree", tw.B, tw.N, tw.V, tw.dtype, 1.0, True, tw.target, None,
+                                tw.node_tokens, np.zeros((tw.B, tw.N + 1), np.float32),
+                                meta=dict(tw.meta))
+        parents_d = torch.from_numpy(parents_h).to(dev)
+    else:
+        wl = workloads.make("greedy" if ngram else args.workload)
     K = wl.K
     ngram_host = None
     if ngram:
@@ -201,7 +217,9 @@ def main():
            torch.empty((wl.B,), dtype=torch.int32, device=dev), None)
     greedy = wl.greedy
     code = 1 if wl.dtype == "bf16" else 0
-    if greedy:
+    if tree:
+        nbytes = int(sd._lib.load().specdec_tree_verify_greedy_workspace_bytes(wl.B, K, wl.V, code))
+    elif greedy:
         nbytes = int(sd._lib.load().specdec_verify_greedy_workspace_bytes(wl.B, K, wl.V, code))
     else:
         nbytes = sd._lib.verify_workspace_bytes(wl.B, K, wl.V, code, wl.draft is None)
@@ -222,7 +240,11 @@ def main():
     ptr = lambda t: None if t is None else t.data_ptr()
     cargs = []
     for st in sets:
-        if greedy:
+        if tree:
+            cargs.append((st["target"].data_ptr(), code, tokens.data_ptr(), parents_d.data_ptr(), None,
+                          wl.B, K, wl.V, out[0].data_ptr(), None, out[1].data_ptr(), ws.ptr(),
+                          ws.nbytes, stream.cuda_stream))
+        elif greedy:
             cargs.append((st["target"].data_ptr(), code, tokens.data_ptr(), ptr(kpr), wl.B, K, wl.V,
                           out[0].data_ptr(), out[1].data_ptr(), None, ws.ptr(), ws.nbytes,
                           stream.cuda_stream))
@@ -242,10 +264,13 @@ def main():
                                            stream.cuda_stream)
             if rc != 0:
                 raise sd.SpecdecError(rc, "bench drafter")
-        if handles is not None:
-            rc = (lib.specdec_verify_greedy_timed if greedy else lib.specdec_verify_timed)(*a, handles[r])
+        if tree:
+            fn, fn_timed = lib.specdec_tree_verify_greedy, lib.specdec_tree_verify_greedy_timed
+        elif greedy:
+            fn, fn_timed = lib.specdec_verify_greedy, lib.specdec_verify_greedy_timed
         else:
-            rc = (lib.specdec_verify_greedy if greedy else lib.specdec_verify)(*a)
+            fn, fn_timed = lib.specdec_verify, lib.specdec_verify_timed
+        rc = fn_timed(*a, handles[r]) if handles is not None else fn(*a)
         if rc == 0 and counters is not None:
             rc = lib.specdec_acceptance_counts(out[1].data_ptr(), kpr_ptr, wl.B, K, counters.data_ptr(),
                                                stream.cuda_stream)
@@ -256,7 +281,9 @@ def main():
         st = sets[r % len(sets)]
         if ngram:
             sd.ngram_propose(ctx_d, lens_d, NGRAM_N_MIN, NGRAM_N_MAX, K, out=(tokens, kpr))
-        if greedy:
+        if tree:
+            sd.tree_verify_greedy(st["target"], tokens, parents_d, workspace=ws, out=out)
+        elif greedy:
             sd.verify_greedy(st["target"], tokens, k_per_req=kpr, workspace=ws, out=out)
         else:
             sd.verify(st["target"], st["draft"], tokens, unif, wl.temperature, k_per_req=kpr,
@@ -322,6 +349,8 @@ def main():
 
     positions = wl.verified_positions()
     alg = algorithmic_bytes(wl, nacc)
+    if tree:
+        alg += wl.B * K * 4                   # the parent links
     drafter = None
     if ngram:
         # The drafter reads every context token once and writes the drafts.
@@ -361,7 +390,8 @@ def main():
                 "frac": round(alg / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                 "traffic": read_counters(args.workload, "hbm_bytes_per_launch"), "algorithmic_bytes": alg,
                 "launch_ms": round(call_ms, 5),
-                "kernels": ("greedy_rows, greedy_decisions" if greedy
+                "kernels": ("greedy_rows, tree_decisions" if tree else
+                            "greedy_rows, greedy_decisions" if greedy
                             else "verify_rows, [verify_decide,] verify_final")}
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
@@ -372,9 +402,13 @@ def main():
                                "specdec_verify call (verify_rows, [verify_decide,] verify_final)"),
                     "algorithmic_bytes": alg, "launch_ms": round(per_launch_ms, 5)}
         call = None
-    metric = METRIC if args.workload == "headline" else (
-        "verified positions/s + HBM GB/s (%% of peak), %s B=%d k=%d V=%d %s"
-        % (args.workload, wl.B, K, wl.V, wl.dtype))
+    if tree:
+        metric = ("verified positions/s (tree nodes + 1 per request) + HBM GB/s (%% of peak), "
+                  "tree B=%d nodes=%d V=%d %s" % (wl.B, K, wl.V, wl.dtype))
+    else:
+        metric = METRIC if args.workload == "headline" else (
+            "verified positions/s + HBM GB/s (%% of peak), %s B=%d k=%d V=%d %s"
+            % (args.workload, wl.B, K, wl.V, wl.dtype))
     line = {
         "metric": metric,
         "value": round(value, 1),
@@ -389,19 +423,26 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded; inputs resident in HBM, %d rotating copies)" % len(sets),
-        "config": {"workload": "%s verify B=%d k=%d V=%d %s T=%g" % (args.workload, wl.B, K, wl.V,
-                                                                        wl.dtype, wl.temperature),
+        "config": {"workload": ("tree verify B=%d nodes=%d (branching %s) V=%d %s"
+                                % (wl.B, K, ",".join(map(str, wl.meta["branching"])), wl.V, wl.dtype)
+                                if tree else
+                                "%s verify B=%d k=%d V=%d %s T=%g" % (args.workload, wl.B, K, wl.V,
+                                                                      wl.dtype, wl.temperature)),
                    "B": wl.B, "k": K, "V": wl.V, "temperature": wl.temperature,
                    "graph_replay": bool(args.graph)},
         "hbm_gbps": round(gbps, 1),
         "hbm_pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
         "algorithmic_bytes_per_step": alg,
-        "rejected_requests": int(np.sum(nacc < (wl.K if wl.k_per_req is None else wl.k_per_req))),
+        "rejected_requests": (None if tree else
+                              int(np.sum(nacc < (wl.K if wl.k_per_req is None else wl.k_per_req)))),
         "roofline": roofline,
         "cpu_baseline": None,
     }
     if call is not None:
         line["call_roofline"] = call
+    if tree:
+        line["tree"] = {"accepted_path_lengths": np.bincount(nacc, minlength=4).tolist(),
+                        "mean_accepted": round(float(np.mean(nacc)), 4)}
     if drafter is not None:
         line["drafter"] = drafter
     if counters is not None:
@@ -420,7 +461,7 @@ def main():
         torch.cuda.synchronize()
         line["calibration_copy_bytes"] = n
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl, args.workload, args.cpu_budget, ngram_host)
+        line["cpu_baseline"] = cpu_baseline(wl, args.workload, args.cpu_budget, ngram_host, parents_h)
     print(json.dumps(line), flush=True)
 
 
