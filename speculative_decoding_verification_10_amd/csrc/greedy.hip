@@ -74,40 +74,49 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A tile word as a key whose unsigned order is the (value, index) order:
+// larger value first, lower index on equal values (-0 and +0 are equal).
+__device__ __forceinline__ uint64_t order_key(uint64_t w) {
+    float v;
+    int i;
+    dec_pair(w, v, i);
+    if (v == 0.0f) v = 0.0f;
+    uint32_t u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)i;
+}
+
+constexpr int kWordBatch = 8;   // tile words per lane in flight
+
 // am[r] = argmax of target row r of request b, r = 0 .. kb, by one wave,
 // from the tile words the row kernel wrote; visible to the whole wave on
-// return.
+// return.  The rows' words are contiguous: lane l takes words l, l + 64,
+// ..., kWordBatch loads in flight at a time, and folds each into its row's
+// key with an LDS atomic max.
 __device__ void row_argmaxes(const GreedyParams& a, int b, int kb, int* am) {
+    __shared__ uint64_t key[kMaxK + 1];
     const int K = a.K, C = a.C;
-    const int lane = threadIdx.x & 63, sub = lane & 15;
-    const uint64_t* slots = a.slot + (size_t)b * (K + 1) * C;
-    // Rows 16 lanes at a time, four rows per pass; every load of a pass is
-    // issued before any is used.
-    for (int base = 0; base <= kb; base += 4) {
-        const int r = base + (lane >> 4);
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-        if (r <= kb) {
-            for (int c0 = sub; c0 < C; c0 += 64) {
-                uint64_t got[4];
+    const int lane = threadIdx.x & 63;
+    const uint64_t* words = a.slot + (size_t)b * (K + 1) * C;
+    const int W = (kb + 1) * C;
+    for (int r = lane; r <= kb; r += 64) key[r] = 0;
+    wave_sync();
+    for (int base = 0; base < W; base += 64 * kWordBatch) {
+        uint64_t got[kWordBatch];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = c0 + 16 * q;
-                    got[q] = (c < C) ? slots[(size_t)r * C + c] : 0;
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (c0 + 16 * q >= C) break;
-                    float v;
-                    int i;
-                    dec_pair(got[q], v, i);
-                    if (better(v, i, bv, bi)) { bv = v; bi = i; }
-                }
-            }
+        for (int q = 0; q < kWordBatch; ++q) {
+            const int w = base + 64 * q + lane;
+            got[q] = (w < W) ? words[w] : 0;
         }
-        row16_best(bv, bi);
-        if (sub == 0 && r <= kb) am[r] = min(max(bi, 0), a.V - 1);
+#pragma unroll
+        for (int q = 0; q < kWordBatch; ++q) {
+            const int w = base + 64 * q + lane;
+            if (w < W) atomicMax(reinterpret_cast<unsigned long long*>(&key[w / C]),
+                                 (unsigned long long)order_key(got[q]));
+        }
     }
+    wave_sync();
+    for (int r = lane; r <= kb; r += 64) am[r] = min(max((int)~(uint32_t)key[r], 0), a.V - 1);
     wave_sync();
 }
 
