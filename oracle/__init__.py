@@ -97,6 +97,9 @@ class Oracle:
         lib.oracle_tree_verify_greedy.restype = ci
         lib.oracle_tree_mask.argtypes = [vp, vp, i32, i32, vp, vp]
         lib.oracle_tree_mask.restype = ci
+        lib.oracle_sampling_floor.argtypes = [vp, ci, ctypes.c_int64, i32, ctypes.c_double, i32,
+                                              ctypes.c_double, vp, vp]
+        lib.oracle_sampling_floor.restype = ci
         self.lib = lib
         self.path = path
 
@@ -243,6 +246,59 @@ class Oracle:
         return mask, depth
 
 
+    def sampling_floor(self, logits, temperature, top_k, top_p):
+        """Per-row floor of the top-k / top-p processed distribution:
+        logits [..., V] float32 or bf16 bits; returns (floor [...] float32,
+        margin [...] float64)."""
+        logits = np.ascontiguousarray(logits)
+        code = _dtype_code(logits)
+        V = logits.shape[-1]
+        rows = logits.size // V
+        fl = np.empty(logits.shape[:-1], np.float32)
+        mg = np.empty(logits.shape[:-1], np.float64)
+        rc = self.lib.oracle_sampling_floor(_ptr(logits), code, rows, V, float(temperature),
+                                            int(top_k), float(top_p), _ptr(fl), _ptr(mg))
+        if rc != 0:
+            raise ValueError("oracle_sampling_floor rejected its arguments")
+        return fl, mg
+
+    def verify_processed(self, target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
+                         k_per_req=None):
+        """One stochastic verify step on the processed distributions: each
+        target and draft row keeps the tokens at or above its floor (every
+        other logit set to -inf), then the plain verify step runs on those
+        rows.  Adds 'target_floor', 'draft_floor' and 'flagged' also for rows
+        whose floor lies within the flag band of a top-p boundary."""
+        target = np.ascontiguousarray(target)
+        tf, tm = self.sampling_floor(target, temperature, top_k, top_p)
+        tv = _as_f32(target)
+        tproc = np.where(tv >= tf[..., None], tv, np.float32(-np.inf)).astype(np.float32)
+        dproc, df, dm = None, None, None
+        if draft is not None:
+            draft = np.ascontiguousarray(draft)
+            df, dm = self.sampling_floor(draft, temperature, top_k, top_p)
+            dv = _as_f32(draft)
+            dproc = np.where(dv >= df[..., None], dv, np.float32(-np.inf)).astype(np.float32)
+        r = self.verify(tproc, dproc, draft_tokens, uniforms, temperature, k_per_req)
+        B, K1 = tf.shape
+        kb = np.full(B, K1 - 1) if k_per_req is None else np.asarray(k_per_req)
+        near = np.zeros(B, bool)
+        for b in range(B):
+            near[b] = np.any(tm[b, :kb[b] + 1] < FLAG_BAND)
+            if dm is not None:
+                near[b] |= np.any(dm[b, :kb[b]] < FLAG_BAND)
+        r.update(target_floor=tf, draft_floor=df, floor_flagged=near,
+                 flagged=r["flagged"] | near)
+        return r
+
+
+def _as_f32(a):
+    """float32 values of float32 logits or bf16 bits (exact)."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32)
+    return a.astype(np.float32)
+
+
 def default() -> Oracle:
     global _default
     with _lock:
@@ -281,3 +337,13 @@ def tree_verify_greedy(target, node_tokens, parents, n_nodes=None):
 
 def tree_mask(parents, n_nodes=None):
     return default().tree_mask(parents, n_nodes)
+
+
+def sampling_floor(logits, temperature, top_k, top_p):
+    return default().sampling_floor(logits, temperature, top_k, top_p)
+
+
+def verify_processed(target, draft, draft_tokens, uniforms, temperature, top_k, top_p,
+                     k_per_req=None):
+    return default().verify_processed(target, draft, draft_tokens, uniforms, temperature, top_k,
+                                      top_p, k_per_req)

@@ -490,3 +490,74 @@ int oracle_tree_mask(const int32_t *parents, const int32_t *n_nodes, int32_t B, 
     }
     return err ? -1 : 0;
 }
+
+/*
+ * Processed distributions: top-k, then top-p, after temperature ([LP]
+ * "Notation": p is the target's distribution after temperature, top-p and
+ * the like; [LP] "Common pitfalls" and [AIA] Key takeaways: the target and
+ * the draft go through the same temperature / top-k / top-p pipeline, else
+ * the guarantee breaks).  The pages name the two filters without defining
+ * them; the plain readings taken:
+ *   - top-k (0 < top_k < V): keep every token whose logit is at least the
+ *     top_k-th largest logit of the row (counted with multiplicity; ties at
+ *     that value are all kept); top_k <= 0 or >= V keeps every token;
+ *   - top-p (0 < top_p < 1), applied to the top-k survivors renormalised:
+ *     keep every token whose logit is at least tau, the largest logit value
+ *     v for which the survivors with logit >= v hold at least top_p of the
+ *     survivors' probability; top_p >= 1 keeps every survivor;
+ *   - the processed distribution is softmax(l / T) restricted to the kept
+ *     tokens and renormalised.
+ * Both filters keep an upper set of logit values, so each row's processing
+ * is one floor: the kept tokens are exactly those with l >= floor (-inf
+ * when nothing is cut).  floor[r] is the floor of row r.  margin[r] (may be
+ * NULL) is, when top-p decides the floor, the distance of top_p * Z_k from
+ * the nearer of the two cumulative masses that bracket it (the mass at or
+ * above tau and the mass strictly above it), relative to Z_k; +inf
+ * otherwise.  A small margin marks a row whose kept set a rounding of the
+ * masses could change.
+ */
+static int cmp_desc(const void *a, const void *b) {
+    const double x = *(const double *)a, y = *(const double *)b;
+    return (x < y) - (x > y);
+}
+
+int oracle_sampling_floor(const void *logits, int dtype, int64_t rows, int32_t V, double T,
+                          int32_t top_k, double top_p, float *floor_out, double *margin) {
+    if (!logits || !floor_out || rows < 0 || V <= 0 || !(T > 0.0) || !(top_p > 0.0))
+        return -1;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+    for (int64_t r = 0; r < rows; ++r) {
+        double *s = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!s) { err |= 1; continue; }
+        for (int32_t t = 0; t < V; ++t) s[t] = load_logit(logits, dtype, (size_t)r * V + t);
+        qsort(s, (size_t)V, sizeof(double), cmp_desc);       /* largest first */
+        /* top-k: the top_k-th largest value, with multiplicity. */
+        const double theta_k = (top_k > 0 && top_k < V) ? s[top_k - 1] : -INFINITY;
+        double fl = theta_k, mg = INFINITY;
+        if (top_p < 1.0) {
+            /* Survivors' masses exp((l - m) / T), m the row max. */
+            const double m = s[0];
+            double zk = 0.0;
+            for (int32_t i = 0; i < V && s[i] >= theta_k; ++i) zk += exp((s[i] - m) / T);
+            const double w = top_p * zk;
+            /* Walk the distinct values from the largest: tau is the first
+             * value at which the mass at or above it reaches w. */
+            double cum = 0.0;
+            for (int32_t i = 0; i < V && s[i] >= theta_k;) {
+                const double v = s[i];
+                const double below = cum;
+                while (i < V && s[i] == v) cum += exp((s[i++] - m) / T);
+                if (cum >= w) {
+                    fl = v;
+                    mg = fmin(cum - w, w - below) / zk;
+                    break;
+                }
+            }
+        }
+        floor_out[r] = (float)fl;
+        if (margin) margin[r] = mg;
+        free(s);
+    }
+    return err ? -1 : 0;
+}

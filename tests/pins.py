@@ -858,6 +858,155 @@ def pin_tree_mask_properties(o):
             assert not mb[i, i + 1:].any()
 
 
+# --------------------------------------------------------------------------
+# Processed distributions (top-k, then top-p, after temperature)
+# --------------------------------------------------------------------------
+
+def _processed_brute(l, T, top_k, top_p):
+    """The processed law of one row by brute force over upper sets: the
+    top-k survivors are the smallest upper set {l >= v} holding at least
+    top_k tokens; top-p keeps the smallest upper set of survivors holding at
+    least top_p of their mass.  Returns the renormalised law."""
+    l = np.asarray(l, np.float64)
+    V = len(l)
+    vals = sorted(set(l.tolist()), reverse=True)
+    keep = np.ones(V, bool)
+    if 0 < top_k < V:
+        v = max(v for v in vals if np.count_nonzero(l >= v) >= top_k)
+        keep = l >= v
+    if top_p < 1:
+        w = np.where(keep, softmax_T(np.where(keep, l, -np.inf), T), 0.0)
+        for v in vals:
+            up = keep & (l >= v)
+            if w[up].sum() >= top_p:
+                keep = up
+                break
+    return np.where(keep, softmax_T(np.where(keep, l, -np.inf), T), 0.0)
+
+
+def pin_processed_floor_closed_forms(o):
+    """Hand-computed cases: l = (0, 1, 2, 3).  At T = 1 the law is
+    e^l / sum = (0.032, 0.087, 0.237, 0.644): top-p 0.6 keeps {3}; 0.7 keeps
+    {2, 3}; 0.9 keeps {1, 2, 3}; top-k 2 keeps {2, 3}; top-k 3 then top-p
+    0.9 renormalises over {1, 2, 3} = (0.090, 0.245, 0.665) and keeps {2, 3}
+    (0.910).  At T = 2 the law is (0.102, 0.167, 0.276, 0.455): top-p 0.4
+    keeps {3}, 0.7 keeps {2, 3}.  Ties at the cut are kept: (1, 1, 1, 0)
+    with top-k 1 or top-p 0.1 keeps the three 1s.  No filter: -inf."""
+    l = np.array([[0, 1, 2, 3]], np.float32)
+    cases = [(1.0, 0, 1.0, -np.inf), (1.0, 0, 0.6, 3), (1.0, 0, 0.7, 2), (1.0, 0, 0.9, 1),
+             (1.0, 2, 1.0, 2), (1.0, 3, 0.9, 2), (1.0, 4, 1.0, -np.inf), (1.0, 0, 0.6438, 3),
+             (1.0, 0, 0.6440, 2), (2.0, 0, 0.4, 3), (2.0, 0, 0.7, 2), (2.0, 1, 0.3, 3)]
+    for T, k, p, want in cases:
+        fl, _ = o.sampling_floor(l, T, k, p)
+        assert fl[0] == want, (T, k, p, fl[0])
+    ties = np.array([[1, 1, 1, 0]], np.float32)
+    assert o.sampling_floor(ties, 1.0, 1, 1.0)[0][0] == 1.0
+    assert o.sampling_floor(ties, 1.0, 0, 0.1)[0][0] == 1.0
+    # bf16 bits of the same values give the same floors.
+    bits = (l.view(np.uint32) >> 16).astype(np.uint16)
+    assert o.sampling_floor(bits, 1.0, 3, 0.9)[0][0] == 2.0
+    # -inf logits count in the top-k ranks but carry no mass.
+    li = np.array([[0.5, -np.inf, -np.inf, 2.0]], np.float32)
+    assert o.sampling_floor(li, 1.0, 3, 1.0)[0][0] == -np.inf
+    assert o.sampling_floor(li, 1.0, 0, 0.99)[0][0] == 0.5
+
+
+def pin_processed_boundary_is_inclusive(o):
+    """The top-p cut keeps the smallest set whose mass reaches top_p: a set
+    holding exactly top_p is enough.  With l = (0, -1, -2) and top_p = 1/Z,
+    the top token alone holds exactly top_p * Z whenever that product rounds
+    to 1 in fp64 (checked here): the floor is then 0, not -1."""
+    import math
+    found = 0
+    for d in np.linspace(0.5, 3.0, 200):
+        z = 1.0 + math.exp(-d) + math.exp(-2 * d)
+        p = 1.0 / z
+        if p * z != 1.0 or not (np.float32(-d) == -d and np.float32(-2 * d) == -2 * d):
+            continue
+        l = np.array([[0.0, -d, -2 * d]], np.float32)
+        fl, mg = o.sampling_floor(l, 1.0, 0, p)
+        assert fl[0] == 0.0 and mg[0] == 0.0, (d, fl, mg)
+        found += 1
+    assert found > 0
+
+
+def pin_processed_law_exact(o):
+    """With the same processing on both sides (3.5 Speculative Decoding,
+    'Common pitfalls'), the emitted token is distributed exactly as the
+    processed target law P': by stratified uniforms, the accept probability
+    of every draft token the processed draft can propose is min(1, P'/Q'),
+    the residual law is max(0, P' - Q') normalised, and the emitted law is
+    P' (P' and Q' by brute force over upper sets)."""
+    V, T, M = 7, 0.9, 1024
+    rng = np.random.default_rng(19)
+    u = grid(M)
+    for top_k, top_p in [(3, 1.0), (0, 0.8), (5, 0.7), (2, 0.95), (6, 0.5)]:
+        lt = (rng.standard_normal((1, 2, V)) * 1.5).astype(np.float32)
+        ld = (lt[:, :1] + rng.standard_normal((1, 1, V)) * 0.8).astype(np.float32)
+        P = _processed_brute(lt[0, 0], T, top_k, top_p)
+        Q = _processed_brute(ld[0, 0], T, top_k, top_p)
+        a = np.zeros(V)
+        tgt = np.repeat(lt, M, axis=0)
+        drf = np.repeat(ld, M, axis=0)
+        for x in np.flatnonzero(Q > 0):
+            uni = np.stack([u, np.full(M, 0.5, np.float32)], axis=1)
+            r = o.verify_processed(tgt, drf, np.full((M, 1), x, np.int32), uni, T, top_k, top_p)
+            a[x] = np.mean(r["num_accepted"] == 1)
+        ok = Q > 0
+        np.testing.assert_allclose(a[ok], np.minimum(1.0, P[ok] / Q[ok]), atol=1.0 / M)
+        x = int(np.flatnonzero(ok)[np.argmin(P[ok] / Q[ok])])
+        uni = np.stack([np.full(M, 1 - 2**-24, np.float32), u], axis=1)
+        r = o.verify_processed(tgt, drf, np.full((M, 1), x, np.int32), uni, T, top_k, top_p)
+        res = np.maximum(P - Q, 0)
+        if res.sum() > 0 and a[x] < 1:
+            assert np.all(r["num_accepted"] == 0)
+            h = np.bincount(r["out_tokens"][:, 0], minlength=V)[:V] / M
+            np.testing.assert_allclose(h, res / res.sum(), atol=2.0 / M)
+            law = Q * a + np.dot(Q, 1 - a) * h
+            np.testing.assert_allclose(law, P, atol=3.0 / M)
+        # Bonus after an accepted draft: the processed law of the last row.
+        Pk = _processed_brute(lt[0, 1], T, top_k, top_p)
+        xs = int(np.argmax(np.where(ok, P / np.maximum(Q, 1e-300), -1)))
+        uni = np.stack([np.zeros(M, np.float32), u], axis=1)
+        r = o.verify_processed(tgt, drf, np.full((M, 1), xs, np.int32), uni, T, top_k, top_p)
+        assert np.all(r["num_accepted"] == 1)
+        h = np.bincount(r["out_tokens"][:, 1], minlength=V)[:V] / M
+        np.testing.assert_allclose(h, Pk, atol=2.0 / M)
+
+
+def pin_top_k_one_is_greedy(o):
+    """top-k = 1 leaves each side a point mass at its argmax, so the
+    stochastic step with any uniforms is the greedy step on the drafts'
+    argmaxes ('Proof', greedy remark); a vanishing top-p does the same."""
+    rng = np.random.default_rng(23)
+    B, K, V = 60, 4, 50
+    lt = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    ld = np.where(rng.random((B, K, 1)) < 0.6, lt[:, :K], rng.standard_normal((B, K, V))).astype(np.float32)
+    toks = ld.argmax(axis=-1).astype(np.int32)
+    uni = rng.random((B, K + 1), dtype=np.float32)
+    g = o.verify_greedy(lt, toks)
+    for k, p in ((1, 1.0), (0, 1e-9), (1, 0.5)):
+        r = o.verify_processed(lt, ld, toks, uni, 1.3, k, p)
+        assert np.array_equal(r["out_tokens"], g["out_tokens"])
+        assert np.array_equal(r["num_accepted"], g["num_accepted"])
+
+
+def pin_no_processing_is_plain_verify(o):
+    """top-k off (0 or >= V) and top-p = 1 leave the step unchanged."""
+    rng = np.random.default_rng(29)
+    B, K, V, T = 40, 3, 64, 0.8
+    lt = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    ld = (lt[:, :K] + rng.standard_normal((B, K, V))).astype(np.float32)
+    toks = rng.integers(0, V, (B, K)).astype(np.int32)
+    uni = rng.random((B, K + 1), dtype=np.float32)
+    ref = o.verify(lt, ld, toks, uni, T)
+    for k in (0, V, V + 5):
+        r = o.verify_processed(lt, ld, toks, uni, T, k, 1.0)
+        assert np.array_equal(r["out_tokens"], ref["out_tokens"])
+        assert np.array_equal(r["num_accepted"], ref["num_accepted"])
+        assert np.all(np.isneginf(r["target_floor"]))
+
+
 ALL_PINS = [
     pin_stats_logsumexp, pin_stats_closed_forms,
     pin_check_your_understanding, pin_single_position_experiment,
@@ -871,5 +1020,6 @@ ALL_PINS = [
     pin_speedup_table_and_choice, pin_acceptance_count_identities,
     pin_alpha_test_estimates_alpha, pin_ngram_drafter, pin_tree_verify_page_trees,
     pin_tree_chain_is_linear_greedy, pin_tree_best_of_paths, pin_tree_mask_page,
-    pin_tree_mask_properties,
+    pin_tree_mask_properties, pin_processed_floor_closed_forms, pin_processed_boundary_is_inclusive,
+    pin_processed_law_exact, pin_top_k_one_is_greedy, pin_no_processing_is_plain_verify,
 ]

@@ -75,6 +75,13 @@ MUTANTS = {
                          "for (int32_t j = i; j >= 0 && j >= par[i]; j = par[j]) m["),
     "mask_transposed": ("m[(size_t)i * N + j] = 1;", "m[(size_t)j * N + i] = 1;"),
     "depth_zero_based": ("d[i] = par[i] < 0 ? 1 : d[par[i]] + 1;", "d[i] = par[i] < 0 ? 0 : d[par[i]] + 1;"),
+    "topk_off_by_one": ("? s[top_k - 1] : -INFINITY;", "? s[top_k] : -INFINITY;"),
+    "topp_strict": ("if (cum >= w) {", "if (cum > w) {"),
+    "topp_over_all_tokens": ("for (int32_t i = 0; i < V && s[i] >= theta_k; ++i) zk +=",
+                             "for (int32_t i = 0; i < V; ++i) zk +="),
+    "topp_without_temperature": ("zk += exp((s[i] - m) / T);", "zk += exp(s[i] - m);"),
+    "topp_floor_next_value": ("                    fl = v;\n", "                    fl = i < V ? s[i] : v;\n"),
+    "topp_ignores_topk": ("        double fl = theta_k, mg = INFINITY;", "        double fl = -INFINITY, mg = INFINITY;"),
     "tree_first_accepted_not_deepest": ("if (acc[n] && depth[n] > end_depth) { end = n; end_depth = depth[n]; }",
                                         "if (acc[n] && end < 0) { end = n; end_depth = depth[n]; }"),
 }
