@@ -182,6 +182,62 @@ int specdec_verify_greedy_timed(const void *target_logits, specdec_dtype_t dtype
                                 size_t workspace_bytes, void *stream, void *const *events);
 
 /*
+ * The verify step on processed distributions ("3.5 Speculative Decoding",
+ * "Notation": p is the target's distribution after temperature, top-p and
+ * the like; "Common pitfalls" and "246 Speculative Decoding", Key takeaways:
+ * the target and the draft must go through the same temperature / top-k /
+ * top-p processing, else the guarantee breaks).  Every target row i <= k_b
+ * and draft row i < k_b is processed the same way, then specdec_verify's
+ * step runs on the processed rows:
+ *   top-k (0 < top_k < V): keep the tokens whose logit is at least the
+ *          top_k-th largest logit of the row (ties at it are all kept);
+ *          top_k <= 0 or >= V keeps every token;
+ *   top-p (0 < top_p < 1), on the top-k survivors renormalised: keep the
+ *          tokens whose logit is at least tau, the largest logit value whose
+ *          upper set {l >= tau} holds at least top_p of the survivors'
+ *          probability; top_p >= 1 keeps every survivor;
+ *   the processed distribution is softmax(l / T) over the kept tokens,
+ *          renormalised; a drafted token cut from the target row has
+ *          p(x) = 0 and is rejected.
+ * Arguments, outputs and preconditions as specdec_verify, plus top_k and
+ * top_p (top_p <= 0 or NaN: SPECDEC_EINVAL).  Workspace:
+ * specdec_verify_processed_workspace_bytes.  accept_prob is min(1, p/q) of
+ * the processed rows.  B * (rows per request) <= 2^22.
+ */
+size_t specdec_verify_processed_workspace_bytes(int32_t B, int32_t K, int32_t V,
+                                                specdec_dtype_t dtype, int one_hot_drafts);
+int specdec_verify_processed(const void *target_logits, const void *draft_logits,
+                             specdec_dtype_t dtype, const int32_t *draft_tokens,
+                             const int32_t *k_per_req, const float *uniforms, float temperature,
+                             int32_t top_k, float top_p, int32_t B, int32_t K, int32_t V,
+                             int32_t *out_tokens, int32_t *num_accepted, float *accept_prob,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * specdec_verify_processed with per-phase timing: events[0] / events[1] are
+ * taken at the start / end of the processing kernel (the pass that reads
+ * every row and finds its cut), events[2] at the end of the call.
+ */
+int specdec_verify_processed_timed(const void *target_logits, const void *draft_logits,
+                                   specdec_dtype_t dtype, const int32_t *draft_tokens,
+                                   const int32_t *k_per_req, const float *uniforms,
+                                   float temperature, int32_t top_k, float top_p, int32_t B,
+                                   int32_t K, int32_t V, int32_t *out_tokens,
+                                   int32_t *num_accepted, float *accept_prob, void *workspace,
+                                   size_t workspace_bytes, void *stream, void *const *events);
+
+/*
+ * The processing alone: floors[r] of each row r of logits [rows, V] after
+ * temperature T, top-k and top-p as in specdec_verify_processed -- the kept
+ * tokens of row r are exactly those with logits[r, t] >= floors[r] (-inf
+ * when nothing is cut).  floors: [rows] float, device.  0 <= rows <= 2^22,
+ * else SPECDEC_EINVAL.  No workspace.
+ */
+int specdec_sampling_floors(const void *logits, specdec_dtype_t dtype, int64_t rows, int32_t V,
+                            float temperature, int32_t top_k, float top_p, float *floors,
+                            void *stream);
+
+/*
  * Greedy tree verification ("3.5 Speculative Decoding", "Tree verification";
  * "Speculative Decoding: Mathematical Foundations ...", "Tree-Based
  * Verification and Custom Attention Masks"): a tree of drafted tokens,

@@ -5,9 +5,9 @@ this package holds the thin ctypes binding over it, the in-tree build and the
 seeded synthetic workloads used by the tests and the benchmark.
 """
 from ._lib import (SpecdecError, Workspace, acceptance_counts, choose_k, load,  # noqa: F401
-                   ngram_propose, softmax_stats, tree_mask, tree_verify_greedy, verify,
+                   ngram_propose, sampling_floors, softmax_stats, tree_mask, tree_verify_greedy, verify,
                    verify_greedy, version)
 
 __all__ = ["SpecdecError", "Workspace", "acceptance_counts", "choose_k", "load", "ngram_propose",
-           "softmax_stats", "tree_mask", "tree_verify_greedy", "verify", "verify_greedy",
+           "sampling_floors", "softmax_stats", "tree_mask", "tree_verify_greedy", "verify", "verify_greedy",
            "version"]

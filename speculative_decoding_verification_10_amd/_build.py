@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecdec.so")
-SOURCES = ["api.cpp", "verify.hip", "greedy.hip", "stats.hip", "telemetry.hip", "ngram.hip", "tree.hip"]
+SOURCES = ["api.cpp", "verify.hip", "greedy.hip", "stats.hip", "telemetry.hip", "ngram.hip", "tree.hip", "sampling.hip"]
 HEADERS = ["device_common.h", "internal.h", "slots.h"]
 
 ARCH = os.environ.get("SPECDEC_OFFLOAD_ARCH", "gfx950")

@@ -76,6 +76,16 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.specdec_verify_greedy_timed.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, vp,
                                                     vp, sz, vp, vp]
         lib.specdec_verify_greedy_timed.restype = ci
+        lib.specdec_verify_processed_workspace_bytes.argtypes = [i32, i32, i32, ci, ci]
+        lib.specdec_verify_processed_workspace_bytes.restype = sz
+        lib.specdec_verify_processed.argtypes = [vp, vp, ci, vp, vp, vp, f32, i32, f32, i32, i32,
+                                                 i32, vp, vp, vp, vp, sz, vp]
+        lib.specdec_verify_processed.restype = ci
+        lib.specdec_verify_processed_timed.argtypes = [vp, vp, ci, vp, vp, vp, f32, i32, f32, i32,
+                                                       i32, i32, vp, vp, vp, vp, sz, vp, vp]
+        lib.specdec_verify_processed_timed.restype = ci
+        lib.specdec_sampling_floors.argtypes = [vp, ci, i64, i32, f32, i32, f32, vp, vp]
+        lib.specdec_sampling_floors.restype = ci
         lib.specdec_tree_verify_greedy_workspace_bytes.argtypes = [i32, i32, i32, ci]
         lib.specdec_tree_verify_greedy_workspace_bytes.restype = sz
         lib.specdec_tree_verify_greedy.argtypes = [vp, ci, vp, vp, vp, i32, i32, i32, vp, vp, vp,
@@ -170,7 +180,7 @@ def verify_workspace_bytes(B, K, V, dtype_code, one_hot) -> int:
 def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
            uniforms: torch.Tensor, temperature: float, k_per_req: Optional[torch.Tensor] = None,
            accept_prob: bool = False, workspace: Optional[Workspace] = None, out=None,
-           events=None):
+           events=None, top_k: Optional[int] = None, top_p: Optional[float] = None):
     """Stochastic verify step (specdec_verify).
 
     target [B, K+1, V], draft [B, K, V] or None (one-hot drafts), both fp32 or
@@ -180,7 +190,9 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
     (out_tokens, num_accepted, accept_prob) tensors.  ``events``: three
     torch.cuda.Event (enable_timing=True) or None entries, taken at the row
     kernel's start, its end and the end of the call's last kernel
-    (specdec_verify_timed).
+    (specdec_verify_timed).  ``top_k`` / ``top_p``: run the step on the
+    top-k / top-p processed distributions (specdec_verify_processed; None =
+    that filter off).
     """
     lib = load()
     if target.dim() != 3:
@@ -206,6 +218,25 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
         _check(nacc, "num_accepted", torch.int32, (B,), dev)
         if ap is not None:
             _check(ap, "accept_prob", torch.float32, (B, K), dev)
+    processed = top_k is not None or top_p is not None
+    if processed:
+        nbytes = int(lib.specdec_verify_processed_workspace_bytes(B, K, V, code, int(draft is None)))
+        ws = _workspace(nbytes, dev, workspace, "verify_processed")
+        args = (_ptr(target), _ptr(draft), code, _ptr(draft_tokens), _ptr(k_per_req), _ptr(uniforms),
+                float(temperature), int(top_k or 0), float(1.0 if top_p is None else top_p), B, K, V,
+                _ptr(out_tokens), _ptr(nacc), _ptr(ap), ws.ptr(), ws.nbytes, _stream(dev))
+        if events is None:
+            rc = lib.specdec_verify_processed(*args)
+            what = "specdec_verify_processed"
+        else:
+            if len(events) != 3:
+                raise ValueError("events must hold three entries")
+            rc = lib.specdec_verify_processed_timed(
+                *args, (ctypes.c_void_p * 3)(*[_event_handle(e, dev) for e in events]))
+            what = "specdec_verify_processed_timed"
+        if rc != 0:
+            raise SpecdecError(rc, what)
+        return out_tokens, nacc, ap
     nbytes = verify_workspace_bytes(B, K, V, code, draft is None)
     ws = _workspace(nbytes, dev, workspace, "verify")
     if events is None:
@@ -356,6 +387,27 @@ def tree_mask(parents: torch.Tensor, n_nodes: Optional[torch.Tensor] = None):
     if rc != 0:
         raise SpecdecError(rc, "specdec_tree_mask")
     return mask, depth
+
+
+def sampling_floors(logits: torch.Tensor, temperature: float, top_k: int = 0, top_p: float = 1.0):
+    """Per-row floor of the top-k / top-p processed distribution of a
+    [..., V] tensor (specdec_sampling_floors): the kept tokens of a row are
+    those with logit >= its floor.  Returns fp32 of shape [...]."""
+    lib = load()
+    if logits.dim() < 1:
+        raise ValueError("logits must have a vocabulary axis")
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V > 0 else 0
+    dev = logits.device
+    code = _dtype_code(logits)
+    if not logits.is_contiguous():
+        raise ValueError("logits must be contiguous")
+    fl = torch.empty(logits.shape[:-1], dtype=torch.float32, device=dev)
+    rc = lib.specdec_sampling_floors(_ptr(logits), code, rows, V, float(temperature), int(top_k),
+                                     float(top_p), _ptr(fl), _stream(dev))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_sampling_floors")
+    return fl
 
 
 def softmax_stats(logits: torch.Tensor, temperature: float, workspace: Optional[Workspace] = None):

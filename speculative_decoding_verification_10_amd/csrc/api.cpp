@@ -17,6 +17,7 @@ constexpr int32_t kMaxV = 1 << 28;
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxBlocks = (size_t)1 << 24;   // gridDim.x * 256 threads < 2^32
 constexpr int32_t kMaxBatch = 65535;              // requests: a grid dimension other than x
+constexpr size_t kMaxFloorRows = (size_t)1 << 22;  // 1,024-thread workgroups: gridDim.x * 1024 < 2^32
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -53,13 +54,14 @@ bool make_scale(float temperature, Scale* s) {
 }
 
 struct VerifyLayout {
-    size_t err, slot_m, slot_s, slot_l, slot_slab, dec, total;
+    size_t err, slot_m, slot_s, slot_l, slot_slab, dec, floors, total;
 };
 
 // Header (error bits), self-validating slots -- tile max / tile sum of every
 // row slot of every request, the logit at the draft token of every row, the
 // slab sums of every request's final row -- and each request's decision.
-VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, bool one_hot) {
+VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, bool one_hot,
+                           bool processed = false) {
     int NV, NVv;
     bool vec;
     row_geometry(V, dt, false, &NV, &vec);        // scalar geometry >= vector geometry
@@ -75,6 +77,7 @@ VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, 
     L.slot_l = off;    off = align_up(off + (size_t)B * R * sizeof(uint32_t));
     L.slot_slab = off; off = align_up(off + (size_t)B * C * kSlabsPerTile * sizeof(uint64_t));
     L.dec = off;       off = align_up(off + (size_t)B * sizeof(Decision));
+    L.floors = off;    if (processed) off = align_up(off + (size_t)B * R * sizeof(float));
     L.total = off;
     return L;
 }
@@ -244,6 +247,121 @@ int specdec_verify_timed(const void* target_logits, const void* draft_logits, sp
     p.dec = reinterpret_cast<Decision*>(ws + L.dec);
     return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream,
                                     reinterpret_cast<hipEvent_t const*>(events)));
+}
+
+size_t specdec_verify_processed_workspace_bytes(int32_t B, int32_t K, int32_t V,
+                                                specdec_dtype_t dtype, int one_hot_drafts) {
+    if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV || !dtype_ok(dtype)) return 0;
+    return verify_layout(B, K, V, dtype, one_hot_drafts != 0, true).total;
+}
+
+int specdec_verify_processed(const void* target_logits, const void* draft_logits,
+                             specdec_dtype_t dtype, const int32_t* draft_tokens,
+                             const int32_t* k_per_req, const float* uniforms, float temperature,
+                             int32_t top_k, float top_p, int32_t B, int32_t K, int32_t V,
+                             int32_t* out_tokens, int32_t* num_accepted, float* accept_prob,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return specdec_verify_processed_timed(target_logits, draft_logits, dtype, draft_tokens, k_per_req,
+                                          uniforms, temperature, top_k, top_p, B, K, V, out_tokens,
+                                          num_accepted, accept_prob, workspace, workspace_bytes,
+                                          stream, nullptr);
+}
+
+int specdec_verify_processed_timed(const void* target_logits, const void* draft_logits,
+                                   specdec_dtype_t dtype, const int32_t* draft_tokens,
+                                   const int32_t* k_per_req, const float* uniforms,
+                                   float temperature, int32_t top_k, float top_p, int32_t B,
+                                   int32_t K, int32_t V, int32_t* out_tokens,
+                                   int32_t* num_accepted, float* accept_prob, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* events) {
+    if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
+    if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
+    if (!(top_p > 0.0f)) return SPECDEC_EINVAL;              // also rejects NaN
+    Scale sc;
+    if (!make_scale(temperature, &sc)) return SPECDEC_EINVAL;
+    if (B == 0) return SPECDEC_OK;
+    if (!target_logits || !uniforms || !out_tokens || !num_accepted) return SPECDEC_EINVAL;
+    if (K > 0 && !draft_tokens) return SPECDEC_EINVAL;
+    const bool one_hot = (draft_logits == nullptr);
+    const VerifyLayout L = verify_layout(B, K, V, dtype, one_hot, true);
+    if (!workspace_ok(workspace, workspace_bytes, L.total)) return SPECDEC_EWORKSPACE;
+    VerifyParams p{};
+    bool vec;
+    row_geometry(V, dtype, aligned16(target_logits) && aligned16(draft_logits), &p.NV, &vec);
+    p.C = tiles_of(p.NV);
+    p.R = K + 1 + (one_hot ? 0 : K);
+    p.NS = (p.NV + kSlab - 1) / kSlab;
+    p.kinds = one_hot ? 1 : 2;
+    if ((size_t)B * p.C > kMaxBlocks || (size_t)B * p.R > kMaxFloorRows || B > kMaxBatch)
+        return SPECDEC_EINVAL;
+    p.target = target_logits;
+    p.draft = draft_logits;
+    p.tokens = draft_tokens;
+    p.kpr = k_per_req;
+    p.unif = uniforms;
+    p.out = out_tokens;
+    p.nacc = num_accepted;
+    p.aprob = accept_prob;
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.sc = sc;
+    char* ws = static_cast<char*>(workspace);
+    p.err = reinterpret_cast<uint32_t*>(ws + L.err);
+    p.slot_m = reinterpret_cast<uint32_t*>(ws + L.slot_m);
+    p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);
+    p.slot_l = reinterpret_cast<uint32_t*>(ws + L.slot_l);
+    p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
+    p.dec = reinterpret_cast<Decision*>(ws + L.dec);
+    p.floors = reinterpret_cast<float*>(ws + L.floors);
+    FloorParams f{};
+    f.target = target_logits;
+    f.draft = draft_logits;
+    f.tokens = draft_tokens;
+    f.kpr = k_per_req;
+    f.B = B;
+    f.K = K;
+    f.V = V;
+    f.NV = p.NV;
+    f.R = p.R;
+    f.C = p.C;
+    f.sc = sc;
+    f.top_k = top_k;
+    f.top_p = (double)top_p;
+    f.floors = reinterpret_cast<float*>(ws + L.floors);
+    f.err = p.err;
+    f.slot_m = p.slot_m;
+    f.slot_s = p.slot_s;
+    f.slot_l = p.slot_l;
+    f.slot_slab = p.slot_slab;
+    return map_launch(launch_verify_processed(f, p, dtype, vec, (hipStream_t)stream,
+                                              reinterpret_cast<hipEvent_t const*>(events)));
+}
+
+int specdec_sampling_floors(const void* logits, specdec_dtype_t dtype, int64_t rows, int32_t V,
+                            float temperature, int32_t top_k, float top_p, float* floors,
+                            void* stream) {
+    if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
+    if (rows < 0 || rows > (int64_t)kMaxFloorRows || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
+    if (!(top_p > 0.0f)) return SPECDEC_EINVAL;
+    Scale sc;
+    if (!make_scale(temperature, &sc)) return SPECDEC_EINVAL;
+    if (rows == 0) return SPECDEC_OK;
+    if (!logits || !floors) return SPECDEC_EINVAL;
+    FloorParams f{};
+    bool vec;
+    row_geometry(V, dtype, aligned16(logits), &f.NV, &vec);
+    f.target = logits;
+    f.B = (int)rows;
+    f.K = 0;
+    f.R = 1;
+    f.C = tiles_of(f.NV);
+    f.V = V;
+    f.sc = sc;
+    f.top_k = top_k;
+    f.top_p = (double)top_p;
+    f.floors = floors;
+    return map_launch(launch_floors(f, dtype, vec, (hipStream_t)stream));
 }
 
 size_t specdec_verify_greedy_workspace_bytes(int32_t B, int32_t K, int32_t V,

@@ -55,6 +55,7 @@ struct VerifyParams {
     uint32_t* slot_l;           // [B * R] logit at the draft token of each row (self-validating)
     uint64_t* slot_slab;        // [B * C * kSlabsPerTile] slab sums of the final draw (self-validating)
     Decision* dec;              // [B] decision of each request
+    const float* floors;        // [B * R] processed-row floors, or null (plain rows)
 };
 
 // Linear greedy verify (launch_greedy) or greedy tree verify
@@ -72,6 +73,28 @@ struct GreedyParams {
     int B, K, V, NV, C;
     uint32_t* err;              // workspace header: error bits
     uint64_t* slot;             // [B * (K+1) * C] tile (max, index) words
+};
+
+// Floors of the top-k / top-p processed distributions, one per row (the
+// kept tokens are those with logit >= floor), and, when slot_m is set, the
+// verify step's row statistics of the processed rows in its slot layout.
+// Row slot rr of request b: target row b * (K + 1) + rr for rr <= K, draft
+// row b * K + (rr - K - 1) otherwise; slots past k_b are skipped.
+struct FloorParams {
+    const void* target;         // [B, K+1, V]
+    const void* draft;          // [B, K, V] or null
+    const int32_t* tokens;      // [B, K] draft tokens (gathers), or null
+    const int32_t* kpr;         // [B] or null (K)
+    int B, K, V, NV, R, C;
+    Scale sc;
+    int top_k;                  // kept: the top_k largest (with ties); <= 0 or >= V: off
+    double top_p;               // kept mass share of the survivors; >= 1: off
+    float* floors;              // [B * R]
+    uint32_t* err;              // workspace header, or null
+    uint32_t* slot_m;           // verify slots (null: floors only)
+    uint64_t* slot_s;
+    uint32_t* slot_l;
+    uint64_t* slot_slab;
 };
 
 // Ancestor masks and depths of flattened draft trees.
@@ -124,6 +147,15 @@ hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t
 hipError_t launch_tree_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,
                               hipEvent_t const* events = nullptr);
 hipError_t launch_tree_mask(const TreeMaskParams& p, hipStream_t s);
+// The floor kernel alone (standalone floors, or the first kernel of the
+// processed verify step; events[0] / events[1] as for the row kernel).
+hipError_t launch_floors(const FloorParams& p, int dtype, bool vec, hipStream_t s,
+                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// The processed verify step: the floor kernel (which also writes the row
+// statistics), then the verify step's decision and final kernels on the
+// floored rows.  p.floors must be set.
+hipError_t launch_verify_processed(const FloorParams& f, const VerifyParams& p, int dtype, bool vec,
+                                   hipStream_t s, hipEvent_t const* events = nullptr);
 hipError_t launch_stats(const StatsParams& p, int dtype, bool vec, hipStream_t s);
 hipError_t launch_acceptance_counts(const TelemetryParams& p, hipStream_t s);
 hipError_t launch_ngram(const NgramParams& p, hipStream_t s);

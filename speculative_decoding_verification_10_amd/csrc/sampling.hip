@@ -1,0 +1,382 @@
+// Top-k / top-p processed distributions on gfx950 ("3.5 Speculative
+// Decoding", "Notation": p and q are the distributions after temperature,
+// top-p and the like; "Common pitfalls" and "246 Speculative Decoding", Key
+// takeaways: the target and the draft go through the same temperature /
+// top-k / top-p processing).
+//
+// Both filters keep an upper set of logit values, so each row's processing is
+// one floor: the kept tokens are those with logit >= floor.
+//   top-k: the floor is the top_k-th largest logit (ties at it are kept);
+//   top-p: on the top-k survivors, the largest logit v whose upper set
+//          {l >= v} holds at least top_p of the survivors' mass.
+//
+// One workgroup of 1,024 threads per row.  The row is read from HBM once;
+// the later passes over it mostly hit the L2 / Infinity Cache.  Per row:
+//   1. the row max m and the offset M = fp32(m * c) of the verify step;
+//   2. coarse levels of d = M - x * c (the base-2 exponent deficit of the
+//      mass exp2(x * c - M)): level 0 holds d < 1, level j d < 2^j, level 8
+//      the rest; counts and masses per level give the smallest level sure
+//      to contain the top-k cut (exact counts) or the top-p cut (masses with
+//      a safety margin).  {d < 2^j} is an upper set of logits, because d is
+//      monotone in x;
+//   3. the elements of that upper set become candidates in LDS (key and
+//      mass); masses are summed in 2^-35 fixed point, so sums are exact and
+//      free of order;
+//   4. radix select over the candidates' order-preserving 32-bit keys
+//      (11-bit digits in LDS histograms): the top_k-th largest key, then the
+//      key at which the mass from the top reaches top_p of the survivors.
+//      Candidates that overflow LDS, or a coarse estimate that missed, fall
+//      back to the same selection over the whole row;
+//   5. the floor, and for the verify step the row statistics of the kept
+//      tokens (max, fp64 sum of exp2(x * c - M)), the logit at the draft
+//      token (-inf when cut), written in the verify step's slot layout.
+#include <hip/hip_ext.h>
+
+#include "internal.h"
+#include "slots.h"
+
+namespace specdec {
+namespace {
+
+constexpr int kFT = 1024;                  // threads per row
+constexpr int kFW = kFT / 64;              // waves per row
+constexpr int kBins = 2048;                // radix bins (11-bit digits)
+constexpr int kCand = 4096;                // LDS candidates
+constexpr int kLevels = 9;                 // coarse levels: d < 2^j (j = 0..7), then the rest
+constexpr double kFix = 34359738368.0;     // 2^35: fixed-point scale of a mass <= 1
+
+// Order-preserving key of a logit (-0 and +0 share a key).
+__device__ __forceinline__ uint32_t key_of(float x) {
+    if (x == 0.0f) x = 0.0f;
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float value_of(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ uint64_t fix_of(float e) { return __double2ull_rn((double)e * kFix); }
+
+// Coarse level of an element from its exponent deficit d.
+__device__ __forceinline__ int level_of(float d) {
+    if (!(d >= 1.0f)) return 0;                       // d < 1 (and the max itself)
+    const int ex = (int)((__float_as_uint(d) >> 23) & 0xFF) - 127;   // floor(log2 d), d >= 1
+    return min(ex + 1, kLevels - 1);
+}
+
+struct FloorShared {
+    uint64_t mass[kBins];               // radix histogram (weights)
+    uint32_t ckey[kCand];               // candidates: key
+    float cexp[kCand];                  //             mass exp2(x * c - M)
+    float red_f[kFW];
+    double red_d[kFW];
+    uint64_t red_u[kFW];
+    uint32_t red_c[kLevels][kFW];
+    double red_m[kLevels][kFW];
+    uint32_t ncand;
+    int guard;
+    uint32_t guard_count;
+    uint32_t pick_bin;
+    uint64_t pick_above;
+};
+
+// The row being processed and its offset.
+struct RowRef {
+    const void* row;
+    int V, NV;
+    float M;
+    Scale sc;
+};
+
+// Workgroup reductions over 1,024 threads (fixed order: deterministic).
+template <typename T, typename Op>
+__device__ __forceinline__ T wg_reduce(T v, T* lds, Op op) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o, 64));
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    T r = lds[0];
+#pragma unroll
+    for (int i = 1; i < kFW; ++i) r = op(r, lds[i]);
+    __syncthreads();
+    return r;
+}
+
+// f(x) for every element of the row this thread visits (vectors t, t + 1024,
+// ...; elements past V skipped).  The first pass over a row reads HBM; the
+// later ones mostly hit the L2 / Infinity Cache.
+template <int DT, bool VEC, typename F>
+__device__ __forceinline__ void for_row(const RowRef& r, F&& f) {
+    constexpr int E = Elem<DT>::E;
+    for (int v = threadIdx.x; v < r.NV; v += kFT) {
+        float x[E];
+        decode<DT>(load_raw<DT, VEC, false>(r.row, r.V, r.NV, v), x);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (v * E + e < r.V) f(x[e]);
+    }
+}
+
+// Sum of the fixed-point masses of the keys >= kmin: over the candidates
+// (from_cand) or over the row.
+template <int DT, bool VEC>
+__device__ __noinline__ uint64_t mass_at_least(const RowRef& r, bool from_cand, uint32_t nc, uint32_t kmin,
+                                               FloorShared& sh) {
+    uint64_t s = 0;
+    if (from_cand) {
+        for (uint32_t c = threadIdx.x; c < nc; c += kFT)
+            if (sh.ckey[c] >= kmin) s += fix_of(sh.cexp[c]);
+    } else {
+        for_row<DT, VEC>(r, [&](float x) {
+            if (key_of(x) >= kmin) s += fix_of(fast_exp2(exponent2(x, r.M, r.sc)));
+        });
+    }
+    return wg_reduce(s, sh.red_u, [](uint64_t p, uint64_t q) { return p + q; });
+}
+
+// Radix select over 32-bit keys, largest first, among the elements with key
+// >= kmin (from the candidates or the row), each weighted by 1 (count) or by
+// its fixed-point mass.  Returns the key at which the weight from the top
+// first reaches `target`: the largest key K with W(keys >= K) >= target.
+// 11-bit digits from the top: bf16 keys have 16 significant bits (two
+// digits), fp32 keys 32 (three).
+template <int DT, bool VEC>
+__device__ __noinline__ uint32_t radix_select(const RowRef& r, bool from_cand, uint32_t nc, bool masses,
+                                              uint32_t kmin, double target, FloorShared& sh) {
+    constexpr int kDigits = (DT == kBF16) ? 2 : 3;
+    uint32_t prefix = 0;
+    uint64_t above = 0;                 // weight strictly above the current prefix
+    for (int dg = 0; dg < kDigits; ++dg) {
+        const int sh_ = dg == 0 ? 21 : dg == 1 ? (DT == kBF16 ? 16 : 10) : 0;
+        const int wd = dg == 0 ? 11 : dg == 1 ? (DT == kBF16 ? 5 : 11) : 10;
+        const int hi = sh_ + wd;        // key bits at and above hi are fixed
+        for (int i = threadIdx.x; i < kBins; i += kFT) sh.mass[i] = 0;
+        __syncthreads();
+        auto add = [&](uint32_t key, uint64_t wgt) {
+            if (key < kmin || (hi < 32 && (key >> hi) != prefix)) return;
+            atomicAdd(reinterpret_cast<unsigned long long*>(&sh.mass[(key >> sh_) & ((1u << wd) - 1)]),
+                      (unsigned long long)wgt);
+        };
+        if (from_cand) {
+            for (uint32_t c = threadIdx.x; c < nc; c += kFT)
+                add(sh.ckey[c], masses ? fix_of(sh.cexp[c]) : (uint64_t)1);
+        } else {
+            for_row<DT, VEC>(r, [&](float x) {
+                add(key_of(x), masses ? fix_of(fast_exp2(exponent2(x, r.M, r.sc))) : (uint64_t)1);
+            });
+        }
+        __syncthreads();
+        // Thread t owns bins 2t and 2t+1; suffix sums from the top bin.
+        const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+        const uint64_t h0 = sh.mass[2 * t], h1 = sh.mass[2 * t + 1];
+        uint64_t s = h0 + h1;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint64_t n = __shfl_down(s, o, 64);
+            if (lane + o < 64) s += n;
+        }
+        if (lane == 0) sh.red_u[w] = s;
+        __syncthreads();
+        for (int i = w + 1; i < kFW; ++i) s += sh.red_u[i];
+        // s = weight of the bins >= 2t within the prefix.
+        const uint64_t incl1 = s - h0, excl1 = incl1 - h1;
+        const uint64_t incl0 = s, excl0 = s - h0;
+        if ((double)(above + excl1) < target && target <= (double)(above + incl1)) {
+            sh.pick_bin = 2 * t + 1;
+            sh.pick_above = above + excl1;
+        } else if ((double)(above + excl0) < target && target <= (double)(above + incl0)) {
+            sh.pick_bin = 2 * t;
+            sh.pick_above = above + excl0;
+        }
+        __syncthreads();
+        prefix = (prefix << wd) | sh.pick_bin;
+        above = sh.pick_above;
+        __syncthreads();
+    }
+    // bf16 keys: the low 16 bits follow from the sign of the value.
+    if (DT == kBF16) prefix = (prefix << 16) | ((prefix & 0x8000u) ? 0u : 0xFFFFu);
+    return prefix;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
+    constexpr int S = Elem<DT>::S;
+    __shared__ FloorShared sh;
+    const int R = a.R, K = a.K;
+    const int b = blockIdx.x / R, rr = blockIdx.x - b * R;
+    const int kb = a.kpr ? min(max(a.kpr[b], 0), K) : K;
+    const bool draft = rr > K;
+    const int i = draft ? rr - K - 1 : rr;
+    if (draft ? i >= kb : i > kb) return;
+    const size_t row_index = draft ? (size_t)b * K + i : (size_t)b * (K + 1) + i;
+    RowRef r;
+    r.row = static_cast<const char*>(draft ? a.draft : a.target) + row_index * (size_t)a.V * S;
+    r.V = a.V;
+    r.NV = a.NV;
+    r.sc = a.sc;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const bool use_k = a.top_k > 0 && a.top_k < a.V;
+    const bool use_p = a.top_p < 1.0;
+
+    // 1. Row max and offset.
+    float m = -INFINITY;
+    for_row<DT, VEC>(r, [&](float x) { m = fmaxf(m, x); });
+    m = wg_reduce(m, sh.red_f, [](float p, float q) { return fmaxf(p, q); });
+    r.M = offset_of(m, a.sc);
+
+    float fl = -INFINITY;
+    double z = 0.0;                     // sum of the kept masses exp2(x * c - M)
+    if (!use_k && !use_p) {
+        for_row<DT, VEC>(r, [&](float x) { z += (double)fast_exp2(exponent2(x, r.M, r.sc)); });
+        z = wg_reduce(z, sh.red_d, [](double p, double q) { return p + q; });
+    } else {
+        // 2. Coarse levels: per-level counts and masses, and the row's mass
+        // in fixed point.
+        uint32_t lc[kLevels];
+        float lm[kLevels];
+        uint64_t zfix = 0;
+#pragma unroll
+        for (int j = 0; j < kLevels; ++j) { lc[j] = 0; lm[j] = 0.0f; }
+        for_row<DT, VEC>(r, [&](float x) {
+            const float d = -exponent2(x, r.M, r.sc);
+            const float e = fast_exp2(-d);
+            const int lv = level_of(d);
+            zfix += fix_of(e);
+#pragma unroll
+            for (int j = 0; j < kLevels; ++j) {
+                lc[j] += (lv == j);
+                lm[j] += (lv == j) ? e : 0.0f;
+            }
+        });
+#pragma unroll
+        for (int j = 0; j < kLevels; ++j) {
+            uint32_t c = lc[j];
+            double ms = (double)lm[j];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                c += __shfl_xor(c, o, 64);
+                ms += __shfl_xor(ms, o, 64);
+            }
+            if (lane == 0) { sh.red_c[j][w] = c; sh.red_m[j][w] = ms; }
+        }
+        // (This reduction's barriers also publish red_c / red_m.)
+        const uint64_t zall = wg_reduce(zfix, sh.red_u, [](uint64_t p, uint64_t q) { return p + q; });
+        // The guard level: the smallest level sure to hold the cut(s).  The
+        // top-k cut bounds the top-p cut from below, so top-k decides when
+        // both are on.  The masses carry a 0.1% margin; an exact check on
+        // the candidates follows.
+        if (t == 0) {
+            uint32_t cc[kLevels];
+            double cm[kLevels];
+            uint32_t c_ = 0;
+            double m_ = 0.0;
+            for (int j = 0; j < kLevels; ++j) {
+                for (int q = 0; q < kFW; ++q) { c_ += sh.red_c[j][q]; m_ += sh.red_m[j][q]; }
+                cc[j] = c_;
+                cm[j] = m_;
+            }
+            int g = kLevels - 1;
+            const double want = a.top_p * cm[kLevels - 1] * 1.001;
+            for (int j = kLevels - 1; j >= 0; --j)
+                if (use_k ? cc[j] >= (uint32_t)a.top_k : cm[j] >= want) g = j;
+            sh.guard = g;
+            sh.guard_count = cc[g];
+        }
+        __syncthreads();
+        const int g = sh.guard;
+        bool cand = g < kLevels - 1 && sh.guard_count <= (uint32_t)kCand;
+        // 3. Candidates: the upper set of the levels <= g.  Each thread
+        // knows how many of its elements lie there; an exclusive scan of
+        // those counts gives it a run of LDS slots, filled in element order
+        // (so the candidates' order is fixed).
+        uint32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < kLevels; ++j) mine += (j <= g) ? lc[j] : 0u;
+        uint32_t base = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t n = __shfl_up(base, o, 64);
+            if (lane >= o) base += n;
+        }
+        if (lane == 63) sh.red_c[0][w] = base;          // wave totals
+        __syncthreads();
+        base -= mine;
+        for (int q = 0; q < w; ++q) base += sh.red_c[0][q];
+        if (t == kFT - 1) sh.ncand = base + mine;
+        if (cand) {
+            uint32_t n = base;
+            for_row<DT, VEC>(r, [&](float x) {
+                const float d = -exponent2(x, r.M, r.sc);
+                if (level_of(d) <= g) {
+                    sh.ckey[n] = key_of(x);
+                    sh.cexp[n] = fast_exp2(-d);
+                    ++n;
+                }
+            });
+        }
+        __syncthreads();
+        const uint32_t nc = sh.ncand;
+        // 4a. top-k: the top_k-th largest key.
+        uint32_t fkey = 0, kkey = 0;
+        if (use_k) {
+            kkey = radix_select<DT, VEC>(r, cand, nc, false, 0u, (double)a.top_k, sh);
+            fkey = kkey;
+        }
+        // 4b. top-p over the survivors (keys >= kkey): the key at which the
+        // mass from the top reaches top_p of theirs.  Without top-k the
+        // candidates must hold that much mass, else the row is used.
+        if (use_p) {
+            const uint64_t zk = use_k ? mass_at_least<DT, VEC>(r, cand, nc, kkey, sh) : zall;
+            const double target = a.top_p * (double)zk;
+            if (cand && !use_k && (double)mass_at_least<DT, VEC>(r, true, nc, 0u, sh) < target) cand = false;
+            fkey = radix_select<DT, VEC>(r, cand, nc, true, kkey, target, sh);
+        }
+        fl = value_of(fkey);
+        // 5. The kept mass: every kept element is a candidate when the
+        // candidates were used (fixed point, exact), else a pass over the row.
+        if (cand) {
+            z = (double)mass_at_least<DT, VEC>(r, true, nc, fkey, sh) / kFix;
+        } else {
+            for_row<DT, VEC>(r, [&](float x) {
+                if (x >= fl) z += (double)fast_exp2(exponent2(x, r.M, r.sc));
+            });
+            z = wg_reduce(z, sh.red_d, [](double p, double q) { return p + q; });
+        }
+    }
+
+    // Outputs: the floor; for the verify step its slots.
+    if (t == 0) a.floors[blockIdx.x] = fl;
+    if (!a.slot_m) return;
+    const size_t rs = (size_t)b * R + rr;
+    const int C = a.C;
+    for (int c = t; c < C; c += kFT) {
+        slot_put(a.slot_m + rs * C + c, enc_f32(c == 0 ? m : -INFINITY));
+        slot_put(a.slot_s + rs * C + c, enc_f64(c == 0 ? z : 0.0));
+    }
+    if (t == 0 && i < kb && a.tokens) {
+        const int x = min(max(a.tokens[(size_t)b * K + i], 0), a.V - 1);
+        const float l = load_one<DT>(r.row, x);
+        slot_put(a.slot_l + rs, enc_f32(l >= fl ? l : -INFINITY));
+    }
+    if (rr == 0)
+        for (int c = t; c < C * kSlabsPerTile; c += kFT)
+            slot_put(a.slot_slab + (size_t)b * C * kSlabsPerTile + c, (uint64_t)0);
+}
+
+template <int DT, bool VEC>
+hipError_t launch_t(const FloorParams& p, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    const size_t blocks = (size_t)p.B * p.R;
+    if (blocks == 0) return hipSuccess;
+    hipExtLaunchKernelGGL((floor_rows<DT, VEC>), dim3((unsigned)blocks), dim3(kFT), 0, s, start, stop, 0, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_floors(const FloorParams& p, int dtype, bool vec, hipStream_t s, hipEvent_t start,
+                         hipEvent_t stop) {
+    if (dtype == kBF16) return vec ? launch_t<kBF16, true>(p, s, start, stop) : launch_t<kBF16, false>(p, s, start, stop);
+    return vec ? launch_t<kFP32, true>(p, s, start, stop) : launch_t<kFP32, false>(p, s, start, stop);
+}
+
+}  // namespace specdec

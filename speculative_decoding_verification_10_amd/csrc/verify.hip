@@ -101,6 +101,32 @@ __device__ __forceinline__ void final_masses(const u32x4& rp, const u32x4& rq, c
     }
 }
 
+// Processed rows: every logit below the row's floor reads as -inf (the
+// top-k / top-p cut; the floor is -inf for an unprocessed row).
+template <int DT>
+__device__ __forceinline__ void apply_floor(u32x4& r, float fl) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if constexpr (DT == kFP32) {
+            r[k] = (__uint_as_float(r[k]) >= fl) ? r[k] : 0xFF800000u;
+        } else {
+            const uint32_t lo = (__uint_as_float(r[k] << 16) >= fl) ? (r[k] & 0x0000FFFFu) : 0x0000FF80u;
+            const uint32_t hi = (__uint_as_float(r[k] & 0xFFFF0000u) >= fl) ? (r[k] & 0xFFFF0000u) : 0xFF800000u;
+            r[k] = hi | lo;
+        }
+    }
+}
+
+// Floors of the final row pair of request b (FL: processed rows).
+template <bool FL>
+__device__ __forceinline__ void final_floors(const VerifyParams& a, int b, const Decision& d, float& fp, float& fq) {
+    fp = fq = -INFINITY;
+    if constexpr (FL) {
+        fp = a.floors[(size_t)b * a.R + d.j];
+        if (d.mode == kResidual) fq = a.floors[(size_t)b * a.R + a.K + 1 + d.j];
+    }
+}
+
 // (m1, z1) <- merge of two partials (max, sum relative to offset_of(max)).
 __device__ __forceinline__ void merge2(float& m1, double& z1, float m2, double z2, const Scale& sc) {
     if (m2 == -INFINITY) return;
@@ -320,13 +346,13 @@ __device__ void publish_aprob(const VerifyParams& a, int b, int kb, const StepSh
 
 constexpr int kSearchLanes = 64;
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool FL>
 __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d);
 
 // ---------------------------------------------------------------------------
 // Final item: tile `tile` of the final row (pair) of request b.
 // ---------------------------------------------------------------------------
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool FL>
 __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided, StepShared& sh) {
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
@@ -342,13 +368,22 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
         rp[u] = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
         rq[u] = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : neg_inf_raw<DT>();
     }
+    if constexpr (FL) {
+        float fp, fq;
+        final_floors<FL>(a, b, d, fp, fq);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            apply_floor<DT>(rp[u], fp);
+            apply_floor<DT>(rq[u], fq);
+        }
+    }
     put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile,
                   min(kSlabsPerTile, a.NS - tile * kSlabsPerTile), sh);
     if (tile == 0 && !decided) publish_aprob(a, b, kb, sh);
     // The request's last tile -- dispatched after its other tiles, which
     // never wait -- searches, with its first wave, once every slab sum of
     // the request is in.
-    if (tile == a.C - 1 && threadIdx.x < kSearchLanes) search_wave<DT, VEC>(a, b, kb, d);
+    if (tile == a.C - 1 && threadIdx.x < kSearchLanes) search_wave<DT, VEC, FL>(a, b, kb, d);
 }
 
 
@@ -371,12 +406,13 @@ constexpr int kHeld = 16;   // slab sums per lane kept in registers
 // Unnormalised mass of slab g of the final row, summed by one lane alone
 // (the fallback draw from p_j when every replacement mass is zero).
 template <int DT, bool VEC>
-__device__ double lane_slab_mass(const VerifyParams& a, const void* rowp, const Decision& d, int g) {
+__device__ double lane_slab_mass(const VerifyParams& a, const void* rowp, const Decision& d, int g, float fp) {
     constexpr int E = Elem<DT>::E;
     double t = 0.0;
     for (int k = 0; k < kSlab; ++k) {
         const int v = g * kSlab + k;
-        const u32x4 bp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
+        u32x4 bp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
+        apply_floor<DT>(bp, fp);
         float r[E];
         final_masses<DT>(bp, bp, d, v, a.sc, r);
         t += (double)pairwise_sum<E>(r);
@@ -384,7 +420,7 @@ __device__ double lane_slab_mass(const VerifyParams& a, const void* rowp, const 
     return t;
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool FL>
 __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     constexpr int E = Elem<DT>::E;
     constexpr int S = Elem<DT>::S;
@@ -411,6 +447,8 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
     const double u = (double)a.unif[(size_t)b * (K + 1) + kb];
+    float fp, fq;
+    final_floors<FL>(a, b, d, fp, fq);
 
     double incl = wave_inclusive_scan(mine);
     double total = __shfl(incl, 63, 64);
@@ -424,12 +462,12 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
 #pragma unroll
         for (int k = 0; k < kHeld; ++k) {
             held[k] = 0.0;
-            if (k < P && g0 + k < NS) held[k] = lane_slab_mass<DT, VEC>(a, rowp, d, g0 + k);
+            if (k < P && g0 + k < NS) held[k] = lane_slab_mass<DT, VEC>(a, rowp, d, g0 + k, fp);
             mine += held[k];
         }
         for (int k = kHeld; k < P; ++k)
             if (g0 + k < NS) {
-                const double t = lane_slab_mass<DT, VEC>(a, rowp, d, g0 + k);
+                const double t = lane_slab_mass<DT, VEC>(a, rowp, d, g0 + k, fp);
                 slot_put(slabs + g0 + k, enc_f64(t));
                 mine += t;
             }
@@ -479,8 +517,12 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     const int v = g * kSlab + lane;
     float r[E];
     {
-        const u32x4 sp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
-        const u32x4 sq = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : sp;
+        u32x4 sp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
+        u32x4 sq = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : sp;
+        if constexpr (FL) {
+            apply_floor<DT>(sp, fp);
+            apply_floor<DT>(sq, rowq ? fq : fp);
+        }
         final_masses<DT>(sp, sq, d, v, a.sc, r);
     }
     const double vs = (double)pairwise_sum<E>(r);
@@ -534,11 +576,12 @@ __global__ __launch_bounds__(kThreads) void verify_decide(VerifyParams a) {
     publish_aprob(a, b, kb, sh);
 }
 
-// Final items: workgroup (x, y) takes tile x of request y.
-template <int DT, bool VEC, bool DECIDED>
+// Final items: workgroup (x, y) takes tile x of request y.  FL: the rows are
+// processed (top-k / top-p floors).
+template <int DT, bool VEC, bool DECIDED, bool FL>
 __global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
     __shared__ StepShared sh;
-    final_item<DT, VEC>(a, blockIdx.y, blockIdx.x, DECIDED, sh);
+    final_item<DT, VEC, FL>(a, blockIdx.y, blockIdx.x, DECIDED, sh);
 }
 
 template <int DT, bool VEC>
@@ -555,10 +598,33 @@ hipError_t launch(const VerifyParams& p, hipStream_t s, hipEvent_t const* events
     // that repeats much work: C tiles each merging R * C row-tile partials.
     if ((int64_t)p.C * p.R * p.C > kDecideOnceAbove) {
         hipLaunchKernelGGL(verify_decide, dim3(p.B), dim3(kThreads), 0, s, p);
-        hipExtLaunchKernelGGL((verify_final<DT, VEC, true>), dim3(p.C, p.B), dim3(kThreads), 0, s,
+        hipExtLaunchKernelGGL((verify_final<DT, VEC, true, false>), dim3(p.C, p.B), dim3(kThreads), 0, s,
                               nullptr, ev[2], 0, p);
     } else {
-        hipExtLaunchKernelGGL((verify_final<DT, VEC, false>), dim3(p.C, p.B), dim3(kThreads), 0, s,
+        hipExtLaunchKernelGGL((verify_final<DT, VEC, false, false>), dim3(p.C, p.B), dim3(kThreads), 0, s,
+                              nullptr, ev[2], 0, p);
+    }
+    return hipGetLastError();
+}
+
+// The processed step: the floor kernel takes the row kernel's place (it
+// writes the same slots for the processed rows), then the same decision and
+// final kernels read the rows through their floors.
+template <int DT, bool VEC>
+hipError_t launch_processed(const FloorParams& f, const VerifyParams& p, hipStream_t s,
+                            hipEvent_t const* events) {
+    if (p.B == 0) return hipSuccess;
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    if (events)
+        for (int k = 0; k < 3; ++k) ev[k] = events[k];
+    hipError_t e = launch_floors(f, DT, VEC, s, ev[0], ev[1]);
+    if (e != hipSuccess) return e;
+    if ((int64_t)p.C * p.R * p.C > kDecideOnceAbove) {
+        hipLaunchKernelGGL(verify_decide, dim3(p.B), dim3(kThreads), 0, s, p);
+        hipExtLaunchKernelGGL((verify_final<DT, VEC, true, true>), dim3(p.C, p.B), dim3(kThreads), 0, s,
+                              nullptr, ev[2], 0, p);
+    } else {
+        hipExtLaunchKernelGGL((verify_final<DT, VEC, false, true>), dim3(p.C, p.B), dim3(kThreads), 0, s,
                               nullptr, ev[2], 0, p);
     }
     return hipGetLastError();
@@ -570,6 +636,14 @@ hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t
                          hipEvent_t const* events) {
     if (dtype == kBF16) return vec ? launch<kBF16, true>(p, s, events) : launch<kBF16, false>(p, s, events);
     return vec ? launch<kFP32, true>(p, s, events) : launch<kFP32, false>(p, s, events);
+}
+
+hipError_t launch_verify_processed(const FloorParams& f, const VerifyParams& p, int dtype, bool vec,
+                                   hipStream_t s, hipEvent_t const* events) {
+    if (!p.floors) return hipErrorInvalidValue;
+    if (dtype == kBF16)
+        return vec ? launch_processed<kBF16, true>(f, p, s, events) : launch_processed<kBF16, false>(f, p, s, events);
+    return vec ? launch_processed<kFP32, true>(f, p, s, events) : launch_processed<kFP32, false>(f, p, s, events);
 }
 
 }  // namespace specdec
