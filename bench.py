@@ -96,7 +96,7 @@ def read_counters(workload, key):
         return None
 
 
-def cpu_baseline(wl, name: str, budget_s: float, ngram=None, parents=None):
+def cpu_baseline(wl, name: str, budget_s: float, ngram=None, parents=None, processing=None):
     """The fp64 oracle as it stands, on the host cores, over a bounded
     number of steps of the same workload (for the n-gram workload: the
     oracle drafter, then the oracle greedy verify; for the tree workload
@@ -119,6 +119,10 @@ def cpu_baseline(wl, name: str, budget_s: float, ngram=None, parents=None):
             pos += wl.verified_positions()
         elif wl.greedy:
             oracle.verify_greedy(wl.target, wl.draft_tokens, wl.k_per_req)
+            pos += wl.verified_positions()
+        elif processing is not None:
+            oracle.verify_processed(wl.target, wl.draft, wl.draft_tokens, wl.uniforms, wl.temperature,
+                                    processing[0], processing[1], wl.k_per_req)
             pos += wl.verified_positions()
         else:
             oracle.verify(wl.target, wl.draft, wl.draft_tokens, wl.uniforms, wl.temperature,
@@ -143,6 +147,10 @@ def main():
                     help="headline (default), tiny, peaked, greedy, ragged, ngram (the n-gram "
                          "drafter over copy-heavy contexts, then the greedy verify of its drafts), "
                          "or tree (greedy verification of 21-node draft trees)")
+    ap.add_argument("--top-k", type=int, default=None,
+                    help="verify on top-k processed distributions (specdec_verify_processed)")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="verify on top-p processed distributions (specdec_verify_processed)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay each call from a captured HIP graph")
@@ -217,7 +225,24 @@ def main():
            torch.empty((wl.B,), dtype=torch.int32, device=dev), None)
     greedy = wl.greedy
     code = 1 if wl.dtype == "bf16" else 0
-    if tree:
+    processed = (args.top_k is not None or args.top_p is not None) and not greedy
+    top_k = int(args.top_k or 0)
+    top_p = float(1.0 if args.top_p is None else args.top_p)
+    if processed and wl.draft is not None:
+        # The drafts are drawn from the processed draft rows (the q that
+        # drew them), the rows cut at the library's own floors.
+        fl = sd.sampling_floors(base["draft"], wl.temperature, top_k, top_p).cpu().numpy()
+        dv = workloads.stored_as_f32(wl.draft)
+        rng = np.random.default_rng(2024)
+        for b in range(wl.B):
+            for i in range(wl.k_of(b)):
+                row = np.where(dv[b, i] >= fl[b, i], dv[b, i], np.float32(-np.inf))
+                wl.draft_tokens[b, i] = workloads.gumbel_draw(row[None], wl.temperature, rng)[0]
+        tokens.copy_(torch.from_numpy(wl.draft_tokens).to(dev))
+    if processed:
+        nbytes = int(sd._lib.load().specdec_verify_processed_workspace_bytes(wl.B, K, wl.V, code,
+                                                                             int(wl.draft is None)))
+    elif tree:
         nbytes = int(sd._lib.load().specdec_tree_verify_greedy_workspace_bytes(wl.B, K, wl.V, code))
     elif greedy:
         nbytes = int(sd._lib.load().specdec_verify_greedy_workspace_bytes(wl.B, K, wl.V, code))
@@ -248,6 +273,11 @@ def main():
             cargs.append((st["target"].data_ptr(), code, tokens.data_ptr(), ptr(kpr), wl.B, K, wl.V,
                           out[0].data_ptr(), out[1].data_ptr(), None, ws.ptr(), ws.nbytes,
                           stream.cuda_stream))
+        elif processed:
+            cargs.append((st["target"].data_ptr(), ptr(st["draft"]), code, tokens.data_ptr(), ptr(kpr),
+                          unif.data_ptr(), float(wl.temperature), top_k, top_p, wl.B, K, wl.V,
+                          out[0].data_ptr(), out[1].data_ptr(), None, ws.ptr(), ws.nbytes,
+                          stream.cuda_stream))
         else:
             cargs.append((st["target"].data_ptr(), ptr(st["draft"]), code, tokens.data_ptr(), ptr(kpr),
                           unif.data_ptr(), float(wl.temperature), wl.B, K, wl.V, out[0].data_ptr(),
@@ -268,6 +298,8 @@ def main():
             fn, fn_timed = lib.specdec_tree_verify_greedy, lib.specdec_tree_verify_greedy_timed
         elif greedy:
             fn, fn_timed = lib.specdec_verify_greedy, lib.specdec_verify_greedy_timed
+        elif processed:
+            fn, fn_timed = lib.specdec_verify_processed, lib.specdec_verify_processed_timed
         else:
             fn, fn_timed = lib.specdec_verify, lib.specdec_verify_timed
         rc = fn_timed(*a, handles[r]) if handles is not None else fn(*a)
@@ -287,7 +319,8 @@ def main():
             sd.verify_greedy(st["target"], tokens, k_per_req=kpr, workspace=ws, out=out)
         else:
             sd.verify(st["target"], st["draft"], tokens, unif, wl.temperature, k_per_req=kpr,
-                      workspace=ws, out=out)
+                      workspace=ws, out=out, top_k=args.top_k if processed else None,
+                      top_p=args.top_p if processed else None)
 
     checked_step(0)
     graphs = None
@@ -348,6 +381,8 @@ def main():
         per_launch_ms = float(np.median([s.elapsed_time(e) for s, e in zip(starts, ends)]))
 
     positions = wl.verified_positions()
+    # Stored counter figures belong to the unprocessed step's kernels.
+    counters_key = args.workload + ("-processed" if processed else "")
     alg = algorithmic_bytes(wl, nacc)
     if tree:
         alg += wl.B * K * 4                   # the parent links
@@ -382,27 +417,32 @@ def main():
         rows_gbps = rb / (rows_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(rows_gbps, 1), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(rows_gbps / PEAK_HBM_GBPS, 4),
-                    "traffic": read_counters(args.workload, "greedy_rows_hbm_bytes_per_launch" if greedy
+                    "traffic": read_counters(counters_key, "greedy_rows_hbm_bytes_per_launch" if greedy
                                              else "verify_rows_hbm_bytes_per_launch"),
-                    "kernel": "greedy_rows" if greedy else "verify_rows", "algorithmic_bytes": rb,
+                    "kernel": ("greedy_rows" if greedy else "floor_rows" if processed else "verify_rows"),
+                    "algorithmic_bytes": rb,
                     "launch_ms": round(rows_ms, 5)}
         call = {"achieved": round(alg / (call_ms * 1e-3) / 1e9, 1),
                 "frac": round(alg / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                "traffic": read_counters(args.workload, "hbm_bytes_per_launch"), "algorithmic_bytes": alg,
+                "traffic": read_counters(counters_key, "hbm_bytes_per_launch"), "algorithmic_bytes": alg,
                 "launch_ms": round(call_ms, 5),
                 "kernels": ("greedy_rows, tree_decisions" if tree else
-                            "greedy_rows, greedy_decisions" if greedy
+                            "greedy_rows, greedy_decisions" if greedy else
+                            "floor_rows, [verify_decide,] verify_final" if processed
                             else "verify_rows, [verify_decide,] verify_final")}
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                    "traffic": read_counters(args.workload, "greedy_rows_hbm_bytes_per_launch" if greedy
+                    "traffic": read_counters(counters_key, "greedy_rows_hbm_bytes_per_launch" if greedy
                                              else "hbm_bytes_per_launch"),
                     "kernel": ("greedy_rows" if greedy else
                                "specdec_verify call (verify_rows, [verify_decide,] verify_final)"),
                     "algorithmic_bytes": alg, "launch_ms": round(per_launch_ms, 5)}
         call = None
-    if tree:
+    if processed:
+        metric = ("verified positions/s + HBM GB/s (%% of peak), %s B=%d k=%d V=%d %s, top-k %d, top-p %g"
+                  % (args.workload, wl.B, K, wl.V, wl.dtype, top_k, top_p))
+    elif tree:
         metric = ("verified positions/s (tree nodes + 1 per request) + HBM GB/s (%% of peak), "
                   "tree B=%d nodes=%d V=%d %s" % (wl.B, K, wl.V, wl.dtype))
     else:
@@ -426,9 +466,11 @@ def main():
         "config": {"workload": ("tree verify B=%d nodes=%d (branching %s) V=%d %s"
                                 % (wl.B, K, ",".join(map(str, wl.meta["branching"])), wl.V, wl.dtype)
                                 if tree else
-                                "%s verify B=%d k=%d V=%d %s T=%g" % (args.workload, wl.B, K, wl.V,
-                                                                      wl.dtype, wl.temperature)),
+                                "%s verify B=%d k=%d V=%d %s T=%g%s" % (
+                                    args.workload, wl.B, K, wl.V, wl.dtype, wl.temperature,
+                                    ", top-k %d, top-p %g" % (top_k, top_p) if processed else "")),
                    "B": wl.B, "k": K, "V": wl.V, "temperature": wl.temperature,
+                   "top_k": top_k if processed else None, "top_p": top_p if processed else None,
                    "graph_replay": bool(args.graph)},
         "hbm_gbps": round(gbps, 1),
         "hbm_pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
@@ -461,7 +503,8 @@ def main():
         torch.cuda.synchronize()
         line["calibration_copy_bytes"] = n
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl, args.workload, args.cpu_budget, ngram_host, parents_h)
+        line["cpu_baseline"] = cpu_baseline(wl, args.workload, args.cpu_budget, ngram_host, parents_h,
+                                            (top_k, top_p) if processed else None)
     print(json.dumps(line), flush=True)
 
 

@@ -105,15 +105,26 @@ __device__ __forceinline__ T wg_reduce(T v, T* lds, Op op) {
 // f(x) for every element of the row this thread visits (vectors t, t + 1024,
 // ...; elements past V skipped).  The first pass over a row reads HBM; the
 // later ones mostly hit the L2 / Infinity Cache.
+// Four vectors per thread are loaded before any is used, so each thread
+// keeps four 16-byte loads in flight.
+constexpr int kRowBatch = 4;
+
 template <int DT, bool VEC, typename F>
 __device__ __forceinline__ void for_row(const RowRef& r, F&& f) {
     constexpr int E = Elem<DT>::E;
-    for (int v = threadIdx.x; v < r.NV; v += kFT) {
-        float x[E];
-        decode<DT>(load_raw<DT, VEC, false>(r.row, r.V, r.NV, v), x);
+    for (int v0 = threadIdx.x; v0 < r.NV; v0 += kRowBatch * kFT) {
+        u32x4 raw[kRowBatch];
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (v * E + e < r.V) f(x[e]);
+        for (int u = 0; u < kRowBatch; ++u) raw[u] = load_raw<DT, VEC, false>(r.row, r.V, r.NV, v0 + u * kFT);
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+            const int v = v0 + u * kFT;
+            float x[E];
+            decode<DT>(raw[u], x);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (v * E + e < r.V) f(x[e]);
+        }
     }
 }
 
@@ -198,22 +209,11 @@ __device__ __noinline__ uint32_t radix_select(const RowRef& r, bool from_cand, u
     return prefix;
 }
 
+// The floor of one row by coarse levels, LDS candidates and radix select
+// (every dtype).  Returns the row max, the floor and the kept mass.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
-    constexpr int S = Elem<DT>::S;
-    __shared__ FloorShared sh;
-    const int R = a.R, K = a.K;
-    const int b = blockIdx.x / R, rr = blockIdx.x - b * R;
-    const int kb = a.kpr ? min(max(a.kpr[b], 0), K) : K;
-    const bool draft = rr > K;
-    const int i = draft ? rr - K - 1 : rr;
-    if (draft ? i >= kb : i > kb) return;
-    const size_t row_index = draft ? (size_t)b * K + i : (size_t)b * (K + 1) + i;
-    RowRef r;
-    r.row = static_cast<const char*>(draft ? a.draft : a.target) + row_index * (size_t)a.V * S;
-    r.V = a.V;
-    r.NV = a.NV;
-    r.sc = a.sc;
+__device__ __noinline__ void floor_by_select(const FloorParams& a, RowRef& r, FloorShared& sh, float& m_out, float& fl_out,
+                                double& z_out) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const bool use_k = a.top_k > 0 && a.top_k < a.V;
     const bool use_p = a.top_p < 1.0;
@@ -344,23 +344,246 @@ __global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
         }
     }
 
-    // Outputs: the floor; for the verify step its slots.
+    m_out = m;
+    fl_out = fl;
+    z_out = z;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 rows: one pass builds the row's full histogram of 16-bit keys (every
+// bf16 value is one bin; two 16-bit counters per LDS word, 128 KB), from
+// which the max, the top-k cut, the survivors' mass and the top-p cut follow
+// exactly: a bin's mass is its count times the mass of its one value.  A
+// counter that overflows (one value more than 65,535 times in a row) shows
+// as a wrong total, and the row is then done by floor_by_select.
+// ---------------------------------------------------------------------------
+constexpr int kKeys16 = 65536;
+constexpr int kHistWords = kKeys16 / 2;
+constexpr int kWordsPerThread = kHistWords / kFT;   // 32: keys [64 t, 64 t + 64)
+
+__device__ __forceinline__ uint32_t key16_of(uint32_t h) {   // h: bf16 bits
+    if (h == 0x8000u) h = 0;                                   // -0 -> +0
+    return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+}
+__device__ __forceinline__ float value16_of(uint32_t k) {
+    const uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+    return __uint_as_float(h << 16);
+}
+
+struct HistShared {
+    uint32_t h[kHistWords];
+    uint64_t red_u[kFW];
+    uint32_t red_c[kFW];
+    uint32_t pick;
+};
+
+// Sum over the threads above t (t' > t), for every t.
+template <typename T>
+__device__ __forceinline__ T sum_above(T v, T* lds) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    T s = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const T n = __shfl_down(s, o, 64);
+        if (lane + o < 64) s += n;
+    }
+    if (lane == 0) lds[w] = s;
+    __syncthreads();
+    T above = s - v;
+    for (int q = w + 1; q < kFW; ++q) above += lds[q];
+    __syncthreads();
+    return above;
+}
+
+template <bool VEC>
+__device__ __forceinline__ bool floor_by_histogram(const FloorParams& a, const RowRef& r0, HistShared& hs, float& m_out,
+                                   float& fl_out, double& z_out) {
+    const int t = threadIdx.x;
+    const bool use_k = a.top_k > 0 && a.top_k < a.V;
+    const bool use_p = a.top_p < 1.0;
+    for (int q = t; q < kHistWords; q += kFT) hs.h[q] = 0;
+    __syncthreads();
+    // One pass: every element adds 1 to its key's counter.  All of a
+    // thread's vectors of a 131,072-logit row are loaded before any is used.
+    constexpr int kHold = 16;
+    for (int v0 = t; v0 < r0.NV; v0 += kHold * kFT) {
+        u32x4 raw[kHold];
+#pragma unroll
+        for (int u = 0; u < kHold; ++u) raw[u] = load_raw<kBF16, VEC, true>(r0.row, r0.V, r0.NV, v0 + u * kFT);
+#pragma unroll
+        for (int u = 0; u < kHold; ++u) {
+            const int v = v0 + u * kFT;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    if (v * 8 + 2 * q + half < r0.V) {
+                        const uint32_t k = key16_of(half ? (raw[u][q] >> 16) : (raw[u][q] & 0xFFFFu));
+                        atomicAdd(&hs.h[k >> 1], (k & 1u) ? 0x10000u : 1u);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // This thread's 64 bins, ascending keys 64 t .. 64 t + 63 (read from LDS
+    // each time they are needed).
+    const uint32_t* wd = hs.h + t * kWordsPerThread;
+    auto count_of = [&](int j) { return (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xFFFFu); };
+    uint32_t ct = 0;
+    int top = -1;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+        const uint32_t c = count_of(j);
+        ct += c;
+        if (c) top = j;
+    }
+    const uint32_t total = wg_reduce(ct, hs.red_c, [](uint32_t p, uint32_t q) { return p + q; });
+    if (total != (uint32_t)r0.V) return false;          // a counter overflowed
+    const uint32_t kmax = (uint32_t)wg_reduce(top < 0 ? 0 : 64 * t + top + 1, reinterpret_cast<int*>(hs.red_c),
+                                              [](int p, int q) { return max(p, q); }) - 1;
+    const float m = value16_of(kmax);
+    const float M = offset_of(m, r0.sc);
+    // Fixed-point mass of this thread's bins j0 .. 63 (keys >= 64 t + j0);
+    // threads without counts skip the work.
+    auto mass_from = [&](int j0) -> uint64_t {
+        uint64_t s_ = 0;
+        if (ct == 0) return s_;
+        for (int j = j0; j < 64; ++j) {
+            const uint32_t c = count_of(j);
+            if (c) s_ += (uint64_t)c * fix_of(fast_exp2(exponent2(value16_of(64 * t + j), M, r0.sc)));
+        }
+        return s_;
+    };
+    const uint64_t wt = mass_from(0);
+    // This thread's mass at keys >= key: all of it, none, or (for the one
+    // thread whose bins hold `key`) a partial sum.
+    auto mass_at_least = [&](uint32_t key) -> uint64_t {
+        const uint32_t lo = 64u * t;
+        if (key <= lo) return wt;
+        if (key > lo + 63) return 0;
+        return mass_from((int)(key - lo));
+    };
+    // top-k: the key at which the count from the top reaches top_k.
+    uint32_t kkey = 0;
+    if (use_k) {
+        const uint32_t above = sum_above(ct, hs.red_c);
+        const uint32_t k = (uint32_t)a.top_k;
+        if (above < k && k <= above + ct) {
+            uint32_t cum = above;
+            for (int j = 63; j >= 0; --j) {
+                cum += count_of(j);
+                if (cum >= k) { hs.pick = 64 * t + j; break; }
+            }
+        }
+        __syncthreads();
+        kkey = hs.pick;
+        __syncthreads();
+    }
+    // top-p over the survivors (keys >= kkey): the key at which their mass
+    // from the top reaches top_p of the total.
+    const uint64_t st = mass_at_least(kkey);
+    uint32_t fkey = kkey;
+    if (use_p) {
+        const uint64_t zk = wg_reduce(st, hs.red_u, [](uint64_t p, uint64_t q) { return p + q; });
+        const double target = a.top_p * (double)zk;
+        const uint64_t above = sum_above(st, hs.red_u);
+        if ((double)above < target && target <= (double)(above + st)) {
+            uint64_t cum = above;
+            for (int j = 63; j >= 0; --j) {
+                if ((uint32_t)(64 * t + j) < kkey) break;
+                const uint32_t c = count_of(j);
+                if (!c) continue;
+                cum += (uint64_t)c * fix_of(fast_exp2(exponent2(value16_of(64 * t + j), M, r0.sc)));
+                if ((double)cum >= target) { hs.pick = 64 * t + j; break; }
+            }
+        }
+        __syncthreads();
+        fkey = hs.pick;
+        __syncthreads();
+    }
+    const bool cut = use_k || use_p;
+    fl_out = cut ? value16_of(fkey) : -INFINITY;
+    uint64_t kept = cut ? mass_at_least(fkey) : wt;
+    kept = wg_reduce(kept, hs.red_u, [](uint64_t p, uint64_t q) { return p + q; });
+    m_out = m;
+    z_out = (double)kept / kFix;
+    return true;
+}
+
+// Row slot of this workgroup, and the outputs.
+struct RowSlot {
+    int b, rr, i, kb;
+    bool skip;
+    const void* row;
+};
+
+template <int DT>
+__device__ __forceinline__ RowSlot row_slot(const FloorParams& a) {
+    constexpr int S = Elem<DT>::S;
+    RowSlot s;
+    const int R = a.R, K = a.K;
+    s.b = blockIdx.x / R;
+    s.rr = blockIdx.x - s.b * R;
+    s.kb = a.kpr ? min(max(a.kpr[s.b], 0), K) : K;
+    const bool draft = s.rr > K;
+    s.i = draft ? s.rr - K - 1 : s.rr;
+    s.skip = draft ? s.i >= s.kb : s.i > s.kb;
+    const size_t row_index = draft ? (size_t)s.b * K + s.i : (size_t)s.b * (K + 1) + s.i;
+    s.row = static_cast<const char*>(draft ? a.draft : a.target) + row_index * (size_t)a.V * S;
+    return s;
+}
+
+// The floor; for the verify step the processed row's slots: tile 0 holds
+// the row max and the kept mass, the other tiles are empty; the logit at
+// the draft token (-inf when cut); row 0 empties the request's slab slots.
+template <int DT>
+__device__ void write_outputs(const FloorParams& a, const RowSlot& s, float m, float fl, double z) {
+    const int t = threadIdx.x;
     if (t == 0) a.floors[blockIdx.x] = fl;
     if (!a.slot_m) return;
-    const size_t rs = (size_t)b * R + rr;
+    const size_t rs = (size_t)s.b * a.R + s.rr;
     const int C = a.C;
     for (int c = t; c < C; c += kFT) {
         slot_put(a.slot_m + rs * C + c, enc_f32(c == 0 ? m : -INFINITY));
         slot_put(a.slot_s + rs * C + c, enc_f64(c == 0 ? z : 0.0));
     }
-    if (t == 0 && i < kb && a.tokens) {
-        const int x = min(max(a.tokens[(size_t)b * K + i], 0), a.V - 1);
-        const float l = load_one<DT>(r.row, x);
+    if (t == 0 && s.i < s.kb && a.tokens) {
+        const int x = min(max(a.tokens[(size_t)s.b * a.K + s.i], 0), a.V - 1);
+        const float l = load_one<DT>(s.row, x);
         slot_put(a.slot_l + rs, enc_f32(l >= fl ? l : -INFINITY));
     }
-    if (rr == 0)
+    if (s.rr == 0)
         for (int c = t; c < C * kSlabsPerTile; c += kFT)
-            slot_put(a.slot_slab + (size_t)b * C * kSlabsPerTile + c, (uint64_t)0);
+            slot_put(a.slot_slab + (size_t)s.b * C * kSlabsPerTile + c, (uint64_t)0);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
+    const RowSlot s = row_slot<DT>(a);
+    if (s.skip) return;
+    RowRef r;
+    r.row = s.row;
+    r.V = a.V;
+    r.NV = a.NV;
+    r.sc = a.sc;
+    float m, fl;
+    double z;
+    if constexpr (DT == kBF16) {
+        // One LDS pool: the histogram, or the selection's arrays when a
+        // histogram counter overflows.
+        __shared__ __align__(16) unsigned char pool[sizeof(HistShared) > sizeof(FloorShared)
+                                                        ? sizeof(HistShared) : sizeof(FloorShared)];
+        HistShared& hs = *reinterpret_cast<HistShared*>(pool);
+        if (!floor_by_histogram<VEC>(a, r, hs, m, fl, z)) {
+            __syncthreads();
+            floor_by_select<DT, VEC>(a, r, *reinterpret_cast<FloorShared*>(pool), m, fl, z);
+        }
+    } else {
+        __shared__ FloorShared sh;
+        floor_by_select<DT, VEC>(a, r, sh, m, fl, z);
+    }
+    write_outputs<DT>(a, s, m, fl, z);
 }
 
 template <int DT, bool VEC>

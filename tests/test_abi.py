@@ -249,3 +249,62 @@ def test_tree_mask_rejects(lib):
     assert lib.specdec_tree_mask(f, None, 4, 6, f, None, None) == EINVAL
     assert lib.specdec_tree_mask(None, None, 0, 6, None, None, None) == OK
     assert lib.specdec_tree_mask(None, None, 4, 0, None, None, None) == OK
+
+
+def call_processed(lib, timed=False, **kw):
+    a = dict(target=FAKE, draft=FAKE, dtype=1, tokens=FAKE, kpr=None, unif=FAKE, T=1.0, top_k=50,
+             top_p=0.9, B=4, K=3, V=1000, out=FAKE, nacc=FAKE, ap=None, ws=FAKE, wsb=1 << 20,
+             stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("target", "draft", "dtype", "tokens", "kpr", "unif", "T", "top_k", "top_p",
+                           "B", "K", "V", "out", "nacc", "ap", "ws", "wsb", "stream")]
+    if timed:
+        return lib.specdec_verify_processed_timed(*args, None)
+    return lib.specdec_verify_processed(*args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), EDTYPE),
+    (dict(B=-1), EINVAL),
+    (dict(K=256), EINVAL),
+    (dict(V=0), EINVAL),
+    (dict(T=0.0), EINVAL),
+    (dict(T=float("nan")), EINVAL),
+    (dict(top_p=0.0), EINVAL),
+    (dict(top_p=-0.5), EINVAL),
+    (dict(top_p=float("nan")), EINVAL),
+    (dict(target=None), EINVAL),
+    (dict(unif=None), EINVAL),
+    (dict(tokens=None), EINVAL),
+    (dict(out=None), EINVAL),
+    (dict(ws=None), EWORKSPACE),
+    (dict(wsb=64), EWORKSPACE),
+    (dict(B=65535, K=255, wsb=1 << 40), EINVAL),          # more rows than the floor grid takes
+    (dict(B=0, target=None, ws=None), OK),
+])
+def test_processed_rejects(lib, kw, status):
+    assert call_processed(lib, **kw) == status
+    assert call_processed(lib, timed=True, **kw) == status
+
+
+def test_processed_workspace_adds_floors(lib):
+    for B, K, V, dt, oh in ((64, 5, 128256, 1, 0), (8, 4, 32000, 1, 1), (1, 0, 7, 0, 0)):
+        n = lib.specdec_verify_processed_workspace_bytes(B, K, V, dt, oh)
+        base = lib.specdec_verify_workspace_bytes(B, K, V, dt, oh)
+        R = K + 1 + (0 if oh else K)
+        assert n % 256 == 0 and n >= base + B * R * 4
+    assert lib.specdec_verify_processed_workspace_bytes(4, 256, 10, 1, 0) == 0
+
+
+def test_sampling_floors_rejects(lib):
+    f = ctypes.c_void_p(0x1000)
+    # logits, dtype, rows, V, T, top_k, top_p, floors, stream
+    assert lib.specdec_sampling_floors(f, 4, 3, 10, 1.0, 2, 0.9, f, None) == EDTYPE
+    assert lib.specdec_sampling_floors(f, 1, -1, 10, 1.0, 2, 0.9, f, None) == EINVAL
+    assert lib.specdec_sampling_floors(f, 1, (1 << 22) + 1, 10, 1.0, 2, 0.9, f, None) == EINVAL
+    assert lib.specdec_sampling_floors(f, 1, 3, 0, 1.0, 2, 0.9, f, None) == EINVAL
+    assert lib.specdec_sampling_floors(f, 1, 3, 10, -1.0, 2, 0.9, f, None) == EINVAL
+    assert lib.specdec_sampling_floors(f, 1, 3, 10, 1.0, 2, 0.0, f, None) == EINVAL
+    assert lib.specdec_sampling_floors(None, 1, 3, 10, 1.0, 2, 0.9, f, None) == EINVAL
+    assert lib.specdec_sampling_floors(f, 1, 3, 10, 1.0, 2, 0.9, None, None) == EINVAL
+    assert lib.specdec_sampling_floors(None, 1, 0, 10, 1.0, 2, 0.9, None, None) == OK
