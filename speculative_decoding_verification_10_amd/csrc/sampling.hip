@@ -350,17 +350,10 @@ __device__ __noinline__ void floor_by_select(const FloorParams& a, RowRef& r, Fl
 }
 
 // ---------------------------------------------------------------------------
-// bf16 rows: one pass builds the row's full histogram of 16-bit keys (every
-// bf16 value is one bin; two 16-bit counters per LDS word, 128 KB), from
-// which the max, the top-k cut, the survivors' mass and the top-p cut follow
-// exactly: a bin's mass is its count times the mass of its one value.  A
-// counter that overflows (one value more than 65,535 times in a row) shows
-// as a wrong total, and the row is then done by floor_by_select.
+// bf16 rows.  Every bf16 value has a 16-bit order-preserving key; a bin per
+// key holds its value's count, and a bin's mass is its count times the mass
+// of its one value, so cuts found over bins are exact.
 // ---------------------------------------------------------------------------
-constexpr int kKeys16 = 65536;
-constexpr int kHistWords = kKeys16 / 2;
-constexpr int kWordsPerThread = kHistWords / kFT;   // 32: keys [64 t, 64 t + 64)
-
 __device__ __forceinline__ uint32_t key16_of(uint32_t h) {   // h: bf16 bits
     if (h == 0x8000u) h = 0;                                   // -0 -> +0
     return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
@@ -369,13 +362,6 @@ __device__ __forceinline__ float value16_of(uint32_t k) {
     const uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
     return __uint_as_float(h << 16);
 }
-
-struct HistShared {
-    uint32_t h[kHistWords];
-    uint64_t red_u[kFW];
-    uint32_t red_c[kFW];
-    uint32_t pick;
-};
 
 // Sum over the threads above t (t' > t), for every t.
 template <typename T>
@@ -395,120 +381,205 @@ __device__ __forceinline__ T sum_above(T v, T* lds) {
     return above;
 }
 
+// bf16 rows (16-byte aligned, whole vectors): the thread's first 12 vectors
+// stay in registers, the rest (of a 128K-logit row, about a quarter) is
+// re-read by each pass from the L2 / Infinity Cache.  The row max comes first; then windows of
+// 4,096 consecutive keys, from the max's key down, get one LDS bin per key
+// (4 per thread).  The first window also sums the mass of everything below
+// it (per thread, fp32), which gives the row's total without bins.  The
+// top-k cut is the bin where the count from the top reaches top_k; the
+// top-p cut is the bin where the survivors' mass from the top reaches
+// top_p of theirs.  A cut below a window moves the search to the next one
+// down.  The first window spans 32 binades below the max, so a second
+// window is needed only for cuts among tokens of mass below ~2^-22 of the
+// max's.  No counter can overflow (32-bit counts).
+constexpr int kWin = 4096;
+constexpr int kWinPerThread = kWin / kFT;              // 4
+
+struct WinShared {
+    uint32_t win[kWin];
+    double red_d[kFW];
+    uint32_t red_c[kFW];
+    float red_f[kFW];
+    uint32_t pick;
+};
+
+// Workgroup-uniform values kept in scalar registers.
+__device__ __forceinline__ double uniform(double v) {
+    return __hiloint2double(__builtin_amdgcn_readfirstlane(__double2hiint(v)),
+                            __builtin_amdgcn_readfirstlane(__double2loint(v)));
+}
+__device__ __forceinline__ float uniform(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 template <bool VEC>
-__device__ __forceinline__ bool floor_by_histogram(const FloorParams& a, const RowRef& r0, HistShared& hs, float& m_out,
-                                   float& fl_out, double& z_out) {
+__device__ __forceinline__ void floor_by_window(const FloorParams& a, const RowRef& r0, WinShared& ws, float& m_out,
+                                                float& fl_out, double& z_out) {
     const int t = threadIdx.x;
     const bool use_k = a.top_k > 0 && a.top_k < a.V;
     const bool use_p = a.top_p < 1.0;
-    for (int q = t; q < kHistWords; q += kFT) hs.h[q] = 0;
-    __syncthreads();
-    // One pass: every element adds 1 to its key's counter.  All of a
-    // thread's vectors of a 131,072-logit row are loaded before any is used.
-    constexpr int kHold = 16;
-    for (int v0 = t; v0 < r0.NV; v0 += kHold * kFT) {
-        u32x4 raw[kHold];
+    constexpr int kHold = 12;   // vectors per thread held in registers (more spill)
+    u32x4 raw[kHold];
 #pragma unroll
-        for (int u = 0; u < kHold; ++u) raw[u] = load_raw<kBF16, VEC, true>(r0.row, r0.V, r0.NV, v0 + u * kFT);
+    for (int u = 0; u < kHold; ++u) raw[u] = load_raw<kBF16, VEC, true>(r0.row, r0.V, r0.NV, t + u * kFT);
+    // Every 32-bit word of this thread's vectors (two bf16 logits; rows on
+    // this path have whole vectors): registers, then the rest re-read.
+    auto each_word = [&](auto&& f) {
+#pragma unroll
+        for (int u = 0; u < kHold; ++u) asm volatile("" : "+v"(raw[u]));
 #pragma unroll
         for (int u = 0; u < kHold; ++u) {
-            const int v = v0 + u * kFT;
+            if (t + u * kFT >= r0.NV) continue;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 4; ++q) f(raw[u][q]);
+        }
+        for (int v = t + kHold * kFT; v < r0.NV; v += kFT) {
+            const u32x4 rv = load_raw<kBF16, VEC, false>(r0.row, r0.V, r0.NV, v);
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    if (v * 8 + 2 * q + half < r0.V) {
-                        const uint32_t k = key16_of(half ? (raw[u][q] >> 16) : (raw[u][q] & 0xFFFFu));
-                        atomicAdd(&hs.h[k >> 1], (k & 1u) ? 0x10000u : 1u);
-                    }
+            for (int q = 0; q < 4; ++q) f(rv[q]);
+        }
+    };
+    float m = -INFINITY;
+    each_word([&](uint32_t w) { m = fmaxf(m, fmaxf(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u))); });
+    m = uniform(wg_reduce(m, ws.red_f, [](float p, float q) { return fmaxf(p, q); }));
+    const float M = offset_of(m, r0.sc);
+    const uint32_t kmax = key16_of(__float_as_uint(m) >> 16);
+    auto sum_d = [&](double v) {
+        return uniform(wg_reduce(v, ws.red_d, [](double p, double q) { return p + q; }));
+    };
+
+    // Window [k0, khi): this thread's 4 bins (keys k0 + 4 t + j) as counts
+    // and masses; with `below`, also the mass of the keys under k0.
+    uint32_t c[kWinPerThread];
+    double mb[kWinPerThread];
+    uint32_t k0 = 0, khi = kmax + 1;
+    auto count_window = [&](bool below) -> double {
+        k0 = khi > (uint32_t)kWin ? khi - kWin : 0u;
+        __syncthreads();
+        for (int q = t; q < kWin; q += kFT) ws.win[q] = 0;
+        __syncthreads();
+        float bm = 0.0f;
+        const uint32_t span = khi - k0;
+        each_word([&](uint32_t w) {
+            // Both keys of the word at once: a half with its sign set is
+            // inverted, the other gets its top bit set; -0 joins +0.
+            const uint32_t neg = ((w >> 15) & 0x00010001u) * 0x7FFFu;
+            const uint32_t keys = w ^ (neg | 0x80008000u);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                uint32_t k = half ? (keys >> 16) : (keys & 0xFFFFu);
+                k = (k == 0x7FFFu) ? 0x8000u : k;
+                if (k - k0 < span) {
+                    atomicAdd(&ws.win[k - k0], 1u);
+                } else if (below && k < k0) {
+                    const float x = __uint_as_float(half ? (w & 0xFFFF0000u) : (w << 16));
+                    bm += fast_exp2(exponent2(x, M, r0.sc));
                 }
             }
-        }
-    }
-    __syncthreads();
-    // This thread's 64 bins, ascending keys 64 t .. 64 t + 63 (read from LDS
-    // each time they are needed).
-    const uint32_t* wd = hs.h + t * kWordsPerThread;
-    auto count_of = [&](int j) { return (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xFFFFu); };
-    uint32_t ct = 0;
-    int top = -1;
+        });
+        __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-        const uint32_t c = count_of(j);
-        ct += c;
-        if (c) top = j;
-    }
-    const uint32_t total = wg_reduce(ct, hs.red_c, [](uint32_t p, uint32_t q) { return p + q; });
-    if (total != (uint32_t)r0.V) return false;          // a counter overflowed
-    const uint32_t kmax = (uint32_t)wg_reduce(top < 0 ? 0 : 64 * t + top + 1, reinterpret_cast<int*>(hs.red_c),
-                                              [](int p, int q) { return max(p, q); }) - 1;
-    const float m = value16_of(kmax);
-    const float M = offset_of(m, r0.sc);
-    // Fixed-point mass of this thread's bins j0 .. 63 (keys >= 64 t + j0);
-    // threads without counts skip the work.
-    auto mass_from = [&](int j0) -> uint64_t {
-        uint64_t s_ = 0;
-        if (ct == 0) return s_;
-        for (int j = j0; j < 64; ++j) {
-            const uint32_t c = count_of(j);
-            if (c) s_ += (uint64_t)c * fix_of(fast_exp2(exponent2(value16_of(64 * t + j), M, r0.sc)));
+        for (int j = 0; j < kWinPerThread; ++j) {
+            c[j] = ws.win[kWinPerThread * t + j];
+            const uint32_t key = k0 + kWinPerThread * t + j;
+            mb[j] = c[j] ? (double)c[j] * (double)fast_exp2(exponent2(value16_of(key), M, r0.sc)) : 0.0;
         }
-        return s_;
+        return below ? sum_d((double)bm) : 0.0;
     };
-    const uint64_t wt = mass_from(0);
-    // This thread's mass at keys >= key: all of it, none, or (for the one
-    // thread whose bins hold `key`) a partial sum.
-    auto mass_at_least = [&](uint32_t key) -> uint64_t {
-        const uint32_t lo = 64u * t;
-        if (key <= lo) return wt;
-        if (key > lo + 63) return 0;
-        return mass_from((int)(key - lo));
-    };
-    // top-k: the key at which the count from the top reaches top_k.
-    uint32_t kkey = 0;
-    if (use_k) {
-        const uint32_t above = sum_above(ct, hs.red_c);
-        const uint32_t k = (uint32_t)a.top_k;
-        if (above < k && k <= above + ct) {
-            uint32_t cum = above;
-            for (int j = 63; j >= 0; --j) {
-                cum += count_of(j);
-                if (cum >= k) { hs.pick = 64 * t + j; break; }
+    // The crossing of a window: the bin where the weight from the top (with
+    // `above` from higher windows) first reaches `target`.
+    auto crossing = [&](auto&& wt, double above, double target) -> uint32_t {
+        double mine = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWinPerThread; ++j) mine += wt(j);
+        const double up = above + sum_above(mine, ws.red_d);
+        if (up < target && target <= up + mine) {
+            double cum = up;
+            for (int j = kWinPerThread - 1; j >= 0; --j) {
+                cum += wt(j);
+                if (cum >= target) { ws.pick = k0 + kWinPerThread * t + j; break; }
             }
         }
         __syncthreads();
-        kkey = hs.pick;
+        const uint32_t key = __builtin_amdgcn_readfirstlane(ws.pick);
         __syncthreads();
-    }
-    // top-p over the survivors (keys >= kkey): the key at which their mass
-    // from the top reaches top_p of the total.
-    const uint64_t st = mass_at_least(kkey);
-    uint32_t fkey = kkey;
-    if (use_p) {
-        const uint64_t zk = wg_reduce(st, hs.red_u, [](uint64_t p, uint64_t q) { return p + q; });
-        const double target = a.top_p * (double)zk;
-        const uint64_t above = sum_above(st, hs.red_u);
-        if ((double)above < target && target <= (double)(above + st)) {
-            uint64_t cum = above;
-            for (int j = 63; j >= 0; --j) {
-                if ((uint32_t)(64 * t + j) < kkey) break;
-                const uint32_t c = count_of(j);
-                if (!c) continue;
-                cum += (uint64_t)c * fix_of(fast_exp2(exponent2(value16_of(64 * t + j), M, r0.sc)));
-                if ((double)cum >= target) { hs.pick = 64 * t + j; break; }
-            }
+        return key;
+    };
+    const uint32_t lo_off = kWinPerThread * t;
+    // One loop, one window count per turn: first the top-k search (counts),
+    // then the top-p search (survivors' masses), each moving down a window
+    // while its cut lies lower.
+    int phase = use_k ? 0 : 1;
+    bool first = true;
+    uint32_t k0_top = 0, kkey = 0, fkey = 0;
+    double below0 = 0.0, above_c = 0.0, above_m = 0.0, zsur = 0.0, target = 0.0, above = 0.0, kept = 0.0;
+    for (;;) {
+        const double b = count_window(first && !use_k);
+        if (first) {
+            below0 = b;
+            k0_top = k0;
+            first = false;
         }
-        __syncthreads();
-        fkey = hs.pick;
-        __syncthreads();
+        double ct = 0.0, mt = 0.0, ms = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWinPerThread; ++j) {
+            ct += (double)c[j];
+            mt += mb[j];
+        }
+        if (phase == 0) {
+            const double cw = sum_d(ct), mw = sum_d(mt);
+            if (above_c + cw < (double)a.top_k) {             // the cut lies lower
+                above_c += cw;
+                above_m += mw;
+                khi = k0;
+                continue;
+            }
+            kkey = crossing([&](int j) { return (double)c[j]; }, above_c, (double)a.top_k);
+#pragma unroll
+            for (int j = 0; j < kWinPerThread; ++j)
+                if (k0 + lo_off + j >= kkey) ms += mb[j];
+            zsur = above_m + sum_d(ms);
+            fkey = kkey;
+            kept = zsur;
+            if (!use_p) break;
+            phase = 1;
+            target = a.top_p * zsur;
+            if (k0 != k0_top) {                                 // search top-p from the top again
+                khi = kmax + 1;
+                continue;
+            }
+        } else if (!use_k && k0 == k0_top && above == 0.0 && zsur == 0.0) {
+            // No top-k: the survivors are the whole row.
+            zsur = sum_d(mt) + below0;
+            fkey = 0;
+            kept = zsur;
+            if (!use_p) break;
+            target = a.top_p * zsur;
+        }
+        // phase 1: the survivors' mass in this window.
+        double mine = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWinPerThread; ++j)
+            if (k0 + lo_off + j >= kkey) mine += mb[j];
+        const double mw = sum_d(mine);
+        if (above + mw < target && k0 > kkey && k0 > 0) {
+            above += mw;
+            khi = k0;
+            continue;
+        }
+        fkey = crossing([&](int j) { return (k0 + lo_off + j >= kkey) ? mb[j] : 0.0; }, above, target);
+        double kp = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWinPerThread; ++j)
+            if (k0 + lo_off + j >= fkey) kp += mb[j];
+        kept = above + sum_d(kp);
+        break;
     }
     const bool cut = use_k || use_p;
     fl_out = cut ? value16_of(fkey) : -INFINITY;
-    uint64_t kept = cut ? mass_at_least(fkey) : wt;
-    kept = wg_reduce(kept, hs.red_u, [](uint64_t p, uint64_t q) { return p + q; });
     m_out = m;
-    z_out = (double)kept / kFix;
-    return true;
+    z_out = kept;
 }
 
 // Row slot of this workgroup, and the outputs.
@@ -570,14 +641,14 @@ __global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
     float m, fl;
     double z;
     if constexpr (DT == kBF16) {
-        // One LDS pool: the histogram, or the selection's arrays when a
-        // histogram counter overflows.
-        __shared__ __align__(16) unsigned char pool[sizeof(HistShared) > sizeof(FloorShared)
-                                                        ? sizeof(HistShared) : sizeof(FloorShared)];
-        HistShared& hs = *reinterpret_cast<HistShared*>(pool);
-        if (!floor_by_histogram<VEC>(a, r, hs, m, fl, z)) {
-            __syncthreads();
-            floor_by_select<DT, VEC>(a, r, *reinterpret_cast<FloorShared*>(pool), m, fl, z);
+        if constexpr (VEC) {
+            __shared__ WinShared ws;
+            floor_by_window<VEC>(a, r, ws, m, fl, z);
+        } else {
+            // Rows off 16-byte alignment (or of an odd length): the general
+            // selection.
+            __shared__ FloorShared sh;
+            floor_by_select<DT, VEC>(a, r, sh, m, fl, z);
         }
     } else {
         __shared__ FloorShared sh;
