@@ -582,6 +582,331 @@ __device__ __forceinline__ void floor_by_window(const FloorParams& a, const RowR
     z_out = kept;
 }
 
+// fp32 rows (16-byte aligned): key windows as for bf16, over coarse keys
+// (the top 16 bits of a logit's 32-bit key: one coarse bin spans 65,536
+// neighbouring fp32 values, 1/128 of a binade).  Each bin holds its count
+// and the exact fixed-point sum of its elements' masses, so every weight
+// below is an exact multiple of 2^-35 and the crossings are exact.  A window
+// count also finds the highest coarse key below the window, so the next
+// window starts there and empty key ranges (between the positive and
+// negative logits, say) cost nothing.
+// A cut found in a coarse bin is resolved to the exact 32-bit key by 8-bit
+// digit selection (counts or masses per digit), which also gives the mass at
+// or above the key: over the bin's elements gathered into LDS when they fit
+// (one pass over the row), else by two digit passes over the row.  When the
+// top-k survivors all fit in LDS, both cuts are resolved there after one
+// gather.  The thread's first 4 vectors stay in registers (more spill).
+struct Win32Shared {
+    uint32_t cnt[kWin];
+    uint64_t msum[kWin];
+    uint32_t ckey[kCand];
+    uint64_t cmass[kCand];
+    uint32_t hc[256];
+    uint64_t hm[256];
+    double red_d[kFW];
+    uint32_t red_c[kFW];
+    float red_f[kFW];
+    uint32_t ncand;
+    uint32_t pick;
+    double pick_above;
+    double pick_mass_above;
+};
+
+template <bool VEC>
+__device__ __forceinline__ void floor_by_window32(const FloorParams& a, const RowRef& r0, Win32Shared& ws,
+                                                  float& m_out, float& fl_out, double& z_out) {
+    const int t = threadIdx.x;
+    const bool use_k = a.top_k > 0 && a.top_k < a.V;
+    const bool use_p = a.top_p < 1.0;
+    constexpr int kHold = 4;
+    u32x4 raw[kHold];
+#pragma unroll
+    for (int u = 0; u < kHold; ++u) raw[u] = load_raw<kFP32, VEC, true>(r0.row, r0.V, r0.NV, t + u * kFT);
+    // Every logit of this thread's vectors (whole vectors on this path):
+    // registers, then the rest re-read.
+    auto each = [&](auto&& f) {
+#pragma unroll
+        for (int u = 0; u < kHold; ++u) asm volatile("" : "+v"(raw[u]));
+#pragma unroll
+        for (int u = 0; u < kHold; ++u) {
+            if (t + u * kFT >= r0.NV) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) f(__uint_as_float(raw[u][q]));
+        }
+        for (int v = t + kHold * kFT; v < r0.NV; v += kFT) {
+            const u32x4 rv = load_raw<kFP32, VEC, false>(r0.row, r0.V, r0.NV, v);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) f(__uint_as_float(rv[q]));
+        }
+    };
+    if (t == 0) {
+        ws.pick = 0;
+        ws.pick_above = 0.0;
+    }
+    float m = -INFINITY;
+    each([&](float x) { m = fmaxf(m, x); });
+    m = uniform(wg_reduce(m, ws.red_f, [](float p, float q) { return fmaxf(p, q); }));
+    const float M = offset_of(m, r0.sc);
+    const uint32_t kcmax = key_of(m) >> 16;
+    auto sum_d = [&](double v) {
+        return uniform(wg_reduce(v, ws.red_d, [](double p, double q) { return p + q; }));
+    };
+    auto mass = [&](float x) { return fix_of(fast_exp2(exponent2(x, M, r0.sc))); };
+
+    // Window [k0, khi): this thread's 4 coarse bins (k0 + 4 t + j) as counts
+    // and masses; `next` = 1 + the highest coarse key under k0 (0: none);
+    // with `below`, the returned value is the fp32 mass of the keys under k0.
+    uint32_t c[kWinPerThread];
+    double mb[kWinPerThread];
+    uint32_t k0 = 0, khi = kcmax + 1, next = 0;
+    auto count_window = [&](bool below) -> double {
+        k0 = khi > (uint32_t)kWin ? khi - kWin : 0u;
+        __syncthreads();
+        for (int q = t; q < kWin; q += kFT) {
+            ws.cnt[q] = 0;
+            ws.msum[q] = 0;
+        }
+        __syncthreads();
+        float bm = 0.0f;
+        uint32_t nb = 0;
+        const uint32_t span = khi - k0;
+        each([&](float x) {
+            const uint32_t kc = key_of(x) >> 16;
+            if (kc - k0 < span) {
+                atomicAdd(&ws.cnt[kc - k0], 1u);
+                atomicAdd(reinterpret_cast<unsigned long long*>(&ws.msum[kc - k0]), (unsigned long long)mass(x));
+            } else if (kc < k0) {
+                nb = max(nb, kc + 1);
+                if (below) bm += fast_exp2(exponent2(x, M, r0.sc));
+            }
+        });
+        next = __builtin_amdgcn_readfirstlane(wg_reduce(nb, ws.red_c, [](uint32_t p, uint32_t q) { return max(p, q); }));
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kWinPerThread; ++j) {
+            c[j] = ws.cnt[kWinPerThread * t + j];
+            mb[j] = (double)ws.msum[kWinPerThread * t + j] / kFix;
+        }
+        return below ? sum_d((double)bm) : 0.0;
+    };
+    // Count of coarse bin cb of the current window (LDS holds the counts
+    // until the next window); above kCand when cb lies outside the window.
+    auto bin_count = [&](uint32_t cb) -> uint32_t {
+        return cb - k0 < (uint32_t)kWin ? __builtin_amdgcn_readfirstlane(ws.cnt[cb - k0]) : kCand + 1u;
+    };
+    // The coarse bin where the weight from the top (with `above` from higher
+    // windows) first reaches `target`; `up` gets the weight above that bin.
+    auto crossing = [&](auto&& wt, double above, double target, double& up) -> uint32_t {
+        double mine = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWinPerThread; ++j) mine += wt(j);
+        const double u = above + sum_above(mine, ws.red_d);
+        if (u < target && target <= u + mine) {
+            double cum = u;
+            for (int j = kWinPerThread - 1; j >= 0; --j) {
+                const double w = wt(j);
+                if (cum + w >= target) {
+                    ws.pick = k0 + kWinPerThread * t + j;
+                    ws.pick_above = cum;
+                    break;
+                }
+                cum += w;
+            }
+        }
+        __syncthreads();
+        const uint32_t key = __builtin_amdgcn_readfirstlane(ws.pick);
+        up = uniform(ws.pick_above);
+        __syncthreads();
+        return key;
+    };
+    // Element sources of the digit selection: f(key, mass getter) for every
+    // logit of the row, or for every candidate in LDS.
+    auto row_src = [&](auto&& f) {
+        each([&](float x) { f(key_of(x), [&] { return mass(x); }); });
+    };
+    auto cand_src = [&](auto&& f) {
+        const uint32_t nc = min(__builtin_amdgcn_readfirstlane(ws.ncand), (uint32_t)kCand);
+        for (uint32_t i = t; i < nc; i += kFT) {
+            const uint64_t q = ws.cmass[i];
+            f(ws.ckey[i], [q] { return q; });
+        }
+    };
+    // The elements of coarse bins [glo, ghi] into LDS (any order).
+    auto gather = [&](uint32_t glo, uint32_t ghi) {
+        __syncthreads();
+        if (t == 0) ws.ncand = 0;
+        __syncthreads();
+        each([&](float x) {
+            const uint32_t k = key_of(x);
+            if ((k >> 16) - glo <= ghi - glo) {
+                const uint32_t i = atomicAdd(&ws.ncand, 1u);
+                if (i < (uint32_t)kCand) {
+                    ws.ckey[i] = k;
+                    ws.cmass[i] = mass(x);
+                }
+            }
+        });
+        __syncthreads();
+    };
+    // One 8-bit digit (at `shift`) of the keys >= kmin whose bits above the
+    // digit are `hi` (all keys at shift 24): the digit where the weight
+    // (masses, else counts) from the top reaches `target`; `up` gets the
+    // weight above that digit and `mup` the mass above it.  The digit
+    // histogram stays in LDS.
+    auto digit = [&](auto&& src, int shift, uint32_t hi, uint32_t kmin, bool masses, double target, double& up,
+                     double& mup) -> uint32_t {
+        __syncthreads();
+        if (t < 256) {
+            ws.hc[t] = 0;
+            ws.hm[t] = 0;
+        }
+        if (t == 0) {
+            ws.pick = 0;
+            ws.pick_above = 0.0;
+            ws.pick_mass_above = 0.0;
+        }
+        __syncthreads();
+        src([&](uint32_t k, auto&& mf) {
+            if ((shift == 24 || (k >> (shift + 8)) == hi) && k >= kmin) {
+                const uint32_t d = (k >> shift) & 255u;
+                atomicAdd(&ws.hc[d], 1u);
+                atomicAdd(reinterpret_cast<unsigned long long*>(&ws.hm[d]), (unsigned long long)mf());
+            }
+        });
+        __syncthreads();
+        const double hm = (t < 256) ? (double)ws.hm[t] / kFix : 0.0;
+        const double w = (t < 256) ? (masses ? hm : (double)ws.hc[t]) : 0.0;
+        const double u = sum_above(w, ws.red_d);
+        const double mu = sum_above(hm, ws.red_d);
+        if (t < 256 && u < target && target <= u + w) {
+            ws.pick = t;
+            ws.pick_above = u;
+            ws.pick_mass_above = mu;
+        }
+        __syncthreads();
+        const uint32_t d = __builtin_amdgcn_readfirstlane(ws.pick);
+        up = uniform(ws.pick_above);
+        mup = uniform(ws.pick_mass_above);
+        __syncthreads();
+        return d;
+    };
+    // The exact key (with the bits above `top_shift + 8` equal to `hi`)
+    // where the weight of the keys >= kmin from the top reaches `target`;
+    // `mass_ge` gets the mass of those keys at or above it.
+    auto select = [&](auto&& src, int top_shift, uint32_t hi, uint32_t kmin, bool masses, double target,
+                      double& mass_ge) -> uint32_t {
+        uint32_t key = hi;
+        double mu_sum = 0.0;
+        for (int sh = top_shift; sh >= 0; sh -= 8) {
+            double up, mup;
+            const uint32_t d = digit(src, sh, key, kmin, masses, target, up, mup);
+            key = (key << 8) | d;
+            target -= up;
+            mu_sum += mup;
+        }
+        mass_ge = mu_sum + uniform((double)ws.hm[key & 255u] / kFix);
+        return key;
+    };
+    // The cut inside coarse bin cb (n elements).
+    auto resolve = [&](uint32_t cb, uint32_t n, uint32_t kmin, bool masses, double target,
+                       double& mass_ge) -> uint32_t {
+        if (n <= (uint32_t)kCand) {
+            gather(cb, cb);
+            return select(cand_src, 8, cb, kmin, masses, target, mass_ge);
+        }
+        return select(row_src, 8, cb, kmin, masses, target, mass_ge);
+    };
+
+    const uint32_t lo_off = kWinPerThread * t;
+    // As for bf16: first the top-k search (counts), then the top-p search
+    // (survivors' masses), each moving down a window while its cut lies
+    // lower.  bk is the coarse bin of the top-k cut kkey; of it only the keys
+    // >= kkey survive (mass part_bk).
+    int phase = use_k ? 0 : 1;
+    bool first = true;
+    uint32_t k0_top = 0, kkey = 0, fkey = 0, bk = 0;
+    double below0 = 0.0, above_c = 0.0, above_m = 0.0, zsur = 0.0, target = 0.0, above = 0.0, kept = 0.0;
+    double part_bk = 0.0;
+    for (;;) {
+        const double b = count_window(first && !use_k);
+        if (first) {
+            below0 = b;
+            k0_top = k0;
+            first = false;
+        }
+        double ct = 0.0, mt = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWinPerThread; ++j) {
+            ct += (double)c[j];
+            mt += mb[j];
+        }
+        if (phase == 0) {
+            const double cw = sum_d(ct), mw = sum_d(mt);
+            if (above_c + cw < (double)a.top_k && next > 0) {       // the cut lies lower
+                above_c += cw;
+                above_m += mw;
+                khi = next;
+                continue;
+            }
+            double upc;
+            bk = crossing([&](int j) { return (double)c[j]; }, above_c, (double)a.top_k, upc);
+            const uint32_t nbk = bin_count(bk);
+            if (use_p && upc + nbk <= (double)kCand) {
+                // Every survivor is among the keys of coarse bins >= bk.
+                gather(bk, kcmax);
+                kkey = select(cand_src, 24, 0u, 0u, false, (double)a.top_k, zsur);
+                fkey = select(cand_src, 24, 0u, kkey, true, a.top_p * zsur, kept);
+                break;
+            }
+            kkey = resolve(bk, nbk, 0u, false, (double)a.top_k - upc, part_bk);
+            double hi_mass = 0.0;
+#pragma unroll
+            for (int j = 0; j < kWinPerThread; ++j)
+                if (k0 + lo_off + j > bk) hi_mass += mb[j];
+            zsur = above_m + sum_d(hi_mass) + part_bk;
+            fkey = kkey;
+            kept = zsur;
+            if (!use_p) break;
+            phase = 1;
+            target = a.top_p * zsur;
+            if (k0 != k0_top) {                                       // search top-p from the top again
+                khi = kcmax + 1;
+                continue;
+            }
+        } else if (!use_k && k0 == k0_top && above == 0.0 && zsur == 0.0) {
+            // No top-k: the survivors are the whole row.
+            zsur = sum_d(mt) + below0;
+            kept = zsur;
+            if (!use_p) break;
+            target = a.top_p * zsur;
+        }
+        // phase 1: the survivors' masses (bins above bk whole, bk in part).
+        auto sur = [&](int j) -> double {
+            const uint32_t cb = k0 + lo_off + j;
+            if (!use_k || cb > bk) return mb[j];
+            return cb == bk ? part_bk : 0.0;
+        };
+        double mine = 0.0;
+#pragma unroll
+        for (int j = 0; j < kWinPerThread; ++j) mine += sur(j);
+        const double mw = sum_d(mine);
+        if (above + mw < target && (!use_k || k0 > bk) && next > 0) {
+            above += mw;
+            khi = next;
+            continue;
+        }
+        double upm, mass_ge;
+        const uint32_t bp = crossing(sur, above, target, upm);
+        fkey = resolve(bp, bin_count(bp), (use_k && bp == bk) ? kkey : 0u, true, target - upm, mass_ge);
+        kept = upm + mass_ge;
+        break;
+    }
+    const bool cut = use_k || use_p;
+    fl_out = cut ? value_of(fkey) : -INFINITY;
+    m_out = m;
+    z_out = kept;
+}
+
 // Row slot of this workgroup, and the outputs.
 struct RowSlot {
     int b, rr, i, kb;
@@ -650,6 +975,9 @@ __global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
             __shared__ FloorShared sh;
             floor_by_select<DT, VEC>(a, r, sh, m, fl, z);
         }
+    } else if constexpr (VEC) {
+        __shared__ Win32Shared ws;
+        floor_by_window32<VEC>(a, r, ws, m, fl, z);
     } else {
         __shared__ FloorShared sh;
         floor_by_select<DT, VEC>(a, r, sh, m, fl, z);
