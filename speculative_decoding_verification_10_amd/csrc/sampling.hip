@@ -582,43 +582,64 @@ __device__ __forceinline__ void floor_by_window(const FloorParams& a, const RowR
     z_out = kept;
 }
 
-// fp32 rows (16-byte aligned): key windows as for bf16, over coarse keys
-// (the top 16 bits of a logit's 32-bit key: one coarse bin spans 65,536
-// neighbouring fp32 values, 1/128 of a binade).  Each bin holds its count
-// and the exact fixed-point sum of its elements' masses, so every weight
-// below is an exact multiple of 2^-35 and the crossings are exact.  A window
-// count also finds the highest coarse key below the window, so the next
-// window starts there and empty key ranges (between the positive and
-// negative logits, say) cost nothing.
-// A cut found in a coarse bin is resolved to the exact 32-bit key by 8-bit
-// digit selection (counts or masses per digit), which also gives the mass at
-// or above the key: over the bin's elements gathered into LDS when they fit
-// (one pass over the row), else by two digit passes over the row.  When the
-// top-k survivors all fit in LDS, both cuts are resolved there after one
-// gather.  The thread's first 4 vectors stay in registers (more spill).
+// fp32 rows (16-byte aligned): windows of 4,096 bins over the mass
+// exponent.  The deficit D(x) = M - x * c is monotone in x, so bins of
+// equal width in D (64 per binade of mass, a window spanning 64 binades
+// below its top value) split the row into ranges of the value order, with
+// equal logits always in one bin.  Each bin holds its count and the exact
+// fixed-point sum of its elements' masses, so every weight below is an
+// exact multiple of 2^-35 and the crossings are exact.  The first window
+// starts at the row max; a window count also finds the largest logit below
+// it, where the next window starts, so empty value ranges cost nothing.
+// The first window's count also keeps in LDS the logits of its top 16
+// binades (when they fit), which usually hold both cuts.
+// A cut found in a bin is resolved to the exact key over the logits of the
+// bin (or, when all top-k survivors fit, over all of them) in a selection
+// set in LDS: taken from the kept logits, else gathered by one more pass
+// over the row.  Up to 256 are ranked directly (every element counts the
+// weight above it); more go through 8-bit digit selection from the first
+// digit in which their keys differ.  A bin too large for the set is
+// resolved by four digit passes over the row.  Histogram updates of a wave
+// whose matching lanes share a digit are combined into one atomic pair.
+// The thread's first vector stays in registers (more spill).
+constexpr float kBinsPerBinade = 64.0f;
+constexpr int kKeepFrom = kWin - 16 * 64;          // first bin of the kept top 16 binades
+constexpr int kSet = 2048;                         // selection set capacity
+constexpr int kRank = 256;                         // largest set ranked directly
+
 struct Win32Shared {
     uint32_t cnt[kWin];
     uint64_t msum[kWin];
-    uint32_t ckey[kCand];
-    uint64_t cmass[kCand];
+    uint32_t ckey[kCand];               // kept logits of the first window: key,
+    uint64_t cmass[kCand];              //   fixed-point mass,
+    uint16_t cpos[kCand];               //   bin
+    uint32_t skey[kSet];                // selection set: key,
+    uint64_t smass[kSet];               //   fixed-point mass
     uint32_t hc[256];
     uint64_t hm[256];
     double red_d[kFW];
     uint32_t red_c[kFW];
     float red_f[kFW];
-    uint32_t ncand;
+    uint32_t nkeep;
+    uint32_t nset;
     uint32_t pick;
     double pick_above;
     double pick_mass_above;
 };
 
+// Number of lanes below this one whose bit is set in mask.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 template <bool VEC>
 __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const RowRef& r0, Win32Shared& ws,
                                                   float& m_out, float& fl_out, double& z_out) {
     const int t = threadIdx.x;
+    const int lane = t & 63;
     const bool use_k = a.top_k > 0 && a.top_k < a.V;
     const bool use_p = a.top_p < 1.0;
-    constexpr int kHold = 4;
+    constexpr int kHold = 1;
     u32x4 raw[kHold];
 #pragma unroll
     for (int u = 0; u < kHold; ++u) raw[u] = load_raw<kFP32, VEC, true>(r0.row, r0.V, r0.NV, t + u * kFT);
@@ -639,46 +660,73 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
             for (int q = 0; q < 4; ++q) f(__uint_as_float(rv[q]));
         }
     };
-    if (t == 0) {
-        ws.pick = 0;
-        ws.pick_above = 0.0;
-    }
     float m = -INFINITY;
     each([&](float x) { m = fmaxf(m, x); });
     m = uniform(wg_reduce(m, ws.red_f, [](float p, float q) { return fmaxf(p, q); }));
     const float M = offset_of(m, r0.sc);
-    const uint32_t kcmax = key_of(m) >> 16;
     auto sum_d = [&](double v) {
         return uniform(wg_reduce(v, ws.red_d, [](double p, double q) { return p + q; }));
     };
+    auto deficit = [&](float x) { return -exponent2(x, M, r0.sc); };
     auto mass = [&](float x) { return fix_of(fast_exp2(exponent2(x, M, r0.sc))); };
 
-    // Window [k0, khi): this thread's 4 coarse bins (k0 + 4 t + j) as counts
-    // and masses; `next` = 1 + the highest coarse key under k0 (0: none);
-    // with `below`, the returned value is the fp32 mass of the keys under k0.
+    // The window: top value hi (its deficit Dh).  pos(x): x's bin 0..4095
+    // (higher = larger logits), -1 above the window (or NaN), -2 below.
+    float hi = m, Dh = deficit(m);
+    bool top_window = true;
+    auto pos = [&](float x) -> int {
+        if (!(x <= hi)) return -1;
+        const float q = (deficit(x) - Dh) * kBinsPerBinade;
+        return q < (float)kWin ? kWin - 1 - (int)q : -2;
+    };
+    // Append the logits with g set (one atomic per wave places a wave's
+    // matches) to LDS arrays with counter n; f(i, x) stores entry i < cap.
+    auto append = [&](bool g, uint32_t& n, uint32_t cap, auto&& f) {
+        const uint64_t mask = __ballot(g);
+        if (mask) {
+            const int leader = __ffsll((unsigned long long)mask) - 1;
+            uint32_t base = 0;
+            if (lane == leader) base = atomicAdd(&n, (uint32_t)__popcll(mask));
+            base = __shfl(base, leader, 64);
+            const uint32_t i = base + lanes_below(mask);
+            if (g && i < cap) f(i);
+        }
+    };
+
+    // This thread's 4 bins (4 t + j) as counts and masses; `next` = 1 + the
+    // key of the largest logit below the window (0: none); with `below`,
+    // the returned value is the fp32 mass below the window; with `keep`,
+    // the logits of bins >= kKeepFrom go to the kept arrays.
     uint32_t c[kWinPerThread];
     double mb[kWinPerThread];
-    uint32_t k0 = 0, khi = kcmax + 1, next = 0;
-    auto count_window = [&](bool below) -> double {
-        k0 = khi > (uint32_t)kWin ? khi - kWin : 0u;
+    uint32_t next = 0;
+    auto count_window = [&](bool below, bool keep) -> double {
         __syncthreads();
         for (int q = t; q < kWin; q += kFT) {
             ws.cnt[q] = 0;
             ws.msum[q] = 0;
         }
+        if (t == 0 && keep) ws.nkeep = 0;
         __syncthreads();
         float bm = 0.0f;
         uint32_t nb = 0;
-        const uint32_t span = khi - k0;
         each([&](float x) {
-            const uint32_t kc = key_of(x) >> 16;
-            if (kc - k0 < span) {
-                atomicAdd(&ws.cnt[kc - k0], 1u);
-                atomicAdd(reinterpret_cast<unsigned long long*>(&ws.msum[kc - k0]), (unsigned long long)mass(x));
-            } else if (kc < k0) {
-                nb = max(nb, kc + 1);
+            const int p = pos(x);
+            uint64_t fm = 0;
+            if (p >= 0) {
+                fm = mass(x);
+                atomicAdd(&ws.cnt[p], 1u);
+                atomicAdd(reinterpret_cast<unsigned long long*>(&ws.msum[p]), (unsigned long long)fm);
+            } else if (p == -2) {
+                nb = max(nb, key_of(x) + 1u);
                 if (below) bm += fast_exp2(exponent2(x, M, r0.sc));
             }
+            if (keep)
+                append(p >= kKeepFrom, ws.nkeep, kCand, [&](uint32_t i) {
+                    ws.ckey[i] = key_of(x);
+                    ws.cmass[i] = fm;
+                    ws.cpos[i] = (uint16_t)p;
+                });
         });
         next = __builtin_amdgcn_readfirstlane(wg_reduce(nb, ws.red_c, [](uint32_t p, uint32_t q) { return max(p, q); }));
         __syncthreads();
@@ -689,14 +737,21 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
         }
         return below ? sum_d((double)bm) : 0.0;
     };
-    // Count of coarse bin cb of the current window (LDS holds the counts
-    // until the next window); above kCand when cb lies outside the window.
-    auto bin_count = [&](uint32_t cb) -> uint32_t {
-        return cb - k0 < (uint32_t)kWin ? __builtin_amdgcn_readfirstlane(ws.cnt[cb - k0]) : kCand + 1u;
+    // A finite window below this one?  Then move to it.
+    auto lower = [&]() -> bool {
+        if (next == 0 || value_of(next - 1u) == -INFINITY) return false;
+        hi = value_of(next - 1u);
+        Dh = deficit(hi);
+        top_window = false;
+        return true;
     };
-    // The coarse bin where the weight from the top (with `above` from higher
+    // The bin where the weight from the top (with `above` from higher
     // windows) first reaches `target`; `up` gets the weight above that bin.
-    auto crossing = [&](auto&& wt, double above, double target, double& up) -> uint32_t {
+    auto crossing = [&](auto&& wt, double above, double target, double& up) -> int {
+        if (t == 0) {
+            ws.pick = 0;
+            ws.pick_above = 0.0;
+        }
         double mine = 0.0;
 #pragma unroll
         for (int j = 0; j < kWinPerThread; ++j) mine += wt(j);
@@ -706,7 +761,7 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
             for (int j = kWinPerThread - 1; j >= 0; --j) {
                 const double w = wt(j);
                 if (cum + w >= target) {
-                    ws.pick = k0 + kWinPerThread * t + j;
+                    ws.pick = kWinPerThread * t + j;
                     ws.pick_above = cum;
                     break;
                 }
@@ -714,47 +769,68 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
             }
         }
         __syncthreads();
-        const uint32_t key = __builtin_amdgcn_readfirstlane(ws.pick);
+        const int p = (int)__builtin_amdgcn_readfirstlane(ws.pick);
         up = uniform(ws.pick_above);
         __syncthreads();
-        return key;
+        return p;
     };
-    // Element sources of the digit selection: f(key, mass getter) for every
-    // logit of the row, or for every candidate in LDS.
-    auto row_src = [&](auto&& f) {
-        each([&](float x) { f(key_of(x), [&] { return mass(x); }); });
+
+    // The selection set: from the kept logits whose bin passes sel(p), or
+    // from the row's logits with in(x).  shift0 / prefix: the first 8-bit
+    // digit in which the set's keys differ and the bits above it.
+    int shift0 = 24;
+    uint32_t prefix = 0;
+    auto set_done = [&](uint32_t kmn, uint32_t kmx) {
+        kmn = __builtin_amdgcn_readfirstlane(wg_reduce(kmn, ws.red_c, [](uint32_t p, uint32_t q) { return min(p, q); }));
+        kmx = __builtin_amdgcn_readfirstlane(wg_reduce(kmx, ws.red_c, [](uint32_t p, uint32_t q) { return max(p, q); }));
+        const uint32_t diff = kmn ^ kmx;
+        shift0 = diff ? (31 - __builtin_clz(diff)) / 8 * 8 : 0;
+        prefix = shift0 >= 24 ? 0u : kmx >> (shift0 + 8);
     };
-    auto cand_src = [&](auto&& f) {
-        const uint32_t nc = min(__builtin_amdgcn_readfirstlane(ws.ncand), (uint32_t)kCand);
-        for (uint32_t i = t; i < nc; i += kFT) {
-            const uint64_t q = ws.cmass[i];
-            f(ws.ckey[i], [q] { return q; });
-        }
-    };
-    // The elements of coarse bins [glo, ghi] into LDS (any order).
-    auto gather = [&](uint32_t glo, uint32_t ghi) {
+    auto set_from_kept = [&](auto&& sel) {
         __syncthreads();
-        if (t == 0) ws.ncand = 0;
+        if (t == 0) ws.nset = 0;
         __syncthreads();
-        each([&](float x) {
-            const uint32_t k = key_of(x);
-            if ((k >> 16) - glo <= ghi - glo) {
-                const uint32_t i = atomicAdd(&ws.ncand, 1u);
-                if (i < (uint32_t)kCand) {
-                    ws.ckey[i] = k;
-                    ws.cmass[i] = mass(x);
-                }
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0;
+        const uint32_t nk = min(__builtin_amdgcn_readfirstlane(ws.nkeep), (uint32_t)kCand);
+        for (uint32_t i0 = 0; i0 < nk; i0 += kFT) {                 // every lane runs every turn
+            const uint32_t i = i0 + t;
+            const bool g = i < nk && sel((int)ws.cpos[i]);
+            const uint32_t k = g ? ws.ckey[i] : 0u;
+            if (g) {
+                kmn = min(kmn, k);
+                kmx = max(kmx, k);
             }
-        });
-        __syncthreads();
+            append(g, ws.nset, kSet, [&](uint32_t o) {
+                ws.skey[o] = k;
+                ws.smass[o] = ws.cmass[i];
+            });
+        }
+        set_done(kmn, kmx);
     };
-    // One 8-bit digit (at `shift`) of the keys >= kmin whose bits above the
-    // digit are `hi` (all keys at shift 24): the digit where the weight
-    // (masses, else counts) from the top reaches `target`; `up` gets the
-    // weight above that digit and `mup` the mass above it.  The digit
-    // histogram stays in LDS.
-    auto digit = [&](auto&& src, int shift, uint32_t hi, uint32_t kmin, bool masses, double target, double& up,
-                     double& mup) -> uint32_t {
+    auto set_from_row = [&](auto&& in) {
+        __syncthreads();
+        if (t == 0) ws.nset = 0;
+        __syncthreads();
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0;
+        each([&](float x) {
+            const bool g = in(x);
+            const uint32_t k = key_of(x);
+            if (g) {
+                kmn = min(kmn, k);
+                kmx = max(kmx, k);
+            }
+            append(g, ws.nset, kSet, [&](uint32_t o) {
+                ws.skey[o] = k;
+                ws.smass[o] = mass(x);
+            });
+        });
+        set_done(kmn, kmx);
+    };
+    // Digit histograms (counts, masses) of the keys >= kmin whose bits above
+    // the digit at `shift` are `hb` (all keys at shift 24): over the set, or
+    // over the row's logits with in(x).
+    auto hist_clear = [&]() {
         __syncthreads();
         if (t < 256) {
             ws.hc[t] = 0;
@@ -766,14 +842,50 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
             ws.pick_mass_above = 0.0;
         }
         __syncthreads();
-        src([&](uint32_t k, auto&& mf) {
-            if ((shift == 24 || (k >> (shift + 8)) == hi) && k >= kmin) {
+    };
+    auto hist_set = [&](int shift, uint32_t hb, uint32_t kmin) {
+        hist_clear();
+        const uint32_t n = min(__builtin_amdgcn_readfirstlane(ws.nset), (uint32_t)kSet);
+        for (uint32_t i0 = 0; i0 < n; i0 += kFT) {                   // every lane runs every turn
+            const uint32_t i = i0 + t;
+            const uint32_t k = i < n ? ws.skey[i] : 0u;
+            const bool g = i < n && (shift == 24 || (k >> (shift + 8)) == hb) && k >= kmin;
+            const uint32_t d = (k >> shift) & 255u;
+            const uint64_t q = g ? ws.smass[i] : 0ull;
+            const uint64_t mask = __ballot(g);
+            if (!mask) continue;
+            const int leader = __ffsll((unsigned long long)mask) - 1;
+            const uint32_t dl = __shfl(d, leader, 64);
+            if (__all(!g || d == dl)) {
+                uint64_t sq = q;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+                if (lane == leader) {
+                    atomicAdd(&ws.hc[dl], (uint32_t)__popcll(mask));
+                    atomicAdd(reinterpret_cast<unsigned long long*>(&ws.hm[dl]), (unsigned long long)sq);
+                }
+            } else if (g) {
+                atomicAdd(&ws.hc[d], 1u);
+                atomicAdd(reinterpret_cast<unsigned long long*>(&ws.hm[d]), (unsigned long long)q);
+            }
+        }
+        __syncthreads();
+    };
+    auto hist_row = [&](auto&& in, int shift, uint32_t hb, uint32_t kmin) {
+        hist_clear();
+        each([&](float x) {
+            const uint32_t k = key_of(x);
+            if (in(x) && (shift == 24 || (k >> (shift + 8)) == hb) && k >= kmin) {
                 const uint32_t d = (k >> shift) & 255u;
                 atomicAdd(&ws.hc[d], 1u);
-                atomicAdd(reinterpret_cast<unsigned long long*>(&ws.hm[d]), (unsigned long long)mf());
+                atomicAdd(reinterpret_cast<unsigned long long*>(&ws.hm[d]), (unsigned long long)mass(x));
             }
         });
         __syncthreads();
+    };
+    // The digit where the weight (masses, else counts) from the top reaches
+    // `target`; `up` gets the weight above it and `mup` the mass above it.
+    auto digit_pick = [&](bool masses, double target, double& up, double& mup) -> uint32_t {
         const double hm = (t < 256) ? (double)ws.hm[t] / kFix : 0.0;
         const double w = (t < 256) ? (masses ? hm : (double)ws.hc[t]) : 0.0;
         const double u = sum_above(w, ws.red_d);
@@ -790,16 +902,17 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
         __syncthreads();
         return d;
     };
-    // The exact key (with the bits above `top_shift + 8` equal to `hi`)
-    // where the weight of the keys >= kmin from the top reaches `target`;
-    // `mass_ge` gets the mass of those keys at or above it.
-    auto select = [&](auto&& src, int top_shift, uint32_t hi, uint32_t kmin, bool masses, double target,
-                      double& mass_ge) -> uint32_t {
-        uint32_t key = hi;
+    // The exact key (bits above shift + 8 equal to hb) where the weight of
+    // the keys >= kmin from the top reaches `target`; `mass_ge` gets the mass
+    // of those keys at or above it.  fill(shift, hb, kmin) builds a level.
+    auto radix = [&](auto&& fill, int top_shift, uint32_t hb, uint32_t kmin, bool masses, double target,
+                     double& mass_ge) -> uint32_t {
+        uint32_t key = hb;
         double mu_sum = 0.0;
         for (int sh = top_shift; sh >= 0; sh -= 8) {
+            fill(sh, key, kmin);
             double up, mup;
-            const uint32_t d = digit(src, sh, key, kmin, masses, target, up, mup);
+            const uint32_t d = digit_pick(masses, target, up, mup);
             key = (key << 8) | d;
             target -= up;
             mu_sum += mup;
@@ -807,32 +920,85 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
         mass_ge = mu_sum + uniform((double)ws.hm[key & 255u] / kFix);
         return key;
     };
-    // The cut inside coarse bin cb (n elements).
-    auto resolve = [&](uint32_t cb, uint32_t n, uint32_t kmin, bool masses, double target,
-                       double& mass_ge) -> uint32_t {
-        if (n <= (uint32_t)kCand) {
-            gather(cb, cb);
-            return select(cand_src, 8, cb, kmin, masses, target, mass_ge);
+    // The same over the selection set: a small set by ranking (each
+    // element sums the weight of the keys above it and equal to it), a
+    // larger one by digits.
+    auto select = [&](uint32_t kmin, bool masses, double target, double& mass_ge) -> uint32_t {
+        const uint32_t n = min(__builtin_amdgcn_readfirstlane(ws.nset), (uint32_t)kSet);
+        if (n > (uint32_t)kRank)
+            return radix([&](int sh, uint32_t hb, uint32_t km) { hist_set(sh, hb, km); }, shift0, prefix, kmin,
+                         masses, target, mass_ge);
+        __syncthreads();
+        if (t == 0) {
+            ws.pick = 0;
+            ws.pick_mass_above = 0.0;
         }
-        return select(row_src, 8, cb, kmin, masses, target, mass_ge);
+        __syncthreads();
+        if ((uint32_t)t < n) {
+            const uint32_t key = ws.skey[t];
+            if (key >= kmin) {
+                uint32_t gc = 0, ec = 0;
+                uint64_t gm = 0, em = 0;
+                for (uint32_t j = 0; j < n; ++j) {
+                    const uint32_t kj = ws.skey[j];
+                    const uint64_t mj = ws.smass[j];
+                    if (kj > key) {
+                        ++gc;
+                        gm += mj;
+                    } else if (kj == key) {
+                        ++ec;
+                        em += mj;
+                    }
+                }
+                const double wg = masses ? (double)gm / kFix : (double)gc;
+                const double we = masses ? (double)(gm + em) / kFix : (double)(gc + ec);
+                if (wg < target && target <= we) {                    // equal keys write equal values
+                    ws.pick = key;
+                    ws.pick_mass_above = (double)(gm + em) / kFix;
+                }
+            }
+        }
+        __syncthreads();
+        const uint32_t key = __builtin_amdgcn_readfirstlane(ws.pick);
+        mass_ge = uniform(ws.pick_mass_above);
+        __syncthreads();
+        return key;
+    };
+    // kept: the kept arrays are this (top) window's logits of bins >=
+    // kKeepFrom, all of them.
+    bool kept_ok = false;
+    // The cut inside bin p (n logits) of the current window.
+    auto resolve = [&](int p, uint32_t n, uint32_t kmin, bool masses, double target, double& mass_ge) -> uint32_t {
+        auto in_bin = [&](float x) { return pos(x) == p; };
+        if (n <= (uint32_t)kSet) {
+            if (kept_ok && top_window && p >= kKeepFrom)
+                set_from_kept([&](int q) { return q == p; });
+            else
+                set_from_row(in_bin);
+            return select(kmin, masses, target, mass_ge);
+        }
+        return radix([&](int sh, uint32_t hb, uint32_t km) { hist_row(in_bin, sh, hb, km); }, 24, 0u, kmin,
+                     masses, target, mass_ge);
     };
 
-    const uint32_t lo_off = kWinPerThread * t;
     // As for bf16: first the top-k search (counts), then the top-p search
     // (survivors' masses), each moving down a window while its cut lies
-    // lower.  bk is the coarse bin of the top-k cut kkey; of it only the keys
-    // >= kkey survive (mass part_bk).
+    // lower.  The top-k cut kkey lies in bin pk of the window with top bk_hi;
+    // of that bin only the keys >= kkey survive (mass part_bk).
+    const int lo_off = kWinPerThread * t;
     int phase = use_k ? 0 : 1;
     bool first = true;
-    uint32_t k0_top = 0, kkey = 0, fkey = 0, bk = 0;
+    int pk = 0;
+    float bk_hi = INFINITY;
+    uint32_t kkey = 0, fkey = 0;
     double below0 = 0.0, above_c = 0.0, above_m = 0.0, zsur = 0.0, target = 0.0, above = 0.0, kept = 0.0;
     double part_bk = 0.0;
     for (;;) {
-        const double b = count_window(first && !use_k);
+        const double b = count_window(first && !use_k, first);
         if (first) {
             below0 = b;
-            k0_top = k0;
             first = false;
+            kept_ok = __builtin_amdgcn_readfirstlane(ws.nkeep) <= (uint32_t)kCand;
         }
         double ct = 0.0, mt = 0.0;
 #pragma unroll
@@ -842,62 +1008,89 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
         }
         if (phase == 0) {
             const double cw = sum_d(ct), mw = sum_d(mt);
-            if (above_c + cw < (double)a.top_k && next > 0) {       // the cut lies lower
+            if (above_c + cw < (double)a.top_k) {                     // the cut lies lower
                 above_c += cw;
                 above_m += mw;
-                khi = next;
+                if (lower()) continue;
+                // Only -inf logits (or none) remain: the cut keeps them all.
+                kkey = key_of(-INFINITY);
+                bk_hi = -INFINITY;
+                zsur = above_m;
+                fkey = kkey;
+                kept = zsur;
+                if (!use_p) break;
+                phase = 1;
+                target = a.top_p * zsur;
+                hi = m;
+                Dh = deficit(m);
+                top_window = true;
                 continue;
             }
             double upc;
-            bk = crossing([&](int j) { return (double)c[j]; }, above_c, (double)a.top_k, upc);
-            const uint32_t nbk = bin_count(bk);
-            if (use_p && upc + nbk <= (double)kCand) {
-                // Every survivor is among the keys of coarse bins >= bk.
-                gather(bk, kcmax);
-                kkey = select(cand_src, 24, 0u, 0u, false, (double)a.top_k, zsur);
-                fkey = select(cand_src, 24, 0u, kkey, true, a.top_p * zsur, kept);
+            pk = crossing([&](int j) { return (double)c[j]; }, above_c, (double)a.top_k, upc);
+            const uint32_t nbk = __builtin_amdgcn_readfirstlane(ws.cnt[pk]);
+            if (use_p && upc + nbk <= (double)kSet) {
+                // Every survivor lies above the window or in its bins >= pk.
+                if (kept_ok && top_window && pk >= kKeepFrom)
+                    set_from_kept([&](int q) { return q >= pk; });
+                else
+                    set_from_row([&](float x) { return x > hi || pos(x) >= pk; });
+                kkey = select(0u, false, (double)a.top_k, zsur);
+                fkey = select(kkey, true, a.top_p * zsur, kept);
                 break;
             }
-            kkey = resolve(bk, nbk, 0u, false, (double)a.top_k - upc, part_bk);
+            kkey = resolve(pk, nbk, 0u, false, (double)a.top_k - upc, part_bk);
             double hi_mass = 0.0;
 #pragma unroll
             for (int j = 0; j < kWinPerThread; ++j)
-                if (k0 + lo_off + j > bk) hi_mass += mb[j];
+                if (lo_off + j > pk) hi_mass += mb[j];
             zsur = above_m + sum_d(hi_mass) + part_bk;
             fkey = kkey;
             kept = zsur;
+            bk_hi = hi;
             if (!use_p) break;
             phase = 1;
             target = a.top_p * zsur;
-            if (k0 != k0_top) {                                       // search top-p from the top again
-                khi = kcmax + 1;
+            if (!top_window) {                                        // search top-p from the top again
+                hi = m;
+                Dh = deficit(m);
+                top_window = true;
                 continue;
             }
-        } else if (!use_k && k0 == k0_top && above == 0.0 && zsur == 0.0) {
+        } else if (!use_k && top_window && above == 0.0 && zsur == 0.0) {
             // No top-k: the survivors are the whole row.
             zsur = sum_d(mt) + below0;
             kept = zsur;
             if (!use_p) break;
             target = a.top_p * zsur;
         }
-        // phase 1: the survivors' masses (bins above bk whole, bk in part).
+        // phase 1: the survivors' masses (windows above bk_hi whole; in
+        // that window, bins above pk whole and pk in part).
+        const bool whole = !use_k || hi > bk_hi;
         auto sur = [&](int j) -> double {
-            const uint32_t cb = k0 + lo_off + j;
-            if (!use_k || cb > bk) return mb[j];
-            return cb == bk ? part_bk : 0.0;
+            if (whole) return mb[j];
+            const int p = lo_off + j;
+            return p > pk ? mb[j] : (p == pk ? part_bk : 0.0);
         };
         double mine = 0.0;
 #pragma unroll
         for (int j = 0; j < kWinPerThread; ++j) mine += sur(j);
         const double mw = sum_d(mine);
-        if (above + mw < target && (!use_k || k0 > bk) && next > 0) {
-            above += mw;
-            khi = next;
-            continue;
+        if (above + mw < target && whole) {
+            if (lower()) {
+                above += mw;
+                continue;
+            }
+            // The row's last window and still short of the target (masses
+            // below the fixed-point step round to zero): keep every survivor.
+            fkey = use_k ? kkey : key_of(-INFINITY);
+            kept = above + mw;
+            break;
         }
         double upm, mass_ge;
-        const uint32_t bp = crossing(sur, above, target, upm);
-        fkey = resolve(bp, bin_count(bp), (use_k && bp == bk) ? kkey : 0u, true, target - upm, mass_ge);
+        const int pp = crossing(sur, above, target, upm);
+        fkey = resolve(pp, __builtin_amdgcn_readfirstlane(ws.cnt[pp]), (!whole && pp == pk) ? kkey : 0u, true,
+                       target - upm, mass_ge);
         kept = upm + mass_ge;
         break;
     }
