@@ -354,12 +354,14 @@ __device__ __noinline__ void floor_by_select(const FloorParams& a, RowRef& r, Fl
 // key holds its value's count, and a bin's mass is its count times the mass
 // of its one value, so cuts found over bins are exact.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t key16_of(uint32_t h) {   // h: bf16 bits
-    if (h == 0x8000u) h = 0;                                   // -0 -> +0
-    return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+// Order-preserving 16-bit key of a bf16 value (bits h): a negative value's
+// key is its inverted bits plus one, so -0 (0x8000) gets +0's key 0x8000 and
+// the other keys stay distinct; keys 1..0x7F are the negative NaNs.
+__device__ __forceinline__ uint32_t key16_of(uint32_t h) {
+    return (h & 0x8000u) ? ((~h + 1u) & 0xFFFFu) : (h | 0x8000u);
 }
 __device__ __forceinline__ float value16_of(uint32_t k) {
-    const uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+    const uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (~(k - 1u) & 0xFFFFu);
     return __uint_as_float(h << 16);
 }
 
@@ -390,10 +392,32 @@ __device__ __forceinline__ T sum_above(T v, T* lds) {
 // top-k cut is the bin where the count from the top reaches top_k; the
 // top-p cut is the bin where the survivors' mass from the top reaches
 // top_p of theirs.  A cut below a window moves the search to the next one
-// down.  The first window spans 32 binades below the max, so a second
-// window is needed only for cuts among tokens of mass below ~2^-22 of the
-// max's.  No counter can overflow (32-bit counts).
+// down.  The first window also stops at the keys whose mass is 2^-24 of the
+// max's: the logits under it are only summed, not binned, which spares the
+// LDS atomics of most of a typical row (its bulk lies far below the max).
+// Their mass together is at most V * 2^-24 of the max's (< 1% for V < 2^17),
+// so top-p cuts up to 0.99 and small top-k cuts almost always lie in it.
+// No counter can overflow (32-bit counts).
+// g(vector) for the vectors v0, v0 + 1,024, ... of a row of whole 16-byte
+// vectors, re-read kTail at a time: the loads of a batch issue back to back
+// (an index past the end re-reads the last vector, which is then skipped),
+// so a pass costs one cache round trip per batch, not per vector.
+constexpr int kTail = 4;
+template <typename G>
+__device__ __forceinline__ void tail_batches(const RowRef& r, int v0, G&& g) {
+    const u32x4* base = reinterpret_cast<const u32x4*>(r.row);
+    for (; v0 < r.NV; v0 += kTail * kFT) {
+        u32x4 rv[kTail];
+#pragma unroll
+        for (int u = 0; u < kTail; ++u) rv[u] = base[min(v0 + u * kFT, r.NV - 1)];
+#pragma unroll
+        for (int u = 0; u < kTail; ++u)
+            if (v0 + u * kFT < r.NV) g(rv[u]);
+    }
+}
+
 constexpr int kWin = 4096;
+constexpr float kFirstDeficit = 24.0f;
 constexpr int kWinPerThread = kWin / kFT;              // 4
 
 struct WinShared {
@@ -434,11 +458,10 @@ __device__ __forceinline__ void floor_by_window(const FloorParams& a, const RowR
 #pragma unroll
             for (int q = 0; q < 4; ++q) f(raw[u][q]);
         }
-        for (int v = t + kHold * kFT; v < r0.NV; v += kFT) {
-            const u32x4 rv = load_raw<kBF16, VEC, false>(r0.row, r0.V, r0.NV, v);
+        tail_batches(r0, t + kHold * kFT, [&](const u32x4& rv) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) f(rv[q]);
-        }
+        });
     };
     float m = -INFINITY;
     each_word([&](uint32_t w) { m = fmaxf(m, fmaxf(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u))); });
@@ -453,31 +476,50 @@ __device__ __forceinline__ void floor_by_window(const FloorParams& a, const RowR
     // and masses; with `below`, also the mass of the keys under k0.
     uint32_t c[kWinPerThread];
     double mb[kWinPerThread];
+    // klow: the lowest key whose mass exceeds 2^-kFirstDeficit of the max's
+    // (the exponent is monotone in the key; the keys under -inf's are NaNs
+    // and fail the test).
+    uint32_t klow = 1;
+    for (uint32_t hi_k = kmax; klow < hi_k;) {
+        const uint32_t mid = (klow + hi_k) >> 1;
+        if (exponent2(value16_of(mid), M, r0.sc) > -kFirstDeficit)
+            hi_k = mid;
+        else
+            klow = mid + 1;
+    }
     uint32_t k0 = 0, khi = kmax + 1;
     auto count_window = [&](bool below) -> double {
         k0 = khi > (uint32_t)kWin ? khi - kWin : 0u;
+        if (khi == kmax + 1) k0 = max(k0, klow);                 // the top window
         __syncthreads();
         for (int q = t; q < kWin; q += kFT) ws.win[q] = 0;
         __syncthreads();
         float bm = 0.0f;
         const uint32_t span = khi - k0;
         each_word([&](uint32_t w) {
-            // Both keys of the word at once: a half with its sign set is
-            // inverted, the other gets its top bit set; -0 joins +0.
-            const uint32_t neg = ((w >> 15) & 0x00010001u) * 0x7FFFu;
-            const uint32_t keys = w ^ (neg | 0x80008000u);
+            // Both keys of the word at once: a negative half is inverted and
+            // incremented (no carry leaves it), the other gets its top bit set.
+            const uint32_t sgn = (w >> 15) & 0x00010001u;
+            const uint32_t keys = (w ^ (sgn * 0x7FFFu | 0x80008000u)) + sgn;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                uint32_t k = half ? (keys >> 16) : (keys & 0xFFFFu);
-                k = (k == 0x7FFFu) ? 0x8000u : k;
-                if (k - k0 < span) {
-                    atomicAdd(&ws.win[k - k0], 1u);
-                } else if (below && k < k0) {
-                    const float x = __uint_as_float(half ? (w & 0xFFFF0000u) : (w << 16));
-                    bm += fast_exp2(exponent2(x, M, r0.sc));
-                }
+                const uint32_t k = half ? (keys >> 16) : (keys & 0xFFFFu);
+                if (k - k0 < span) atomicAdd(&ws.win[k - k0], 1u);
             }
         });
+        // The mass under the window, when asked for, in a pass of its own:
+        // a count-only pass then carries no exponential.
+        if (below)
+            each_word([&](uint32_t w) {
+                const uint32_t sgn = (w >> 15) & 0x00010001u;
+                const uint32_t keys = (w ^ (sgn * 0x7FFFu | 0x80008000u)) + sgn;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint32_t k = half ? (keys >> 16) : (keys & 0xFFFFu);
+                    const float x = __uint_as_float(half ? (w & 0xFFFF0000u) : (w << 16));
+                    bm += k < k0 ? fast_exp2(exponent2(x, M, r0.sc)) : 0.0f;
+                }
+            });
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kWinPerThread; ++j) {
@@ -602,8 +644,8 @@ __device__ __forceinline__ void floor_by_window(const FloorParams& a, const RowR
 // resolved by four digit passes over the row.  Histogram updates of a wave
 // whose matching lanes share a digit are combined into one atomic pair.
 // The thread's first vector stays in registers (more spill).
-constexpr float kBinsPerBinade = 64.0f;
-constexpr int kKeepFrom = kWin - 16 * 64;          // first bin of the kept top 16 binades
+constexpr int kBinsPerBinade = 64;
+constexpr int kKeepFrom = kWin - 16 * kBinsPerBinade;   // first bin of the kept top 16 binades
 constexpr int kSet = 2048;                         // selection set capacity
 constexpr int kRank = 256;                         // largest set ranked directly
 
@@ -654,11 +696,10 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
 #pragma unroll
             for (int q = 0; q < 4; ++q) f(__uint_as_float(raw[u][q]));
         }
-        for (int v = t + kHold * kFT; v < r0.NV; v += kFT) {
-            const u32x4 rv = load_raw<kFP32, VEC, false>(r0.row, r0.V, r0.NV, v);
+        tail_batches(r0, t + kHold * kFT, [&](const u32x4& rv) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) f(__uint_as_float(rv[q]));
-        }
+        });
     };
     float m = -INFINITY;
     each([&](float x) { m = fmaxf(m, x); });
@@ -676,7 +717,7 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
     bool top_window = true;
     auto pos = [&](float x) -> int {
         if (!(x <= hi)) return -1;
-        const float q = (deficit(x) - Dh) * kBinsPerBinade;
+        const float q = (deficit(x) - Dh) * (float)kBinsPerBinade;
         return q < (float)kWin ? kWin - 1 - (int)q : -2;
     };
     // Append the logits with g set (one atomic per wave places a wave's
