@@ -50,6 +50,8 @@ def _rows(rng, n, V, kind):
         x = np.round(rng.standard_normal((n, V)) * 2)
     elif kind == "flat":
         x = rng.standard_normal((n, V)) * 0.05
+    elif kind == "zeros":  # mostly -0 and +0, which are one value to every cut
+        x = rng.choice(np.array([-0.0, 0.0, -0.0, 0.0, 1.0, -1.0, 2.0]), size=(n, V))
     else:  # "neginf": a third of each row cut to -inf
         x = rng.standard_normal((n, V)) * 2
         x[:, : V // 3] = -np.inf
@@ -58,7 +60,7 @@ def _rows(rng, n, V, kind):
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("V", [7, 1001, 32000, 128256])
-@pytest.mark.parametrize("kind", ["normal", "peaked", "ties", "flat", "neginf"])
+@pytest.mark.parametrize("kind", ["normal", "peaked", "ties", "flat", "neginf", "zeros"])
 def test_floors(dtype, V, kind):
     rng = np.random.default_rng(V * 7 + len(kind))
     n = 12 if V > 40000 else 40
