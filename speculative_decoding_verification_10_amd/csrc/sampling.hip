@@ -508,18 +508,20 @@ __device__ __forceinline__ void floor_by_window(const FloorParams& a, const RowR
             }
         });
         // The mass under the window, when asked for, in a pass of its own:
-        // a count-only pass then carries no exponential.
-        if (below)
+        // a count-only pass then carries no exponential.  The keys under k0
+        // are the values under k0's value (a NaN for k0 < 0x80: none), and
+        // one FMA gives the exponent: each of these masses is below 2^-24
+        // of the max's, so its few-ulp error is far below the row total's.
+        if (below) {
+            const float xk0 = value16_of(k0), c1 = (float)r0.sc.c;
             each_word([&](uint32_t w) {
-                const uint32_t sgn = (w >> 15) & 0x00010001u;
-                const uint32_t keys = (w ^ (sgn * 0x7FFFu | 0x80008000u)) + sgn;
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    const uint32_t k = half ? (keys >> 16) : (keys & 0xFFFFu);
                     const float x = __uint_as_float(half ? (w & 0xFFFF0000u) : (w << 16));
-                    bm += k < k0 ? fast_exp2(exponent2(x, M, r0.sc)) : 0.0f;
+                    bm += x < xk0 ? fast_exp2(__fmaf_rn(x, c1, -M)) : 0.0f;
                 }
             });
+        }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kWinPerThread; ++j) {
