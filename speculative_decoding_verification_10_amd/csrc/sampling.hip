@@ -102,6 +102,29 @@ __device__ __forceinline__ T wg_reduce(T v, T* lds, Op op) {
     return r;
 }
 
+// The same for an fp64 sum and an fp32 max, the wave step done by DPP moves
+// instead of lane shuffles (no LDS round trips).
+__device__ __forceinline__ double wg_sum(double v, double* lds) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = lds[0];
+#pragma unroll
+    for (int i = 1; i < kFW; ++i) r += lds[i];
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ float wg_max(float v, float* lds) {
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = lds[0];
+#pragma unroll
+    for (int i = 1; i < kFW; ++i) r = fmaxf(r, lds[i]);
+    __syncthreads();
+    return r;
+}
+
 // f(x) for every element of the row this thread visits (vectors t, t + 1024,
 // ...; elements past V skipped).  The first pass over a row reads HBM; the
 // later ones mostly hit the L2 / Infinity Cache.
@@ -465,11 +488,11 @@ __device__ __forceinline__ void floor_by_window(const FloorParams& a, const RowR
     };
     float m = -INFINITY;
     each_word([&](uint32_t w) { m = fmaxf(m, fmaxf(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u))); });
-    m = uniform(wg_reduce(m, ws.red_f, [](float p, float q) { return fmaxf(p, q); }));
+    m = uniform(wg_max(m, ws.red_f));
     const float M = offset_of(m, r0.sc);
     const uint32_t kmax = key16_of(__float_as_uint(m) >> 16);
     auto sum_d = [&](double v) {
-        return uniform(wg_reduce(v, ws.red_d, [](double p, double q) { return p + q; }));
+        return uniform(wg_sum(v, ws.red_d));
     };
 
     // Window [k0, khi): this thread's 4 bins (keys k0 + 4 t + j) as counts
@@ -534,6 +557,8 @@ __device__ __forceinline__ void floor_by_window(const FloorParams& a, const RowR
     // The crossing of a window: the bin where the weight from the top (with
     // `above` from higher windows) first reaches `target`.
     auto crossing = [&](auto&& wt, double above, double target) -> uint32_t {
+        if (t == 0) ws.pick = k0;        // no thread matches only if rounding left
+                                         // the target past the window's weight
         double mine = 0.0;
 #pragma unroll
         for (int j = 0; j < kWinPerThread; ++j) mine += wt(j);
@@ -705,10 +730,10 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
     };
     float m = -INFINITY;
     each([&](float x) { m = fmaxf(m, x); });
-    m = uniform(wg_reduce(m, ws.red_f, [](float p, float q) { return fmaxf(p, q); }));
+    m = uniform(wg_max(m, ws.red_f));
     const float M = offset_of(m, r0.sc);
     auto sum_d = [&](double v) {
-        return uniform(wg_reduce(v, ws.red_d, [](double p, double q) { return p + q; }));
+        return uniform(wg_sum(v, ws.red_d));
     };
     auto deficit = [&](float x) { return -exponent2(x, M, r0.sc); };
     auto mass = [&](float x) { return fix_of(fast_exp2(exponent2(x, M, r0.sc))); };
