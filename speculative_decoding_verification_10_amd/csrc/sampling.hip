@@ -388,19 +388,15 @@ __device__ __forceinline__ float value16_of(uint32_t k) {
     return __uint_as_float(h << 16);
 }
 
-// Sum over the threads above t (t' > t), for every t.
-template <typename T>
-__device__ __forceinline__ T sum_above(T v, T* lds) {
+// Sum over the threads above t (t' > t), for every t: within the wave the
+// wave total less a DPP inclusive prefix sum, then the waves above.
+__device__ __forceinline__ double sum_above(double v, double* lds) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    T s = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const T n = __shfl_down(s, o, 64);
-        if (lane + o < 64) s += n;
-    }
-    if (lane == 0) lds[w] = s;
+    const double incl = wave_inclusive_scan(v);
+    const double tot = lane63(incl);
+    if (lane == 0) lds[w] = tot;
     __syncthreads();
-    T above = s - v;
+    double above = tot - incl;
     for (int q = w + 1; q < kFW; ++q) above += lds[q];
     __syncthreads();
     return above;
