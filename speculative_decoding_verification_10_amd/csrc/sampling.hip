@@ -11,7 +11,10 @@
 //          {l >= v} holds at least top_p of the survivors' mass.
 //
 // One workgroup of 1,024 threads per row.  The row is read from HBM once;
-// the later passes over it mostly hit the L2 / Infinity Cache.  Per row:
+// the later passes over it mostly hit the L2 / Infinity Cache.  Rows of
+// whole 16-byte vectors take window paths (bins over 16-bit keys for bf16,
+// over the mass exponent for fp32; each is described where it is defined).
+// Other rows (misaligned or of a ragged length) take the general selection:
 //   1. the row max m and the offset M = fp32(m * c) of the verify step;
 //   2. coarse levels of d = M - x * c (the base-2 exponent deficit of the
 //      mass exp2(x * c - M)): level 0 holds d < 1, level j d < 2^j, level 8
