@@ -35,12 +35,14 @@
  *   - Workspace: device memory of at least the size the matching
  *     *_workspace_bytes() function returns, 256-byte aligned.  The first 4
  *     bytes hold error bits: a call ORs in a bit when an internal bounded
- *     wait gives up (never in a correct run); specdec_workspace_init clears
- *     them.  Every call sets each other scratch word it reads earlier in the
- *     same call, so a workspace needs no initialisation beyond a clear error
- *     word, may hold anything else, and may be shared by calls of different
- *     entry points and shapes that do not run concurrently.  Calls that may
- *     run concurrently need distinct workspaces.
+ *     wait gives up, which a correct run on an unshared GPU never does (the
+ *     affected outputs are then marked invalid); specdec_workspace_errors
+ *     reads them, specdec_workspace_init clears them.  Every call sets each
+ *     other scratch word it reads earlier in the same call, so a workspace
+ *     needs no initialisation beyond a clear error word, may hold anything
+ *     else, and may be shared by calls of different entry points and shapes
+ *     that do not run concurrently.  Calls that may run concurrently need
+ *     distinct workspaces.
  *   - Preconditions not checked on the fast path (a violation gives
  *     unspecified tokens, never an out-of-bounds access): logits finite or
  *     -inf (-inf = probability 0; a row may not be all -inf); 0 <=
@@ -80,6 +82,20 @@ const char *specdec_version(void);
 
 /* Zero-fill `bytes` of workspace on `stream` (asynchronous); clears the error bits. */
 int specdec_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/*
+ * The error word of a workspace: the bits that calls on it OR in when one of
+ * their bounded in-kernel waits gives up (bit 0: the final draw of the
+ * stochastic verify step, whose affected requests then read num_accepted = -1
+ * and out_tokens = -1 throughout).  Copies the word to errors[0] (4 bytes of
+ * DEVICE memory, owned by the caller) on `stream`, after every call enqueued
+ * before it on that stream, and clears it in the same atomic step when
+ * `clear` is non-zero.  Asynchronous like every call: errors[0] is valid once
+ * the stream has reached it.  A call on a workspace also used on another
+ * stream sees that stream's calls only as ordered by the caller.
+ * SPECDEC_EINVAL for a NULL or misaligned workspace or a NULL errors.
+ */
+int specdec_workspace_errors(void *workspace, uint32_t *errors, int clear, void *stream);
 
 /*
  * Row statistics of the temperature softmax ("3.5 Speculative Decoding",

@@ -6,8 +6,8 @@ seeded synthetic workloads used by the tests and the benchmark.
 """
 from ._lib import (SpecdecError, Workspace, acceptance_counts, choose_k, load,  # noqa: F401
                    ngram_propose, sampling_floors, softmax_stats, tree_mask, tree_verify_greedy, verify,
-                   verify_greedy, version)
+                   verify_greedy, version, workspace_errors)
 
 __all__ = ["SpecdecError", "Workspace", "acceptance_counts", "choose_k", "load", "ngram_propose",
            "sampling_floors", "softmax_stats", "tree_mask", "tree_verify_greedy", "verify", "verify_greedy",
-           "version"]
+           "version", "workspace_errors"]

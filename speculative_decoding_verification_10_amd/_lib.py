@@ -56,6 +56,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.specdec_version.restype = ctypes.c_char_p
         lib.specdec_workspace_init.argtypes = [vp, sz, vp]
         lib.specdec_workspace_init.restype = ci
+        lib.specdec_workspace_errors.argtypes = [vp, vp, ci, vp]
+        lib.specdec_workspace_errors.restype = ci
         lib.specdec_softmax_stats_workspace_bytes.argtypes = [i64, i32, ci]
         lib.specdec_softmax_stats_workspace_bytes.restype = sz
         lib.specdec_softmax_stats.argtypes = [vp, ci, i64, i32, f32, vp, vp, vp, sz, vp]
@@ -158,6 +160,23 @@ class Workspace:
 
     def ptr(self) -> int:
         return self.tensor.data_ptr()
+
+
+def workspace_errors(ws: Workspace, clear: bool = True) -> int:
+    """The workspace's error word (specdec_workspace_errors), read after
+    every call enqueued on the current stream; cleared when ``clear``.
+    Synchronises with that stream to return the value."""
+    out = torch.empty((1,), dtype=torch.int32, device=ws.device)
+    rc = load().specdec_workspace_errors(ws.ptr(), out.data_ptr(), int(bool(clear)), _stream(ws.device))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_workspace_errors")
+    return int(out.item()) & 0xFFFFFFFF
+
+
+def cached_workspaces():
+    """The workspaces this module allocated for calls made without one, keyed
+    by (device index, stream, entry point)."""
+    return dict(_workspaces)
 
 
 def _workspace(nbytes: int, device: torch.device, ws: Optional[Workspace], kind: str) -> Workspace:

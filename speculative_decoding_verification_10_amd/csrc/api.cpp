@@ -54,12 +54,13 @@ bool make_scale(float temperature, Scale* s) {
 }
 
 struct VerifyLayout {
-    size_t err, slot_m, slot_s, slot_l, slot_slab, dec, floors, total;
+    size_t err, slot_m, slot_s, slot_l, slot_slab, slot_tile, dec, floors, total;
 };
 
 // Header (error bits), self-validating slots -- tile max / tile sum of every
 // row slot of every request, the logit at the draft token of every row, the
-// slab sums of every request's final row -- and each request's decision.
+// slab sums and per-tile sums of every request's final row -- and each
+// request's decision.
 VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, bool one_hot,
                            bool processed = false) {
     int NV, NVv;
@@ -76,6 +77,7 @@ VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, 
     L.slot_s = off;    off = align_up(off + parts * sizeof(uint64_t));
     L.slot_l = off;    off = align_up(off + (size_t)B * R * sizeof(uint32_t));
     L.slot_slab = off; off = align_up(off + (size_t)B * C * kSlabsPerTile * sizeof(uint64_t));
+    L.slot_tile = off; off = align_up(off + (size_t)B * C * sizeof(uint64_t));
     L.dec = off;       off = align_up(off + (size_t)B * sizeof(Decision));
     L.floors = off;    if (processed) off = align_up(off + (size_t)B * R * sizeof(float));
     L.total = off;
@@ -151,6 +153,12 @@ int specdec_workspace_init(void* workspace, size_t bytes, void* stream) {
     if (workspace == nullptr && bytes != 0) return SPECDEC_EINVAL;
     if (bytes == 0) return SPECDEC_OK;
     return map_launch(hipMemsetAsync(workspace, 0, bytes, (hipStream_t)stream));
+}
+
+int specdec_workspace_errors(void* workspace, uint32_t* errors, int clear, void* stream) {
+    if (!workspace || !errors || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SPECDEC_EINVAL;
+    return map_launch(launch_workspace_errors(static_cast<uint32_t*>(workspace), errors, clear,
+                                              (hipStream_t)stream));
 }
 
 size_t specdec_softmax_stats_workspace_bytes(int64_t rows, int32_t V, specdec_dtype_t dtype) {
@@ -244,6 +252,7 @@ int specdec_verify_timed(const void* target_logits, const void* draft_logits, sp
     p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);
     p.slot_l = reinterpret_cast<uint32_t*>(ws + L.slot_l);
     p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
+    p.slot_tile = reinterpret_cast<uint64_t*>(ws + L.slot_tile);
     p.dec = reinterpret_cast<Decision*>(ws + L.dec);
     return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream,
                                     reinterpret_cast<hipEvent_t const*>(events)));
@@ -312,6 +321,7 @@ int specdec_verify_processed_timed(const void* target_logits, const void* draft_
     p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);
     p.slot_l = reinterpret_cast<uint32_t*>(ws + L.slot_l);
     p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
+    p.slot_tile = reinterpret_cast<uint64_t*>(ws + L.slot_tile);
     p.dec = reinterpret_cast<Decision*>(ws + L.dec);
     p.floors = reinterpret_cast<float*>(ws + L.floors);
     FloorParams f{};
@@ -334,6 +344,7 @@ int specdec_verify_processed_timed(const void* target_logits, const void* draft_
     f.slot_s = p.slot_s;
     f.slot_l = p.slot_l;
     f.slot_slab = p.slot_slab;
+    f.slot_tile = p.slot_tile;
     return map_launch(launch_verify_processed(f, p, dtype, vec, (hipStream_t)stream,
                                               reinterpret_cast<hipEvent_t const*>(events)));
 }

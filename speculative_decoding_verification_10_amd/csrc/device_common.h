@@ -137,7 +137,10 @@ __device__ __forceinline__ float load_one(const void* row, int t) {
 
 template <int E>
 __device__ __forceinline__ float pairwise_sum(const float (&v)[E]) {
-    if constexpr (E == 4) {
+    static_assert(E == 2 || E == 4 || E == 8, "pairwise_sum: 2, 4 or 8 terms");
+    if constexpr (E == 2) {
+        return __fadd_rn(v[0], v[1]);
+    } else if constexpr (E == 4) {
         return __fadd_rn(__fadd_rn(v[0], v[1]), __fadd_rn(v[2], v[3]));
     } else {
         return __fadd_rn(__fadd_rn(__fadd_rn(v[0], v[1]), __fadd_rn(v[2], v[3])),
@@ -199,6 +202,12 @@ __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp<kDppRowHalfMirror>(v, -INFINITY));
     return fmaxf(v, dpp<kDppRowMirror>(v, -INFINITY));
 }
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<kDppQuad1032>(v, 0.0f);
+    v += dpp<kDppQuad2301>(v, 0.0f);
+    v += dpp<kDppRowHalfMirror>(v, 0.0f);
+    return v + dpp<kDppRowMirror>(v, 0.0f);
+}
 __device__ __forceinline__ double row16_sum(double v) {
     v += dpp<kDppQuad1032>(v, 0.0);
     v += dpp<kDppQuad2301>(v, 0.0);
@@ -211,6 +220,12 @@ __device__ __forceinline__ float wave_max(float v) {
     v = row16_max(v);
     v = fmaxf(v, dpp<kDppRowBcast15, 0xA>(v, -INFINITY));
     v = fmaxf(v, dpp<kDppRowBcast31, 0xC>(v, -INFINITY));
+    return lane63(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    v += dpp<kDppRowBcast15, 0xA>(v, 0.0f);
+    v += dpp<kDppRowBcast31, 0xC>(v, 0.0f);
     return lane63(v);
 }
 __device__ __forceinline__ double wave_sum(double v) {

@@ -27,10 +27,12 @@ struct Decision {
     int32_t j;        // position of the first rejection (k_b if none)
     int32_t mode;     // FinalMode
     int32_t tok;      // rejected draft token (one-hot residual), else -1
+    int32_t pad;
     float Mp;         // offset fp32(max * c) of target row j
     float Mq;         // offset of draft row j (residual with draft logits)
-    float rho;        // Z_p / Z_q of row j (residual with draft logits)
-    int32_t pad0, pad1;
+    double rho;       // Z_p / Z_q of row pair j from the row statistics (residual with draft logits)
+    double zq;        // Z_q, the draft row's sum relative to Mq
+    double K0;        // ln(rho) + ln 2 (Mp - Mq): rho e_q / e_p = exp(K0 + (l_q - l_p) / T)
 };
 
 struct VerifyParams {
@@ -53,7 +55,10 @@ struct VerifyParams {
     uint32_t* slot_m;           // [B * R * C] tile max (self-validating)
     uint64_t* slot_s;           // [B * R * C] tile sum (self-validating)
     uint32_t* slot_l;           // [B * R] logit at the draft token of each row (self-validating)
-    uint64_t* slot_slab;        // [B * C * kSlabsPerTile] slab sums of the final draw (self-validating)
+    uint64_t* slot_slab;        // [B * C * kSlabsPerTile] slab sums of the final draw: the masses
+                                // and, for a replacement with draft logits, their q part (self-validating)
+    uint64_t* slot_tile;        // [B * C] per final tile: signed replacement sum and near-tie q mass
+                                // (self-validating)
     Decision* dec;              // [B] decision of each request
     const float* floors;        // [B * R] processed-row floors, or null (plain rows)
 };
@@ -95,6 +100,7 @@ struct FloorParams {
     uint64_t* slot_s;
     uint32_t* slot_l;
     uint64_t* slot_slab;
+    uint64_t* slot_tile;
 };
 
 // Ancestor masks and depths of flattened draft trees.
@@ -139,6 +145,8 @@ struct NgramParams {
 
 hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s,
                          hipEvent_t const* events = nullptr);
+// Copy the workspace error word at err to out[0], clearing it when clear.
+hipError_t launch_workspace_errors(uint32_t* err, uint32_t* out, int clear, hipStream_t s);
 // events: null, or three events (each may be null) taken by the dispatches:
 // the row kernel's start and end, and the end of the call's last kernel.
 hipError_t launch_greedy(const GreedyParams& p, int dtype, bool vec, hipStream_t s,

@@ -1192,7 +1192,8 @@ __device__ __forceinline__ RowSlot row_slot(const FloorParams& a) {
 
 // The floor; for the verify step the processed row's slots: tile 0 holds
 // the row max and the kept mass, the other tiles are empty; the logit at
-// the draft token (-inf when cut); row 0 empties the request's slab slots.
+// the draft token (-inf when cut); row 0 empties the request's slab and
+// final-tile slots.
 template <int DT>
 __device__ void write_outputs(const FloorParams& a, const RowSlot& s, float m, float fl, double z) {
     const int t = threadIdx.x;
@@ -1209,9 +1210,11 @@ __device__ void write_outputs(const FloorParams& a, const RowSlot& s, float m, f
         const float l = load_one<DT>(s.row, x);
         slot_put(a.slot_l + rs, enc_f32(l >= fl ? l : -INFINITY));
     }
-    if (s.rr == 0)
+    if (s.rr == 0) {
         for (int c = t; c < C * kSlabsPerTile; c += kFT)
             slot_put(a.slot_slab + (size_t)s.b * C * kSlabsPerTile + c, (uint64_t)0);
+        for (int c = t; c < C; c += kFT) slot_put(a.slot_tile + (size_t)s.b * C + c, (uint64_t)0);
+    }
 }
 
 template <int DT, bool VEC>

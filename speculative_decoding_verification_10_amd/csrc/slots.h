@@ -13,9 +13,10 @@
 // Waiting is safe because a consumer only waits for workgroups with a lower
 // index in the same grid: the hardware dispatches those no later than the
 // consumer, and they never wait themselves, so they finish.  A poll gives up
-// after kWaitTicks (far beyond any legitimate wait), raises an error bit in
-// the workspace header and continues with a harmless value, so every wave
-// always exits.
+// only after kWaitTicks (far beyond any legitimate wait) have passed AND one
+// more read still finds the slot empty; it then raises an error bit in the
+// workspace header, tells its caller (which marks the affected outputs
+// invalid) and continues with a harmless value, so every wave always exits.
 //
 // A slot must read zero before its producer runs: an earlier kernel of the
 // same call empties it.
@@ -39,6 +40,14 @@ __device__ __forceinline__ uint64_t enc_f64(double d) {
 }
 __device__ __forceinline__ double dec_f64(uint64_t u) { return __longlong_as_double((long long)~u); }
 
+// Two floats in one self-validating 64-bit slot: each half is enc_f32 of its
+// value, so the word is never zero once written.
+__device__ __forceinline__ uint64_t enc_f32x2(float hi, float lo) {
+    return ((uint64_t)enc_f32(hi) << 32) | (uint64_t)enc_f32(lo);
+}
+__device__ __forceinline__ float dec_hi(uint64_t u) { return dec_f32((uint32_t)(u >> 32)); }
+__device__ __forceinline__ float dec_lo(uint64_t u) { return dec_f32((uint32_t)u); }
+
 __device__ __forceinline__ void slot_put(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -53,25 +62,29 @@ __device__ __forceinline__ uint64_t slot_peek(const uint64_t* p) {
 }
 
 // Finish a poll that began with a value v already loaded from p: poll until
-// the slot is written; on time-out flag the error and return `fallback`.
+// the slot is written.  The deadline is checked only after a read that still
+// found the slot empty, so a wave that was descheduled past the deadline
+// reads once more before it gives up.  On giving up: flag the error word, set
+// `lost` and return `fallback`.
 template <typename T>
-__device__ __forceinline__ T settle(const T* p, T v, uint32_t* err, T fallback) {
+__device__ __forceinline__ T settle(const T* p, T v, uint32_t* err, T fallback, bool& lost) {
     if (v != 0) return v;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (v == 0) {
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-            atomicOr(err, 1u);
-            return fallback;
-        }
+    for (;;) {
         __builtin_amdgcn_s_sleep(2);
         v = slot_peek(p);
+        if (v != 0) return v;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            atomicOr(err, 1u);
+            lost = true;
+            return fallback;
+        }
     }
-    return v;
 }
 
 template <typename T>
-__device__ __forceinline__ T slot_wait(const T* p, uint32_t* err, T fallback) {
-    return settle(p, slot_peek(p), err, fallback);
+__device__ __forceinline__ T slot_wait(const T* p, uint32_t* err, T fallback, bool& lost) {
+    return settle(p, slot_peek(p), err, fallback, lost);
 }
 
 }  // namespace specdec

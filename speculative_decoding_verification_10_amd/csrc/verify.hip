@@ -22,14 +22,19 @@
 //                 instead taken once per request by verify_decide, launched
 //                 before it.
 //
-// Only the search waits inside a kernel, on the slab slots of its own
-// request's other tiles (self-validating, slots.h); everything else reads
-// what earlier kernels wrote.
+// Only the search waits inside a kernel, on the slab and tile slots of its
+// own request's other tiles (self-validating, slots.h); everything else
+// reads what earlier kernels wrote.
 //
 // Masses are kept unnormalised: the replacement is Z_p * max(0, p - q) =
-// max(0, e_p - (Z_p/Z_q) e_q) with e = exp2(x * c - M) against each row's
-// offset M, the bonus is e_p.  An inverse CDF only needs the masses up to a
-// common factor.
+// max(0, e_p - rho e_q) with e = exp2(x * c - M) against each row's offset M
+// and rho = Z_p / Z_q, the bonus is e_p.  An inverse CDF only needs the
+// masses up to a common factor.  Where p and q nearly agree (a good drafter:
+// "Speculative Decoding from First Principles", "What the numbers say") the
+// replacement is a small difference of two large numbers, so it is formed
+// without cancellation (-e_p expm1(z) from the exact logit difference) and
+// rho, known from the row statistics only to ~1e-7, is refined inside the
+// final pass from the signed sum of the replacement (see search_wave).
 #include <hip/hip_ext.h>
 
 #include "internal.h"
@@ -65,9 +70,10 @@ struct StepShared {
     double z[kMaxRows];                 // row sum relative to offset_of(max)
     float ratio[kMaxK];
     unsigned long long rej[kWaves];
-    float red_f[kWaves];
-    double red_d[kWaves];
-    double slab[kSlabsPerTile];
+    float red_f[kWaves];                // per wave: near-tie q mass of the tile
+    double red_d[kWaves];               // per wave: signed replacement sum of the tile
+    double slab[kSlabsPerTile];         // slab sums of the masses
+    float slabq[kSlabsPerTile];         // slab sums of the q part (replacement with draft logits)
 };
 
 // k_b, clamped to [0, K] so that a bad value can never address memory
@@ -76,10 +82,68 @@ __device__ __forceinline__ int kb_of(const VerifyParams& a, int b) {
     return a.kpr ? min(max(a.kpr[b], 0), a.K) : a.K;
 }
 
-// Unnormalised final-draw masses of one vector.
+// expm1(z) for |z| < 1: z times a degree-8 polynomial in z, a weighted
+// least-squares fit of expm1(z)/z on [-1, 1] (relative error 1e-8 in exact
+// arithmetic, 1.2e-7 evaluated in fp32 by Horner's rule).
+__device__ __forceinline__ float expm1_unit(float z) {
+    float p = 2.7556084205571096e-06f;
+    p = __fmaf_rn(z, p, 2.542029324104078e-05f);
+    p = __fmaf_rn(z, p, 1.9848310330417007e-04f);
+    p = __fmaf_rn(z, p, 1.3884315267205238e-03f);
+    p = __fmaf_rn(z, p, 8.333275094628334e-03f);
+    p = __fmaf_rn(z, p, 4.166679084300995e-02f);
+    p = __fmaf_rn(z, p, 0.1666666865348816f);
+    p = __fmaf_rn(z, p, 0.5f);
+    p = __fmaf_rn(z, p, 1.0f);
+    return __fmul_rn(z, p);
+}
+
+// |z| below which a token's replacement sign may flip between the ratio the
+// tiles use and the refined one (|delta rho| / rho is checked against half
+// of it in the search).
+constexpr float kNearTie = 1.9073486328125e-06f;   // 2^-19
+
+// Constants of the replacement with draft logits at one ratio rho:
+// a = e_p - rho e_q = -e_p expm1(z), z = K0 + (x_q - x_p) / T.
+struct ResConst {
+    float Mp, Mq;
+    float rho;          // rho rounded to fp32 (direct difference)
+    double K0;          // ln(rho) + ln 2 (Mp - Mq)
+    double invT;        // 1 / T
+};
+
+__device__ __forceinline__ ResConst res_const(const Decision& d, const Scale& sc, double rho, double K0) {
+    ResConst k;
+    k.Mp = d.Mp;
+    k.Mq = d.Mq;
+    k.rho = (float)rho;
+    k.K0 = K0;
+    k.invT = sc.c * 0.69314718055994530942;
+    return k;
+}
+
+// Signed replacement a = e_p - rho e_q of one token, relative to Z_p.  Where
+// |z| < 1 (p and q within a factor e) it is -e_p expm1(z) with z formed in
+// fp64 from the exact logit difference, so it keeps the relative accuracy
+// of e_p however closely p and q agree; elsewhere the direct difference
+// loses at most a factor (1 + e) / (e - 1).  -inf logits give e = 0 and
+// z = +-inf or NaN, which take the direct branch: a = -rho e_q, e_p or 0.
+__device__ __forceinline__ float residual_signed(float xp, float xq, const ResConst& k, const Scale& sc,
+                                                 float& eq, float& az) {
+    const float ep = fast_exp2(exponent2(xp, k.Mp, sc));
+    eq = fast_exp2(exponent2(xq, k.Mq, sc));
+    const float z = (float)__fma_rn((double)xq - (double)xp, k.invT, k.K0);
+    az = fabsf(z);
+    return (az < 1.0f) ? -__fmul_rn(ep, expm1_unit(z)) : __fmaf_rn(-k.rho, eq, ep);
+}
+
+// Final-draw masses (>= 0, relative to Z_p) of one vector: the replacement
+// max(0, e_p - rho e_q) at the constants k, p without the rejected token
+// (one-hot drafts), or the bonus e_p.
 template <int DT>
 __device__ __forceinline__ void final_masses(const u32x4& rp, const u32x4& rq, const Decision& d,
-                                             int v, const Scale& sc, float (&r)[Elem<DT>::E]) {
+                                             const ResConst& k, int v, const Scale& sc,
+                                             float (&r)[Elem<DT>::E]) {
     constexpr int E = Elem<DT>::E;
     float xp[E];
     decode<DT>(rp, xp);
@@ -88,9 +152,8 @@ __device__ __forceinline__ void final_masses(const u32x4& rp, const u32x4& rq, c
         decode<DT>(rq, xq);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const float ep = fast_exp2(exponent2(xp[e], d.Mp, sc));
-            const float eq = fast_exp2(exponent2(xq[e], d.Mq, sc));
-            r[e] = fmaxf(__fsub_rn(ep, __fmul_rn(d.rho, eq)), 0.0f);
+            float eq, az;
+            r[e] = fmaxf(residual_signed(xp[e], xq[e], k, sc, eq, az), 0.0f);
         }
     } else {
 #pragma unroll
@@ -266,10 +329,12 @@ __device__ Decision decide(const VerifyParams& a, int b, int kb, StepShared& sh)
     Decision d;
     d.j = j;
     d.tok = -1;
+    d.pad = 0;
     d.Mp = offset_of(sh.m[j], a.sc);
     d.Mq = 0.0f;
-    d.rho = 0.0f;
-    d.pad0 = d.pad1 = 0;
+    d.rho = 0.0;
+    d.zq = 0.0;
+    d.K0 = 0.0;
     if (j == kb) {
         d.mode = kBonus;
     } else if (one_hot) {
@@ -278,7 +343,9 @@ __device__ Decision decide(const VerifyParams& a, int b, int kb, StepShared& sh)
     } else {
         d.mode = kResidual;
         d.Mq = offset_of(sh.m[K + 1 + j], a.sc);
-        d.rho = (float)(sh.z[j] / sh.z[K + 1 + j]);
+        d.zq = sh.z[K + 1 + j];
+        d.rho = sh.z[j] / d.zq;
+        d.K0 = log(d.rho) + 0.69314718055994530942 * ((double)d.Mp - (double)d.Mq);
     }
     return d;
 }
@@ -312,29 +379,94 @@ __device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* 
         slot_put(a.slot_s + idx, enc_f64(z));
         slot_put(a.slot_m + idx, enc_f32(m));
     }
-    // Row 0 (always read) empties the tile's slab slots for the final kernel.
+    // Row 0 (always read) empties the tile's slab and tile slots for the
+    // final kernel.
     if (rr == 0 && threadIdx.x < kSlabsPerTile)
         slot_put(a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile + threadIdx.x, (uint64_t)0);
+    if (rr == 0 && threadIdx.x == kSlabsPerTile) slot_put(a.slot_tile + (size_t)b * a.C + tile, (uint64_t)0);
 }
 
 // Slab sums of one tile: slab u * kWaves + w of the tile holds the 64
 // vectors that wave w loaded in unroll step u, summed by that wave; the
-// tile's first nslabs sums (the slabs that start inside the row) leave in
-// one batch of stores.
+// tile's first nslabs slots (the slabs that start inside the row) leave in
+// one batch of stores, each holding the slab's mass and, for a replacement
+// with draft logits, its q part sum_{a > 0} e_q.  The tile's own slot holds
+// the signed replacement sum sum_t (e_p - rho e_q) over the tile and the q
+// mass of its near-ties (|z| <= 2^-19), for the search's refinement of rho.
 template <int DT>
 __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], const u32x4 (&rq)[kUnroll],
-                          const Decision& d, int v0, uint64_t* slabs_of_tile, int nslabs, StepShared& sh) {
+                          const Decision& d, int v0, int b, int tile, int nslabs, StepShared& sh) {
     constexpr int E = Elem<DT>::E;
     const int w = threadIdx.x >> 6;
+    const bool lead = (threadIdx.x & 63) == 0;
+    if (d.mode == kResidual) {
+        const ResConst k = res_const(d, a.sc, d.rho, d.K0);
+        double dsum = 0.0;
+        float xsum = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        float r[E];
-        final_masses<DT>(rp[u], rq[u], d, v0 + u * kThreads, a.sc, r);
-        const double t = wave_sum((double)pairwise_sum<E>(r));
-        if ((threadIdx.x & 63) == 0) sh.slab[u * kWaves + w] = t;
+        for (int u = 0; u < kUnroll; ++u) {
+            // Element by element: the masses and signed values in pairs
+            // (summed pairwise), the q part and near-tie mass as running
+            // sums (they need only ~1e-6 relative accuracy).
+            float xp[E], xq[E], r[E / 2], av[E / 2];
+            decode<DT>(rp[u], xp);
+            decode<DT>(rq[u], xq);
+            float sq = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; e += 2) {
+                float eq0, az0, eq1, az1;
+                const float a0 = residual_signed(xp[e], xq[e], k, a.sc, eq0, az0);
+                const float a1 = residual_signed(xp[e + 1], xq[e + 1], k, a.sc, eq1, az1);
+                r[e / 2] = __fadd_rn(fmaxf(a0, 0.0f), fmaxf(a1, 0.0f));
+                av[e / 2] = __fadd_rn(a0, a1);
+                sq += (a0 > 0.0f ? eq0 : 0.0f) + (a1 > 0.0f ? eq1 : 0.0f);
+                xsum += (az0 <= kNearTie ? eq0 : 0.0f) + (az1 <= kNearTie ? eq1 : 0.0f);
+            }
+            const double ts = wave_sum((double)pairwise_sum<E / 2>(r));
+            const float tq = wave_sum(sq);
+            dsum += (double)pairwise_sum<E / 2>(av);
+            if (lead) {
+                sh.slab[u * kWaves + w] = ts;
+                sh.slabq[u * kWaves + w] = tq;
+            }
+        }
+        dsum = wave_sum(dsum);
+        xsum = wave_sum(xsum);
+        if (lead) {
+            sh.red_d[w] = dsum;
+            sh.red_f[w] = xsum;
+        }
+    } else {
+        const ResConst k{};
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float r[E];
+            final_masses<DT>(rp[u], rq[u], d, k, v0 + u * kThreads, a.sc, r);
+            const double t = wave_sum((double)pairwise_sum<E>(r));
+            if (lead) {
+                sh.slab[u * kWaves + w] = t;
+                sh.slabq[u * kWaves + w] = 0.0f;
+            }
+        }
+        if (lead) {
+            sh.red_d[w] = 0.0;
+            sh.red_f[w] = 0.0f;
+        }
     }
     __syncthreads();
-    if (threadIdx.x < nslabs) slot_put(slabs_of_tile + threadIdx.x, enc_f64(sh.slab[threadIdx.x]));
+    uint64_t* slabs = a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile;
+    if (threadIdx.x < nslabs)
+        slot_put(slabs + threadIdx.x, enc_f32x2((float)sh.slab[threadIdx.x], sh.slabq[threadIdx.x]));
+    if (threadIdx.x == 64) {
+        double ds = 0.0;
+        float xs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            ds += sh.red_d[i];
+            xs += sh.red_f[i];
+        }
+        slot_put(a.slot_tile + (size_t)b * a.C + tile, enc_f32x2((float)ds, xs));
+    }
 }
 
 // The accept probabilities of request b.
@@ -377,8 +509,7 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
             apply_floor<DT>(rq[u], fq);
         }
     }
-    put_slabs<DT>(a, rp, rq, d, v0, a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile,
-                  min(kSlabsPerTile, a.NS - tile * kSlabsPerTile), sh);
+    put_slabs<DT>(a, rp, rq, d, v0, b, tile, min(kSlabsPerTile, a.NS - tile * kSlabsPerTile), sh);
     if (tile == 0 && !decided) publish_aprob(a, b, kb, sh);
     // The request's last tile -- dispatched after its other tiles, which
     // never wait -- searches, with its first wave, once every slab sum of
@@ -391,6 +522,19 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
 // Token search of request b, by the first wave of its last final tile (no
 // workgroup barriers; the other waves have left).
 //
+// Refinement (replacement with draft logits).  The tiles used rho0 = Z_p/Z_q
+// of the row statistics, accurate to ~1e-7; near p = q the replacement's
+// total S is a small multiple TV of Z_p, so that error would move C_t / S by
+// ~1e-7 / TV.  The tiles' signed sums give D = sum_t (e_p - rho0 e_q) =
+// Z_p - rho0 Z_q with the relative accuracy of each term, hence the refined
+// rho = rho0 + D / Z_q.  A slab's mass at rho is its mass at rho0 less
+// (rho - rho0) times its q part, except for tokens whose sign flips between
+// the two ratios; those have |z| <= |rho - rho0| / rho, so their error is
+// at most |rho - rho0| times the tiles' near-tie q mass X.  When that bound
+// is not negligible (or rho moved by more than the near-tie band) every
+// slab is recomputed exactly at rho instead.  The slab finally re-read is
+// always evaluated exactly at rho.
+//
 // Slab g covers vectors [64 g, 64 g + 64).  Lane L owns the P = ceil(NS/64)
 // consecutive slabs from L * P: one inclusive scan of the lanes' sums gives S
 // (lane 63) and the lane whose range holds w = u * S; that lane walks its
@@ -400,21 +544,36 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
 // with w < C_t is taken (the last token with mass when rounding leaves w past
 // every C_t).  Only entries with mass can be taken at any level, so a token
 // of zero probability is never drawn, however the sums round.
+//
+// A wait that gives up (slots.h) leaves the request's outputs at -1
+// (num_accepted and every token): a visibly invalid result, never a token
+// drawn from missing sums.
 // ---------------------------------------------------------------------------
 constexpr int kHeld = 16;   // slab sums per lane kept in registers
 
-// Unnormalised mass of slab g of the final row, summed by one lane alone
-// (the fallback draw from p_j when every replacement mass is zero).
+// Bound on the crossing error of the corrected slab sums, relative to S,
+// beyond which the slabs are recomputed exactly.
+constexpr double kCrossingBound = 1e-7;
+
+// Mass of slab g of the final row (pair), summed by one lane alone (the
+// exact recomputation and the fallback draw from p_j).
 template <int DT, bool VEC>
-__device__ double lane_slab_mass(const VerifyParams& a, const void* rowp, const Decision& d, int g, float fp) {
+__device__ double lane_slab_mass(const VerifyParams& a, const void* rowp, const void* rowq, const Decision& d,
+                                 const ResConst& k, int g, float fp, float fq) {
     constexpr int E = Elem<DT>::E;
     double t = 0.0;
-    for (int k = 0; k < kSlab; ++k) {
-        const int v = g * kSlab + k;
+#pragma unroll 1
+    for (int i = 0; i < kSlab; ++i) {
+        const int v = g * kSlab + i;
         u32x4 bp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
         apply_floor<DT>(bp, fp);
+        u32x4 bq = bp;
+        if (rowq) {
+            bq = load_raw<DT, VEC, false>(rowq, a.V, a.NV, v);
+            apply_floor<DT>(bq, fq);
+        }
         float r[E];
-        final_masses<DT>(bp, bp, d, v, a.sc, r);
+        final_masses<DT>(bp, bq, d, k, v, a.sc, r);
         t += (double)pairwise_sum<E>(r);
     }
     return t;
@@ -430,19 +589,43 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     const int P = (NS + 63) >> 6;             // slabs per lane
     const int g0 = lane * P;                  // this lane's first slab
     uint64_t* slabs = a.slot_slab + (size_t)b * a.C * kSlabsPerTile;
+    uint64_t* tiles = a.slot_tile + (size_t)b * a.C;
+    const uint64_t none = enc_f32x2(0.0f, 0.0f);
+    bool lost = false;
 
-    // This lane's slab sums (the first kHeld kept in registers) and their
-    // sum in slab order.
+    // The tiles' signed sums and near-tie masses first (the refinement needs
+    // them before any slab sum can be corrected), then this lane's slab sums;
+    // every slot is waited for on its own.
+    double dsum = 0.0;
+    float xsum = 0.0f;
+    for (int c = lane; c < a.C; c += 64) {
+        const uint64_t t = slot_wait(tiles + c, a.err, none, lost);
+        dsum += (double)dec_hi(t);
+        xsum += dec_lo(t);
+    }
+    dsum = wave_sum(dsum);
+    xsum = wave_sum(xsum);
+
+    // The refined ratio (uniform over the wave).
+    double delta = 0.0;
+    ResConst rk{};
+    if (d.mode == kResidual) {
+        if (d.zq > 0.0 && d.rho > 0.0) delta = dsum / d.zq;
+        if (!(fabs(delta) < d.rho)) delta = 0.0;     // a broken row: keep rho0
+        rk = res_const(d, a.sc, d.rho + delta, d.K0 + log1p(delta / d.rho));
+    }
+    auto corrected = [&](uint64_t word) { return fmax(0.0, (double)dec_hi(word) - delta * (double)dec_lo(word)); };
+
     double held[kHeld];
     double mine = 0.0;
 #pragma unroll
     for (int k = 0; k < kHeld; ++k) {
         held[k] = 0.0;
-        if (k < P && g0 + k < NS) held[k] = dec_f64(slot_wait(slabs + g0 + k, a.err, enc_f64(0.0)));
+        if (k < P && g0 + k < NS) held[k] = corrected(slot_wait(slabs + g0 + k, a.err, none, lost));
         mine += held[k];
     }
     for (int k = kHeld; k < P; ++k)
-        if (g0 + k < NS) mine += dec_f64(slot_wait(slabs + g0 + k, a.err, enc_f64(0.0)));
+        if (g0 + k < NS) mine += corrected(slot_wait(slabs + g0 + k, a.err, none, lost));
 
     const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
@@ -452,27 +635,35 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
 
     double incl = wave_inclusive_scan(mine);
     double total = __shfl(incl, 63, 64);
-    if (!(total > 0.0)) {
-        // Every replacement mass is zero: draw from p_j itself, its slab sums
-        // taking the place of the residual ones (rare; each lane sums its
-        // own slabs).
-        d.mode = kBonus;
-        rowq = nullptr;
-        mine = 0.0;
-#pragma unroll
-        for (int k = 0; k < kHeld; ++k) {
-            held[k] = 0.0;
-            if (k < P && g0 + k < NS) held[k] = lane_slab_mass<DT, VEC>(a, rowp, d, g0 + k, fp);
-            mine += held[k];
+    // Recompute every slab exactly at the refined ratio (exact), or from p_j
+    // itself when every replacement mass is zero (rare; each lane sums its
+    // own slabs).  The sums go back to the slots, rounded as the slots hold
+    // them, and the registers reload from there, so that the walk below reads
+    // the same values.
+    int redo = d.mode == kResidual && (fabs(delta) > 0.5 * (double)kNearTie * d.rho ||
+                                       fabs(delta) * (double)xsum > kCrossingBound * total)
+                   ? 1
+                   : (total > 0.0 ? 0 : 2);
+    while (redo) {
+        if (redo == 2) {
+            d.mode = kBonus;
+            rowq = nullptr;
         }
-        for (int k = kHeld; k < P; ++k)
+        delta = 0.0;
+        mine = 0.0;
+#pragma unroll 1
+        for (int k = 0; k < P; ++k)
             if (g0 + k < NS) {
-                const double t = lane_slab_mass<DT, VEC>(a, rowp, d, g0 + k, fp);
-                slot_put(slabs + g0 + k, enc_f64(t));
-                mine += t;
+                const float t = (float)lane_slab_mass<DT, VEC>(a, rowp, rowq, d, rk, g0 + k, fp, fq);
+                slot_put(slabs + g0 + k, enc_f32x2(t, 0.0f));
+                mine += (double)t;
             }
+#pragma unroll
+        for (int k = 0; k < kHeld; ++k) held[k] = (k < P && g0 + k < NS) ? corrected(slot_peek(slabs + g0 + k)) : 0.0;
         incl = wave_inclusive_scan(mine);
         total = __shfl(incl, 63, 64);
+        // Every exact replacement mass is zero as well: draw from p_j.
+        redo = (redo == 1 && !(total > 0.0)) ? 2 : 0;
     }
     const double w = u * total;
 
@@ -502,7 +693,7 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
 #pragma unroll
         for (int k = 0; k < kHeld; ++k) visit(k, held[k]);
         for (int k = kHeld; k < P; ++k)
-            if (g0 + k < NS) visit(k, dec_f64(slot_peek(slabs + g0 + k)));
+            if (g0 + k < NS) visit(k, corrected(slot_peek(slabs + g0 + k)));
         if (kk < 0) {
             kk = max(klast, 0);
             kbefore = klast_before;
@@ -512,8 +703,10 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     const double base = __shfl(kbefore, L, 64);
     // Every slab sum has been read: empty this lane's slots for the next call.
     for (int k = 0; k < P && g0 + k < NS; ++k) slot_put(slabs + g0 + k, (uint64_t)0);
+    for (int c = lane; c < a.C; c += 64) slot_put(tiles + c, (uint64_t)0);
 
-    // Slab g, one vector per lane in ascending order.
+    // Slab g, one vector per lane in ascending order, exact at the refined
+    // ratio.
     const int v = g * kSlab + lane;
     float r[E];
     {
@@ -523,7 +716,7 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
             apply_floor<DT>(sp, fp);
             apply_floor<DT>(sq, rowq ? fq : fp);
         }
-        final_masses<DT>(sp, sq, d, v, a.sc, r);
+        final_masses<DT>(sp, sq, d, rk, v, a.sc, r);
     }
     const double vs = (double)pairwise_sum<E>(r);
     const double vincl = base + wave_inclusive_scan(vs);
@@ -547,14 +740,17 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     }
     tok = __shfl(tok, L2, 64);
     if (tok < 0) tok = 0;
+    const bool invalid = __ballot(lost) != 0;
     const int j = d.j;
     for (int i = lane; i <= K; i += 64) {
         int32_t o = -1;
-        if (i < j) o = a.tokens[(size_t)b * K + i];
-        else if (i == j) o = tok;
+        if (!invalid) {
+            if (i < j) o = a.tokens[(size_t)b * K + i];
+            else if (i == j) o = tok;
+        }
         a.out[(size_t)b * (K + 1) + i] = o;
     }
-    if (lane == 0) a.nacc[b] = j;
+    if (lane == 0) a.nacc[b] = invalid ? -1 : j;
 }
 
 // Row items: workgroup (x, y, z) takes tile x of row slot y of request z
@@ -630,7 +826,19 @@ hipError_t launch_processed(const FloorParams& f, const VerifyParams& p, hipStre
     return hipGetLastError();
 }
 
+// The workspace error word, copied to the caller and optionally cleared in
+// one atomic step (one thread).
+__global__ void workspace_errors_kernel(uint32_t* err, uint32_t* out, int clear) {
+    out[0] = clear ? atomicExch(err, 0u)
+                   : __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
+
+hipError_t launch_workspace_errors(uint32_t* err, uint32_t* out, int clear, hipStream_t s) {
+    hipLaunchKernelGGL(workspace_errors_kernel, dim3(1), dim3(1), 0, s, err, out, clear);
+    return hipGetLastError();
+}
 
 hipError_t launch_verify(const VerifyParams& p, int dtype, bool vec, hipStream_t s,
                          hipEvent_t const* events) {

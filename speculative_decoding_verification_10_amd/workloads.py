@@ -215,6 +215,52 @@ def make(name: str, set_index: int = 0, B: Optional[int] = None, V: Optional[int
                     k_per_req=k_per_req, meta=meta)
 
 
+def near_drafts(sigma: float, dtype: str = "bf16", B: int = 1024, distinct: int = 32,
+                V: int = 128256, K: int = 1, set_index: int = 0,
+                force_reject: bool = True) -> Workload:
+    """The high-acceptance regime: a draft distribution close to the target
+    one, as a good drafter gives ("Speculative Decoding from First
+    Principles", "What the numbers say": most first drafts accepted).
+
+    `distinct` peaked target row blocks (N(0, 3^2) + 8 on 20 ids per row,
+    the headline recipe, T = 0.8) with draft rows = target + N(0, sigma^2),
+    each block repeated over B / distinct requests; every request draws its
+    own drafted tokens from the stored draft rows (Gumbel-max at T) and its
+    own uniforms.  With force_reject the accept uniforms are 1 - 2^-18, so a
+    draft is rejected whenever p(x)/q(x) < 1 - 2^-18 -- about half of the
+    requests -- while an accepted draft (ratio 1) stays 3.8e-6 away from its
+    threshold; the final uniform sweeps [0, 1) over the requests that share
+    a block.
+    Seed 1008; the stream set is SeedSequence([1008, set_index, round(sigma
+    * 1e6), dtype])."""
+    if B % distinct:
+        raise ValueError("B must be a multiple of distinct")
+    T = 0.8
+    ss = np.random.SeedSequence([1008, set_index, int(round(sigma * 1e6)), 1 if dtype == "bf16" else 0])
+    r_logit, r_noise, r_draft, r_unif = [np.random.Generator(np.random.Philox(s)) for s in ss.spawn(4)]
+    l = _peaked_target(r_logit, distinct, K + 1, V, 3.0, 8.0, min(20, V))
+    d = l[:, :K, :] + r_noise.standard_normal((distinct, K, V)) * sigma
+    t_blk, d_blk = _store(l, dtype), _store(d, dtype)
+    del l, d
+    rep = B // distinct
+    target = np.ascontiguousarray(np.repeat(t_blk, rep, axis=0))
+    draft = np.ascontiguousarray(np.repeat(d_blk, rep, axis=0))
+    dv = stored_as_f32(d_blk)
+    tokens = np.empty((B, K), np.int32)
+    inv_t = 1.0 / T
+    for g in range(distinct):
+        for i in range(K):
+            gum = r_draft.gumbel(size=(rep, V))
+            tokens[g * rep:(g + 1) * rep, i] = np.argmax(dv[g, i].astype(np.float64) * inv_t + gum, axis=-1)
+    uniforms = r_unif.random((B, K + 1), dtype=np.float32)
+    if force_reject:
+        uniforms[:, :K] = np.float32(1.0 - 2.0 ** -18)
+    return Workload(name="near", B=B, K=K, V=V, dtype=dtype, temperature=T, greedy=False,
+                    target=target, draft=draft, draft_tokens=tokens, uniforms=uniforms,
+                    meta={"seed": 1008, "set_index": set_index, "sigma": sigma,
+                          "distinct": distinct})
+
+
 def tiny_steps(n_steps: int, set_index: int = 0) -> Workload:
     """The tiny workload run for many steps: the logits stay fixed and every
     step draws fresh drafts and uniforms.  The steps are laid out as a batch

@@ -308,3 +308,10 @@ def test_sampling_floors_rejects(lib):
     assert lib.specdec_sampling_floors(None, 1, 3, 10, 1.0, 2, 0.9, f, None) == EINVAL
     assert lib.specdec_sampling_floors(f, 1, 3, 10, 1.0, 2, 0.9, None, None) == EINVAL
     assert lib.specdec_sampling_floors(None, 1, 0, 10, 1.0, 2, 0.9, None, None) == OK
+
+
+def test_workspace_errors_rejects(lib):
+    lib.specdec_workspace_errors.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert lib.specdec_workspace_errors(None, FAKE, 1, None) == EINVAL
+    assert lib.specdec_workspace_errors(FAKE, None, 1, None) == EINVAL
+    assert lib.specdec_workspace_errors(ctypes.c_void_p(0x10010), FAKE, 0, None) == EINVAL   # misaligned
