@@ -5,9 +5,10 @@
 
 One step = one specdec_verify call over one batch of the headline workload
 (B=64 requests, k=5 drafts, V=128256, bf16 target and draft logits, T=0.8),
-with inputs already resident in HBM.  The timed steps rotate over several
-device-resident copies of the input set, so that the working set (>= 900 MB)
-exceeds the 256 MB Infinity Cache and every step streams its logits from HBM.
+with inputs already resident in HBM.  The timed steps rotate over five
+distinct seeded input sets (set_index 0..4, each with its own logits, drafts
+and uniforms), so that the working set (>= 900 MB) exceeds the 256 MB
+Infinity Cache and every step streams its logits from HBM.
 
 Prints one JSON line: verified positions/s (sum over requests of k_b + 1 per
 step), the algorithmic HBM bytes per step and their rate against the MI355X
@@ -33,7 +34,9 @@ NGRAM_N_MIN, NGRAM_N_MAX = 1, 4     # suffix lengths the n-gram workload's draft
 METRIC = "verified positions/s + HBM GB/s (% of peak), B=64 k=5 V=128256 bf16"
 PROFILE_COUNTERS = {"headline": os.path.join(ROOT, "profiles", "verify_headline_counters.txt"),
                     "greedy": os.path.join(ROOT, "profiles", "verify_greedy_counters.txt")}
-KERNEL_SOURCES = ["device_common.h", "internal.h", "slots.h", "verify.hip", "greedy.hip"]
+# Every source whose change can change a kernel or its launch geometry.
+KERNEL_SOURCES = ["device_common.h", "internal.h", "slots.h", "verify.hip", "greedy.hip", "sampling.hip",
+                  "api.cpp"]
 
 
 def kernel_digest() -> str:
@@ -134,7 +137,35 @@ def cpu_baseline(wl, name: str, budget_s: float, ngram=None, parents=None, proce
             break
     return {"value": pos / el, "unit": "verified positions/s", "cores": cores, "kind": "oracle",
             "sample": "%d full steps of the %s workload (%d verified positions) in %.1f s"
-                      % (n, name, pos, el)}
+                      % (n, name, pos, el),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first /proc/cpuinfo entry), and the core
+    count the OS reports."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return "%s (%d logical cores visible)" % (name, os.cpu_count() or 0)
+
+
+def default_sets(workload: str) -> int:
+    """Input sets to rotate over: enough distinct seeded sets that one
+    rotation's logits (>= ~1 GB) exceed the 256 MB Infinity Cache, at most 5;
+    one for the workloads whose single step is already larger."""
+    per_set_mb = {"tiny": 0.04, "peaked": 4.6, "headline": 180.6, "greedy": 311.2, "ngram": 311.2,
+                  "tree": 361.2, "ragged": 3110.0}
+    mb = per_set_mb.get(workload, 200.0)
+    if mb >= 1000.0:
+        return 1
+    return 5 if mb < 50.0 else max(2, min(5, int(-(-1000.0 // mb))))
 
 
 def main():
@@ -142,7 +173,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sets", type=int, default=5, help="device-resident input copies to rotate over")
+    ap.add_argument("--sets", type=int, default=None,
+                    help="distinct seeded input sets (set_index 0..N-1), device-resident, rotated over "
+                         "(default: enough for ~1 GB of logits per rotation, at most 5)")
+    ap.add_argument("--phase-every", type=int, default=1,
+                    help="take the kernels' own events on every N-th timed step only (the others run "
+                         "the plain entry point, and the step before each sampled one records its "
+                         "end-of-call event alone as a fence).  Default 1: every step, which matches "
+                         "rocprofv3's kernel durations; sparser sampling leaves the events' cost "
+                         "(~1.5 us per step) out of the step time but reads the row kernel ~1 us long. "
+                         "Use a value coprime with the set count so that the samples visit every set.")
     ap.add_argument("--workload", default="headline",
                     help="headline (default), tiny, peaked, greedy, ragged, ngram (the n-gram "
                          "drafter over copy-heavy contexts, then the greedy verify of its drafts), "
@@ -187,17 +227,29 @@ def main():
     # the greedy verify of its drafts against the greedy workload's logits.
     ngram = args.workload == "ngram"
     tree = args.workload == "tree"
-    parents_h = None
+    nsets = args.sets if args.sets is not None else default_sets(args.workload)
+    nsets = max(1, nsets)
+
+    def make_set(r):
+        if tree:
+            # Node i's token is "draft position" i; row i + 1 follows node i.
+            tw = workloads.tree(set_index=r)
+            w = workloads.Workload("tree", tw.B, tw.N, tw.V, tw.dtype, 1.0, True, tw.target, None,
+                                   tw.node_tokens, np.zeros((tw.B, tw.N + 1), np.float32),
+                                   meta=dict(tw.meta))
+            w.meta["parents"] = tw.parents
+            return w
+        return workloads.make("greedy" if ngram else args.workload, set_index=r)
+
+    # Distinct seeded input sets (set_index 0..nsets-1), generated on the host
+    # in parallel, then made device-resident.
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(nsets, 5)) as pool:
+        hosts = list(pool.map(make_set, range(nsets)))
+    wl = hosts[0]
+    parents_h = wl.meta.get("parents") if tree else None
     if tree:
-        # Node i's token is "draft position" i; row i + 1 follows node i.
-        tw = workloads.tree()
-        parents_h = tw.parents
-        wl = workloads.Workload("tree", tw.B, tw.N, tw.V, tw.dtype, 1.0, True, tw.target, None,
-                                tw.node_tokens, np.zeros((tw.B, tw.N + 1), np.float32),
-                                meta=dict(tw.meta))
         parents_d = torch.from_numpy(parents_h).to(dev)
-    else:
-        wl = workloads.make("greedy" if ngram else args.workload)
     K = wl.K
     ngram_host = None
     if ngram:
@@ -205,40 +257,39 @@ def main():
         ngram_host = (ctx_h, lens_h, NGRAM_N_MIN, NGRAM_N_MAX)
         ctx_d = torch.from_numpy(ctx_h).to(dev)
         lens_d = torch.from_numpy(lens_h).to(dev)
-    sets = []
-    base = {
-        "target": dev_logits(wl.target, dev),
-        "draft": None if wl.draft is None else dev_logits(wl.draft, dev),
-    }
-    for r in range(max(1, args.sets)):
-        sets.append({
-            "target": base["target"] if r == 0 else base["target"].clone(),
-            "draft": None if base["draft"] is None else (base["draft"] if r == 0 else base["draft"].clone()),
-        })
-    tokens = torch.from_numpy(wl.draft_tokens).to(dev)
-    unif = torch.from_numpy(wl.uniforms).to(dev)
-    kpr = None if wl.k_per_req is None else torch.from_numpy(wl.k_per_req).to(dev)
-    if ngram:                      # the drafter writes these every step
-        tokens = torch.zeros_like(tokens)
-        kpr = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
-    out = (torch.empty((wl.B, K + 1), dtype=torch.int32, device=dev),
-           torch.empty((wl.B,), dtype=torch.int32, device=dev), None)
     greedy = wl.greedy
     code = 1 if wl.dtype == "bf16" else 0
     processed = (args.top_k is not None or args.top_p is not None) and not greedy
     top_k = int(args.top_k or 0)
     top_p = float(1.0 if args.top_p is None else args.top_p)
-    if processed and wl.draft is not None:
-        # The drafts are drawn from the processed draft rows (the q that
-        # drew them), the rows cut at the library's own floors.
-        fl = sd.sampling_floors(base["draft"], wl.temperature, top_k, top_p).cpu().numpy()
-        dv = workloads.stored_as_f32(wl.draft)
-        rng = np.random.default_rng(2024)
-        for b in range(wl.B):
-            for i in range(wl.k_of(b)):
-                row = np.where(dv[b, i] >= fl[b, i], dv[b, i], np.float32(-np.inf))
-                wl.draft_tokens[b, i] = workloads.gumbel_draw(row[None], wl.temperature, rng)[0]
-        tokens.copy_(torch.from_numpy(wl.draft_tokens).to(dev))
+    sets = []
+    for h in hosts:
+        st = {"wl": h, "target": dev_logits(h.target, dev),
+              "draft": None if h.draft is None else dev_logits(h.draft, dev)}
+        if processed and h.draft is not None:
+            # The drafts are drawn from the processed draft rows (the q that
+            # drew them), the rows cut at the library's own floors.
+            fl = sd.sampling_floors(st["draft"], h.temperature, top_k, top_p).cpu().numpy()
+            dv = workloads.stored_as_f32(h.draft)
+            rng = np.random.default_rng(2024 + h.meta.get("set_index", 0))
+            for b in range(h.B):
+                for i in range(h.k_of(b)):
+                    row = np.where(dv[b, i] >= fl[b, i], dv[b, i], np.float32(-np.inf))
+                    h.draft_tokens[b, i] = workloads.gumbel_draw(row[None], h.temperature, rng)[0]
+        if ngram:                  # the drafter writes these every step (shared)
+            st["tokens"] = torch.zeros((h.B, K), dtype=torch.int32, device=dev)
+            st["kpr"] = torch.zeros((h.B,), dtype=torch.int32, device=dev)
+        else:
+            st["tokens"] = torch.from_numpy(h.draft_tokens).to(dev)
+            st["kpr"] = None if h.k_per_req is None else torch.from_numpy(h.k_per_req).to(dev)
+        st["unif"] = torch.from_numpy(h.uniforms).to(dev)
+        sets.append(st)
+    if ngram:
+        for st in sets[1:]:
+            st["tokens"], st["kpr"] = sets[0]["tokens"], sets[0]["kpr"]
+    tokens, kpr = sets[0]["tokens"], sets[0]["kpr"]
+    out = (torch.empty((wl.B, K + 1), dtype=torch.int32, device=dev),
+           torch.empty((wl.B,), dtype=torch.int32, device=dev), None)
     if processed:
         nbytes = int(sd._lib.load().specdec_verify_processed_workspace_bytes(wl.B, K, wl.V, code,
                                                                              int(wl.draft is None)))
@@ -265,29 +316,30 @@ def main():
     ptr = lambda t: None if t is None else t.data_ptr()
     cargs = []
     for st in sets:
+        t_, u_, k_ = st["tokens"], st["unif"], st["kpr"]
         if tree:
-            cargs.append((st["target"].data_ptr(), code, tokens.data_ptr(), parents_d.data_ptr(), None,
+            cargs.append((st["target"].data_ptr(), code, t_.data_ptr(), parents_d.data_ptr(), None,
                           wl.B, K, wl.V, out[0].data_ptr(), None, out[1].data_ptr(), ws.ptr(),
                           ws.nbytes, stream.cuda_stream))
         elif greedy:
-            cargs.append((st["target"].data_ptr(), code, tokens.data_ptr(), ptr(kpr), wl.B, K, wl.V,
+            cargs.append((st["target"].data_ptr(), code, t_.data_ptr(), ptr(k_), wl.B, K, wl.V,
                           out[0].data_ptr(), out[1].data_ptr(), None, ws.ptr(), ws.nbytes,
                           stream.cuda_stream))
         elif processed:
-            cargs.append((st["target"].data_ptr(), ptr(st["draft"]), code, tokens.data_ptr(), ptr(kpr),
-                          unif.data_ptr(), float(wl.temperature), top_k, top_p, wl.B, K, wl.V,
+            cargs.append((st["target"].data_ptr(), ptr(st["draft"]), code, t_.data_ptr(), ptr(k_),
+                          u_.data_ptr(), float(wl.temperature), top_k, top_p, wl.B, K, wl.V,
                           out[0].data_ptr(), out[1].data_ptr(), None, ws.ptr(), ws.nbytes,
                           stream.cuda_stream))
         else:
-            cargs.append((st["target"].data_ptr(), ptr(st["draft"]), code, tokens.data_ptr(), ptr(kpr),
-                          unif.data_ptr(), float(wl.temperature), wl.B, K, wl.V, out[0].data_ptr(),
+            cargs.append((st["target"].data_ptr(), ptr(st["draft"]), code, t_.data_ptr(), ptr(k_),
+                          u_.data_ptr(), float(wl.temperature), wl.B, K, wl.V, out[0].data_ptr(),
                           out[1].data_ptr(), None, ws.ptr(), ws.nbytes, stream.cuda_stream))
 
     counters = torch.zeros((3, max(K, 1)), dtype=torch.int64, device=dev) if args.telemetry else None
-    kpr_ptr = ptr(kpr)
 
-    def step(r):
+    def step(r, handle=None):
         a = cargs[r % len(cargs)]
+        st = sets[r % len(sets)]
         if ngram:
             rc = lib.specdec_ngram_propose(ctx_d.data_ptr(), lens_d.data_ptr(), wl.B, ctx_d.shape[1],
                                            NGRAM_N_MIN, NGRAM_N_MAX, K, tokens.data_ptr(), kpr.data_ptr(),
@@ -302,10 +354,10 @@ def main():
             fn, fn_timed = lib.specdec_verify_processed, lib.specdec_verify_processed_timed
         else:
             fn, fn_timed = lib.specdec_verify, lib.specdec_verify_timed
-        rc = fn_timed(*a, handles[r]) if handles is not None else fn(*a)
+        rc = fn_timed(*a, handle) if handle is not None else fn(*a)
         if rc == 0 and counters is not None:
-            rc = lib.specdec_acceptance_counts(out[1].data_ptr(), kpr_ptr, wl.B, K, counters.data_ptr(),
-                                               stream.cuda_stream)
+            rc = lib.specdec_acceptance_counts(out[1].data_ptr(), ptr(st["kpr"]), wl.B, K,
+                                               counters.data_ptr(), stream.cuda_stream)
         if rc != 0:
             raise sd.SpecdecError(rc, "bench step")
 
@@ -314,15 +366,24 @@ def main():
         if ngram:
             sd.ngram_propose(ctx_d, lens_d, NGRAM_N_MIN, NGRAM_N_MAX, K, out=(tokens, kpr))
         if tree:
-            sd.tree_verify_greedy(st["target"], tokens, parents_d, workspace=ws, out=out)
+            sd.tree_verify_greedy(st["target"], st["tokens"], parents_d, workspace=ws, out=out)
         elif greedy:
-            sd.verify_greedy(st["target"], tokens, k_per_req=kpr, workspace=ws, out=out)
+            sd.verify_greedy(st["target"], st["tokens"], k_per_req=st["kpr"], workspace=ws, out=out)
         else:
-            sd.verify(st["target"], st["draft"], tokens, unif, wl.temperature, k_per_req=kpr,
-                      workspace=ws, out=out, top_k=args.top_k if processed else None,
+            sd.verify(st["target"], st["draft"], st["tokens"], st["unif"], wl.temperature,
+                      k_per_req=st["kpr"], workspace=ws, out=out, top_k=args.top_k if processed else None,
                       top_p=args.top_p if processed else None)
 
-    checked_step(0)
+    # Each set once through the checked binding: its accepted counts give its
+    # rejected requests and so its algorithmic bytes.
+    set_nacc = []
+    for r in range(len(sets)):
+        checked_step(r)
+        torch.cuda.synchronize()
+        set_nacc.append(out[1].cpu().numpy().copy())
+    if ngram:                      # the step's drafted positions come from the drafter
+        for st in sets:
+            st["wl"].k_per_req = kpr.cpu().numpy()
     graphs = None
     if args.graph:
         # Captured through the binding, which launches on the capture stream.
@@ -336,37 +397,47 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
 
-    def run(r):
+    def run(r, handle=None):
         if graphs is not None:
             graphs[r % len(graphs)].replay()
         else:
-            step(r)
+            step(r, handle)
 
     for r in range(args.warmup):
         run(r)
     torch.cuda.synchronize()
-    nacc = out[1].cpu().numpy()
-    if ngram:                      # the step's drafted positions come from the drafter
-        wl.k_per_req = kpr.cpu().numpy()
+    nacc = set_nacc[0]
 
+    # The kernels' own events (or, with --no-phase-events / --graph, stream
+    # events around the call) are taken on every phase_every-th timed step
+    # only: recording them costs the GPU several microseconds between kernels,
+    # which the other steps -- and so the wall-clock figure -- do not pay.
+    # A sampled step's start event is only exact when the step before it
+    # also took an event at its end (otherwise it also counts the previous
+    # kernel's tail), so that step records its end-of-call event alone.
+    every = max(1, args.phase_every)
+    sampled = [r for r in range(args.steps) if r % every == every - 1]
+    fences = [r - 1 for r in sampled if r >= 1 and (r - 1) not in sampled]
     if phase:
         nev = 3
-        phase_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-        for evs in phase_ev:          # torch creates an event at its first record
-            for e in evs:
-                e.record(stream)
-        handles = [(ctypes.c_void_p * nev)(*[e.cuda_event for e in evs]) for evs in phase_ev]
+        phase_ev = {r: [torch.cuda.Event(enable_timing=True) for _ in range(nev)] for r in sampled}
+        fence_ev = {r: torch.cuda.Event(enable_timing=True) for r in fences}
+        for e in list(fence_ev.values()) + [e for evs in phase_ev.values() for e in evs]:
+            e.record(stream)              # torch creates an event at its first record
+        handles = {r: (ctypes.c_void_p * nev)(*[e.cuda_event for e in evs]) for r, evs in phase_ev.items()}
+        handles.update({r: (ctypes.c_void_p * nev)(None, None, e.cuda_event) for r, e in fence_ev.items()})
         starts = ends = None
     else:
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        handles = {}
+        starts = {r: torch.cuda.Event(enable_timing=True) for r in sampled}
+        ends = {r: torch.cuda.Event(enable_timing=True) for r in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in range(args.steps):
-        if starts is not None:
+        if starts is not None and r in starts:
             starts[r].record(stream)
-        run(r)
-        if ends is not None:
+        run(r, handles.get(r))
+        if ends is not None and r in ends:
             ends[r].record(stream)
     host = time.perf_counter() - t0       # time to enqueue the steps
     torch.cuda.synchronize()
@@ -374,23 +445,35 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     rows_ms = None
     if phase:
-        rows_ms = float(np.median([e[0].elapsed_time(e[1]) for e in phase_ev]))
-        call_ms = float(np.median([e[0].elapsed_time(e[-1]) for e in phase_ev]))
+        rows_ms = float(np.median([e[0].elapsed_time(e[1]) for e in phase_ev.values()]))
+        call_ms = float(np.median([e[0].elapsed_time(e[-1]) for e in phase_ev.values()]))
         per_launch_ms = call_ms
     else:
-        per_launch_ms = float(np.median([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+        per_launch_ms = float(np.median([starts[r].elapsed_time(ends[r]) for r in sampled]))
 
-    positions = wl.verified_positions()
-    # Stored counter figures belong to the unprocessed step's kernels.
-    counters_key = args.workload + ("-processed" if processed else "")
-    alg = algorithmic_bytes(wl, nacc)
+    # Per set: verified positions and algorithmic bytes; the timed steps
+    # visit set r % nsets.
+    set_pos = [st["wl"].verified_positions() for st in sets]
+    set_alg = [algorithmic_bytes(st["wl"], set_nacc[i]) for i, st in enumerate(sets)]
+    set_rows = [row_pass_bytes(st["wl"]) for st in sets]
     if tree:
-        alg += wl.B * K * 4                   # the parent links
+        set_alg = [a + wl.B * K * 4 for a in set_alg]      # the parent links
     drafter = None
     if ngram:
         # The drafter reads every context token once and writes the drafts.
         dbytes = int(np.sum(lens_h.astype(np.int64))) * 4 + wl.B * 4 + wl.B * (K + 1) * 4
-        alg += dbytes
+        set_alg = [a + dbytes for a in set_alg]
+    visits = [r % len(sets) for r in range(args.steps)]
+    positions_total = sum(set_pos[i] for i in visits)
+    alg_total = sum(set_alg[i] for i in visits)
+    positions = positions_total / args.steps
+    alg = alg_total / args.steps
+    sampled_sets = [r % len(sets) for r in sampled]
+    alg_sampled = float(np.mean([set_alg[i] for i in sampled_sets]))
+    rows_sampled = float(np.mean([set_rows[i] for i in sampled_sets]))
+    # Stored counter figures belong to the unprocessed step's kernels.
+    counters_key = args.workload + ("-processed" if processed else "")
+    if ngram:
         n_dr = 200
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -407,13 +490,13 @@ def main():
                    "timing": "%d back-to-back calls between two stream events" % n_dr,
                    "drafted_requests": int(np.count_nonzero(wl.k_per_req)),
                    "n_min": NGRAM_N_MIN, "n_max": NGRAM_N_MAX}
-    value = positions / (ms_per_step * 1e-3)
-    gbps = alg / (ms_per_step * 1e-3) / 1e9
-    achieved = alg / (per_launch_ms * 1e-3) / 1e9
+    value = positions_total / wall
+    gbps = alg_total / wall / 1e9
+    achieved = alg_sampled / (per_launch_ms * 1e-3) / 1e9
     if phase:
         # The dominant kernel: the pass over the rows (all of the greedy
         # path's bytes, ~85% of the stochastic path's).
-        rb = row_pass_bytes(wl)
+        rb = int(round(rows_sampled))
         rows_gbps = rb / (rows_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(rows_gbps, 1), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(rows_gbps / PEAK_HBM_GBPS, 4),
@@ -422,9 +505,10 @@ def main():
                     "kernel": ("greedy_rows" if greedy else "floor_rows" if processed else "verify_rows"),
                     "algorithmic_bytes": rb,
                     "launch_ms": round(rows_ms, 5)}
-        call = {"achieved": round(alg / (call_ms * 1e-3) / 1e9, 1),
-                "frac": round(alg / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                "traffic": read_counters(counters_key, "hbm_bytes_per_launch"), "algorithmic_bytes": alg,
+        call = {"achieved": round(alg_sampled / (call_ms * 1e-3) / 1e9, 1),
+                "frac": round(alg_sampled / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                "traffic": read_counters(counters_key, "hbm_bytes_per_launch"),
+                "algorithmic_bytes": int(round(alg_sampled)),
                 "launch_ms": round(call_ms, 5),
                 "kernels": ("greedy_rows, tree_decisions" if tree else
                             "greedy_rows, greedy_decisions" if greedy else
@@ -437,7 +521,7 @@ def main():
                                              else "hbm_bytes_per_launch"),
                     "kernel": ("greedy_rows" if greedy else
                                "specdec_verify call (verify_rows, [verify_decide,] verify_final)"),
-                    "algorithmic_bytes": alg, "launch_ms": round(per_launch_ms, 5)}
+                    "algorithmic_bytes": int(round(alg_sampled)), "launch_ms": round(per_launch_ms, 5)}
         call = None
     if processed:
         metric = ("verified positions/s + HBM GB/s (%% of peak), %s B=%d k=%d V=%d %s, top-k %d, top-p %g"
@@ -462,7 +546,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded; inputs resident in HBM, %d rotating copies)" % len(sets),
+        "data": ("synthetic (seeded; inputs resident in HBM; %d distinct input sets, set_index 0..%d, "
+                 "rotated)" % (len(sets), len(sets) - 1)),
         "config": {"workload": ("tree verify B=%d nodes=%d (branching %s) V=%d %s"
                                 % (wl.B, K, ",".join(map(str, wl.meta["branching"])), wl.V, wl.dtype)
                                 if tree else
@@ -474,15 +559,27 @@ def main():
                    "graph_replay": bool(args.graph)},
         "hbm_gbps": round(gbps, 1),
         "hbm_pct_peak": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
-        "algorithmic_bytes_per_step": alg,
+        "algorithmic_bytes_per_step": int(round(alg)),
+        "verified_positions_per_step": round(positions, 2),
+        "bytes_per_verified_position": {
+            "algorithmic": round(alg / positions, 1),
+            "counters": (None if (call or roofline).get("traffic") is None else
+                         round((call or roofline)["traffic"] / set_pos[0], 1)),
+            "note": "counters: rocprofv3 FETCH_SIZE + WRITE_SIZE of one call on input set 0, scaled "
+                    "by the copy calibration, per verified position"},
         "rejected_requests": (None if tree else
-                              int(np.sum(nacc < (wl.K if wl.k_per_req is None else wl.k_per_req)))),
+                              [int(np.sum(n_ < (st["wl"].K if st["wl"].k_per_req is None
+                                                else st["wl"].k_per_req)))
+                               for n_, st in zip(set_nacc, sets)]),
+        "phase_events": {"every": every, "sampled_steps": len(sampled),
+                         "fence_steps": len(fences) if phase else 0},
         "roofline": roofline,
         "cpu_baseline": None,
     }
     if call is not None:
         line["call_roofline"] = call
     if tree:
+        nacc = set_nacc[0]
         line["tree"] = {"accepted_path_lengths": np.bincount(nacc, minlength=4).tolist(),
                         "mean_accepted": round(float(np.mean(nacc)), 4)}
     if drafter is not None:

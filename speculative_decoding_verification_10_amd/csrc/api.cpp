@@ -50,6 +50,7 @@ bool make_scale(float temperature, Scale* s) {
     s->hi = hi;
     s->lo = lo;
     s->c = c;
+    s->inv_t = 1.0 / (double)temperature;
     return true;
 }
 

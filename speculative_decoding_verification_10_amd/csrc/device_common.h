@@ -40,9 +40,10 @@ template <> struct Elem<kFP32> { static constexpr int E = 4; static constexpr in
 template <> struct Elem<kBF16> { static constexpr int E = 8; static constexpr int S = 2; };
 
 struct Scale {
-    float hi;   // largest float strictly below log2(e)/T
-    float lo;   // log2(e)/T - hi, rounded to float (> 0)
-    double c;   // log2(e)/T in double
+    float hi;       // largest float strictly below log2(e)/T
+    float lo;       // log2(e)/T - hi, rounded to float (> 0)
+    double c;       // log2(e)/T in double
+    double inv_t;   // 1/T in double
 };
 
 // The reference offset of a max m: M = fp32(m * c).

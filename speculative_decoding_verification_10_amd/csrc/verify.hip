@@ -70,7 +70,7 @@ struct StepShared {
     double z[kMaxRows];                 // row sum relative to offset_of(max)
     float ratio[kMaxK];
     unsigned long long rej[kWaves];
-    float red_f[kWaves];                // per wave: near-tie q mass of the tile
+    float red_f[kWaves];                // per wave: near-tie p mass of the tile
     double red_d[kWaves];               // per wave: signed replacement sum of the tile
     double slab[kSlabsPerTile];         // slab sums of the masses
     float slabq[kSlabsPerTile];         // slab sums of the q part (replacement with draft logits)
@@ -98,9 +98,9 @@ __device__ __forceinline__ float expm1_unit(float z) {
     return __fmul_rn(z, p);
 }
 
-// |z| below which a token's replacement sign may flip between the ratio the
-// tiles use and the refined one (|delta rho| / rho is checked against half
-// of it in the search).
+// |a| / e_p (~|z|) below which a token's replacement sign may flip between
+// the ratio the tiles use and the refined one (|delta rho| / rho is checked
+// against half of it in the search).
 constexpr float kNearTie = 1.9073486328125e-06f;   // 2^-19
 
 // Constants of the replacement with draft logits at one ratio rho:
@@ -109,16 +109,14 @@ struct ResConst {
     float Mp, Mq;
     float rho;          // rho rounded to fp32 (direct difference)
     double K0;          // ln(rho) + ln 2 (Mp - Mq)
-    double invT;        // 1 / T
 };
 
-__device__ __forceinline__ ResConst res_const(const Decision& d, const Scale& sc, double rho, double K0) {
+__device__ __forceinline__ ResConst res_const(const Decision& d, double rho, double K0) {
     ResConst k;
     k.Mp = d.Mp;
     k.Mq = d.Mq;
     k.rho = (float)rho;
     k.K0 = K0;
-    k.invT = sc.c * 0.69314718055994530942;
     return k;
 }
 
@@ -128,13 +126,24 @@ __device__ __forceinline__ ResConst res_const(const Decision& d, const Scale& sc
 // of e_p however closely p and q agree; elsewhere the direct difference
 // loses at most a factor (1 + e) / (e - 1).  -inf logits give e = 0 and
 // z = +-inf or NaN, which take the direct branch: a = -rho e_q, e_p or 0.
+// Also returns e_q, and in xv the token's e_p when it is a near-tie
+// (|a| <= 2^-19 e_p, i.e. |z| <= ~2^-19), else 0.
+__device__ __forceinline__ float residual_exact(float xp, float xq, float ep, float eq, const ResConst& k,
+                                                const Scale& sc, float& xv) {
+    const float z = (float)__fma_rn((double)xq - (double)xp, sc.inv_t, k.K0);
+    // Both forms are evaluated and one is selected (no branch per token).
+    const float near = -__fmul_rn(ep, expm1_unit(z));
+    const float far = __fmaf_rn(-k.rho, eq, ep);
+    const bool in = fabsf(z) < 1.0f;
+    xv = (in && fabsf(near) <= kNearTie * ep) ? ep : 0.0f;
+    return in ? near : far;
+}
+
 __device__ __forceinline__ float residual_signed(float xp, float xq, const ResConst& k, const Scale& sc,
-                                                 float& eq, float& az) {
+                                                 float& eq, float& xv) {
     const float ep = fast_exp2(exponent2(xp, k.Mp, sc));
     eq = fast_exp2(exponent2(xq, k.Mq, sc));
-    const float z = (float)__fma_rn((double)xq - (double)xp, k.invT, k.K0);
-    az = fabsf(z);
-    return (az < 1.0f) ? -__fmul_rn(ep, expm1_unit(z)) : __fmaf_rn(-k.rho, eq, ep);
+    return residual_exact(xp, xq, ep, eq, k, sc, xv);
 }
 
 // Final-draw masses (>= 0, relative to Z_p) of one vector: the replacement
@@ -152,8 +161,8 @@ __device__ __forceinline__ void final_masses(const u32x4& rp, const u32x4& rq, c
         decode<DT>(rq, xq);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            float eq, az;
-            r[e] = fmaxf(residual_signed(xp[e], xq[e], k, sc, eq, az), 0.0f);
+            float eq, xv;
+            r[e] = fmaxf(residual_signed(xp[e], xq[e], k, sc, eq, xv), 0.0f);
         }
     } else {
 #pragma unroll
@@ -386,13 +395,106 @@ __device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* 
     if (rr == 0 && threadIdx.x == kSlabsPerTile) slot_put(a.slot_tile + (size_t)b * a.C + tile, (uint64_t)0);
 }
 
+// A slab's replacement terms (the 512 tokens one wave holds for one unroll
+// step) are formed by the direct difference e_p - rho e_q when the slab's
+// own cancellation is mild -- sum e_p at most kCheapRatio times sum |a|,
+// i.e. p and q differ over the slab by a total variation of at least ~1/8
+// -- where its rounding (~1e-7 of e_p + rho e_q per token, random in sign)
+// moves C_t / S by under 1e-7; otherwise the wave re-forms the slab's terms
+// in the cancellation-free form (residual_exact) from the same
+// exponentials.  Rows with low acceptance, which reject often, take the
+// direct form almost everywhere; rows where p and q nearly agree, which
+// rarely reject, take both.
+constexpr float kCheapRatio = 4.0f;
+
+// The direct difference of one token; returns a and sets e_p, e_q.
+__device__ __forceinline__ float residual_direct(float xp, float xq, const ResConst& k, const Scale& sc,
+                                                 float& ep, float& eq) {
+    ep = fast_exp2(exponent2(xp, k.Mp, sc));
+    eq = fast_exp2(exponent2(xq, k.Mq, sc));
+    return __fmaf_rn(-k.rho, eq, ep);
+}
+
+// The tile's replacement terms: per slab its mass and q part into LDS, per
+// wave the signed sum and the near-tie p mass.
+template <int DT>
+__device__ __forceinline__ void residual_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll],
+                                               const u32x4 (&rq)[kUnroll], const ResConst& k, StepShared& sh) {
+    constexpr int E = Elem<DT>::E;
+    const int w = threadIdx.x >> 6;
+    const bool lead = (threadIdx.x & 63) == 0;
+    double dsum = 0.0;
+    float xsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        float ep[E], eq[E], av[E];
+        float cp = 0.0f, ca = 0.0f;
+        {
+            float xp[E], xq[E];
+            decode<DT>(rp[u], xp);
+            decode<DT>(rq[u], xq);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                av[e] = residual_direct(xp[e], xq[e], k, a.sc, ep[e], eq[e]);
+                cp += ep[e];
+                ca += fabsf(av[e]);
+            }
+        }
+        float xv[E];
+        cp = wave_sum(cp);
+        ca = wave_sum(ca);
+        if (!(cp <= kCheapRatio * ca)) {
+            // Strong cancellation in this slab (uniform over the wave): the
+            // logits are decoded again rather than kept alive.
+            u32x4 vp = rp[u], vq = rq[u];
+            asm volatile("" : "+v"(vp), "+v"(vq));
+            float xp[E], xq[E];
+            decode<DT>(vp, xp);
+            decode<DT>(vq, xq);
+#pragma unroll
+            for (int e = 0; e < E; ++e) av[e] = residual_exact(xp[e], xq[e], ep[e], eq[e], k, a.sc, xv[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) xv[e] = fabsf(av[e]) <= kNearTie * ep[e] ? ep[e] : 0.0f;
+        }
+        // The masses and signed values summed pairwise, the q part and
+        // near-tie mass as running sums (they need only ~1e-6 relative
+        // accuracy).
+        float r[E];
+        float sq = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            r[e] = fmaxf(av[e], 0.0f);
+            sq += av[e] > 0.0f ? eq[e] : 0.0f;
+            xsum += xv[e];
+        }
+        const double ts = wave_sum((double)pairwise_sum<E>(r));
+        const float tq = wave_sum(sq);
+        dsum += (double)pairwise_sum<E>(av);
+        if (lead) {
+            sh.slab[u * kWaves + w] = ts;
+            sh.slabq[u * kWaves + w] = tq;
+        }
+        // One vector at a time: the scheduler may not interleave the vectors
+        // (their temporaries would not fit the registers of the occupancy
+        // every final item needs to be resident at once).
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    dsum = wave_sum(dsum);
+    xsum = wave_sum(xsum);
+    if (lead) {
+        sh.red_d[w] = dsum;
+        sh.red_f[w] = xsum;
+    }
+}
+
 // Slab sums of one tile: slab u * kWaves + w of the tile holds the 64
 // vectors that wave w loaded in unroll step u, summed by that wave; the
 // tile's first nslabs slots (the slabs that start inside the row) leave in
 // one batch of stores, each holding the slab's mass and, for a replacement
 // with draft logits, its q part sum_{a > 0} e_q.  The tile's own slot holds
-// the signed replacement sum sum_t (e_p - rho e_q) over the tile and the q
-// mass of its near-ties (|z| <= 2^-19), for the search's refinement of rho.
+// the signed replacement sum sum_t (e_p - rho e_q) over the tile and the p
+// mass of its near-ties (|z| <= ~2^-19), for the search's refinement of rho.
 template <int DT>
 __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], const u32x4 (&rq)[kUnroll],
                           const Decision& d, int v0, int b, int tile, int nslabs, StepShared& sh) {
@@ -400,42 +502,7 @@ __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], con
     const int w = threadIdx.x >> 6;
     const bool lead = (threadIdx.x & 63) == 0;
     if (d.mode == kResidual) {
-        const ResConst k = res_const(d, a.sc, d.rho, d.K0);
-        double dsum = 0.0;
-        float xsum = 0.0f;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            // Element by element: the masses and signed values in pairs
-            // (summed pairwise), the q part and near-tie mass as running
-            // sums (they need only ~1e-6 relative accuracy).
-            float xp[E], xq[E], r[E / 2], av[E / 2];
-            decode<DT>(rp[u], xp);
-            decode<DT>(rq[u], xq);
-            float sq = 0.0f;
-#pragma unroll
-            for (int e = 0; e < E; e += 2) {
-                float eq0, az0, eq1, az1;
-                const float a0 = residual_signed(xp[e], xq[e], k, a.sc, eq0, az0);
-                const float a1 = residual_signed(xp[e + 1], xq[e + 1], k, a.sc, eq1, az1);
-                r[e / 2] = __fadd_rn(fmaxf(a0, 0.0f), fmaxf(a1, 0.0f));
-                av[e / 2] = __fadd_rn(a0, a1);
-                sq += (a0 > 0.0f ? eq0 : 0.0f) + (a1 > 0.0f ? eq1 : 0.0f);
-                xsum += (az0 <= kNearTie ? eq0 : 0.0f) + (az1 <= kNearTie ? eq1 : 0.0f);
-            }
-            const double ts = wave_sum((double)pairwise_sum<E / 2>(r));
-            const float tq = wave_sum(sq);
-            dsum += (double)pairwise_sum<E / 2>(av);
-            if (lead) {
-                sh.slab[u * kWaves + w] = ts;
-                sh.slabq[u * kWaves + w] = tq;
-            }
-        }
-        dsum = wave_sum(dsum);
-        xsum = wave_sum(xsum);
-        if (lead) {
-            sh.red_d[w] = dsum;
-            sh.red_f[w] = xsum;
-        }
+        residual_slabs<DT>(a, rp, rq, res_const(d, d.rho, d.K0), sh);
     } else {
         const ResConst k{};
 #pragma unroll
@@ -481,6 +548,19 @@ constexpr int kSearchLanes = 64;
 template <int DT, bool VEC, bool FL>
 __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d);
 
+// The decision is the same in every lane: keep it in scalar registers.
+__device__ __forceinline__ Decision to_scalar(const Decision& d) {
+    static_assert(sizeof(Decision) % 4 == 0, "Decision is a whole number of words");
+    constexpr int W = sizeof(Decision) / 4;
+    uint32_t w[W];
+    __builtin_memcpy(w, &d, sizeof(Decision));
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+    Decision r;
+    __builtin_memcpy(&r, w, sizeof(Decision));
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // Final item: tile `tile` of the final row (pair) of request b.
 // ---------------------------------------------------------------------------
@@ -489,7 +569,7 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
     const int kb = kb_of(a, b);
-    const Decision d = decided ? a.dec[b] : decide(a, b, kb, sh);
+    const Decision d = to_scalar(decided ? a.dec[b] : decide(a, b, kb, sh));
     const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;
     const int v0 = tile * kTileVec + threadIdx.x;
@@ -500,9 +580,9 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
         rp[u] = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
         rq[u] = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : neg_inf_raw<DT>();
     }
+    float fp, fq;
+    final_floors<FL>(a, b, d, fp, fq);
     if constexpr (FL) {
-        float fp, fq;
-        final_floors<FL>(a, b, d, fp, fq);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             apply_floor<DT>(rp[u], fp);
@@ -530,7 +610,8 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
 // rho = rho0 + D / Z_q.  A slab's mass at rho is its mass at rho0 less
 // (rho - rho0) times its q part, except for tokens whose sign flips between
 // the two ratios; those have |z| <= |rho - rho0| / rho, so their error is
-// at most |rho - rho0| times the tiles' near-tie q mass X.  When that bound
+// at most |rho - rho0| / rho times the tiles' near-tie p mass X (e_p and
+// rho e_q agree to 1e-6 there).  When that bound
 // is not negligible (or rho moved by more than the near-tie band) every
 // slab is recomputed exactly at rho instead.  The slab finally re-read is
 // always evaluated exactly at rho.
@@ -549,7 +630,7 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
 // (num_accepted and every token): a visibly invalid result, never a token
 // drawn from missing sums.
 // ---------------------------------------------------------------------------
-constexpr int kHeld = 16;   // slab sums per lane kept in registers
+constexpr int kHeld = 8;    // slab sums per lane kept in registers
 
 // Bound on the crossing error of the corrected slab sums, relative to S,
 // beyond which the slabs are recomputed exactly.
@@ -593,12 +674,46 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     const uint64_t none = enc_f32x2(0.0f, 0.0f);
     bool lost = false;
 
-    // The tiles' signed sums and near-tie masses first (the refinement needs
-    // them before any slab sum can be corrected), then this lane's slab sums;
-    // every slot is waited for on its own.
-    double dsum = 0.0;
-    float xsum = 0.0f;
-    for (int c = lane; c < a.C; c += 64) {
+    // Every slot this lane reads goes out in one batch of loads (its first
+    // tile word and its first kHeld slab words); then each poll is finished.
+    // The tiles' signed sums and near-tie masses come first: the refinement
+    // needs them before any slab sum can be corrected.
+    uint64_t tw = lane < a.C ? slot_peek(tiles + lane) : none;
+    uint64_t hw[kHeld];
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) hw[k] = (k < P && g0 + k < NS) ? slot_peek(slabs + g0 + k) : none;
+    {
+        // While any of these words is still empty: sleep, then reload every
+        // empty one in one batch (one round trip per round, not per word).
+        // The deadline is checked only after a reload that still found one
+        // empty (slots.h).
+        auto missing = [&]() {
+            bool m = tw == 0;
+#pragma unroll
+            for (int k = 0; k < kHeld; ++k) m |= hw[k] == 0;
+            return m;
+        };
+        uint64_t t0 = 0;
+        while (missing()) {
+            if (t0 == 0) t0 = __builtin_amdgcn_s_memrealtime();
+            __builtin_amdgcn_s_sleep(2);
+            if (tw == 0) tw = slot_peek(tiles + lane);
+#pragma unroll
+            for (int k = 0; k < kHeld; ++k)
+                if (hw[k] == 0) hw[k] = slot_peek(slabs + g0 + k);
+            if (missing() && __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+                atomicOr(a.err, 1u);
+                lost = true;
+                if (tw == 0) tw = none;
+#pragma unroll
+                for (int k = 0; k < kHeld; ++k)
+                    if (hw[k] == 0) hw[k] = none;
+            }
+        }
+    }
+    double dsum = (double)dec_hi(tw);
+    float xsum = dec_lo(tw);
+    for (int c = lane + 64; c < a.C; c += 64) {
         const uint64_t t = slot_wait(tiles + c, a.err, none, lost);
         dsum += (double)dec_hi(t);
         xsum += dec_lo(t);
@@ -612,7 +727,10 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     if (d.mode == kResidual) {
         if (d.zq > 0.0 && d.rho > 0.0) delta = dsum / d.zq;
         if (!(fabs(delta) < d.rho)) delta = 0.0;     // a broken row: keep rho0
-        rk = res_const(d, a.sc, d.rho + delta, d.K0 + log1p(delta / d.rho));
+        // ln(rho / rho0) = log1p(delta / rho0); |delta / rho0| is ~1e-7, where
+        // two terms of the series are exact in fp64.
+        const double e = delta / d.rho;
+        rk = res_const(d, d.rho + delta, d.K0 + (fabs(e) < 1e-4 ? e * (1.0 - 0.5 * e) : log1p(e)));
     }
     auto corrected = [&](uint64_t word) { return fmax(0.0, (double)dec_hi(word) - delta * (double)dec_lo(word)); };
 
@@ -620,8 +738,7 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     double mine = 0.0;
 #pragma unroll
     for (int k = 0; k < kHeld; ++k) {
-        held[k] = 0.0;
-        if (k < P && g0 + k < NS) held[k] = corrected(slot_wait(slabs + g0 + k, a.err, none, lost));
+        held[k] = corrected(hw[k]);
         mine += held[k];
     }
     for (int k = kHeld; k < P; ++k)
@@ -641,7 +758,7 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     // them, and the registers reload from there, so that the walk below reads
     // the same values.
     int redo = d.mode == kResidual && (fabs(delta) > 0.5 * (double)kNearTie * d.rho ||
-                                       fabs(delta) * (double)xsum > kCrossingBound * total)
+                                       fabs(delta / d.rho) * (double)xsum > kCrossingBound * total)
                    ? 1
                    : (total > 0.0 ? 0 : 2);
     while (redo) {
