@@ -71,8 +71,12 @@ typedef enum {
     SPECDEC_EDTYPE = -2,     /* unknown dtype */
     SPECDEC_EWORKSPACE = -3, /* workspace missing, too small or misaligned */
     SPECDEC_ELAUNCH = -4,    /* a kernel launch failed (HIP error) */
-    SPECDEC_EDEVICE = -5     /* no usable gfx950 device */
+    SPECDEC_EDEVICE = -5,    /* no usable gfx950 device */
+    SPECDEC_ESCRATCH = -6    /* too large for the static scratch of specdec_verify_noalloc */
 } specdec_status_t;
+
+/* Size of the static scratch behind specdec_verify_noalloc, per GPU. */
+#define SPECDEC_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 
 /* Human-readable name of a status code (static storage). */
 const char *specdec_status_string(int status);
@@ -143,6 +147,33 @@ int specdec_verify(const void *target_logits, const void *draft_logits, specdec_
                    float temperature, int32_t B, int32_t K, int32_t V,
                    int32_t *out_tokens, int32_t *num_accepted, float *accept_prob,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * specdec_verify for callers that cannot allocate device memory -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc: the same operation, arguments, results and preconditions, with
+ * no workspace argument.  Its scratch is a static array of
+ * SPECDEC_NOALLOC_SCRATCH_BYTES (16 MiB) inside the library, one copy on
+ * every GPU the library runs on, held until the process ends; the call
+ * allocates nothing (its first call on a device only looks the array up).
+ *   - It runs on the current HIP device, which must be the stream's.
+ *   - Calls whose specdec_verify_workspace_bytes() exceeds the scratch
+ *     return SPECDEC_ESCRATCH before anything is launched (at V = 128256
+ *     bf16 with draft logits: up to B = 3,830 requests at K = 5; at
+ *     V = 151936 fp32, K = 8: B = 1,286).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents: calls that may overlap on one GPU (other streams,
+ *     other host threads) race and must be serialised by the caller.
+ *   - The scratch's error word is cleared at the start of every call; a
+ *     request whose bounded in-kernel wait gave up reads num_accepted = -1
+ *     and out_tokens = -1 (specdec_workspace_errors does not apply: the
+ *     scratch is not the caller's).
+ */
+int specdec_verify_noalloc(const void *target_logits, const void *draft_logits,
+                           specdec_dtype_t dtype, const int32_t *draft_tokens,
+                           const int32_t *k_per_req, const float *uniforms, float temperature,
+                           int32_t B, int32_t K, int32_t V, int32_t *out_tokens,
+                           int32_t *num_accepted, float *accept_prob, void *stream);
 
 /*
  * specdec_verify with per-phase timing, for telemetry and benchmarks: the

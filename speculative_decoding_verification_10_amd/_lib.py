@@ -70,6 +70,9 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.specdec_verify_timed.argtypes = [vp, vp, ci, vp, vp, vp, f32, i32, i32, i32,
                                              vp, vp, vp, vp, sz, vp, vp]
         lib.specdec_verify_timed.restype = ci
+        lib.specdec_verify_noalloc.argtypes = [vp, vp, ci, vp, vp, vp, f32, i32, i32, i32,
+                                               vp, vp, vp, vp]
+        lib.specdec_verify_noalloc.restype = ci
         lib.specdec_verify_greedy_workspace_bytes.argtypes = [i32, i32, i32, ci]
         lib.specdec_verify_greedy_workspace_bytes.restype = sz
         lib.specdec_verify_greedy.argtypes = [vp, ci, vp, vp, i32, i32, i32, vp, vp, vp,

@@ -3,6 +3,7 @@
 // here synchronises with the device.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -129,6 +130,87 @@ bool workspace_ok(const void* ws, size_t have, size_t need) {
 
 int map_launch(hipError_t e) { return e == hipSuccess ? SPECDEC_OK : SPECDEC_ELAUNCH; }
 
+// Scratch of the allocation-free entry point (specdec_verify_noalloc): a
+// file-scope device array, one copy per GPU, held until the process ends.
+// In host code its name is only a stand-in; its device address, found once
+// per device with hipGetSymbolAddress, is what the kernels are given.
+constexpr size_t kScratchBytes = SPECDEC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The current device's scratch address (found on the first call on that
+// device, with that device current).
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPECDEC_EDEVICE;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SPECDEC_EDEVICE;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return SPECDEC_OK;
+}
+
+// The stochastic verify step on a caller workspace, or (noalloc) on the
+// library's static scratch.
+int verify_impl(const void* target_logits, const void* draft_logits, specdec_dtype_t dtype,
+                const int32_t* draft_tokens, const int32_t* k_per_req, const float* uniforms,
+                float temperature, int32_t B, int32_t K, int32_t V, int32_t* out_tokens,
+                int32_t* num_accepted, float* accept_prob, void* workspace, size_t workspace_bytes,
+                void* stream, void* const* events, bool noalloc) {
+    if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
+    if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
+    Scale sc;
+    if (!make_scale(temperature, &sc)) return SPECDEC_EINVAL;
+    if (B == 0) return SPECDEC_OK;
+    if (!target_logits || !uniforms || !out_tokens || !num_accepted) return SPECDEC_EINVAL;
+    if (K > 0 && !draft_tokens) return SPECDEC_EINVAL;
+    const bool one_hot = (draft_logits == nullptr);
+    const VerifyLayout L = verify_layout(B, K, V, dtype, one_hot);
+    if (noalloc) {
+        // The library's static scratch instead of a caller workspace.
+        if (L.total > kScratchBytes) return SPECDEC_ESCRATCH;
+        const int st = scratch_on_current_device(&workspace);
+        if (st != SPECDEC_OK) return st;
+        workspace_bytes = kScratchBytes;
+    }
+    if (!workspace_ok(workspace, workspace_bytes, L.total)) return SPECDEC_EWORKSPACE;
+    VerifyParams p{};
+    bool vec;
+    row_geometry(V, dtype, aligned16(target_logits) && aligned16(draft_logits), &p.NV, &vec);
+    p.C = tiles_of(p.NV);
+    p.R = K + 1 + (one_hot ? 0 : K);
+    p.NS = (p.NV + kSlab - 1) / kSlab;
+    p.kinds = one_hot ? 1 : 2;
+    p.clear_err = noalloc ? 1 : 0;
+    // One workgroup per row item and per final item.
+    if ((size_t)B * p.R * p.C > kMaxBlocks || B > kMaxBatch) return SPECDEC_EINVAL;
+    p.target = target_logits;
+    p.draft = draft_logits;
+    p.tokens = draft_tokens;
+    p.kpr = k_per_req;
+    p.unif = uniforms;
+    p.out = out_tokens;
+    p.nacc = num_accepted;
+    p.aprob = accept_prob;
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.sc = sc;
+    char* ws = static_cast<char*>(workspace);
+    p.err = reinterpret_cast<uint32_t*>(ws + L.err);
+    p.slot_m = reinterpret_cast<uint32_t*>(ws + L.slot_m);
+    p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);
+    p.slot_l = reinterpret_cast<uint32_t*>(ws + L.slot_l);
+    p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
+    p.slot_tile = reinterpret_cast<uint64_t*>(ws + L.slot_tile);
+    p.dec = reinterpret_cast<Decision*>(ws + L.dec);
+    return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream,
+                                    reinterpret_cast<hipEvent_t const*>(events)));
+}
 }  // namespace
 }  // namespace specdec
 
@@ -144,6 +226,7 @@ const char* specdec_status_string(int status) {
         case SPECDEC_EWORKSPACE: return "workspace missing, too small or misaligned";
         case SPECDEC_ELAUNCH: return "kernel launch failed";
         case SPECDEC_EDEVICE: return "no usable gfx950 device";
+        case SPECDEC_ESCRATCH: return "call too large for the library's static scratch (specdec_verify_noalloc)";
         default: return "unknown status";
     }
 }
@@ -211,53 +294,25 @@ int specdec_verify(const void* target_logits, const void* draft_logits, specdec_
                                 accept_prob, workspace, workspace_bytes, stream, nullptr);
 }
 
+int specdec_verify_noalloc(const void* target_logits, const void* draft_logits, specdec_dtype_t dtype,
+                           const int32_t* draft_tokens, const int32_t* k_per_req, const float* uniforms,
+                           float temperature, int32_t B, int32_t K, int32_t V, int32_t* out_tokens,
+                           int32_t* num_accepted, float* accept_prob, void* stream) {
+    return verify_impl(target_logits, draft_logits, dtype, draft_tokens, k_per_req, uniforms, temperature,
+                       B, K, V, out_tokens, num_accepted, accept_prob, nullptr, 0, stream, nullptr, true);
+}
+
 int specdec_verify_timed(const void* target_logits, const void* draft_logits, specdec_dtype_t dtype,
                          const int32_t* draft_tokens, const int32_t* k_per_req, const float* uniforms,
                          float temperature, int32_t B, int32_t K, int32_t V, int32_t* out_tokens,
                          int32_t* num_accepted, float* accept_prob, void* workspace,
                          size_t workspace_bytes, void* stream, void* const* events) {
-    if (!dtype_ok(dtype)) return SPECDEC_EDTYPE;
-    if (B < 0 || K < 0 || K > kMaxK || V < 1 || V > kMaxV) return SPECDEC_EINVAL;
-    Scale sc;
-    if (!make_scale(temperature, &sc)) return SPECDEC_EINVAL;
-    if (B == 0) return SPECDEC_OK;
-    if (!target_logits || !uniforms || !out_tokens || !num_accepted) return SPECDEC_EINVAL;
-    if (K > 0 && !draft_tokens) return SPECDEC_EINVAL;
-    const bool one_hot = (draft_logits == nullptr);
-    const VerifyLayout L = verify_layout(B, K, V, dtype, one_hot);
-    if (!workspace_ok(workspace, workspace_bytes, L.total)) return SPECDEC_EWORKSPACE;
-    VerifyParams p{};
-    bool vec;
-    row_geometry(V, dtype, aligned16(target_logits) && aligned16(draft_logits), &p.NV, &vec);
-    p.C = tiles_of(p.NV);
-    p.R = K + 1 + (one_hot ? 0 : K);
-    p.NS = (p.NV + kSlab - 1) / kSlab;
-    p.kinds = one_hot ? 1 : 2;
-    // One workgroup per row item and per final item.
-    if ((size_t)B * p.R * p.C > kMaxBlocks || B > kMaxBatch) return SPECDEC_EINVAL;
-    p.target = target_logits;
-    p.draft = draft_logits;
-    p.tokens = draft_tokens;
-    p.kpr = k_per_req;
-    p.unif = uniforms;
-    p.out = out_tokens;
-    p.nacc = num_accepted;
-    p.aprob = accept_prob;
-    p.B = B;
-    p.K = K;
-    p.V = V;
-    p.sc = sc;
-    char* ws = static_cast<char*>(workspace);
-    p.err = reinterpret_cast<uint32_t*>(ws + L.err);
-    p.slot_m = reinterpret_cast<uint32_t*>(ws + L.slot_m);
-    p.slot_s = reinterpret_cast<uint64_t*>(ws + L.slot_s);
-    p.slot_l = reinterpret_cast<uint32_t*>(ws + L.slot_l);
-    p.slot_slab = reinterpret_cast<uint64_t*>(ws + L.slot_slab);
-    p.slot_tile = reinterpret_cast<uint64_t*>(ws + L.slot_tile);
-    p.dec = reinterpret_cast<Decision*>(ws + L.dec);
-    return map_launch(launch_verify(p, dtype, vec, (hipStream_t)stream,
-                                    reinterpret_cast<hipEvent_t const*>(events)));
+    return verify_impl(target_logits, draft_logits, dtype, draft_tokens, k_per_req, uniforms, temperature,
+                       B, K, V, out_tokens, num_accepted, accept_prob, workspace, workspace_bytes, stream,
+                       events, false);
 }
+
+
 
 size_t specdec_verify_processed_workspace_bytes(int32_t B, int32_t K, int32_t V,
                                                 specdec_dtype_t dtype, int one_hot_drafts) {

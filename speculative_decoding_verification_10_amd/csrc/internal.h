@@ -61,6 +61,7 @@ struct VerifyParams {
                                 // (self-validating)
     Decision* dec;              // [B] decision of each request
     const float* floors;        // [B * R] processed-row floors, or null (plain rows)
+    int clear_err;              // non-zero: the row kernel clears the error word first
 };
 
 // Linear greedy verify (launch_greedy) or greedy tree verify

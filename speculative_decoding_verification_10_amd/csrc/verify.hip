@@ -876,6 +876,10 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_rows(VerifyParams a) {
     __shared__ float lds_f[kWaves];
     __shared__ double lds_d[kWaves];
+    // A call whose error word starts clear (the allocation-free entry point:
+    // its scratch keeps the previous call's word): the first workgroup clears
+    // it; the only writer of the word, the final kernel, runs after this one.
+    if (a.clear_err && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.err = 0u;
     row_item<DT, VEC>(a, blockIdx.z, blockIdx.y, blockIdx.x, lds_f, lds_d);
 }
 

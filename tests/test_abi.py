@@ -315,3 +315,23 @@ def test_workspace_errors_rejects(lib):
     assert lib.specdec_workspace_errors(None, FAKE, 1, None) == EINVAL
     assert lib.specdec_workspace_errors(FAKE, None, 1, None) == EINVAL
     assert lib.specdec_workspace_errors(ctypes.c_void_p(0x10010), FAKE, 0, None) == EINVAL   # misaligned
+
+
+def test_verify_noalloc_rejects_on_host(lib):
+    """Arguments the allocation-free entry point rejects before any device
+    call: bad sizes, and calls whose workspace would exceed its static
+    scratch (SPECDEC_ESCRATCH)."""
+    ESCRATCH = -6
+    f = lib.specdec_verify_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(FAKE, FAKE, 1, FAKE, None, FAKE, 0.8, 4000, 5, 128256, FAKE, FAKE, None, None) == ESCRATCH
+    assert f(FAKE, FAKE, 0, FAKE, None, FAKE, 0.6, 1300, 8, 151936, FAKE, FAKE, None, None) == ESCRATCH
+    assert f(FAKE, FAKE, 1, FAKE, None, FAKE, 0.0, 4, 5, 1000, FAKE, FAKE, None, None) == EINVAL
+    assert f(FAKE, FAKE, 9, FAKE, None, FAKE, 1.0, 4, 5, 1000, FAKE, FAKE, None, None) == EDTYPE
+    assert f(None, FAKE, 1, FAKE, None, FAKE, 1.0, 4, 5, 1000, FAKE, FAKE, None, None) == EINVAL
+    assert f(FAKE, FAKE, 1, FAKE, None, FAKE, 1.0, 0, 5, 1000, FAKE, FAKE, None, None) == OK
+    n = lib.specdec_verify_workspace_bytes(3830, 5, 128256, 1, 0)
+    assert n <= (16 << 20) < lib.specdec_verify_workspace_bytes(3831, 5, 128256, 1, 0)
