@@ -168,6 +168,48 @@ def default_sets(workload: str) -> int:
     return 5 if mb < 50.0 else max(2, min(5, int(-(-1000.0 // mb))))
 
 
+def run_stream(args, torch, sd, dev):
+    """The read-stream ceiling: the row pass's load pattern alone
+    (specdec_read_stream) over the headline's row bytes (704 rows of
+    V = 128256 bf16), rotating over distinct device buffers."""
+    import ctypes
+    import numpy as np
+    lib = sd._lib.load()
+    nbytes = 704 * 128256 * 2
+    nsets = args.sets if args.sets is not None else 5
+    bufs = [torch.randint(-2**15, 2**15, (nbytes // 2,), dtype=torch.int16, device=dev) for _ in range(nsets)]
+    sink = torch.zeros(((nbytes // 16 + 1023) // 1024,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    handles = [(ctypes.c_void_p * 2)(a.cuda_event, b.cuda_event) for a, b in evs]
+    for r in range(args.warmup):
+        lib.specdec_read_stream(bufs[r % nsets].data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(args.steps):
+        rc = lib.specdec_read_stream(bufs[r % nsets].data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream,
+                                     handles[r])
+        if rc != 0:
+            raise sd.SpecdecError(rc, "specdec_read_stream")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    line = {"metric": "HBM read GB/s of the row pass's load pattern alone (read-stream ceiling)",
+            "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u8", "data": "synthetic (random bits, %d distinct device buffers)" % nsets,
+            "config": {"workload": "read stream over 180.6 MB (704 rows x 128256 bf16) in 16 KB tiles"},
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": "read_stream",
+                         "algorithmic_bytes": nbytes, "launch_ms": round(ms, 5)},
+            "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,7 +228,8 @@ def main():
     ap.add_argument("--workload", default="headline",
                     help="headline (default), tiny, peaked, greedy, ragged, ngram (the n-gram "
                          "drafter over copy-heavy contexts, then the greedy verify of its drafts), "
-                         "or tree (greedy verification of 21-node draft trees)")
+                         "tree (greedy verification of 21-node draft trees), or stream (the row "
+                         "pass's read pattern alone: the device's read-stream ceiling)")
     ap.add_argument("--top-k", type=int, default=None,
                     help="verify on top-k processed distributions (specdec_verify_processed)")
     ap.add_argument("--top-p", type=float, default=None,
@@ -222,6 +265,9 @@ def main():
     sd.load(build_if_missing=True)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.workload == "stream":
+        run_stream(args, torch, sd, dev)
+        return
 
     # The n-gram workload: the drafter over seeded copy-heavy contexts, then
     # the greedy verify of its drafts against the greedy workload's logits.

@@ -426,6 +426,22 @@ int specdec_choose_k(const uint64_t *counters, int32_t K, double c, int32_t k_mi
                      double *alpha_test, double *alpha_draft, int32_t *k_out,
                      double *speedup_out);
 
+/*
+ * Measurement helper, not a step of the method: the read pattern of the row
+ * pass alone -- one 256-thread workgroup per 16 KB tile of `data`, four
+ * 16-byte nontemporal loads per thread issued before any use, no other work
+ * -- over `bytes` of DEVICE memory (a multiple of 16, 16-byte aligned).  It
+ * gives the read bandwidth this access pattern can reach on the device, the
+ * ceiling the row pass is compared with.  sink: DEVICE uint32 array of
+ * ceil(bytes / 16384) words, written only when a tile's bits fold to one
+ * particular value (so that the loads are not dropped).  events: NULL or two
+ * caller HIP events (either may be NULL) taken by the kernel's dispatch at
+ * its start and end.  SPECDEC_EINVAL for a NULL pointer, a misaligned or
+ * ragged size, or more than 2^24 tiles.
+ */
+int specdec_read_stream(const void *data, size_t bytes, uint32_t *sink, void *stream,
+                        void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

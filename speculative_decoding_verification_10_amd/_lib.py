@@ -105,6 +105,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.specdec_acceptance_counts.restype = ci
         lib.specdec_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
         lib.specdec_ngram_propose.restype = ci
+        lib.specdec_read_stream.argtypes = [vp, sz, vp, vp, vp]
+        lib.specdec_read_stream.restype = ci
         dbl = ctypes.c_double
         lib.specdec_choose_k.argtypes = [vp, i32, dbl, i32, i32, vp, vp, vp, vp]
         lib.specdec_choose_k.restype = ci

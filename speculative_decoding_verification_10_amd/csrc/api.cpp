@@ -581,6 +581,18 @@ int specdec_ngram_propose(const int32_t* context, const int32_t* context_len, in
     return map_launch(launch_ngram(p, (hipStream_t)stream));
 }
 
+int specdec_read_stream(const void* data, size_t bytes, uint32_t* sink, void* stream, void* const* events) {
+    if (bytes == 0) return SPECDEC_OK;
+    if (!data || !sink || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(data) % 16) != 0) return SPECDEC_EINVAL;
+    if ((bytes / 16 + kTileVec - 1) / kTileVec > kMaxBlocks) return SPECDEC_EINVAL;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    if (events) {
+        ev[0] = static_cast<hipEvent_t>(events[0]);
+        ev[1] = static_cast<hipEvent_t>(events[1]);
+    }
+    return map_launch(launch_read_stream(data, bytes, sink, (hipStream_t)stream, ev[0], ev[1]));
+}
+
 int specdec_choose_k(const uint64_t* counters, int32_t K, double c, int32_t k_min, int32_t k_max,
                      double* alpha_test, double* alpha_draft, int32_t* k_out,
                      double* speedup_out) {

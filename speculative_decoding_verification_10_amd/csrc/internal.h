@@ -166,6 +166,10 @@ hipError_t launch_floors(const FloorParams& p, int dtype, bool vec, hipStream_t 
 hipError_t launch_verify_processed(const FloorParams& f, const VerifyParams& p, int dtype, bool vec,
                                    hipStream_t s, hipEvent_t const* events = nullptr);
 hipError_t launch_stats(const StatsParams& p, int dtype, bool vec, hipStream_t s);
+// The row pass's read pattern alone over `bytes` of data (a multiple of 16);
+// sink holds one word per 16 KB tile; start / stop events may be null.
+hipError_t launch_read_stream(const void* data, size_t bytes, uint32_t* sink, hipStream_t s,
+                              hipEvent_t start, hipEvent_t stop);
 hipError_t launch_acceptance_counts(const TelemetryParams& p, hipStream_t s);
 hipError_t launch_ngram(const NgramParams& p, hipStream_t s);
 

@@ -4,6 +4,11 @@
 //
 //  1. stats_partial  one workgroup per (row, tile): tile max and sum.
 //  2. stats_merge    one thread per row: merges the tiles in fp64.
+//
+// Also the read-stream measurement helper (read_stream): the row pass's load
+// pattern alone, the ceiling the row pass is measured against.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 
 namespace specdec {
@@ -53,7 +58,33 @@ hipError_t launch(const StatsParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The read pattern of the row pass with no other work: workgroup x reads
+// the 16 KB tile x of `data` (nv 16-byte vectors), four branch-free
+// nontemporal loads per thread issued before any use, and stores a word
+// only when the tile's bits fold to a value no data is expected to give,
+// so that the loads cannot be dropped while almost nothing is written.
+__global__ __launch_bounds__(kThreads) void read_stream(const u32x4* data, int64_t nv, uint32_t* sink) {
+    const int64_t v0 = (int64_t)blockIdx.x * kTileVec + threadIdx.x;
+    u32x4 r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) r[u] = __builtin_nontemporal_load(data + min(v0 + u * kThreads, nv - 1));
+    uint32_t x = 0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x ^= r[u][0] ^ r[u][1] ^ r[u][2] ^ r[u][3];
+    if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+
 }  // namespace
+
+hipError_t launch_read_stream(const void* data, size_t bytes, uint32_t* sink, hipStream_t s,
+                              hipEvent_t start, hipEvent_t stop) {
+    const int64_t nv = (int64_t)(bytes / 16);
+    if (nv == 0) return hipSuccess;
+    const int64_t tiles = (nv + kTileVec - 1) / kTileVec;
+    hipExtLaunchKernelGGL(read_stream, dim3((unsigned)tiles), dim3(kThreads), 0, s, start, stop, 0,
+                          static_cast<const u32x4*>(data), nv, sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_stats(const StatsParams& p, int dtype, bool vec, hipStream_t s) {
     if (dtype == kBF16) return vec ? launch<kBF16, true>(p, s) : launch<kBF16, false>(p, s);

@@ -237,13 +237,12 @@ __device__ Decision decide(const VerifyParams& a, int b, int kb, StepShared& sh)
     const int nrs = rows_of(kb, a.kinds);
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, sub = lane & 15;
 
-    uint32_t rl = 0, rd = 0;
-    float u = 0.0f;
-    if (t < kb) {
-        rl = a.slot_l[(size_t)b * R + t];
-        if (!one_hot) rd = a.slot_l[(size_t)b * R + K + 1 + t];
-        u = a.unif[(size_t)b * (K + 1) + t];
-    }
+    // The gathered logits and the uniform of this thread's position,
+    // branch-free (a thread past k_b reads position 0 and never uses it).
+    const int tt = t < kb ? t : 0;
+    uint32_t rl = a.slot_l[(size_t)b * R + tt];
+    uint32_t rd = (one_hot || K == 0) ? 0u : a.slot_l[(size_t)b * R + K + 1 + tt];
+    float u = a.unif[(size_t)b * (K + 1) + tt];
     for (int base = 0; base < nrs; base += kRowsPerPass) {
         float lm[kRowGroups];
         double ls[kRowGroups];
@@ -261,19 +260,27 @@ __device__ Decision decide(const VerifyParams& a, int b, int kb, StepShared& sh)
         for (int c0 = 0; c0 < C; c0 += 16 * kTilesPerLoad) {
             uint32_t um[kRowGroups][kTilesPerLoad];
             uint64_t us[kRowGroups][kTilesPerLoad];
+            // Branch-free, so that every load goes out before any is waited
+            // for: a lane past the end reads the request's first slot and
+            // drops the value.
 #pragma unroll
             for (int g = 0; g < kRowGroups; ++g) {
 #pragma unroll
                 for (int q = 0; q < kTilesPerLoad; ++q) {
                     const int c = c0 + sub + 16 * q;
-                    um[g][q] = 0;
-                    us[g][q] = 0;
-                    if (base + g * (kWaves * 4) < nrs && c0 + 16 * q < C && rs[g] < nrs && c < C) {
-                        um[g][q] = a.slot_m[row0[g] + c];
-                        us[g][q] = a.slot_s[row0[g] + c];
-                    }
+                    const bool ok = rs[g] < nrs && c < C;
+                    const size_t at = ok ? row0[g] + c : (size_t)b * R * C;
+                    um[g][q] = a.slot_m[at];
+                    us[g][q] = a.slot_s[at];
                 }
             }
+            // The values enter an empty asm statement here, so that the
+            // compiler issues every load above before the first wait instead
+            // of sinking each into the branch that merges it.
+#pragma unroll
+            for (int g = 0; g < kRowGroups; ++g)
+#pragma unroll
+                for (int q = 0; q < kTilesPerLoad; ++q) asm volatile("" : "+v"(um[g][q]), "+v"(us[g][q]));
 #pragma unroll
             for (int g = 0; g < kRowGroups; ++g) {
                 if (base + g * (kWaves * 4) >= nrs) continue;
@@ -373,12 +380,15 @@ __device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* 
     if (draft ? i >= kb : i > kb) return;   // row past k_b: nothing to read
     const void* row = draft ? row_ptr(a.draft, (size_t)b * K + i, a.V, S)
                             : row_ptr(a.target, (size_t)b * (K + 1) + i, a.V, S);
-    // Thread 0 of the tile that holds the draft token x_i reads its logit
-    // (issued before the tile's loads, stored after them).
+    // The tile that holds the draft token x_i reads its logit (issued before
+    // the tile's loads, stored by thread 0 after them).  Every lane of every
+    // tile issues the same-address load -- of the row's first logit when the
+    // tile is not the holder -- so that no branch makes the wave wait for it
+    // before the tile's loads go out.
     const int gx = (i < kb) ? token_of(a, b, i) : -1;
-    const bool holder = gx >= 0 && threadIdx.x == 0 && gx / (kTileVec * Elem<DT>::E) == tile;
-    float gval = 0.0f;
-    if (holder) gval = load_one<DT>(row, gx);
+    const bool holds = gx >= 0 && gx / (kTileVec * Elem<DT>::E) == tile;
+    const bool holder = holds && threadIdx.x == 0;
+    const float gval = load_one<DT>(row, holds ? gx : 0);
     float m;
     double z;
     tile_stats<DT, VEC>(row, a.V, a.NV, tile, a.sc, m, z, lds_f, lds_d);
@@ -876,11 +886,13 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void verify_rows(VerifyParams a) {
     __shared__ float lds_f[kWaves];
     __shared__ double lds_d[kWaves];
+    row_item<DT, VEC>(a, blockIdx.z, blockIdx.y, blockIdx.x, lds_f, lds_d);
     // A call whose error word starts clear (the allocation-free entry point:
     // its scratch keeps the previous call's word): the first workgroup clears
-    // it; the only writer of the word, the final kernel, runs after this one.
+    // it, after its loads (a store ahead of them would keep the compiler from
+    // reading k_b and the draft tokens through the scalar cache); the only
+    // writer of the word, the final kernel, runs after this one.
     if (a.clear_err && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.err = 0u;
-    row_item<DT, VEC>(a, blockIdx.z, blockIdx.y, blockIdx.x, lds_f, lds_d);
 }
 
 // Decisions, when taken once per request: workgroup x takes request x.

@@ -335,3 +335,13 @@ def test_verify_noalloc_rejects_on_host(lib):
     assert f(FAKE, FAKE, 1, FAKE, None, FAKE, 1.0, 0, 5, 1000, FAKE, FAKE, None, None) == OK
     n = lib.specdec_verify_workspace_bytes(3830, 5, 128256, 1, 0)
     assert n <= (16 << 20) < lib.specdec_verify_workspace_bytes(3831, 5, 128256, 1, 0)
+
+
+def test_read_stream_rejects(lib):
+    f = lib.specdec_read_stream
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(FAKE, 0, FAKE, None, None) == OK               # nothing to read
+    assert f(None, 1 << 20, FAKE, None, None) == EINVAL
+    assert f(FAKE, 1 << 20, None, None, None) == EINVAL
+    assert f(FAKE, (1 << 20) + 8, FAKE, None, None) == EINVAL          # not a multiple of 16
+    assert f(ctypes.c_void_p(0x10008), 1 << 20, FAKE, None, None) == EINVAL   # misaligned
