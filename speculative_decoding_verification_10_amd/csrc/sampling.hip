@@ -1195,7 +1195,7 @@ __device__ __forceinline__ RowSlot row_slot(const FloorParams& a) {
 // the draft token (-inf when cut); row 0 empties the request's slab and
 // final-tile slots.
 template <int DT>
-__device__ void write_outputs(const FloorParams& a, const RowSlot& s, float m, float fl, double z) {
+__device__ __forceinline__ void write_outputs(const FloorParams& a, const RowSlot& s, float m, float fl, double z) {
     const int t = threadIdx.x;
     if (t == 0) a.floors[blockIdx.x] = fl;
     if (!a.slot_m) return;

@@ -80,3 +80,27 @@ def run_verify(wl: workloads.Workload, accept_prob=True, device="cuda"):
 def oracle_verify(wl: workloads.Workload):
     return oracle.verify(wl.target, wl.draft, wl.draft_tokens, wl.uniforms, wl.temperature,
                          wl.k_per_req)
+
+
+def seeded_sets(name: str, n: int, workers: int = 8, ahead: int = 8, ref_fn=None):
+    """Yield (set_index, workload, oracle result) for set_index 0..n-1 of a
+    named workload, in order.  Generation and the oracle run in a pool of
+    threads (the bulk numpy work releases the GIL), at most `ahead` sets
+    ahead of the consumer so host memory stays bounded."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    if ref_fn is None:
+        ref_fn = oracle_verify
+
+    def build(s):
+        wl = workloads.make(name, set_index=s)
+        return wl, ref_fn(wl)
+
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        pending = [pool.submit(build, s) for s in range(min(n, ahead))]
+        for s in range(n):
+            wl, ref = pending[0].result()
+            pending.pop(0)
+            if s + ahead < n:
+                pending.append(pool.submit(build, s + ahead))
+            yield s, wl, ref

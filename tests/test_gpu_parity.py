@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from speculative_decoding_verification_10_amd import workloads
-from tests.gpu_util import (assert_workspace_clean, compare_verify, dev_logits,
+from tests.gpu_util import (seeded_sets, assert_workspace_clean, compare_verify, dev_logits,
                             oracle_verify, run_verify)
 
 pytestmark = pytest.mark.gpu
@@ -77,28 +77,39 @@ def test_verify_tiny_10000_steps():
     assert nd <= 1e-4 * wl.B
 
 
-@pytest.mark.parametrize("name,sets", [("peaked", 40), ("headline", 6)])
+@pytest.mark.parametrize("name,sets", [("peaked", 1000), ("headline", 20)])
 def test_verify_full_size(name, sets):
+    """Distinct seeded sets (set_index 0..sets-1): 1,000 steps of the peaked
+    batch, 20 of the headline batch."""
     flagged = differ = total = 0
-    for s in range(sets):
-        say("verify", name, "set", s)
-        wl = workloads.make(name, set_index=s)
-        ref = oracle_verify(wl)
+    for s, wl, ref in seeded_sets(name, sets, ahead=16 if name == "peaked" else 4):
+        if s % 50 == 0 or name != "peaked":
+            say("verify", name, "set", s)
         nf, nd = compare_verify("%s/%d" % (name, s), run_verify(wl), ref)
         flagged += nf
         differ += nd
         total += wl.B
-    say("flagged", flagged, "differ", differ, "of", total)
-    assert differ <= 1e-4 * total
+    say("counts", name, "sets", sets, "requests", total, "flagged", flagged, "differ", differ)
+    # Every differing request is flagged (compare_verify).  A flagged final
+    # draw lies within 1e-6 of a CDF boundary -- on peaked rows, any draw
+    # among the tail tokens, whose own masses are below 2e-6 of S -- and the
+    # fp32 path places boundaries to ~1e-7 of S, so it may decide at most
+    # about a tenth of the flagged requests the other way.
+    assert differ <= 1 + 0.1 * flagged, (differ, flagged)
 
 
 def test_verify_ragged_full_size():
-    say("verify ragged")
-    wl = workloads.make("ragged")
-    ref = oracle_verify(wl)
-    nf, nd = compare_verify("ragged", run_verify(wl), ref)
-    say("flagged", nf, "differ", nd, "of", wl.B)
-    assert nd == 0
+    """Three distinct seeded sets of the ragged batch (B = 512, k_b from 1 to
+    8, V = 151,936, fp32)."""
+    flagged = differ = total = 0
+    for s, wl, ref in seeded_sets("ragged", 3, workers=3, ahead=2):
+        say("verify ragged set", s)
+        nf, nd = compare_verify("ragged/%d" % s, run_verify(wl), ref)
+        flagged += nf
+        differ += nd
+        total += wl.B
+    say("counts ragged sets 3 requests", total, "flagged", flagged, "differ", differ)
+    assert differ == 0
 
 
 @pytest.mark.parametrize("name,B,V,K", [
@@ -454,14 +465,19 @@ def test_greedy_timed_matches_and_records():
 
 
 def test_greedy_full_size():
-    for s in range(3):
-        say("greedy set", s)
-        wl = workloads.make("greedy", set_index=s)
+    """Fifty distinct seeded sets of the greedy batch (B = 256, K = 3,
+    V = 151,936, bf16): argmax, counts and tokens bit-exact."""
+    n = 0
+    for s, wl, ref in seeded_sets("greedy", 50, ahead=6,
+                                  ref_fn=lambda w: oracle.verify_greedy(w.target, w.draft_tokens)):
+        if s % 10 == 0:
+            say("greedy set", s)
         out, nacc, am = _greedy(wl)
-        ref = oracle.verify_greedy(wl.target, wl.draft_tokens)
-        assert np.array_equal(am, ref["argmax"])
-        assert np.array_equal(nacc, ref["num_accepted"])
-        assert np.array_equal(out, ref["out_tokens"])
+        assert np.array_equal(am, ref["argmax"]), s
+        assert np.array_equal(nacc, ref["num_accepted"]), s
+        assert np.array_equal(out, ref["out_tokens"]), s
+        n += wl.B
+    say("counts greedy sets 50 requests", n, "differ 0")
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
