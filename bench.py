@@ -611,8 +611,8 @@ def main():
             "algorithmic": round(alg / positions, 1),
             "counters": (None if (call or roofline).get("traffic") is None else
                          round((call or roofline)["traffic"] / set_pos[0], 1)),
-            "note": "counters: rocprofv3 FETCH_SIZE + WRITE_SIZE of one call on input set 0, scaled "
-                    "by the copy calibration, per verified position"},
+            "note": "counters: rocprofv3 FETCH_SIZE + WRITE_SIZE per call (mean over the profiled calls), "
+                    "scaled by the copy calibration, over the verified positions of one call"},
         "rejected_requests": (None if tree else
                               [int(np.sum(n_ < (st["wl"].K if st["wl"].k_per_req is None
                                                 else st["wl"].k_per_req)))
