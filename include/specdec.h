@@ -71,7 +71,9 @@ typedef enum {
     SPECDEC_EDTYPE = -2,     /* unknown dtype */
     SPECDEC_EWORKSPACE = -3, /* workspace missing, too small or misaligned */
     SPECDEC_ELAUNCH = -4,    /* a kernel launch failed (HIP error) */
-    SPECDEC_EDEVICE = -5,    /* no usable gfx950 device */
+    SPECDEC_EDEVICE = -5,    /* no usable gfx950 device: a launch failed on a device of another
+                                architecture (the library holds gfx950 code only), or the
+                                allocation-free entry point found no current device */
     SPECDEC_ESCRATCH = -6    /* too large for the static scratch of specdec_verify_noalloc */
 } specdec_status_t;
 

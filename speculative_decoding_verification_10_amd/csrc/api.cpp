@@ -128,7 +128,20 @@ bool workspace_ok(const void* ws, size_t have, size_t need) {
     return ws != nullptr && have >= need && (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0;
 }
 
-int map_launch(hipError_t e) { return e == hipSuccess ? SPECDEC_OK : SPECDEC_ELAUNCH; }
+// The library holds gfx950 code only.  A launch that fails on a device of
+// another architecture reports SPECDEC_EDEVICE; the check runs only after a
+// failure, so a successful call pays nothing for it.
+bool current_device_is_gfx950() {
+    int dev = -1;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+    return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+}
+
+int map_launch(hipError_t e) {
+    if (e == hipSuccess) return SPECDEC_OK;
+    return current_device_is_gfx950() ? SPECDEC_ELAUNCH : SPECDEC_EDEVICE;
+}
 
 // Scratch of the allocation-free entry point (specdec_verify_noalloc): a
 // file-scope device array, one copy per GPU, held until the process ends.
