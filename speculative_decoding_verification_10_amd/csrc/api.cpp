@@ -56,13 +56,14 @@ bool make_scale(float temperature, Scale* s) {
 }
 
 struct VerifyLayout {
-    size_t err, slot_m, slot_s, slot_l, slot_slab, slot_tile, dec, floors, total;
+    size_t err, slot_m, slot_s, slot_l, slot_slab, slot_tile, dec, floors, cand_head, cand_ent, cand_done, total;
 };
 
 // Header (error bits), self-validating slots -- tile max / tile sum of every
 // row slot of every request, the logit at the draft token of every row, the
 // slab sums and per-tile sums of every request's final row -- and each
-// request's decision.
+// request's decision; for the processed step also the row floors and the
+// tile candidates of a small top-k.
 VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, bool one_hot,
                            bool processed = false) {
     int NV, NVv;
@@ -82,6 +83,9 @@ VerifyLayout verify_layout(int32_t B, int32_t K, int32_t V, specdec_dtype_t dt, 
     L.slot_tile = off; off = align_up(off + (size_t)B * C * sizeof(uint64_t));
     L.dec = off;       off = align_up(off + (size_t)B * sizeof(Decision));
     L.floors = off;    if (processed) off = align_up(off + (size_t)B * R * sizeof(float));
+    L.cand_head = off; if (processed) off = align_up(off + parts * 4 * sizeof(uint32_t));
+    L.cand_ent = off;  if (processed) off = align_up(off + parts * kCandPerTile * sizeof(uint32_t));
+    L.cand_done = off; if (processed) off = align_up(off + (size_t)B * R * sizeof(uint32_t));
     L.total = off;
     return L;
 }
@@ -414,6 +418,9 @@ int specdec_verify_processed_timed(const void* target_logits, const void* draft_
     f.slot_l = p.slot_l;
     f.slot_slab = p.slot_slab;
     f.slot_tile = p.slot_tile;
+    f.cand_head = reinterpret_cast<uint32_t*>(ws + L.cand_head);
+    f.cand_ent = reinterpret_cast<uint32_t*>(ws + L.cand_ent);
+    f.cand_done = reinterpret_cast<uint32_t*>(ws + L.cand_done);
     return map_launch(launch_verify_processed(f, p, dtype, vec, (hipStream_t)stream,
                                               reinterpret_cast<hipEvent_t const*>(events)));
 }

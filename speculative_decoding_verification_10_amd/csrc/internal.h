@@ -102,7 +102,16 @@ struct FloorParams {
     uint32_t* slot_l;
     uint64_t* slot_slab;
     uint64_t* slot_tile;
+    // Candidates of a small top-k (null: none), per (request, row slot, tile):
+    // a head of four words (largest key, the key from which the candidates
+    // are complete, their number, 0) and up to kCandPerTile entries.
+    uint32_t* cand_head;        // [B * R * C * 4]
+    uint32_t* cand_ent;         // [B * R * C * kCandPerTile]
+    uint32_t* cand_done;        // [B * R]: 1 where the candidates decided the row
 };
+
+// Entries a tile leaves for a top-k of at most this size.
+constexpr int kCandPerTile = 64;
 
 // Ancestor masks and depths of flattened draft trees.
 struct TreeMaskParams {

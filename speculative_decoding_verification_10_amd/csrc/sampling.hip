@@ -1167,6 +1167,222 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
     z_out = kept;
 }
 
+// ---------------------------------------------------------------------------
+// A small top-k (1 <= top_k <= kCandPerTile) on rows of whole 16-byte
+// vectors: the cuts from tile candidates, so that no row is read more than
+// once.
+//
+// floor_cands, one workgroup of 256 threads per 16 KB tile (grid: tile, row
+// slot, request, as the verify row pass), leaves the tile's largest logits:
+//   bf16: one bin per key for the 256 keys from the tile's largest down, so
+//         a bin is one value; the entries are (key, count) of the nonzero
+//         bins from the top down to the bin where the count reaches top_k;
+//   fp32: 256 bins over the mass exponent below the tile's largest logit, 8
+//         per binade (monotone in the logit: equal logits share a bin); the
+//         entries are the logits of the bins down to the one where the count
+//         reaches top_k.
+// The entries stop one bin early where kCandPerTile would overflow.  The
+// head holds the tile's largest key; L, the smallest key such that every
+// logit of the tile with key >= L is an entry; the number of entries; and G,
+// a key at or below the tile's own top_k-th largest (0 when the window holds
+// fewer than top_k logits).
+//
+// floor_merge, one wave per row, merges the row's entries.  The row's
+// top_k-th largest K* is at least every tile's own, so at least G of every
+// tile: entries below the largest G are dropped.  The top_k-th largest of
+// the rest is the row's when it is >= L of every tile (each tile then holds
+// all its logits >= it, so every count from the top down to it is the
+// row's), and then every top-k survivor is an entry, so the top-p cut over
+// the survivors comes from the entries too.  Otherwise (the cut lies below
+// some tile's entries, or the entries overflow the wave's LDS) the row is
+// left to floor_rows.  The row max is the largest head key.
+// ---------------------------------------------------------------------------
+constexpr int kCandBins = kThreads;             // one bin per thread of floor_cands
+constexpr float kCandBinsPerBinade = 8.0f;      // fp32: bins over the mass exponent
+
+__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = (uint32_t)__shfl_up((int)v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void floor_cands(FloorParams a) {
+    constexpr int E = Elem<DT>::E;
+    static_assert(kCandBins == kThreads && kWaves == 4, "one bin per thread");
+    __shared__ uint32_t hist[kCandBins];
+    __shared__ float red_f[kWaves];
+    __shared__ uint32_t sel[4];                           // b_emit, b*, then fp32: L, G
+    __shared__ uint32_t nout;
+    const int tile = blockIdx.x, rr = blockIdx.y, b = blockIdx.z;
+    const int K = a.K;
+    const int kb = a.kpr ? min(max(a.kpr[b], 0), K) : K;
+    const bool draft = rr > K;
+    const int i = draft ? rr - K - 1 : rr;
+    if (draft ? i >= kb : i > kb) return;                // row past k_b
+    const size_t ri = draft ? (size_t)b * K + i : (size_t)b * (K + 1) + i;
+    const void* row = static_cast<const char*>(draft ? a.draft : a.target) + ri * (size_t)a.V * Elem<DT>::S;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    u32x4 raw[kUnroll];
+    tile_load<DT, true, true>(row, a.V, a.NV, tile, raw);
+    hist[t] = 0u;
+    if (t == 0) {
+        nout = 0u;
+        sel[2] = 0xFFFFFFFFu;
+        sel[3] = 0xFFFFFFFFu;
+    }
+    // Vectors past the row end were read as -inf: they add nothing to the
+    // max and lie below every window.
+    float xm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        float x[E];
+        decode<DT>(raw[u], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) xm = fmaxf(xm, x[e]);
+    }
+    xm = block_max(xm, red_f);
+    uint32_t km;
+    float M = 0.0f, Dh = 0.0f, xlo = -INFINITY;
+    if constexpr (DT == kBF16) {
+        km = key16_of(__float_as_uint(xm) >> 16);
+        // The window's smallest value (keys below 0x80 are NaNs: none).
+        if (km >= 0x0080u + (uint32_t)(kCandBins - 1)) xlo = value16_of(km - (uint32_t)(kCandBins - 1));
+    } else {
+        km = key_of(xm);
+        M = offset_of(xm, a.sc);
+        Dh = -exponent2(xm, M, a.sc);
+    }
+    // Bin of a logit: 0 (the largest) to 255, -1 outside the window.
+    auto bin_of = [&](float x) -> int {
+        if constexpr (DT == kBF16) {
+            if (!(x >= xlo)) return -1;
+            return (int)(km - key16_of(__float_as_uint(x) >> 16));
+        } else {
+            // -inf gives +inf (or NaN when the largest is -inf): outside.
+            const float q = (-exponent2(x, M, a.sc) - Dh) * kCandBinsPerBinade;
+            return q < (float)kCandBins ? (int)q : -1;
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        float x[E];
+        decode<DT>(raw[u], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int bn = bin_of(x[e]);
+            if (bn >= 0) atomicAdd(&hist[bn], 1u);
+        }
+    }
+    __syncthreads();
+
+    const size_t at = ((size_t)b * a.R + rr) * a.C + tile;
+    uint32_t* head = a.cand_head + at * 4;
+    uint32_t* ent = a.cand_ent + at * kCandPerTile;
+    // Wave 0 alone selects: lane l holds the bins 4l .. 4l + 3.
+    if (w == 0) {
+        uint32_t c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
+        // The counts and the nonzero bins from the top, inclusive, in one
+        // 32-bit scan (a tile holds at most 8,192 logits).
+        uint32_t pk[4];
+        pk[0] = (c[0] << 16) | (c[0] ? 1u : 0u);
+#pragma unroll
+        for (int q = 1; q < 4; ++q) pk[q] = pk[q - 1] + ((c[q] << 16) | (c[q] ? 1u : 0u));
+        const uint32_t before = wave_incl_u32(pk[3]) - pk[3];
+        uint32_t cnt_incl[4], nz_incl[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            cnt_incl[q] = (before + pk[q]) >> 16;
+            nz_incl[q] = (before + pk[q]) & 0xFFFFu;
+        }
+        // b*: the first bin where the count from the top reaches top_k.
+        int first = -1;
+#pragma unroll
+        for (int q = 3; q >= 0; --q)
+            if (cnt_incl[q] >= (uint32_t)a.top_k) first = 4 * lane + q;
+        const uint64_t mr = __ballot(first >= 0);
+        const uint32_t bstar =
+            mr ? (uint32_t)__shfl(first, __ffsll((unsigned long long)mr) - 1, 64) : 0xFFFFFFFFu;
+        const uint32_t blast = bstar == 0xFFFFFFFFu ? (uint32_t)(kCandBins - 1) : bstar;
+        // The emitted bins: a prefix (at most kCandPerTile entries); b_emit is its last.
+        int last = -1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t used = (DT == kBF16) ? nz_incl[q] : cnt_incl[q];
+            if ((uint32_t)(4 * lane + q) <= blast && used <= (uint32_t)kCandPerTile) last = 4 * lane + q;
+        }
+        const uint64_t ml = __ballot(last >= 0);
+        const int b_emit = ml ? __shfl(last, 63 - __clzll((long long)ml), 64) : -1;
+        if constexpr (DT == kBF16) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int bn = 4 * lane + q;
+                if (bn <= b_emit && c[q] != 0u) ent[nz_incl[q] - 1] = ((km - (uint32_t)bn) << 16) | c[q];
+                if (bn == b_emit) {                       // bin 0 (the largest) always fits
+                    head[0] = km;
+                    head[1] = km - (uint32_t)bn;
+                    head[2] = nz_incl[q];
+                    head[3] = bstar == 0xFFFFFFFFu ? 0u : km - bstar;
+                }
+            }
+        } else if (lane == 0) {
+            sel[0] = (uint32_t)b_emit;
+            sel[1] = bstar;
+        }
+    }
+    if constexpr (DT == kFP32) {
+        __syncthreads();
+        // The logits of bins <= b_emit (a few: appended one by one), the
+        // smallest of them (L), and the smallest logit of bin b* (G).
+        const int b_emit = (int)sel[0];
+        const uint32_t bstar = sel[1];
+        uint32_t lmin = 0xFFFFFFFFu, gmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float x = __uint_as_float(raw[u][e]);
+                const int bn = bin_of(x);
+                if (bn >= 0 && bn <= b_emit) {
+                    const uint32_t key = key_of(x);
+                    lmin = min(lmin, key);
+                    ent[atomicAdd(&nout, 1u)] = key;
+                }
+                if (bn >= 0 && (uint32_t)bn == bstar) gmin = min(gmin, key_of(x));
+            }
+        lmin = wave_min_u32(lmin);
+        gmin = wave_min_u32(gmin);
+        if (lane == 0) {
+            atomicMin(&sel[2], lmin);
+            atomicMin(&sel[3], gmin);
+        }
+        __syncthreads();
+        if (t == 0) {
+            head[0] = km;
+            // A tile of -inf only: nothing at or above key(-inf) + 1.
+            head[1] = (xm == -INFINITY) ? km + 1u : sel[2];
+            head[2] = nout;
+            head[3] = sel[3] == 0xFFFFFFFFu ? 0u : sel[3];
+        }
+    }
+}
+
 // Row slot of this workgroup, and the outputs.
 struct RowSlot {
     int b, rr, i, kb;
@@ -1175,12 +1391,12 @@ struct RowSlot {
 };
 
 template <int DT>
-__device__ __forceinline__ RowSlot row_slot(const FloorParams& a) {
+__device__ __forceinline__ RowSlot row_slot_of(const FloorParams& a, int rs) {
     constexpr int S = Elem<DT>::S;
     RowSlot s;
     const int R = a.R, K = a.K;
-    s.b = blockIdx.x / R;
-    s.rr = blockIdx.x - s.b * R;
+    s.b = rs / R;
+    s.rr = rs - s.b * R;
     s.kb = a.kpr ? min(max(a.kpr[s.b], 0), K) : K;
     const bool draft = s.rr > K;
     s.i = draft ? s.rr - K - 1 : s.rr;
@@ -1189,38 +1405,313 @@ __device__ __forceinline__ RowSlot row_slot(const FloorParams& a) {
     s.row = static_cast<const char*>(draft ? a.draft : a.target) + row_index * (size_t)a.V * S;
     return s;
 }
+template <int DT>
+__device__ __forceinline__ RowSlot row_slot(const FloorParams& a) {
+    return row_slot_of<DT>(a, blockIdx.x);
+}
+
+__host__ __device__ __forceinline__ bool cands_usable(const FloorParams& a) {
+    return a.cand_head != nullptr && a.top_k >= 1 && a.top_k <= kCandPerTile && a.top_k < a.V;
+}
 
 // The floor; for the verify step the processed row's slots: tile 0 holds
 // the row max and the kept mass, the other tiles are empty; the logit at
 // the draft token (-inf when cut); row 0 empties the request's slab and
 // final-tile slots.
 template <int DT>
-__device__ __forceinline__ void write_outputs(const FloorParams& a, const RowSlot& s, float m, float fl, double z) {
-    const int t = threadIdx.x;
-    if (t == 0) a.floors[blockIdx.x] = fl;
-    if (!a.slot_m) return;
+__device__ __forceinline__ void write_outputs(const FloorParams& a, const RowSlot& s, float m, float fl, double z,
+                                              int t = threadIdx.x, int stride = kFT, bool have_l = false,
+                                              float l_in = 0.0f) {
     const size_t rs = (size_t)s.b * a.R + s.rr;
+    if (t == 0) a.floors[rs] = fl;
+    if (!a.slot_m) return;
     const int C = a.C;
-    for (int c = t; c < C; c += kFT) {
+    for (int c = t; c < C; c += stride) {
         slot_put(a.slot_m + rs * C + c, enc_f32(c == 0 ? m : -INFINITY));
         slot_put(a.slot_s + rs * C + c, enc_f64(c == 0 ? z : 0.0));
     }
     if (t == 0 && s.i < s.kb && a.tokens) {
-        const int x = min(max(a.tokens[(size_t)s.b * a.K + s.i], 0), a.V - 1);
-        const float l = load_one<DT>(s.row, x);
+        float l = l_in;
+        if (!have_l) l = load_one<DT>(s.row, min(max(a.tokens[(size_t)s.b * a.K + s.i], 0), a.V - 1));
         slot_put(a.slot_l + rs, enc_f32(l >= fl ? l : -INFINITY));
     }
     if (s.rr == 0) {
-        for (int c = t; c < C * kSlabsPerTile; c += kFT)
+        for (int c = t; c < C * kSlabsPerTile; c += stride)
             slot_put(a.slot_slab + (size_t)s.b * C * kSlabsPerTile + c, (uint64_t)0);
-        for (int c = t; c < C; c += kFT) slot_put(a.slot_tile + (size_t)s.b * C + c, (uint64_t)0);
+        for (int c = t; c < C; c += stride) slot_put(a.slot_tile + (size_t)s.b * C + c, (uint64_t)0);
     }
+}
+
+// floor_merge: one wave per row of a small top-k (see floor_cands).  Lane l
+// holds entry l of every tile, in registers.  One histogram over 256 bins
+// from the row's largest key down decides both cuts: bf16 bins are exact
+// keys (every kept entry lies within 256 keys of the largest: the tile that
+// holds it keeps its own top_k within its window); fp32 bins are the mass
+// exponent at 8 per binade, and the bin holding a cut is resolved exactly by
+// ranking its few entries.  Rows it decides get their outputs here and
+// done[row] = 1; the others done[row] = 0, and floor_rows takes them.
+constexpr int kMergeWaves = 4;                  // rows per workgroup
+constexpr int kMergeTiles = 40;                 // tiles of a row the merge takes (more: floor_rows)
+constexpr int kMergeList = 256;                 // fp32: entries of one bin ranked in LDS
+
+struct MergeShared {
+    uint32_t hist[256];
+    uint64_t mhist[256];
+    uint32_t lkey[kMergeList];
+    uint64_t lmass[kMergeList];
+    uint32_t nlist;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
+    static_assert(kCandPerTile == 64, "lane l holds entry l of every tile");
+    __shared__ MergeShared ms_all[kMergeWaves];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int rs = blockIdx.x * kMergeWaves + wv;                // row slot b * R + rr
+    if (rs >= a.B * a.R) return;
+    MergeShared& ms = ms_all[wv];
+    const int C = a.C;
+    uint32_t* done = a.cand_done + rs;
+    if (C > kMergeTiles) {
+        const RowSlot s = row_slot_of<DT>(a, rs);
+        if (!s.skip && lane == 0) *done = 0u;
+        return;
+    }
+    // Within one wave LDS accesses complete in program order; this keeps the
+    // compiler from moving them across each other.
+    auto lds_order = [] { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+    // One batch of loads: k_b (in row_slot_of), the heads, entry `lane` of
+    // every tile (checked against the counts afterwards) and the draft
+    // token; then the logit at the draft token.
+    const size_t at0 = (size_t)rs * C;
+    const uint32_t* head = a.cand_head + at0 * 4;
+    const uint32_t* ent = a.cand_ent + at0 * kCandPerTile;
+    uint32_t h0 = 0u, h1 = 0u, h2 = 0u, h3 = 0u;
+    if (lane < C) {
+        h0 = head[4 * lane];
+        h1 = head[4 * lane + 1];
+        h2 = min(head[4 * lane + 2], (uint32_t)kCandPerTile);
+        h3 = head[4 * lane + 3];
+    }
+    uint32_t ev[kMergeTiles];
+#pragma unroll
+    for (int c = 0; c < kMergeTiles; ++c) ev[c] = c < C ? ent[c * kCandPerTile + lane] : 0u;
+    const RowSlot s = row_slot_of<DT>(a, rs);
+    if (s.skip) return;
+    const bool gathers = s.i < s.kb && a.tokens;
+    const int tok = gathers ? min(max(a.tokens[(size_t)s.b * a.K + s.i], 0), a.V - 1) : 0;
+    const float l_tok = gathers ? load_one<DT>(s.row, tok) : 0.0f;
+    const uint32_t km = wave_max_u32(h0);
+    const uint32_t lmax = wave_max_u32(h1);
+    const uint32_t gmax = wave_max_u32(h3);
+    auto val = [](uint32_t k) { return (DT == kBF16) ? value16_of(k) : value_of(k); };
+    const float mx = val(km);
+    const float M = offset_of(mx, a.sc);
+    const float Dh = -exponent2(mx, M, a.sc);
+    // Bin of a key: 0 (the largest) upward; >= 256 below the histogram.
+    auto bin_of = [&](uint32_t k) -> uint32_t {
+        if constexpr (DT == kBF16) {
+            return km - k;
+        } else {
+            const float q = (-exponent2(value_of(k), M, a.sc) - Dh) * kCandBinsPerBinade;
+            return q < 256.0f ? (uint32_t)(int)q : 256u;
+        }
+    };
+    auto key_at = [&](int c) -> uint32_t { return (DT == kBF16) ? (ev[c] >> 16) : ev[c]; };
+    auto cnt_at = [&](int c) -> uint32_t { return (DT == kBF16) ? (ev[c] & 0xFFFFu) : 1u; };
+    auto mass_of = [&](uint32_t k) -> uint64_t { return fix_of(fast_exp2(exponent2(val(k), M, a.sc))); };
+    // 0 where a tile has no entry `lane`, where it lies below gmax (below
+    // every cut), or below the histogram: when the histogram still holds
+    // top_k entries, those lie below the cut too; else the row is left to
+    // floor_rows.
+#pragma unroll
+    for (int c = 0; c < kMergeTiles; ++c)
+        if (c >= C || (uint32_t)lane >= (uint32_t)__shfl((int)h2, c, 64) || key_at(c) < gmax ||
+            bin_of(key_at(c)) >= 256u)
+            ev[c] = 0u;
+    auto give_up = [&] {
+        if (lane == 0) *done = 0u;
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        ms.hist[4 * lane + q] = 0u;
+        ms.mhist[4 * lane + q] = 0ull;
+    }
+    if (lane == 0) ms.nlist = 0u;
+    lds_order();
+#pragma unroll
+    for (int c = 0; c < kMergeTiles; ++c)
+        if (ev[c] != 0u) atomicAdd(&ms.hist[bin_of(key_at(c))], cnt_at(c));
+    lds_order();
+    // Lane l holds the bins 4l .. 4l + 3 (descending keys); the first bin
+    // where a running weight from the top reaches target, and the weight
+    // above it.  The bins' weights must reach target in total.
+    auto crossing = [&](const double (&wb)[4], double target, double& above_out) -> int {
+        const double mine = (wb[0] + wb[1]) + (wb[2] + wb[3]);
+        double run = wave_inclusive_scan(mine) - mine;          // the lanes before this one
+        int pick = -1;
+        double pa = 0.0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (pick < 0 && run < target && target <= run + wb[q]) {
+                pick = 4 * lane + q;
+                pa = run;
+            }
+            run += wb[q];
+        }
+        const uint64_t hit = __ballot(pick >= 0);
+        if (!hit) return -1;
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        above_out = __shfl(pa, src, 64);
+        return __shfl(pick, src, 64);
+    };
+    double wc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wc[q] = (double)ms.hist[4 * lane + q];
+    double cabove = 0.0;
+    const int kbin = crossing(wc, (double)a.top_k, cabove);
+    if (kbin < 0) {                                              // fewer than top_k in the histogram
+        give_up();
+        return;
+    }
+    // K*: the bin's key (bf16), or the (top_k - cabove)-th largest key of the
+    // bin's entries (fp32).
+    uint32_t kstar;
+    if constexpr (DT == kBF16) {
+        kstar = km - (uint32_t)kbin;
+    } else {
+#pragma unroll
+        for (int c = 0; c < kMergeTiles; ++c) {
+            const bool g = ev[c] != 0u && bin_of(key_at(c)) == (uint32_t)kbin;
+            const uint64_t mask = __ballot(g);
+            if (mask) {
+                const uint32_t base = ms.nlist;
+                lds_order();
+                const uint32_t i = base + lanes_below(mask);
+                if (g && i < (uint32_t)kMergeList) ms.lkey[i] = key_at(c);
+                if (lane == 0) ms.nlist = base + (uint32_t)__popcll(mask);
+                lds_order();
+            }
+        }
+        const uint32_t nl = ms.nlist;
+        if (nl > (uint32_t)kMergeList) {
+            give_up();
+            return;
+        }
+        const uint32_t need = (uint32_t)a.top_k - (uint32_t)cabove;
+        uint32_t found = 0u;
+        for (uint32_t i = lane; i < nl; i += 64) {
+            const uint32_t ki = ms.lkey[i];
+            uint32_t gt = 0u, ge = 0u;
+            for (uint32_t j = 0; j < nl; ++j) {
+                const uint32_t kj = ms.lkey[j];
+                gt += kj > ki;
+                ge += kj >= ki;
+            }
+            if (gt < need && need <= ge) found = ki;                  // equal keys find the same
+        }
+        kstar = wave_max_u32(found);
+        lds_order();
+        if (kstar == 0u) {
+            give_up();
+            return;
+        }
+    }
+    if (kstar < lmax) {                                           // a tile's entries stop above the cut
+        give_up();
+        return;
+    }
+    // The survivors' masses per bin (fp32: in bin kbin only keys >= K*).
+#pragma unroll
+    for (int c = 0; c < kMergeTiles; ++c) {
+        if (ev[c] != 0u && key_at(c) >= kstar) {
+            const uint32_t k = key_at(c);
+            atomicAdd(reinterpret_cast<unsigned long long*>(&ms.mhist[bin_of(k)]),
+                      (unsigned long long)((uint64_t)cnt_at(c) * mass_of(k)));
+        }
+    }
+    lds_order();
+    double wm[4];
+    uint64_t zs = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        zs += ms.mhist[4 * lane + q];
+        wm[q] = (double)ms.mhist[4 * lane + q];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o, 64);
+    uint32_t fkey = kstar;
+    double kept = (double)zs;
+    if (a.top_p < 1.0) {
+        const double target = a.top_p * (double)zs;
+        double mabove = 0.0;
+        const int pbin = crossing(wm, target, mabove);
+        if constexpr (DT == kBF16) {
+            fkey = km - (uint32_t)pbin;
+            kept = mabove + (double)ms.mhist[pbin];
+        } else {
+            // The largest key of bin pbin whose weight from the top reaches
+            // target: rank the bin's survivors.
+            lds_order();
+            if (lane == 0) ms.nlist = 0u;
+            lds_order();
+#pragma unroll
+            for (int c = 0; c < kMergeTiles; ++c) {
+                const bool g = ev[c] != 0u && key_at(c) >= kstar && bin_of(key_at(c)) == (uint32_t)pbin;
+                const uint64_t mask = __ballot(g);
+                if (mask) {
+                    const uint32_t base = ms.nlist;
+                    lds_order();
+                    const uint32_t i = base + lanes_below(mask);
+                    if (g && i < (uint32_t)kMergeList) {
+                        ms.lkey[i] = key_at(c);
+                        ms.lmass[i] = mass_of(key_at(c));
+                    }
+                    if (lane == 0) ms.nlist = base + (uint32_t)__popcll(mask);
+                    lds_order();
+                }
+            }
+            const uint32_t nl = ms.nlist;
+            if (nl > (uint32_t)kMergeList) {
+                give_up();
+                return;
+            }
+            uint32_t found = 0u;
+            double fkept = 0.0;
+            for (uint32_t i = lane; i < nl; i += 64) {
+                const uint32_t ki = ms.lkey[i];
+                uint64_t gt = 0, ge = 0;
+                for (uint32_t j = 0; j < nl; ++j) {
+                    const uint32_t kj = ms.lkey[j];
+                    const uint64_t mj = ms.lmass[j];
+                    gt += kj > ki ? mj : 0ull;
+                    ge += kj >= ki ? mj : 0ull;
+                }
+                if (mabove + (double)gt < target && target <= mabove + (double)ge && ki >= found) {
+                    found = ki;
+                    fkept = mabove + (double)ge;
+                }
+            }
+            const uint32_t best = wave_max_u32(found);
+            const uint64_t who = __ballot(found == best && found != 0u);
+            if (!who) {
+                give_up();
+                return;
+            }
+            fkey = best;
+            kept = __shfl(fkept, who ? __ffsll((unsigned long long)who) - 1 : 0, 64);
+        }
+    }
+    write_outputs<DT>(a, s, mx, val(fkey), kept / kFix, lane, 64, true, l_tok);
+    if (lane == 0) *done = 1u;
 }
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
     const RowSlot s = row_slot<DT>(a);
     if (s.skip) return;
+    // A row floor_merge decided (written by the previous kernel).
+    if (a.cand_done && a.cand_done[blockIdx.x] != 0u) return;
     RowRef r;
     r.row = s.row;
     r.V = a.V;
@@ -1252,7 +1743,21 @@ template <int DT, bool VEC>
 hipError_t launch_t(const FloorParams& p, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     const size_t blocks = (size_t)p.B * p.R;
     if (blocks == 0) return hipSuccess;
-    hipExtLaunchKernelGGL((floor_rows<DT, VEC>), dim3((unsigned)blocks), dim3(kFT), 0, s, start, stop, 0, p);
+    if (VEC && cands_usable(p)) {
+        // A small top-k: the tiles' candidates (the start event is this
+        // dispatch's), their merge per row, then the full-row path for the
+        // rows the merge left.
+        hipExtLaunchKernelGGL(floor_cands<DT>, dim3((unsigned)p.C, (unsigned)p.R, (unsigned)p.B), dim3(kThreads), 0,
+                              s, start, nullptr, 0, p);
+        hipLaunchKernelGGL(floor_merge<DT>, dim3((unsigned)((blocks + kMergeWaves - 1) / kMergeWaves)),
+                           dim3(kMergeWaves * 64), 0, s, p);
+        hipExtLaunchKernelGGL((floor_rows<DT, VEC>), dim3((unsigned)blocks), dim3(kFT), 0, s, nullptr, stop, 0, p);
+        return hipGetLastError();
+    }
+    FloorParams q = p;
+    q.cand_head = nullptr;                                // the window paths alone
+    q.cand_done = nullptr;
+    hipExtLaunchKernelGGL((floor_rows<DT, VEC>), dim3((unsigned)blocks), dim3(kFT), 0, s, start, stop, 0, q);
     return hipGetLastError();
 }
 

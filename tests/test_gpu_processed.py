@@ -184,6 +184,53 @@ def test_processed_fallback_paths():
     assert nd == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("kind", ["spikes", "ties", "neginf", "normal"])
+def test_processed_small_top_k_edges(dtype, kind):
+    """A small top-k (at most 64) takes its cuts from each 16 KB tile's
+    largest logits; rows whose cut lies below some tile's candidates (a tile
+    holding a few far larger logits), coarse ties, a third of each row -inf,
+    and top-k 64 / 65 (the limit and past it) against the oracle."""
+    rng = np.random.default_rng(31 + len(kind) + (dtype == "bf16"))
+    B, K, V = 6, 2, 40000
+    lt = (rng.standard_normal((B, K + 1, V)) * 2.0).astype(np.float32)
+    if kind == "spikes":
+        # A few logits far above the rest in one tile: that tile's candidates
+        # stop near its spikes, above the row's top-k cut.
+        lt[:, :, 100:103] += 60.0
+    elif kind == "ties":
+        lt = np.round(lt).astype(np.float32)
+    elif kind == "neginf":
+        lt[:, :, : V // 3] = -np.inf
+    ld = (lt[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32) * 0.5).astype(np.float32)
+    if kind == "neginf":
+        ld[:, :, : V // 3] = -np.inf
+    T = 0.9
+    arr_t = workloads.bf16_bits(lt) if dtype == "bf16" else lt
+    arr_d = workloads.bf16_bits(ld) if dtype == "bf16" else ld
+    toks = rng.integers(0, V, (B, K)).astype(np.int32)
+    unif = rng.random((B, K + 1), dtype=np.float32)
+    wl = workloads.Workload("edges", B, K, V, dtype, T, False, arr_t, arr_d, toks, unif)
+    for k, p in [(1, 1.0), (5, 0.9), (50, 1.0), (50, 0.8), (64, 0.95), (65, 0.9)]:
+        _processed_case("edges-%s-%s" % (kind, dtype), wl, k, p)
+
+
+@pytest.mark.parametrize("dtype,V", [("fp32", 200000), ("bf16", 340000)])
+def test_processed_small_top_k_long_rows(dtype, V):
+    """Rows of more 16 KB tiles than the one-wave merge takes: their small
+    top-k cuts come from the full-row path, after the candidates pass."""
+    rng = np.random.default_rng(V)
+    B, K = 2, 1
+    lt = (rng.standard_normal((B, K + 1, V)) * 2.5).astype(np.float32)
+    ld = (lt[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32)).astype(np.float32)
+    arr_t = workloads.bf16_bits(lt) if dtype == "bf16" else lt
+    arr_d = workloads.bf16_bits(ld) if dtype == "bf16" else ld
+    wl = workloads.Workload("long", B, K, V, dtype, 0.8, False, arr_t, arr_d,
+                            rng.integers(0, V, (B, K)).astype(np.int32), rng.random((B, K + 1), dtype=np.float32))
+    for k, p in [(50, 0.9), (10, 1.0)]:
+        _processed_case("long-%s" % dtype, wl, k, p)
+
+
 def test_processed_timed_records_events():
     import speculative_decoding_verification_10_amd as sd
     wl = workloads.make("peaked", set_index=5)
