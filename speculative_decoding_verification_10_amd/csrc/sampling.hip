@@ -1284,8 +1284,15 @@ __global__ __launch_bounds__(kThreads) void floor_cands(FloorParams a) {
         decode<DT>(raw[u], x);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const int bn = bin_of(x[e]);
-            if (bn >= 0) atomicAdd(&hist[bn], 1u);
+            if constexpr (DT == kBF16) {
+                // The key of every logit (branch-free), the atomic under the
+                // window test alone.
+                const uint32_t d = km - key16_of(__float_as_uint(x[e]) >> 16);
+                if (x[e] >= xlo) atomicAdd(&hist[d], 1u);
+            } else {
+                const int bn = bin_of(x[e]);
+                if (bn >= 0) atomicAdd(&hist[bn], 1u);
+            }
         }
     }
     __syncthreads();
