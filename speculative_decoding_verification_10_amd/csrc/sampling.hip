@@ -10,8 +10,12 @@
 //   top-p: on the top-k survivors, the largest logit v whose upper set
 //          {l >= v} holds at least top_p of the survivors' mass.
 //
-// One workgroup of 1,024 threads per row.  The row is read from HBM once;
-// the later passes over it mostly hit the L2 / Infinity Cache.  Rows of
+// A small top-k (at most kCandPerTile) in the processed verify step takes
+// its cuts from tile candidates (floor_cands, floor_merge, described where
+// they are defined); floor_rows then takes only the rows those leave.
+//
+// floor_rows: one workgroup of 1,024 threads per row.  The row is read from
+// HBM once; the later passes over it mostly hit the L2 / Infinity Cache.  Rows of
 // whole 16-byte vectors take window paths (bins over 16-bit keys for bf16,
 // over the mass exponent for fp32; each is described where it is defined).
 // Other rows (misaligned or of a ragged length) take the general selection:
