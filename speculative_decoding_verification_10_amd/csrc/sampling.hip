@@ -1271,16 +1271,12 @@ __global__ __launch_bounds__(kThreads) void floor_cands(FloorParams a) {
         M = offset_of(xm, a.sc);
         Dh = -exponent2(xm, M, a.sc);
     }
-    // Bin of a logit: 0 (the largest) to 255, -1 outside the window.
+    // fp32: bin of a logit, 0 (the largest) to 255, -1 outside the window
+    // (-inf gives +inf, or NaN when the largest is -inf: outside).  bf16
+    // bins are km - key, inside the window x >= xlo.
     auto bin_of = [&](float x) -> int {
-        if constexpr (DT == kBF16) {
-            if (!(x >= xlo)) return -1;
-            return (int)(km - key16_of(__float_as_uint(x) >> 16));
-        } else {
-            // -inf gives +inf (or NaN when the largest is -inf): outside.
-            const float q = (-exponent2(x, M, a.sc) - Dh) * kCandBinsPerBinade;
-            return q < (float)kCandBins ? (int)q : -1;
-        }
+        const float q = (-exponent2(x, M, a.sc) - Dh) * kCandBinsPerBinade;
+        return q < (float)kCandBins ? (int)q : -1;
     };
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
