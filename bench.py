@@ -242,6 +242,9 @@ def main():
                          "(specdec_acceptance_counts) to device counters")
     ap.add_argument("--no-phase-events", action="store_true",
                     help="time whole calls only (no events recorded inside specdec_verify)")
+    ap.add_argument("--no-events", action="store_true",
+                    help="no events at all: the wall clock alone (the roofline and call figures are "
+                         "omitted); events cost the host ~15 us per call, which bounds small configs")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy a MIB-MiB device buffer 10 times (a plain copy "
                          "of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -349,7 +352,7 @@ def main():
 
     # The row pass is timed inside each stochastic call by events that its
     # kernel dispatches take themselves (specdec_verify_timed).
-    phase = not args.graph and not args.no_phase_events
+    phase = not args.graph and not args.no_phase_events and not args.no_events
     phase_ev = None
     handles = None
 
@@ -462,7 +465,7 @@ def main():
     # also took an event at its end (otherwise it also counts the previous
     # kernel's tail), so that step records its end-of-call event alone.
     every = max(1, args.phase_every)
-    sampled = [r for r in range(args.steps) if r % every == every - 1]
+    sampled = [] if args.no_events else [r for r in range(args.steps) if r % every == every - 1]
     fences = [r - 1 for r in sampled if r >= 1 and (r - 1) not in sampled]
     if phase:
         nev = 3
@@ -489,13 +492,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    # The same number of steps again without any event (events cost the host
+    # ~15 us per call, which bounds small configs): reported beside the
+    # timed figures, which keep the events that the roofline is measured by.
+    no_event_ms = None
+    if sampled:
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for r in range(args.steps):
+            run(r, None)
+        torch.cuda.synchronize()
+        no_event_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     rows_ms = None
     if phase:
         rows_ms = float(np.median([e[0].elapsed_time(e[1]) for e in phase_ev.values()]))
         call_ms = float(np.median([e[0].elapsed_time(e[-1]) for e in phase_ev.values()]))
         per_launch_ms = call_ms
-    else:
+    elif sampled:
         per_launch_ms = float(np.median([starts[r].elapsed_time(ends[r]) for r in sampled]))
+    else:
+        per_launch_ms = None
 
     # Per set: verified positions and algorithmic bytes; the timed steps
     # visit set r % nsets.
@@ -514,7 +530,7 @@ def main():
     alg_total = sum(set_alg[i] for i in visits)
     positions = positions_total / args.steps
     alg = alg_total / args.steps
-    sampled_sets = [r % len(sets) for r in sampled]
+    sampled_sets = [r % len(sets) for r in sampled] or list(range(len(sets)))
     alg_sampled = float(np.mean([set_alg[i] for i in sampled_sets]))
     rows_sampled = float(np.mean([set_rows[i] for i in sampled_sets]))
     # Stored counter figures belong to the unprocessed step's kernels.
@@ -538,7 +554,7 @@ def main():
                    "n_min": NGRAM_N_MIN, "n_max": NGRAM_N_MAX}
     value = positions_total / wall
     gbps = alg_total / wall / 1e9
-    achieved = alg_sampled / (per_launch_ms * 1e-3) / 1e9
+    achieved = None if per_launch_ms is None else alg_sampled / (per_launch_ms * 1e-3) / 1e9
     if phase:
         # The dominant kernel: the pass over the rows (all of the greedy
         # path's bytes, ~85% of the stochastic path's).
@@ -560,6 +576,9 @@ def main():
                             "greedy_rows, greedy_decisions" if greedy else
                             "floor_rows, [verify_decide,] verify_final" if processed
                             else "verify_rows, [verify_decide,] verify_final")}
+    elif per_launch_ms is None:
+        roofline = None                   # --no-events: no per-launch figures
+        call = None
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
@@ -609,7 +628,7 @@ def main():
         "verified_positions_per_step": round(positions, 2),
         "bytes_per_verified_position": {
             "algorithmic": round(alg / positions, 1),
-            "counters": (None if (call or roofline).get("traffic") is None else
+            "counters": (None if (call or roofline or {}).get("traffic") is None else
                          round((call or roofline)["traffic"] / set_pos[0], 1)),
             "note": "counters: rocprofv3 FETCH_SIZE + WRITE_SIZE per call (mean over the profiled calls), "
                     "scaled by the copy calibration, over the verified positions of one call"},
@@ -619,6 +638,10 @@ def main():
                                for n_, st in zip(set_nacc, sets)]),
         "phase_events": {"every": every, "sampled_steps": len(sampled),
                          "fence_steps": len(fences) if phase else 0},
+        "without_events": (None if no_event_ms is None else
+                           {"ms_per_step": round(no_event_ms, 5),
+                            "value": round(positions_total / args.steps / (no_event_ms * 1e-3), 1),
+                            "note": "the same steps again right after the timed ones, with no event"}),
         "roofline": roofline,
         "cpu_baseline": None,
     }
