@@ -12,7 +12,8 @@
 //
 // A small top-k (at most kCandPerTile) in the processed verify step takes
 // its cuts from tile candidates (floor_cands, floor_merge, described where
-// they are defined); floor_rows then takes only the rows those leave.
+// they are defined); floor_rows then takes only the rows those leave, each
+// of its workgroups every kRowsGrid-th row slot.
 //
 // floor_rows: one workgroup of 1,024 threads per row.  The row is read from
 // HBM once; the later passes over it mostly hit the L2 / Infinity Cache.  Rows of
@@ -1191,7 +1192,7 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
 // a key at or below the tile's own top_k-th largest (0 when the window holds
 // fewer than top_k logits).
 //
-// floor_merge, one wave per row, merges the row's entries.  The row's
+// floor_merge, one workgroup per row, merges the row's entries.  The row's
 // top_k-th largest K* is at least every tile's own, so at least G of every
 // tile: entries below the largest G are dropped.  The top_k-th largest of
 // the rest is the row's when it is >= L of every tile (each tile then holds
@@ -1204,25 +1205,32 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
 constexpr int kCandBins = kThreads;             // one bin per thread of floor_cands
 constexpr float kCandBinsPerBinade = 8.0f;      // fp32: bins over the mass exponent
 
+// Inclusive prefix sum, min and max of a u32 over the wave (DPP: rows of
+// 16 lanes, then the row broadcasts; min and max in every lane).
 __device__ __forceinline__ uint32_t wave_incl_u32(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t u = (uint32_t)__shfl_up((int)v, o, 64);
-        if (lane >= o) v += u;
-    }
-    return v;
+    int x = (int)v;
+    x += dpp<kDppRowShr1>(x, 0);
+    x += dpp<kDppRowShr2>(x, 0);
+    x += dpp<kDppRowShr4>(x, 0);
+    x += dpp<kDppRowShr8>(x, 0);
+    x += dpp<kDppRowBcast15, 0xA>(x, 0);
+    x += dpp<kDppRowBcast31, 0xC>(x, 0);
+    return (uint32_t)x;
 }
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
+    constexpr int id = MAX ? 0 : -1;
+    auto f = [](uint32_t p, int q) { return MAX ? max(p, (uint32_t)q) : min(p, (uint32_t)q); };
+    v = f(v, dpp<kDppQuad1032>((int)v, id));
+    v = f(v, dpp<kDppQuad2301>((int)v, id));
+    v = f(v, dpp<kDppRowHalfMirror>((int)v, id));
+    v = f(v, dpp<kDppRowMirror>((int)v, id));
+    v = f(v, dpp<kDppRowBcast15, 0xA>((int)v, id));
+    v = f(v, dpp<kDppRowBcast31, 0xC>((int)v, id));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
-}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_ext_u32<false>(v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_ext_u32<true>(v); }
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void floor_cands(FloorParams a) {
@@ -1278,20 +1286,37 @@ __global__ __launch_bounds__(kThreads) void floor_cands(FloorParams a) {
         const float q = (-exponent2(x, M, a.sc) - Dh) * kCandBinsPerBinade;
         return q < (float)kCandBins ? (int)q : -1;
     };
+    if (DT == kBF16 && xlo > 0.0f) {
+        // A window of positive values: the bin of the 16-bit pattern h is
+        // hm - h, and every pattern outside the window (smaller, negative,
+        // -inf past the row end, or NaN) gives a difference above 255 as an
+        // unsigned number.
+        const uint32_t hm = km & 0x7FFFu;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        float x[E];
-        decode<DT>(raw[u], x);
+        for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if constexpr (DT == kBF16) {
-                // The key of every logit (branch-free), the atomic under the
-                // window test alone.
-                const uint32_t d = km - key16_of(__float_as_uint(x[e]) >> 16);
-                if (x[e] >= xlo) atomicAdd(&hist[d], 1u);
-            } else {
-                const int bn = bin_of(x[e]);
-                if (bn >= 0) atomicAdd(&hist[bn], 1u);
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t d0 = hm - (raw[u][q] & 0xFFFFu);
+                const uint32_t d1 = hm - (raw[u][q] >> 16);
+                if (d0 < (uint32_t)kCandBins) atomicAdd(&hist[d0], 1u);
+                if (d1 < (uint32_t)kCandBins) atomicAdd(&hist[d1], 1u);
+            }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float x[E];
+            decode<DT>(raw[u], x);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if constexpr (DT == kBF16) {
+                    // The key of every logit (branch-free), the atomic under
+                    // the window test alone.
+                    const uint32_t d = km - key16_of(__float_as_uint(x[e]) >> 16);
+                    if (x[e] >= xlo) atomicAdd(&hist[d], 1u);
+                } else {
+                    const int bn = bin_of(x[e]);
+                    if (bn >= 0) atomicAdd(&hist[bn], 1u);
+                }
             }
         }
     }
@@ -1325,7 +1350,7 @@ __global__ __launch_bounds__(kThreads) void floor_cands(FloorParams a) {
             if (cnt_incl[q] >= (uint32_t)a.top_k) first = 4 * lane + q;
         const uint64_t mr = __ballot(first >= 0);
         const uint32_t bstar =
-            mr ? (uint32_t)__shfl(first, __ffsll((unsigned long long)mr) - 1, 64) : 0xFFFFFFFFu;
+            mr ? (uint32_t)__builtin_amdgcn_readlane(first, __ffsll((unsigned long long)mr) - 1) : 0xFFFFFFFFu;
         const uint32_t blast = bstar == 0xFFFFFFFFu ? (uint32_t)(kCandBins - 1) : bstar;
         // The emitted bins: a prefix (at most kCandPerTile entries); b_emit is its last.
         int last = -1;
@@ -1335,7 +1360,7 @@ __global__ __launch_bounds__(kThreads) void floor_cands(FloorParams a) {
             if ((uint32_t)(4 * lane + q) <= blast && used <= (uint32_t)kCandPerTile) last = 4 * lane + q;
         }
         const uint64_t ml = __ballot(last >= 0);
-        const int b_emit = ml ? __shfl(last, 63 - __clzll((long long)ml), 64) : -1;
+        const int b_emit = ml ? __builtin_amdgcn_readlane(last, 63 - __clzll((long long)ml)) : -1;
         if constexpr (DT == kBF16) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1449,16 +1474,20 @@ __device__ __forceinline__ void write_outputs(const FloorParams& a, const RowSlo
     }
 }
 
-// floor_merge: one wave per row of a small top-k (see floor_cands).  Lane l
-// holds entry l of every tile, in registers.  One histogram over 256 bins
-// from the row's largest key down decides both cuts: bf16 bins are exact
-// keys (every kept entry lies within 256 keys of the largest: the tile that
-// holds it keeps its own top_k within its window); fp32 bins are the mass
-// exponent at 8 per binade, and the bin holding a cut is resolved exactly by
-// ranking its few entries.  Rows it decides get their outputs here and
-// done[row] = 1; the others done[row] = 0, and floor_rows takes them.
-constexpr int kMergeWaves = 4;                  // rows per workgroup
+// floor_merge: one workgroup of four waves per row of a small top-k (see
+// floor_cands).  Wave w takes the row's tiles w, w + 4, w + 8, ...; lane l
+// holds entry l of each of them, in registers.  One histogram over 256 bins
+// from the row's largest key down, shared by the waves, decides both cuts:
+// bf16 bins are exact keys (every kept entry lies within 256 keys of the
+// largest: the tile that holds it keeps its own top_k within its window);
+// fp32 bins are the mass exponent at 8 per binade, and the bin holding a cut
+// is resolved exactly by ranking its few entries.  Every wave reads the whole
+// histogram and takes the same decisions.  Rows it decides get their outputs
+// here and done[row] = 1; the others done[row] = 0, and floor_rows takes them.
+constexpr int kMergeWaves = 4;                  // waves per row
+constexpr int kMergeThreads = kMergeWaves * 64;
 constexpr int kMergeTiles = 40;                 // tiles of a row the merge takes (more: floor_rows)
+constexpr int kMergeHeld = kMergeTiles / kMergeWaves;   // tiles per wave
 constexpr int kMergeList = 256;                 // fp32: entries of one bin ranked in LDS
 
 struct MergeShared {
@@ -1466,30 +1495,29 @@ struct MergeShared {
     uint64_t mhist[256];
     uint32_t lkey[kMergeList];
     uint64_t lmass[kMergeList];
-    uint32_t nlist;
+    uint32_t nlist[2];                          // listed entries: the top-k bin, the top-p bin
+    uint32_t best[2];                           // ranked keys: K*, the top-p cut
+    double kept;                                // mass at and above the top-p cut
 };
 
 template <int DT>
-__global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
+__global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
     static_assert(kCandPerTile == 64, "lane l holds entry l of every tile");
-    __shared__ MergeShared ms_all[kMergeWaves];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int rs = blockIdx.x * kMergeWaves + wv;                // row slot b * R + rr
-    if (rs >= a.B * a.R) return;
-    MergeShared& ms = ms_all[wv];
+    static_assert(kMergeThreads == 256 && kMergeHeld * kMergeWaves == kMergeTiles, "one bin per thread");
+    __shared__ MergeShared ms;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int rs = blockIdx.x;                                   // row slot b * R + rr
     const int C = a.C;
     uint32_t* done = a.cand_done + rs;
     if (C > kMergeTiles) {
         const RowSlot s = row_slot_of<DT>(a, rs);
-        if (!s.skip && lane == 0) *done = 0u;
+        if (!s.skip && t == 0) *done = 0u;
         return;
     }
-    // Within one wave LDS accesses complete in program order; this keeps the
-    // compiler from moving them across each other.
-    auto lds_order = [] { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
-    // One batch of loads: k_b (in row_slot_of), the heads, entry `lane` of
-    // every tile (checked against the counts afterwards) and the draft
-    // token; then the logit at the draft token.
+    // One batch of loads: k_b (in row_slot_of), the heads (in every wave),
+    // entry `lane` of the wave's tiles (checked against the counts
+    // afterwards) and the draft token; then (wave 0) the logit at it.
     const size_t at0 = (size_t)rs * C;
     const uint32_t* head = a.cand_head + at0 * 4;
     const uint32_t* ent = a.cand_ent + at0 * kCandPerTile;
@@ -1500,12 +1528,15 @@ __global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
         h2 = min(head[4 * lane + 2], (uint32_t)kCandPerTile);
         h3 = head[4 * lane + 3];
     }
-    uint32_t ev[kMergeTiles];
+    uint32_t ev[kMergeHeld];
 #pragma unroll
-    for (int c = 0; c < kMergeTiles; ++c) ev[c] = c < C ? ent[c * kCandPerTile + lane] : 0u;
+    for (int j = 0; j < kMergeHeld; ++j) {
+        const int c = wv + kMergeWaves * j;
+        ev[j] = c < C ? ent[c * kCandPerTile + lane] : 0u;
+    }
     const RowSlot s = row_slot_of<DT>(a, rs);
     if (s.skip) return;
-    const bool gathers = s.i < s.kb && a.tokens;
+    const bool gathers = wv == 0 && s.i < s.kb && a.tokens;
     const int tok = gathers ? min(max(a.tokens[(size_t)s.b * a.K + s.i], 0), a.V - 1) : 0;
     const float l_tok = gathers ? load_one<DT>(s.row, tok) : 0.0f;
     const uint32_t km = wave_max_u32(h0);
@@ -1524,32 +1555,35 @@ __global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
             return q < 256.0f ? (uint32_t)(int)q : 256u;
         }
     };
-    auto key_at = [&](int c) -> uint32_t { return (DT == kBF16) ? (ev[c] >> 16) : ev[c]; };
-    auto cnt_at = [&](int c) -> uint32_t { return (DT == kBF16) ? (ev[c] & 0xFFFFu) : 1u; };
+    auto key_at = [&](int j) -> uint32_t { return (DT == kBF16) ? (ev[j] >> 16) : ev[j]; };
+    auto cnt_at = [&](int j) -> uint32_t { return (DT == kBF16) ? (ev[j] & 0xFFFFu) : 1u; };
     auto mass_of = [&](uint32_t k) -> uint64_t { return fix_of(fast_exp2(exponent2(val(k), M, a.sc))); };
     // 0 where a tile has no entry `lane`, where it lies below gmax (below
     // every cut), or below the histogram: when the histogram still holds
     // top_k entries, those lie below the cut too; else the row is left to
-    // floor_rows.
+    // floor_rows.  (The entry count of tile c is lane c of h2.)
 #pragma unroll
-    for (int c = 0; c < kMergeTiles; ++c)
-        if (c >= C || (uint32_t)lane >= (uint32_t)__shfl((int)h2, c, 64) || key_at(c) < gmax ||
-            bin_of(key_at(c)) >= 256u)
-            ev[c] = 0u;
-    auto give_up = [&] {
-        if (lane == 0) *done = 0u;
-    };
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        ms.hist[4 * lane + q] = 0u;
-        ms.mhist[4 * lane + q] = 0ull;
+    for (int j = 0; j < kMergeHeld; ++j) {
+        const int c = wv + kMergeWaves * j;
+        const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)h2, min(c, 63));
+        if (c >= C || (uint32_t)lane >= n || key_at(j) < gmax || bin_of(key_at(j)) >= 256u) ev[j] = 0u;
     }
-    if (lane == 0) ms.nlist = 0u;
-    lds_order();
+    // Every give-up below follows from shared data, so it is taken by all
+    // waves alike, past the last barrier any of them reaches.
+    auto give_up = [&] {
+        if (t == 0) *done = 0u;
+    };
+    ms.hist[t] = 0u;
+    ms.mhist[t] = 0ull;
+    if (t < 2) {
+        ms.nlist[t] = 0u;
+        ms.best[t] = 0u;
+    }
+    __syncthreads();
 #pragma unroll
-    for (int c = 0; c < kMergeTiles; ++c)
-        if (ev[c] != 0u) atomicAdd(&ms.hist[bin_of(key_at(c))], cnt_at(c));
-    lds_order();
+    for (int j = 0; j < kMergeHeld; ++j)
+        if (ev[j] != 0u) atomicAdd(&ms.hist[bin_of(key_at(j))], cnt_at(j));
+    __syncthreads();
     // Lane l holds the bins 4l .. 4l + 3 (descending keys); the first bin
     // where a running weight from the top reaches target, and the weight
     // above it.  The bins' weights must reach target in total.
@@ -1572,6 +1606,20 @@ __global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
         above_out = __shfl(pa, src, 64);
         return __shfl(pick, src, 64);
     };
+    // The entries of one bin, listed in LDS (slot `which`), the wave's
+    // ballot placed at an offset taken by its first lane.
+    auto append = [&](int which, bool g, uint32_t key, bool with_mass) {
+        const uint64_t mask = __ballot(g);
+        if (mask == 0ull) return;
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&ms.nlist[which], (uint32_t)__popcll(mask));
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, 0);
+        const uint32_t i = base + lanes_below(mask);
+        if (g && i < (uint32_t)kMergeList) {
+            ms.lkey[i] = key;
+            if (with_mass) ms.lmass[i] = mass_of(key);
+        }
+    };
     double wc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wc[q] = (double)ms.hist[4 * lane + q];
@@ -1588,26 +1636,17 @@ __global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
         kstar = km - (uint32_t)kbin;
     } else {
 #pragma unroll
-        for (int c = 0; c < kMergeTiles; ++c) {
-            const bool g = ev[c] != 0u && bin_of(key_at(c)) == (uint32_t)kbin;
-            const uint64_t mask = __ballot(g);
-            if (mask) {
-                const uint32_t base = ms.nlist;
-                lds_order();
-                const uint32_t i = base + lanes_below(mask);
-                if (g && i < (uint32_t)kMergeList) ms.lkey[i] = key_at(c);
-                if (lane == 0) ms.nlist = base + (uint32_t)__popcll(mask);
-                lds_order();
-            }
-        }
-        const uint32_t nl = ms.nlist;
+        for (int j = 0; j < kMergeHeld; ++j)
+            append(0, ev[j] != 0u && bin_of(key_at(j)) == (uint32_t)kbin, key_at(j), false);
+        __syncthreads();
+        const uint32_t nl = ms.nlist[0];
         if (nl > (uint32_t)kMergeList) {
             give_up();
             return;
         }
         const uint32_t need = (uint32_t)a.top_k - (uint32_t)cabove;
         uint32_t found = 0u;
-        for (uint32_t i = lane; i < nl; i += 64) {
+        for (uint32_t i = t; i < nl; i += kMergeThreads) {
             const uint32_t ki = ms.lkey[i];
             uint32_t gt = 0u, ge = 0u;
             for (uint32_t j = 0; j < nl; ++j) {
@@ -1617,8 +1656,10 @@ __global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
             }
             if (gt < need && need <= ge) found = ki;                  // equal keys find the same
         }
-        kstar = wave_max_u32(found);
-        lds_order();
+        found = wave_max_u32(found);
+        if (lane == 0 && found != 0u) atomicMax(&ms.best[0], found);
+        __syncthreads();
+        kstar = ms.best[0];
         if (kstar == 0u) {
             give_up();
             return;
@@ -1630,14 +1671,14 @@ __global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
     }
     // The survivors' masses per bin (fp32: in bin kbin only keys >= K*).
 #pragma unroll
-    for (int c = 0; c < kMergeTiles; ++c) {
-        if (ev[c] != 0u && key_at(c) >= kstar) {
-            const uint32_t k = key_at(c);
+    for (int j = 0; j < kMergeHeld; ++j) {
+        if (ev[j] != 0u && key_at(j) >= kstar) {
+            const uint32_t k = key_at(j);
             atomicAdd(reinterpret_cast<unsigned long long*>(&ms.mhist[bin_of(k)]),
-                      (unsigned long long)((uint64_t)cnt_at(c) * mass_of(k)));
+                      (unsigned long long)((uint64_t)cnt_at(j) * mass_of(k)));
         }
     }
-    lds_order();
+    __syncthreads();
     double wm[4];
     uint64_t zs = 0;
 #pragma unroll
@@ -1653,39 +1694,29 @@ __global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
         const double target = a.top_p * (double)zs;
         double mabove = 0.0;
         const int pbin = crossing(wm, target, mabove);
+        if (pbin < 0) {                                          // (top_p > 0 and the largest key's mass make one)
+            give_up();
+            return;
+        }
         if constexpr (DT == kBF16) {
             fkey = km - (uint32_t)pbin;
             kept = mabove + (double)ms.mhist[pbin];
         } else {
             // The largest key of bin pbin whose weight from the top reaches
             // target: rank the bin's survivors.
-            lds_order();
-            if (lane == 0) ms.nlist = 0u;
-            lds_order();
 #pragma unroll
-            for (int c = 0; c < kMergeTiles; ++c) {
-                const bool g = ev[c] != 0u && key_at(c) >= kstar && bin_of(key_at(c)) == (uint32_t)pbin;
-                const uint64_t mask = __ballot(g);
-                if (mask) {
-                    const uint32_t base = ms.nlist;
-                    lds_order();
-                    const uint32_t i = base + lanes_below(mask);
-                    if (g && i < (uint32_t)kMergeList) {
-                        ms.lkey[i] = key_at(c);
-                        ms.lmass[i] = mass_of(key_at(c));
-                    }
-                    if (lane == 0) ms.nlist = base + (uint32_t)__popcll(mask);
-                    lds_order();
-                }
-            }
-            const uint32_t nl = ms.nlist;
+            for (int j = 0; j < kMergeHeld; ++j)
+                append(1, ev[j] != 0u && key_at(j) >= kstar && bin_of(key_at(j)) == (uint32_t)pbin, key_at(j),
+                       true);
+            __syncthreads();
+            const uint32_t nl = ms.nlist[1];
             if (nl > (uint32_t)kMergeList) {
                 give_up();
                 return;
             }
             uint32_t found = 0u;
             double fkept = 0.0;
-            for (uint32_t i = lane; i < nl; i += 64) {
+            for (uint32_t i = t; i < nl; i += kMergeThreads) {
                 const uint32_t ki = ms.lkey[i];
                 uint64_t gt = 0, ge = 0;
                 for (uint32_t j = 0; j < nl; ++j) {
@@ -1699,30 +1730,33 @@ __global__ __launch_bounds__(kMergeWaves * 64) void floor_merge(FloorParams a) {
                     fkept = mabove + (double)ge;
                 }
             }
-            const uint32_t best = wave_max_u32(found);
-            const uint64_t who = __ballot(found == best && found != 0u);
-            if (!who) {
+            const uint32_t wbest = wave_max_u32(found);
+            if (lane == 0 && wbest != 0u) atomicMax(&ms.best[1], wbest);
+            __syncthreads();
+            const uint32_t best = ms.best[1];
+            if (best == 0u) {
                 give_up();
                 return;
             }
+            // Equal keys rank alike: whichever thread found it writes the same mass.
+            if (found == best) ms.kept = fkept;
+            __syncthreads();
             fkey = best;
-            kept = __shfl(fkept, who ? __ffsll((unsigned long long)who) - 1 : 0, 64);
+            kept = ms.kept;
         }
     }
-    write_outputs<DT>(a, s, mx, val(fkey), kept / kFix, lane, 64, true, l_tok);
-    if (lane == 0) *done = 1u;
+    write_outputs<DT>(a, s, mx, val(fkey), kept / kFix, t, kMergeThreads, true, l_tok);
+    if (t == 0) *done = 1u;
 }
 
+// The floor of one row and its outputs; nv is the row's length in 16-byte
+// vectors.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
-    const RowSlot s = row_slot<DT>(a);
-    if (s.skip) return;
-    // A row floor_merge decided (written by the previous kernel).
-    if (a.cand_done && a.cand_done[blockIdx.x] != 0u) return;
+__device__ __forceinline__ void floor_row(const FloorParams& a, const RowSlot& s, int nv) {
     RowRef r;
     r.row = s.row;
     r.V = a.V;
-    r.NV = a.NV;
+    r.NV = nv;
     r.sc = a.sc;
     float m, fl;
     double z;
@@ -1746,25 +1780,78 @@ __global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
     write_outputs<DT>(a, s, m, fl, z);
 }
 
+// Workgroups of floor_rows after floor_merge: one per compute unit of the
+// chip (a workgroup of the full-row path fills one), each taking every
+// kRowsGrid-th row slot that the merge left.
+constexpr int kRowsGrid = 256;
+
+template <int DT, bool VEC, bool LISTED>
+__global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
+    if constexpr (!LISTED) {
+        // One workgroup per row slot.
+        const RowSlot s = row_slot<DT>(a);
+        if (s.skip) return;
+        floor_row<DT, VEC>(a, s, a.NV);
+    } else {
+        // After floor_merge: the flags of a batch of the workgroup's row
+        // slots in one load per thread, then the undecided rows one after
+        // another.  The first batch is listed before the loop, so that a
+        // workgroup with nothing to do leaves before the row path's set-up.
+        __shared__ int todo[kFT];
+        __shared__ int ntodo;
+        const int rows = a.B * a.R;
+        const int step = (int)gridDim.x * kFT;
+        auto list = [&](int first) -> int {
+            if (threadIdx.x == 0) ntodo = 0;
+            __syncthreads();
+            const int rs = first + (int)threadIdx.x * (int)gridDim.x;
+            if (rs < rows && a.cand_done[rs] == 0u && !row_slot_of<DT>(a, rs).skip)
+                todo[atomicAdd(&ntodo, 1)] = rs;
+            __syncthreads();
+            return __builtin_amdgcn_readfirstlane(ntodo);
+        };
+        int first = blockIdx.x;
+        int n = list(first);
+        while (n > 0 || first + step < rows) {
+            for (int i = 0; i < n; ++i) {
+                // The row length made opaque to the compiler, so that the
+                // loads' offsets are formed where they are used rather than
+                // kept (spilled) across the rows.
+                int nv = a.NV;
+                asm volatile("" : "+v"(nv));
+                floor_row<DT, VEC>(a, row_slot_of<DT>(a, __builtin_amdgcn_readfirstlane(todo[i])),
+                                   __builtin_amdgcn_readfirstlane(nv));
+                __syncthreads();                          // the shared memory is the next row's
+            }
+            first += step;
+            if (first >= rows) break;
+            n = list(first);
+        }
+    }
+}
+
 template <int DT, bool VEC>
 hipError_t launch_t(const FloorParams& p, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     const size_t blocks = (size_t)p.B * p.R;
     if (blocks == 0) return hipSuccess;
-    if (VEC && cands_usable(p)) {
-        // A small top-k: the tiles' candidates (the start event is this
-        // dispatch's), their merge per row, then the full-row path for the
-        // rows the merge left.
-        hipExtLaunchKernelGGL(floor_cands<DT>, dim3((unsigned)p.C, (unsigned)p.R, (unsigned)p.B), dim3(kThreads), 0,
-                              s, start, nullptr, 0, p);
-        hipLaunchKernelGGL(floor_merge<DT>, dim3((unsigned)((blocks + kMergeWaves - 1) / kMergeWaves)),
-                           dim3(kMergeWaves * 64), 0, s, p);
-        hipExtLaunchKernelGGL((floor_rows<DT, VEC>), dim3((unsigned)blocks), dim3(kFT), 0, s, nullptr, stop, 0, p);
-        return hipGetLastError();
+    if constexpr (VEC) {
+        if (cands_usable(p)) {
+            // A small top-k: the tiles' candidates (the start event is this
+            // dispatch's), their merge per row, then the full-row path for
+            // the rows the merge left.
+            hipExtLaunchKernelGGL(floor_cands<DT>, dim3((unsigned)p.C, (unsigned)p.R, (unsigned)p.B), dim3(kThreads),
+                                  0, s, start, nullptr, 0, p);
+            hipLaunchKernelGGL(floor_merge<DT>, dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, p);
+            hipExtLaunchKernelGGL((floor_rows<DT, true, true>),
+                                  dim3((unsigned)(blocks < (size_t)kRowsGrid ? blocks : (size_t)kRowsGrid)), dim3(kFT),
+                                  0, s, nullptr, stop, 0, p);
+            return hipGetLastError();
+        }
     }
     FloorParams q = p;
     q.cand_head = nullptr;                                // the window paths alone
     q.cand_done = nullptr;
-    hipExtLaunchKernelGGL((floor_rows<DT, VEC>), dim3((unsigned)blocks), dim3(kFT), 0, s, start, stop, 0, q);
+    hipExtLaunchKernelGGL((floor_rows<DT, VEC, false>), dim3((unsigned)blocks), dim3(kFT), 0, s, start, stop, 0, q);
     return hipGetLastError();
 }
 
