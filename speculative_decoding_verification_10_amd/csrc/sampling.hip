@@ -1474,19 +1474,21 @@ __device__ __forceinline__ void write_outputs(const FloorParams& a, const RowSlo
     }
 }
 
-// floor_merge: one workgroup of four waves per row of a small top-k (see
-// floor_cands).  Wave w takes the row's tiles w, w + 4, w + 8, ...; lane l
-// holds entry l of each of them, in registers.  One histogram over 256 bins
-// from the row's largest key down, shared by the waves, decides both cuts:
-// bf16 bins are exact keys (every kept entry lies within 256 keys of the
-// largest: the tile that holds it keeps its own top_k within its window);
-// fp32 bins are the mass exponent at 8 per binade, and the bin holding a cut
-// is resolved exactly by ranking its few entries.  Every wave reads the whole
-// histogram and takes the same decisions.  Rows it decides get their outputs
-// here and done[row] = 1; the others done[row] = 0, and floor_rows takes them.
+// The merge of one row of a small top-k (see floor_cands), by a group of
+// four waves (256 threads, t the thread within the group).  Wave w takes the
+// row's tiles w, w + 4, w + 8, ...; lane l holds entry l of each of them, in
+// registers.  One histogram over 256 bins from the row's largest key down,
+// shared by the waves, decides both cuts: bf16 bins are exact keys (every
+// kept entry lies within 256 keys of the largest: the tile that holds it
+// keeps its own top_k within its window); fp32 bins are the mass exponent at
+// 8 per binade, and the bin holding a cut is resolved exactly by ranking its
+// few entries.  Every wave reads the whole histogram and takes the same
+// decisions.  A decided row gets its outputs here; a row left undecided goes
+// to the full-row path.  The workgroup barriers are the same for every row
+// (none depends on the row's data), so several groups share a workgroup.
 constexpr int kMergeWaves = 4;                  // waves per row
 constexpr int kMergeThreads = kMergeWaves * 64;
-constexpr int kMergeTiles = 40;                 // tiles of a row the merge takes (more: floor_rows)
+constexpr int kMergeTiles = 40;                 // tiles of a row the merge takes (more: the full-row path)
 constexpr int kMergeHeld = kMergeTiles / kMergeWaves;   // tiles per wave
 constexpr int kMergeList = 256;                 // fp32: entries of one bin ranked in LDS
 
@@ -1500,25 +1502,22 @@ struct MergeShared {
     double kept;                                // mass at and above the top-p cut
 };
 
+enum : int { kMergeNone = 0, kMergeDecided = 1, kMergeLeft = 2 };   // no row, decided, left
+
 template <int DT>
-__global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
+__device__ __forceinline__ int merge_row(const FloorParams& a, int rs, MergeShared& ms, int t) {
     static_assert(kCandPerTile == 64, "lane l holds entry l of every tile");
     static_assert(kMergeThreads == 256 && kMergeHeld * kMergeWaves == kMergeTiles, "one bin per thread");
-    __shared__ MergeShared ms;
-    const int t = threadIdx.x, lane = t & 63;
+    const int lane = t & 63;
     const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int rs = blockIdx.x;                                   // row slot b * R + rr
+    const int rows = a.B * a.R;
     const int C = a.C;
-    uint32_t* done = a.cand_done + rs;
-    if (C > kMergeTiles) {
-        const RowSlot s = row_slot_of<DT>(a, rs);
-        if (!s.skip && t == 0) *done = 0u;
-        return;
-    }
+    // A slot past the last one works on the last (and writes nothing).
+    const int rsc = rs < rows ? rs : rows - 1;
     // One batch of loads: k_b (in row_slot_of), the heads (in every wave),
     // entry `lane` of the wave's tiles (checked against the counts
     // afterwards) and the draft token; then (wave 0) the logit at it.
-    const size_t at0 = (size_t)rs * C;
+    const size_t at0 = (size_t)rsc * C;
     const uint32_t* head = a.cand_head + at0 * 4;
     const uint32_t* ent = a.cand_ent + at0 * kCandPerTile;
     uint32_t h0 = 0u, h1 = 0u, h2 = 0u, h3 = 0u;
@@ -1534,9 +1533,11 @@ __global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
         const int c = wv + kMergeWaves * j;
         ev[j] = c < C ? ent[c * kCandPerTile + lane] : 0u;
     }
-    const RowSlot s = row_slot_of<DT>(a, rs);
-    if (s.skip) return;
-    const bool gathers = wv == 0 && s.i < s.kb && a.tokens;
+    const RowSlot s = row_slot_of<DT>(a, rsc);
+    // A skipped row (past k_b) holds no candidates: its workspace is stale
+    // but read within bounds, and nothing of it is written.
+    const bool live = rs < rows && !s.skip;
+    const bool gathers = live && wv == 0 && s.i < s.kb && a.tokens;
     const int tok = gathers ? min(max(a.tokens[(size_t)s.b * a.K + s.i], 0), a.V - 1) : 0;
     const float l_tok = gathers ? load_one<DT>(s.row, tok) : 0.0f;
     const uint32_t km = wave_max_u32(h0);
@@ -1561,18 +1562,13 @@ __global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
     // 0 where a tile has no entry `lane`, where it lies below gmax (below
     // every cut), or below the histogram: when the histogram still holds
     // top_k entries, those lie below the cut too; else the row is left to
-    // floor_rows.  (The entry count of tile c is lane c of h2.)
+    // the full-row path.  (The entry count of tile c is lane c of h2.)
 #pragma unroll
     for (int j = 0; j < kMergeHeld; ++j) {
         const int c = wv + kMergeWaves * j;
         const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)h2, min(c, 63));
         if (c >= C || (uint32_t)lane >= n || key_at(j) < gmax || bin_of(key_at(j)) >= 256u) ev[j] = 0u;
     }
-    // Every give-up below follows from shared data, so it is taken by all
-    // waves alike, past the last barrier any of them reaches.
-    auto give_up = [&] {
-        if (t == 0) *done = 0u;
-    };
     ms.hist[t] = 0u;
     ms.mhist[t] = 0ull;
     if (t < 2) {
@@ -1586,7 +1582,7 @@ __global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
     __syncthreads();
     // Lane l holds the bins 4l .. 4l + 3 (descending keys); the first bin
     // where a running weight from the top reaches target, and the weight
-    // above it.  The bins' weights must reach target in total.
+    // above it (-1 when the bins' weights fall short of target).
     auto crossing = [&](const double (&wb)[4], double target, double& above_out) -> int {
         const double mine = (wb[0] + wb[1]) + (wb[2] + wb[3]);
         double run = wave_inclusive_scan(mine) - mine;          // the lanes before this one
@@ -1603,8 +1599,9 @@ __global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
         const uint64_t hit = __ballot(pick >= 0);
         if (!hit) return -1;
         const int src = __ffsll((unsigned long long)hit) - 1;
-        above_out = __shfl(pa, src, 64);
-        return __shfl(pick, src, 64);
+        above_out = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(pa), src),
+                                     __builtin_amdgcn_readlane(__double2loint(pa), src));
+        return __builtin_amdgcn_readlane(pick, src);
     };
     // The entries of one bin, listed in LDS (slot `which`), the wave's
     // ballot placed at an offset taken by its first lane.
@@ -1625,28 +1622,24 @@ __global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
     for (int q = 0; q < 4; ++q) wc[q] = (double)ms.hist[4 * lane + q];
     double cabove = 0.0;
     const int kbin = crossing(wc, (double)a.top_k, cabove);
-    if (kbin < 0) {                                              // fewer than top_k in the histogram
-        give_up();
-        return;
-    }
+    // ok: the row can still be decided here (uniform over the group; every
+    // step below runs either way, so that the barriers stay the same).
+    bool ok = live && kbin >= 0;                                // else fewer than top_k in the histogram
     // K*: the bin's key (bf16), or the (top_k - cabove)-th largest key of the
     // bin's entries (fp32).
-    uint32_t kstar;
+    uint32_t kstar = 0u;
     if constexpr (DT == kBF16) {
         kstar = km - (uint32_t)kbin;
     } else {
 #pragma unroll
         for (int j = 0; j < kMergeHeld; ++j)
-            append(0, ev[j] != 0u && bin_of(key_at(j)) == (uint32_t)kbin, key_at(j), false);
+            append(0, ok && ev[j] != 0u && bin_of(key_at(j)) == (uint32_t)kbin, key_at(j), false);
         __syncthreads();
         const uint32_t nl = ms.nlist[0];
-        if (nl > (uint32_t)kMergeList) {
-            give_up();
-            return;
-        }
+        ok = ok && nl <= (uint32_t)kMergeList;
         const uint32_t need = (uint32_t)a.top_k - (uint32_t)cabove;
         uint32_t found = 0u;
-        for (uint32_t i = t; i < nl; i += kMergeThreads) {
+        for (uint32_t i = t; ok && i < nl; i += kMergeThreads) {
             const uint32_t ki = ms.lkey[i];
             uint32_t gt = 0u, ge = 0u;
             for (uint32_t j = 0; j < nl; ++j) {
@@ -1660,19 +1653,13 @@ __global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
         if (lane == 0 && found != 0u) atomicMax(&ms.best[0], found);
         __syncthreads();
         kstar = ms.best[0];
-        if (kstar == 0u) {
-            give_up();
-            return;
-        }
+        ok = ok && kstar != 0u;
     }
-    if (kstar < lmax) {                                           // a tile's entries stop above the cut
-        give_up();
-        return;
-    }
+    ok = ok && kstar >= lmax;                                    // else a tile's entries stop above the cut
     // The survivors' masses per bin (fp32: in bin kbin only keys >= K*).
 #pragma unroll
     for (int j = 0; j < kMergeHeld; ++j) {
-        if (ev[j] != 0u && key_at(j) >= kstar) {
+        if (ok && ev[j] != 0u && key_at(j) >= kstar) {
             const uint32_t k = key_at(j);
             atomicAdd(reinterpret_cast<unsigned long long*>(&ms.mhist[bin_of(k)]),
                       (unsigned long long)((uint64_t)cnt_at(j) * mass_of(k)));
@@ -1694,29 +1681,25 @@ __global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
         const double target = a.top_p * (double)zs;
         double mabove = 0.0;
         const int pbin = crossing(wm, target, mabove);
-        if (pbin < 0) {                                          // (top_p > 0 and the largest key's mass make one)
-            give_up();
-            return;
-        }
+        ok = ok && pbin >= 0;                                    // (top_p > 0 and the largest key's mass make one)
         if constexpr (DT == kBF16) {
-            fkey = km - (uint32_t)pbin;
-            kept = mabove + (double)ms.mhist[pbin];
+            if (ok) {
+                fkey = km - (uint32_t)pbin;
+                kept = mabove + (double)ms.mhist[pbin];
+            }
         } else {
             // The largest key of bin pbin whose weight from the top reaches
             // target: rank the bin's survivors.
 #pragma unroll
             for (int j = 0; j < kMergeHeld; ++j)
-                append(1, ev[j] != 0u && key_at(j) >= kstar && bin_of(key_at(j)) == (uint32_t)pbin, key_at(j),
-                       true);
+                append(1, ok && ev[j] != 0u && key_at(j) >= kstar && bin_of(key_at(j)) == (uint32_t)pbin,
+                       key_at(j), true);
             __syncthreads();
             const uint32_t nl = ms.nlist[1];
-            if (nl > (uint32_t)kMergeList) {
-                give_up();
-                return;
-            }
+            ok = ok && nl <= (uint32_t)kMergeList;
             uint32_t found = 0u;
             double fkept = 0.0;
-            for (uint32_t i = t; i < nl; i += kMergeThreads) {
+            for (uint32_t i = t; ok && i < nl; i += kMergeThreads) {
                 const uint32_t ki = ms.lkey[i];
                 uint64_t gt = 0, ge = 0;
                 for (uint32_t j = 0; j < nl; ++j) {
@@ -1734,25 +1717,47 @@ __global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
             if (lane == 0 && wbest != 0u) atomicMax(&ms.best[1], wbest);
             __syncthreads();
             const uint32_t best = ms.best[1];
-            if (best == 0u) {
-                give_up();
-                return;
-            }
+            ok = ok && best != 0u;
             // Equal keys rank alike: whichever thread found it writes the same mass.
-            if (found == best) ms.kept = fkept;
+            if (ok && found == best) ms.kept = fkept;
             __syncthreads();
-            fkey = best;
-            kept = ms.kept;
+            if (ok) {
+                fkey = best;
+                kept = ms.kept;
+            }
         }
     }
+    if (!live) return kMergeNone;
+    if (!ok) return kMergeLeft;
     write_outputs<DT>(a, s, mx, val(fkey), kept / kFix, t, kMergeThreads, true, l_tok);
-    if (t == 0) *done = 1u;
+    return kMergeDecided;
 }
+
+// floor_merge: one group (workgroup) per row slot; done[row] = 1 for a row
+// it decides, 0 for one it leaves to floor_rows.
+template <int DT>
+__global__ __launch_bounds__(kMergeThreads) void floor_merge(FloorParams a) {
+    __shared__ MergeShared ms;
+    const int rs = blockIdx.x;
+    if (a.C > kMergeTiles) {
+        const RowSlot s = row_slot_of<DT>(a, rs);
+        if (!s.skip && threadIdx.x == 0) a.cand_done[rs] = 0u;
+        return;
+    }
+    const int st = merge_row<DT>(a, rs, ms, threadIdx.x);
+    if (threadIdx.x == 0 && st != kMergeNone) a.cand_done[rs] = st == kMergeDecided ? 1u : 0u;
+}
+
+// Shared memory of the full-row path for one row.
+template <int DT, bool VEC> struct RowSmem { using type = FloorShared; };
+template <> struct RowSmem<kBF16, true> { using type = WinShared; };
+template <> struct RowSmem<kFP32, true> { using type = Win32Shared; };
 
 // The floor of one row and its outputs; nv is the row's length in 16-byte
 // vectors.
 template <int DT, bool VEC>
-__device__ __forceinline__ void floor_row(const FloorParams& a, const RowSlot& s, int nv) {
+__device__ __forceinline__ void floor_row(const FloorParams& a, const RowSlot& s, int nv,
+                                          typename RowSmem<DT, VEC>::type& sm) {
     RowRef r;
     r.row = s.row;
     r.V = a.V;
@@ -1760,24 +1765,33 @@ __device__ __forceinline__ void floor_row(const FloorParams& a, const RowSlot& s
     r.sc = a.sc;
     float m, fl;
     double z;
-    if constexpr (DT == kBF16) {
-        if constexpr (VEC) {
-            __shared__ WinShared ws;
-            floor_by_window<VEC>(a, r, ws, m, fl, z);
-        } else {
-            // Rows off 16-byte alignment (or of an odd length): the general
-            // selection.
-            __shared__ FloorShared sh;
-            floor_by_select<DT, VEC>(a, r, sh, m, fl, z);
-        }
-    } else if constexpr (VEC) {
-        __shared__ Win32Shared ws;
-        floor_by_window32<VEC>(a, r, ws, m, fl, z);
+    if constexpr (DT == kBF16 && VEC) {
+        floor_by_window<VEC>(a, r, sm, m, fl, z);
+    } else if constexpr (DT == kFP32 && VEC) {
+        floor_by_window32<VEC>(a, r, sm, m, fl, z);
     } else {
-        __shared__ FloorShared sh;
-        floor_by_select<DT, VEC>(a, r, sh, m, fl, z);
+        // Rows off 16-byte alignment (or of an odd length): the general
+        // selection.
+        floor_by_select<DT, VEC>(a, r, sm, m, fl, z);
     }
     write_outputs<DT>(a, s, m, fl, z);
+}
+
+// The row path for the rows listed in todo[0 .. n) (a workgroup-uniform
+// count), one after another.
+template <int DT, bool VEC>
+__device__ __forceinline__ void floor_listed(const FloorParams& a, const int* todo, int n,
+                                             typename RowSmem<DT, VEC>::type& sm) {
+    for (int i = 0; i < n; ++i) {
+        // The row length made opaque to the compiler, so that the loads'
+        // offsets are formed where they are used rather than kept (spilled)
+        // across the rows.
+        int nv = a.NV;
+        asm volatile("" : "+v"(nv));
+        floor_row<DT, VEC>(a, row_slot_of<DT>(a, __builtin_amdgcn_readfirstlane(todo[i])),
+                           __builtin_amdgcn_readfirstlane(nv), sm);
+        __syncthreads();                                  // the shared memory is the next row's
+    }
 }
 
 // Workgroups of floor_rows after floor_merge: one per compute unit of the
@@ -1787,11 +1801,12 @@ constexpr int kRowsGrid = 256;
 
 template <int DT, bool VEC, bool LISTED>
 __global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
+    __shared__ typename RowSmem<DT, VEC>::type sm;
     if constexpr (!LISTED) {
         // One workgroup per row slot.
         const RowSlot s = row_slot<DT>(a);
         if (s.skip) return;
-        floor_row<DT, VEC>(a, s, a.NV);
+        floor_row<DT, VEC>(a, s, a.NV, sm);
     } else {
         // After floor_merge: the flags of a batch of the workgroup's row
         // slots in one load per thread, then the undecided rows one after
@@ -1813,21 +1828,48 @@ __global__ __launch_bounds__(kFT) void floor_rows(FloorParams a) {
         int first = blockIdx.x;
         int n = list(first);
         while (n > 0 || first + step < rows) {
-            for (int i = 0; i < n; ++i) {
-                // The row length made opaque to the compiler, so that the
-                // loads' offsets are formed where they are used rather than
-                // kept (spilled) across the rows.
-                int nv = a.NV;
-                asm volatile("" : "+v"(nv));
-                floor_row<DT, VEC>(a, row_slot_of<DT>(a, __builtin_amdgcn_readfirstlane(todo[i])),
-                                   __builtin_amdgcn_readfirstlane(nv));
-                __syncthreads();                          // the shared memory is the next row's
-            }
+            floor_listed<DT, VEC>(a, todo, n, sm);
             first += step;
             if (first >= rows) break;
             n = list(first);
         }
     }
+}
+
+// floor_finish: the merge and the full-row path in one kernel, for a call
+// with few row slots (at most kFinishRows per compute unit: one round of
+// workgroups).  A workgroup of 1,024 threads merges kFinishRows row slots,
+// one per group of four waves, then takes the rows they left with all its
+// threads; the merge's shared memory and the row path's overlap.
+constexpr int kFinishRows = kFT / kMergeThreads;         // 4
+constexpr int kFinishMaxRows = kFinishRows * kRowsGrid;
+
+template <int DT>
+union FinishShared {
+    MergeShared m[kFinishRows];
+    typename RowSmem<DT, true>::type r;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kFT) void floor_finish(FloorParams a) {
+    __shared__ FinishShared<DT> sm;
+    __shared__ int todo[kFinishRows];
+    __shared__ int ntodo;
+    const int g = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kMergeThreads);
+    const int tl = (int)threadIdx.x % kMergeThreads;
+    const int rs = (int)blockIdx.x * kFinishRows + g;
+    const int rows = a.B * a.R;
+    if (threadIdx.x == 0) ntodo = 0;
+    __syncthreads();
+    int st;
+    if (a.C <= kMergeTiles) {
+        st = merge_row<DT>(a, rs, sm.m[g], tl);
+    } else {
+        st = (rs < rows && !row_slot_of<DT>(a, rs).skip) ? kMergeLeft : kMergeNone;
+    }
+    if (tl == 0 && st == kMergeLeft) todo[atomicAdd(&ntodo, 1)] = rs;
+    __syncthreads();
+    floor_listed<DT, true>(a, todo, __builtin_amdgcn_readfirstlane(ntodo), sm.r);
 }
 
 template <int DT, bool VEC>
@@ -1838,13 +1880,18 @@ hipError_t launch_t(const FloorParams& p, hipStream_t s, hipEvent_t start, hipEv
         if (cands_usable(p)) {
             // A small top-k: the tiles' candidates (the start event is this
             // dispatch's), their merge per row, then the full-row path for
-            // the rows the merge left.
+            // the rows the merge left -- in one kernel when the row slots
+            // fit one round of workgroups, else in two.
             hipExtLaunchKernelGGL(floor_cands<DT>, dim3((unsigned)p.C, (unsigned)p.R, (unsigned)p.B), dim3(kThreads),
                                   0, s, start, nullptr, 0, p);
-            hipLaunchKernelGGL(floor_merge<DT>, dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, p);
-            hipExtLaunchKernelGGL((floor_rows<DT, true, true>),
-                                  dim3((unsigned)(blocks < (size_t)kRowsGrid ? blocks : (size_t)kRowsGrid)), dim3(kFT),
-                                  0, s, nullptr, stop, 0, p);
+            if (blocks <= (size_t)kFinishMaxRows) {
+                hipExtLaunchKernelGGL(floor_finish<DT>, dim3((unsigned)((blocks + kFinishRows - 1) / kFinishRows)),
+                                      dim3(kFT), 0, s, nullptr, stop, 0, p);
+            } else {
+                hipLaunchKernelGGL(floor_merge<DT>, dim3((unsigned)blocks), dim3(kMergeThreads), 0, s, p);
+                hipExtLaunchKernelGGL((floor_rows<DT, true, true>), dim3((unsigned)kRowsGrid), dim3(kFT), 0, s,
+                                      nullptr, stop, 0, p);
+            }
             return hipGetLastError();
         }
     }

@@ -215,9 +215,28 @@ def test_processed_small_top_k_edges(dtype, kind):
         _processed_case("edges-%s-%s" % (kind, dtype), wl, k, p)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_processed_small_top_k_many_rows(dtype):
+    """More row slots than one round of the combined merge kernel takes
+    (1,080 > 1,024): the merge and the full-row path run as two kernels.
+    Every request holds a row with spikes in one tile, so rows are left to
+    the full-row path there too."""
+    rng = np.random.default_rng(57 + (dtype == "bf16"))
+    B, K, V = 120, 4, 20000
+    lt = (rng.standard_normal((B, K + 1, V)) * 2.0).astype(np.float32)
+    lt[:, 1, 300:303] += 60.0
+    ld = (lt[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32) * 0.5).astype(np.float32)
+    arr_t = workloads.bf16_bits(lt) if dtype == "bf16" else lt
+    arr_d = workloads.bf16_bits(ld) if dtype == "bf16" else ld
+    wl = workloads.Workload("many", B, K, V, dtype, 0.9, False, arr_t, arr_d,
+                            rng.integers(0, V, (B, K)).astype(np.int32), rng.random((B, K + 1), dtype=np.float32))
+    for k, p in [(50, 0.9), (8, 1.0)]:
+        _processed_case("many-%s" % dtype, wl, k, p)
+
+
 @pytest.mark.parametrize("dtype,V", [("fp32", 200000), ("bf16", 340000)])
 def test_processed_small_top_k_long_rows(dtype, V):
-    """Rows of more 16 KB tiles than the one-wave merge takes: their small
+    """Rows of more 16 KB tiles than the merge takes: their small
     top-k cuts come from the full-row path, after the candidates pass."""
     rng = np.random.default_rng(V)
     B, K = 2, 1
