@@ -236,6 +236,58 @@ __device__ __forceinline__ double wave_sum(double v) {
     return lane63(v);
 }
 
+// Sums over the wave of four values per lane, returned to every lane.  Two
+// half-wave swaps leave values 0 and 2 summed over lane pairs (l, l + 32) in
+// lanes 0-31 and values 1 and 3 in lanes 32-63; one row swap then leaves
+// value 0, 2, 1, 3 in rows 0, 1, 2, 3, each summed over four lanes; the rows
+// of 16 lanes are reduced with DPP.  (Against four separate wave sums: one
+// reduction's instructions for four.)
+__device__ __forceinline__ float swap_add32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_add16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ double swap_add32(double a, double b) {
+    const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false,
+                                                     false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false,
+                                                     false);
+    return __hiloint2double((int)hi[0], (int)lo[0]) + __hiloint2double((int)hi[1], (int)lo[1]);
+}
+__device__ __forceinline__ double swap_add16(double a, double b) {
+    const auto lo = __builtin_amdgcn_permlane16_swap((unsigned)__double2loint(a), (unsigned)__double2loint(b), false,
+                                                     false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((unsigned)__double2hiint(a), (unsigned)__double2hiint(b), false,
+                                                     false);
+    return __hiloint2double((int)hi[0], (int)lo[0]) + __hiloint2double((int)hi[1], (int)lo[1]);
+}
+__device__ __forceinline__ float lane_at(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double lane_at(double v, int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+// Two values: after the half-wave swap, lanes 0-31 hold a and lanes 32-63 b;
+// a row swap of that with itself leaves a in rows 0-1 and b in rows 2-3.
+__device__ __forceinline__ void wave_sum2(float& a, float& b) {
+    const float w = swap_add32(a, b);
+    const float x = row16_sum(swap_add16(w, w));
+    a = lane_at(x, 0);
+    b = lane_at(x, 32);
+}
+template <typename T>
+__device__ __forceinline__ void wave_sum4(const T (&v)[4], T (&out)[4]) {
+    const T x = row16_sum(swap_add16(swap_add32(v[0], v[1]), swap_add32(v[2], v[3])));
+    out[0] = lane_at(x, 0);
+    out[2] = lane_at(x, 16);
+    out[1] = lane_at(x, 32);
+    out[3] = lane_at(x, 48);
+}
+
 // Inclusive prefix sum over the 64 lanes.
 __device__ __forceinline__ double wave_inclusive_scan(double v) {
     v += dpp<kDppRowShr1>(v, 0.0);

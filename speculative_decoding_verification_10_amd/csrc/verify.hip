@@ -426,15 +426,20 @@ __device__ __forceinline__ float residual_direct(float xp, float xq, const ResCo
 }
 
 // The tile's replacement terms: per slab its mass and q part into LDS, per
-// wave the signed sum and the near-tie p mass.
+// wave the signed sum and the near-tie p mass.  The slab test's two sums are
+// reduced together per slab; the four slabs' masses and q parts together
+// after the last.
 template <int DT>
 __device__ __forceinline__ void residual_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll],
                                                const u32x4 (&rq)[kUnroll], const ResConst& k, StepShared& sh) {
     constexpr int E = Elem<DT>::E;
+    static_assert(kUnroll == 4, "the four slabs of a wave are reduced together");
     const int w = threadIdx.x >> 6;
     const bool lead = (threadIdx.x & 63) == 0;
     double dsum = 0.0;
     float xsum = 0.0f;
+    double rs[kUnroll];                                   // per slab: the lane's mass
+    float qs[kUnroll];                                    //           and q part
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         float ep[E], eq[E], av[E];
@@ -451,8 +456,7 @@ __device__ __forceinline__ void residual_slabs(const VerifyParams& a, const u32x
             }
         }
         float xv[E];
-        cp = wave_sum(cp);
-        ca = wave_sum(ca);
+        wave_sum2(cp, ca);
         if (!(cp <= kCheapRatio * ca)) {
             // Strong cancellation in this slab (uniform over the wave): the
             // logits are decoded again rather than kept alive.
@@ -478,21 +482,26 @@ __device__ __forceinline__ void residual_slabs(const VerifyParams& a, const u32x
             sq += av[e] > 0.0f ? eq[e] : 0.0f;
             xsum += xv[e];
         }
-        const double ts = wave_sum((double)pairwise_sum<E>(r));
-        const float tq = wave_sum(sq);
+        rs[u] = (double)pairwise_sum<E>(r);
+        qs[u] = sq;
         dsum += (double)pairwise_sum<E>(av);
-        if (lead) {
-            sh.slab[u * kWaves + w] = ts;
-            sh.slabq[u * kWaves + w] = tq;
-        }
         // One vector at a time: the scheduler may not interleave the vectors
         // (their temporaries would not fit the registers of the occupancy
         // every final item needs to be resident at once).
         __builtin_amdgcn_sched_barrier(0);
     }
+    double ts[kUnroll];
+    float tq[kUnroll];
+    wave_sum4(rs, ts);
+    wave_sum4(qs, tq);
     dsum = wave_sum(dsum);
     xsum = wave_sum(xsum);
     if (lead) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            sh.slab[u * kWaves + w] = ts[u];
+            sh.slabq[u * kWaves + w] = tq[u];
+        }
         sh.red_d[w] = dsum;
         sh.red_f[w] = xsum;
     }
@@ -515,17 +524,20 @@ __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], con
         residual_slabs<DT>(a, rp, rq, res_const(d, d.rho, d.K0), sh);
     } else {
         const ResConst k{};
+        double rsd[kUnroll], ts[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             float r[E];
             final_masses<DT>(rp[u], rq[u], d, k, v0 + u * kThreads, a.sc, r);
-            const double t = wave_sum((double)pairwise_sum<E>(r));
-            if (lead) {
-                sh.slab[u * kWaves + w] = t;
+            rsd[u] = (double)pairwise_sum<E>(r);
+        }
+        wave_sum4(rsd, ts);
+        if (lead) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                sh.slab[u * kWaves + w] = ts[u];
                 sh.slabq[u * kWaves + w] = 0.0f;
             }
-        }
-        if (lead) {
             sh.red_d[w] = 0.0;
             sh.red_f[w] = 0.0f;
         }
