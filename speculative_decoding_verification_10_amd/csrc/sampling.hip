@@ -1192,15 +1192,16 @@ __device__ __forceinline__ void floor_by_window32(const FloorParams& a, const Ro
 // a key at or below the tile's own top_k-th largest (0 when the window holds
 // fewer than top_k logits).
 //
-// floor_merge, one workgroup per row, merges the row's entries.  The row's
-// top_k-th largest K* is at least every tile's own, so at least G of every
-// tile: entries below the largest G are dropped.  The top_k-th largest of
-// the rest is the row's when it is >= L of every tile (each tile then holds
-// all its logits >= it, so every count from the top down to it is the
-// row's), and then every top-k survivor is an entry, so the top-p cut over
-// the survivors comes from the entries too.  Otherwise (the cut lies below
-// some tile's entries, or the entries overflow the wave's LDS) the row is
-// left to floor_rows.  The row max is the largest head key.
+// The merge (merge_row, in floor_merge or floor_finish) takes each row's
+// entries.  The row's top_k-th largest K* is at least every tile's own, so
+// at least G of every tile: entries below the largest G are dropped.  The
+// top_k-th largest of the rest is the row's when it is >= L of every tile
+// (each tile then holds all its logits >= it, so every count from the top
+// down to it is the row's), and then every top-k survivor is an entry, so
+// the top-p cut over the survivors comes from the entries too.  Otherwise
+// (the cut lies below some tile's entries, or a bin's entries overflow the
+// LDS list) the row is left to the full-row path.  The row max is the
+// largest head key.
 // ---------------------------------------------------------------------------
 constexpr int kCandBins = kThreads;             // one bin per thread of floor_cands
 constexpr float kCandBinsPerBinade = 8.0f;      // fp32: bins over the mass exponent
