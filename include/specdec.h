@@ -104,6 +104,20 @@ int specdec_workspace_init(void *workspace, size_t bytes, void *stream);
 int specdec_workspace_errors(void *workspace, uint32_t *errors, int clear, void *stream);
 
 /*
+ * For tests of the error path above (callers that must see a wait give up
+ * without a fault or a hang; not for production use).  Every stochastic
+ * verify call issued after this one, from any thread, gives up a bounded
+ * wait after `wait_ticks` ticks of the GPU's 100 MHz clock instead of the
+ * library's 5,000,000 (50 ms), and, when `withhold_tile` >= 0, final tile
+ * `withhold_tile` of every request publishes no slab sums, so that the
+ * request's search waits for them and gives up: its outputs read -1 and bit
+ * 0 of the workspace's error word is set, every kernel still exits.
+ * specdec_debug_bounded_wait(0, -1) restores the defaults.  SPECDEC_EINVAL
+ * for withhold_tile < -1.
+ */
+int specdec_debug_bounded_wait(uint64_t wait_ticks, int32_t withhold_tile);
+
+/*
  * Row statistics of the temperature softmax ("3.5 Speculative Decoding",
  * section "Notation": p is the distribution after temperature).
  *   logits      [rows, V]

@@ -58,6 +58,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.specdec_workspace_init.restype = ci
         lib.specdec_workspace_errors.argtypes = [vp, vp, ci, vp]
         lib.specdec_workspace_errors.restype = ci
+        lib.specdec_debug_bounded_wait.argtypes = [ctypes.c_uint64, ctypes.c_int32]
+        lib.specdec_debug_bounded_wait.restype = ci
         lib.specdec_softmax_stats_workspace_bytes.argtypes = [i64, i32, ci]
         lib.specdec_softmax_stats_workspace_bytes.restype = sz
         lib.specdec_softmax_stats.argtypes = [vp, ci, i64, i32, f32, vp, vp, vp, sz, vp]
@@ -176,6 +178,14 @@ def workspace_errors(ws: Workspace, clear: bool = True) -> int:
     if rc != 0:
         raise SpecdecError(rc, "specdec_workspace_errors")
     return int(out.item()) & 0xFFFFFFFF
+
+
+def debug_bounded_wait(wait_ticks: int = 0, withhold_tile: int = -1) -> None:
+    """specdec_debug_bounded_wait: for tests of the error path only; (0, -1)
+    restores the defaults."""
+    rc = load().specdec_debug_bounded_wait(int(wait_ticks), int(withhold_tile))
+    if rc != 0:
+        raise SpecdecError(rc, "specdec_debug_bounded_wait")
 
 
 def cached_workspaces():

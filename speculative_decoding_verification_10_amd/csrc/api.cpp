@@ -147,6 +147,11 @@ int map_launch(hipError_t e) {
     return current_device_is_gfx950() ? SPECDEC_ELAUNCH : SPECDEC_EDEVICE;
 }
 
+// The bounded waits' limit and the withheld final tile of the next calls
+// (specdec_debug_bounded_wait; the defaults outside tests of the error path).
+std::atomic<uint64_t> g_wait_ticks{kWaitTicks};
+std::atomic<int32_t> g_withhold_tile{-1};
+
 // Scratch of the allocation-free entry point (specdec_verify_noalloc): a
 // file-scope device array, one copy per GPU, held until the process ends.
 // In host code its name is only a stand-in; its device address, found once
@@ -203,6 +208,8 @@ int verify_impl(const void* target_logits, const void* draft_logits, specdec_dty
     p.NS = (p.NV + kSlab - 1) / kSlab;
     p.kinds = one_hot ? 1 : 2;
     p.clear_err = noalloc ? 1 : 0;
+    p.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
+    p.withhold_tile = g_withhold_tile.load(std::memory_order_relaxed);
     // One workgroup per row item and per final item.
     if ((size_t)B * p.R * p.C > kMaxBlocks || B > kMaxBatch) return SPECDEC_EINVAL;
     p.target = target_logits;
@@ -254,6 +261,14 @@ int specdec_workspace_init(void* workspace, size_t bytes, void* stream) {
     if (workspace == nullptr && bytes != 0) return SPECDEC_EINVAL;
     if (bytes == 0) return SPECDEC_OK;
     return map_launch(hipMemsetAsync(workspace, 0, bytes, (hipStream_t)stream));
+}
+
+int specdec_debug_bounded_wait(uint64_t wait_ticks, int32_t withhold_tile) {
+    if (wait_ticks == 0) wait_ticks = kWaitTicks;
+    if (withhold_tile < -1) return SPECDEC_EINVAL;
+    g_wait_ticks.store(wait_ticks, std::memory_order_relaxed);
+    g_withhold_tile.store(withhold_tile, std::memory_order_relaxed);
+    return SPECDEC_OK;
 }
 
 int specdec_workspace_errors(void* workspace, uint32_t* errors, int clear, void* stream) {
@@ -374,6 +389,8 @@ int specdec_verify_processed_timed(const void* target_logits, const void* draft_
     p.R = K + 1 + (one_hot ? 0 : K);
     p.NS = (p.NV + kSlab - 1) / kSlab;
     p.kinds = one_hot ? 1 : 2;
+    p.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
+    p.withhold_tile = g_withhold_tile.load(std::memory_order_relaxed);
     if ((size_t)B * p.C > kMaxBlocks || (size_t)B * p.R > kMaxFloorRows || B > kMaxBatch)
         return SPECDEC_EINVAL;
     p.target = target_logits;

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "slots.h"
 
 namespace specdec {
 
@@ -62,6 +63,8 @@ struct VerifyParams {
     Decision* dec;              // [B] decision of each request
     const float* floors;        // [B * R] processed-row floors, or null (plain rows)
     int clear_err;              // non-zero: the row kernel clears the error word first
+    uint64_t wait_ticks = kWaitTicks;   // a bounded wait gives up after this many 100 MHz ticks
+    int withhold_tile = -1;     // >= 0 (error-path tests only): that final tile publishes no sums
 };
 
 // Linear greedy verify (launch_greedy) or greedy tree verify

@@ -28,7 +28,8 @@
 namespace specdec {
 
 // A wait gives up after 50 ms of wall-clock time (100 MHz counter), far
-// beyond any legitimate wait.
+// beyond any legitimate wait (the library's default; tests of the error
+// path set a shorter limit through specdec_debug_bounded_wait).
 constexpr uint64_t kWaitTicks = 5000000;
 
 __device__ __forceinline__ uint32_t enc_f32(float f) {
@@ -67,14 +68,15 @@ __device__ __forceinline__ uint64_t slot_peek(const uint64_t* p) {
 // reads once more before it gives up.  On giving up: flag the error word, set
 // `lost` and return `fallback`.
 template <typename T>
-__device__ __forceinline__ T settle(const T* p, T v, uint32_t* err, T fallback, bool& lost) {
+__device__ __forceinline__ T settle(const T* p, T v, uint32_t* err, T fallback, bool& lost,
+                                   uint64_t ticks = kWaitTicks) {
     if (v != 0) return v;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     for (;;) {
         __builtin_amdgcn_s_sleep(2);
         v = slot_peek(p);
         if (v != 0) return v;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) {
             atomicOr(err, 1u);
             lost = true;
             return fallback;
@@ -83,8 +85,9 @@ __device__ __forceinline__ T settle(const T* p, T v, uint32_t* err, T fallback, 
 }
 
 template <typename T>
-__device__ __forceinline__ T slot_wait(const T* p, uint32_t* err, T fallback, bool& lost) {
-    return settle(p, slot_peek(p), err, fallback, lost);
+__device__ __forceinline__ T slot_wait(const T* p, uint32_t* err, T fallback, bool& lost,
+                                      uint64_t ticks = kWaitTicks) {
+    return settle(p, slot_peek(p), err, fallback, lost, ticks);
 }
 
 }  // namespace specdec

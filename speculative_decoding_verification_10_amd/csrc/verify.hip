@@ -543,6 +543,7 @@ __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], con
         }
     }
     __syncthreads();
+    if (tile == a.withhold_tile) return;                  // (error-path tests: sums never published)
     uint64_t* slabs = a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile;
     if (threadIdx.x < nslabs)
         slot_put(slabs + threadIdx.x, enc_f32x2((float)sh.slab[threadIdx.x], sh.slabq[threadIdx.x]));
@@ -723,7 +724,7 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
 #pragma unroll
             for (int k = 0; k < kHeld; ++k)
                 if (hw[k] == 0) hw[k] = slot_peek(slabs + g0 + k);
-            if (missing() && __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            if (missing() && __builtin_amdgcn_s_memrealtime() - t0 > a.wait_ticks) {
                 atomicOr(a.err, 1u);
                 lost = true;
                 if (tw == 0) tw = none;
@@ -736,7 +737,7 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     double dsum = (double)dec_hi(tw);
     float xsum = dec_lo(tw);
     for (int c = lane + 64; c < a.C; c += 64) {
-        const uint64_t t = slot_wait(tiles + c, a.err, none, lost);
+        const uint64_t t = slot_wait(tiles + c, a.err, none, lost, a.wait_ticks);
         dsum += (double)dec_hi(t);
         xsum += dec_lo(t);
     }
@@ -764,7 +765,7 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
         mine += held[k];
     }
     for (int k = kHeld; k < P; ++k)
-        if (g0 + k < NS) mine += corrected(slot_wait(slabs + g0 + k, a.err, none, lost));
+        if (g0 + k < NS) mine += corrected(slot_wait(slabs + g0 + k, a.err, none, lost, a.wait_ticks));
 
     const void* rowp = row_ptr(a.target, (size_t)b * (K + 1) + d.j, a.V, S);
     const void* rowq = (d.mode == kResidual) ? row_ptr(a.draft, (size_t)b * K + d.j, a.V, S) : nullptr;

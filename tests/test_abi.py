@@ -317,6 +317,13 @@ def test_workspace_errors_rejects(lib):
     assert lib.specdec_workspace_errors(ctypes.c_void_p(0x10010), FAKE, 0, None) == EINVAL   # misaligned
 
 
+def test_debug_bounded_wait_arguments(lib):
+    lib.specdec_debug_bounded_wait.argtypes = [ctypes.c_uint64, ctypes.c_int32]
+    assert lib.specdec_debug_bounded_wait(0, -2) == EINVAL
+    assert lib.specdec_debug_bounded_wait(1000, 3) == OK
+    assert lib.specdec_debug_bounded_wait(0, -1) == OK          # the defaults again
+
+
 def test_verify_noalloc_rejects_on_host(lib):
     """Arguments the allocation-free entry point rejects before any device
     call: bad sizes, and calls whose workspace would exceed its static
