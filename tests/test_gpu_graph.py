@@ -4,10 +4,10 @@ on other inputs, other work and synchronisations between the replays.  The
 library's kernels clear what they read within the call (no memset nodes), so
 a replay needs nothing from the host.  Covered: the stochastic step, the
 allocation-free entry point (for callers that capture, which cannot
-allocate), the processed step and the greedy step."""
+allocate), the processed step and the greedy step; and calls on two streams
+at once."""
 import ctypes
 
-import numpy as np
 import pytest
 import torch
 
@@ -135,3 +135,36 @@ def test_greedy_graph_replays():
         sd.verify_greedy(t, toks, argmax=True, workspace=ws, out=out)
     _replay_and_check(g, list(out), ref, lambda: sd.verify_greedy(t2, toks2, argmax=True, workspace=ws))
     assert_workspace_clean(ws)
+
+
+def test_two_streams_at_once():
+    """Calls on two streams at the same time, each with its own workspace
+    and inputs, give the bits of the same calls made one after the other:
+    no state is shared between calls on different workspaces."""
+    import speculative_decoding_verification_10_amd as sd
+    wl, x = _inputs(17)
+    _, y = _inputs(18)
+    code = 1 if wl.dtype == "bf16" else 0
+    nb = int(sd._lib.verify_workspace_bytes(wl.B, wl.K, wl.V, code, False))
+    ws_a, ws_b = sd.Workspace(nb, torch.device("cuda")), sd.Workspace(nb, torch.device("cuda"))
+    ref_x = [r.clone() for r in sd.verify(x["t"], x["d"], x["toks"], x["u"], wl.temperature, accept_prob=True,
+                                          workspace=ws_a)]
+    ref_y = [r.clone() for r in sd.verify(y["t"], y["d"], y["toks"], y["u"], wl.temperature, accept_prob=True,
+                                          workspace=ws_b)]
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    got_x, got_y = [], []
+    for _ in range(10):
+        with torch.cuda.stream(sa):
+            got_x.append(sd.verify(x["t"], x["d"], x["toks"], x["u"], wl.temperature, accept_prob=True,
+                                   workspace=ws_a))
+        with torch.cuda.stream(sb):
+            got_y.append(sd.verify(y["t"], y["d"], y["toks"], y["u"], wl.temperature, accept_prob=True,
+                                   workspace=ws_b))
+    torch.cuda.synchronize()
+    for g in got_x:
+        assert all(torch.equal(a, b) for a, b in zip(g, ref_x))
+    for g in got_y:
+        assert all(torch.equal(a, b) for a, b in zip(g, ref_y))
+    assert_workspace_clean(ws_a)
+    assert_workspace_clean(ws_b)
