@@ -514,7 +514,7 @@ __device__ __forceinline__ void residual_slabs(const VerifyParams& a, const u32x
 // with draft logits, its q part sum_{a > 0} e_q.  The tile's own slot holds
 // the signed replacement sum sum_t (e_p - rho e_q) over the tile and the p
 // mass of its near-ties (|z| <= ~2^-19), for the search's refinement of rho.
-template <int DT>
+template <int DT, bool ONE>
 __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], const u32x4 (&rq)[kUnroll],
                           const Decision& d, int v0, int b, int tile, int nslabs, StepShared& sh) {
     constexpr int E = Elem<DT>::E;
@@ -543,6 +543,7 @@ __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], con
         }
     }
     __syncthreads();
+    if (ONE) return;                                      // (a one-tile row: the search reads the LDS sums)
     if (tile == a.withhold_tile) return;                  // (error-path tests: sums never published)
     uint64_t* slabs = a.slot_slab + ((size_t)b * a.C + tile) * kSlabsPerTile;
     if (threadIdx.x < nslabs)
@@ -568,8 +569,9 @@ __device__ void publish_aprob(const VerifyParams& a, int b, int kb, const StepSh
 
 constexpr int kSearchLanes = 64;
 
-template <int DT, bool VEC, bool FL>
-__device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d);
+template <int DT, bool VEC, bool FL, bool ONE>
+__device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d, const StepShared& sh,
+                            const u32x4* stage);
 
 // The decision is the same in every lane: keep it in scalar registers.
 __device__ __forceinline__ Decision to_scalar(const Decision& d) {
@@ -587,8 +589,12 @@ __device__ __forceinline__ Decision to_scalar(const Decision& d) {
 // ---------------------------------------------------------------------------
 // Final item: tile `tile` of the final row (pair) of request b.
 // ---------------------------------------------------------------------------
-template <int DT, bool VEC, bool FL>
-__device__ void final_item(const VerifyParams& a, int b, int tile, bool decided, StepShared& sh) {
+// ONE: the row is a single tile (C = 1): the workgroup keeps the final
+// row (pair) in LDS (stage: p at [0, kTileVec), q after it) and its search
+// reads the slab sums and the final slab from there, not from the slots and
+// the row again.
+template <int DT, bool VEC, bool FL, bool ONE>
+__device__ void final_item(const VerifyParams& a, int b, int tile, bool decided, StepShared& sh, u32x4* stage) {
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
     const int kb = kb_of(a, b);
@@ -612,12 +618,19 @@ __device__ void final_item(const VerifyParams& a, int b, int tile, bool decided,
             apply_floor<DT>(rq[u], fq);
         }
     }
-    put_slabs<DT>(a, rp, rq, d, v0, b, tile, min(kSlabsPerTile, a.NS - tile * kSlabsPerTile), sh);
+    if constexpr (ONE) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            stage[threadIdx.x + u * kThreads] = rp[u];
+            if (rowq) stage[kTileVec + threadIdx.x + u * kThreads] = rq[u];
+        }
+    }
+    put_slabs<DT, ONE>(a, rp, rq, d, v0, b, tile, min(kSlabsPerTile, a.NS - tile * kSlabsPerTile), sh);
     if (tile == 0 && !decided) publish_aprob(a, b, kb, sh);
     // The request's last tile -- dispatched after its other tiles, which
     // never wait -- searches, with its first wave, once every slab sum of
     // the request is in.
-    if (tile == a.C - 1 && threadIdx.x < kSearchLanes) search_wave<DT, VEC, FL>(a, b, kb, d);
+    if (tile == a.C - 1 && threadIdx.x < kSearchLanes) search_wave<DT, VEC, FL, ONE>(a, b, kb, d, sh, stage);
 }
 
 
@@ -683,8 +696,9 @@ __device__ double lane_slab_mass(const VerifyParams& a, const void* rowp, const 
     return t;
 }
 
-template <int DT, bool VEC, bool FL>
-__device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
+template <int DT, bool VEC, bool FL, bool ONE>
+__device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d, const StepShared& sh,
+                            const u32x4* stage) {
     constexpr int E = Elem<DT>::E;
     constexpr int S = Elem<DT>::S;
     const int K = a.K;
@@ -701,11 +715,29 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     // tile word and its first kHeld slab words); then each poll is finished.
     // The tiles' signed sums and near-tie masses come first: the refinement
     // needs them before any slab sum can be corrected.
-    uint64_t tw = lane < a.C ? slot_peek(tiles + lane) : none;
+    uint64_t tw = none;
     uint64_t hw[kHeld];
+    if constexpr (ONE) {
+        // The tile's own sums, in LDS (the words put_slabs would publish).
+        if (lane == 0) {
+            double ds = 0.0;
+            float xs = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kHeld; ++k) hw[k] = (k < P && g0 + k < NS) ? slot_peek(slabs + g0 + k) : none;
-    {
+            for (int i = 0; i < kWaves; ++i) {
+                ds += sh.red_d[i];
+                xs += sh.red_f[i];
+            }
+            tw = enc_f32x2((float)ds, xs);
+        }
+#pragma unroll
+        for (int k = 0; k < kHeld; ++k)
+            hw[k] = (k < P && g0 + k < NS) ? enc_f32x2((float)sh.slab[g0 + k], sh.slabq[g0 + k]) : none;
+    } else {
+        tw = lane < a.C ? slot_peek(tiles + lane) : none;
+#pragma unroll
+        for (int k = 0; k < kHeld; ++k) hw[k] = (k < P && g0 + k < NS) ? slot_peek(slabs + g0 + k) : none;
+    }
+    if (!ONE) {
         // While any of these words is still empty: sleep, then reload every
         // empty one in one batch (one round trip per round, not per word).
         // The deadline is checked only after a reload that still found one
@@ -850,8 +882,14 @@ __device__ void search_wave(const VerifyParams& a, int b, int kb, Decision d) {
     const int v = g * kSlab + lane;
     float r[E];
     {
-        u32x4 sp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
-        u32x4 sq = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : sp;
+        u32x4 sp, sq;
+        if constexpr (ONE) {
+            sp = stage[v];                                // (v < NS * kSlab <= kTileVec)
+            sq = rowq ? stage[kTileVec + v] : sp;
+        } else {
+            sp = load_raw<DT, VEC, false>(rowp, a.V, a.NV, v);
+            sq = rowq ? load_raw<DT, VEC, false>(rowq, a.V, a.NV, v) : sp;
+        }
         if constexpr (FL) {
             apply_floor<DT>(sp, fp);
             apply_floor<DT>(sq, rowq ? fq : fp);
@@ -920,10 +958,11 @@ __global__ __launch_bounds__(kThreads) void verify_decide(VerifyParams a) {
 
 // Final items: workgroup (x, y) takes tile x of request y.  FL: the rows are
 // processed (top-k / top-p floors).
-template <int DT, bool VEC, bool DECIDED, bool FL>
+template <int DT, bool VEC, bool DECIDED, bool FL, bool ONE = false>
 __global__ __launch_bounds__(kThreads) void verify_final(VerifyParams a) {
     __shared__ StepShared sh;
-    final_item<DT, VEC, FL>(a, blockIdx.y, blockIdx.x, DECIDED, sh);
+    __shared__ u32x4 stage[ONE ? 2 * kTileVec : 1];
+    final_item<DT, VEC, FL, ONE>(a, blockIdx.y, blockIdx.x, DECIDED, sh, stage);
 }
 
 template <int DT, bool VEC>
@@ -941,6 +980,10 @@ hipError_t launch(const VerifyParams& p, hipStream_t s, hipEvent_t const* events
     if ((int64_t)p.C * p.R * p.C > kDecideOnceAbove) {
         hipLaunchKernelGGL(verify_decide, dim3(p.B), dim3(kThreads), 0, s, p);
         hipExtLaunchKernelGGL((verify_final<DT, VEC, true, false>), dim3(p.C, p.B), dim3(kThreads), 0, s,
+                              nullptr, ev[2], 0, p);
+    } else if (p.C == 1) {
+        // Rows of one tile: the search works from LDS.
+        hipExtLaunchKernelGGL((verify_final<DT, VEC, false, false, true>), dim3(1, p.B), dim3(kThreads), 0, s,
                               nullptr, ev[2], 0, p);
     } else {
         hipExtLaunchKernelGGL((verify_final<DT, VEC, false, false>), dim3(p.C, p.B), dim3(kThreads), 0, s,
@@ -964,6 +1007,10 @@ hipError_t launch_processed(const FloorParams& f, const VerifyParams& p, hipStre
     if ((int64_t)p.C * p.R * p.C > kDecideOnceAbove) {
         hipLaunchKernelGGL(verify_decide, dim3(p.B), dim3(kThreads), 0, s, p);
         hipExtLaunchKernelGGL((verify_final<DT, VEC, true, true>), dim3(p.C, p.B), dim3(kThreads), 0, s,
+                              nullptr, ev[2], 0, p);
+    } else if (p.C == 1) {
+        // Rows of one tile: the search works from LDS.
+        hipExtLaunchKernelGGL((verify_final<DT, VEC, false, true, true>), dim3(1, p.B), dim3(kThreads), 0, s,
                               nullptr, ev[2], 0, p);
     } else {
         hipExtLaunchKernelGGL((verify_final<DT, VEC, false, true>), dim3(p.C, p.B), dim3(kThreads), 0, s,
