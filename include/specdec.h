@@ -111,7 +111,9 @@ int specdec_workspace_errors(void *workspace, uint32_t *errors, int clear, void 
  * library's 5,000,000 (50 ms), and, when `withhold_tile` >= 0, final tile
  * `withhold_tile` of every request publishes no slab sums, so that the
  * request's search waits for them and gives up: its outputs read -1 and bit
- * 0 of the workspace's error word is set, every kernel still exits.
+ * 0 of the workspace's error word is set, every kernel still exits.  Rows
+ * of a single 16 KB tile (fp32 V <= 4,096, bf16 V <= 8,192) have no such
+ * wait (their search reads its own workgroup's sums) and are not affected.
  * specdec_debug_bounded_wait(0, -1) restores the defaults.  SPECDEC_EINVAL
  * for withhold_tile < -1.
  */
