@@ -380,18 +380,26 @@ __device__ void row_item(const VerifyParams& a, int b, int rr, int tile, float* 
     if (draft ? i >= kb : i > kb) return;   // row past k_b: nothing to read
     const void* row = draft ? row_ptr(a.draft, (size_t)b * K + i, a.V, S)
                             : row_ptr(a.target, (size_t)b * (K + 1) + i, a.V, S);
-    // The tile that holds the draft token x_i reads its logit (issued before
-    // the tile's loads, stored by thread 0 after them).  Every lane of every
-    // tile issues the same-address load -- of the row's first logit when the
-    // tile is not the holder -- so that no branch makes the wave wait for it
-    // before the tile's loads go out.
-    const int gx = (i < kb) ? token_of(a, b, i) : -1;
+    // The tile that holds the draft token x_i reads its logit (stored by
+    // thread 0 after the reduction).  The token's id is a vector load issued
+    // just before the tile's loads: waiting for it, to address the logit,
+    // leaves the tile's loads in flight (a scalar load there made every tile
+    // wait for it, and for the kernel arguments, before its loads went out).
+    // Every lane of every tile issues the same-address logit load -- of the
+    // row's first logit when the tile is not the holder -- so that no branch
+    // sits among the loads.
+    // (No branch: a row without a drafted token reads a uniform, dropped.)
+    const int32_t* tp = (i < kb) ? a.tokens + (size_t)b * a.K + i : reinterpret_cast<const int32_t*>(a.unif);
+    const int tok = __hip_atomic_load(const_cast<int32_t*>(tp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    u32x4 raw[kUnroll];
+    tile_load<DT, VEC>(row, a.V, a.NV, tile, raw);
+    const int gx = (i < kb) ? min(max(tok, 0), a.V - 1) : -1;
     const bool holds = gx >= 0 && gx / (kTileVec * Elem<DT>::E) == tile;
     const bool holder = holds && threadIdx.x == 0;
     const float gval = load_one<DT>(row, holds ? gx : 0);
     float m;
     double z;
-    tile_stats<DT, VEC>(row, a.V, a.NV, tile, a.sc, m, z, lds_f, lds_d);
+    tile_reduce<DT>(raw, a.sc, m, z, lds_f, lds_d);
     if (holder) slot_put(a.slot_l + (size_t)b * a.R + rr, enc_f32(gval));
     if (threadIdx.x == 0) {
         const size_t idx = ((size_t)b * a.R + rr) * a.C + tile;
