@@ -1230,6 +1230,26 @@ __device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
     v = f(v, dpp<kDppRowBcast31, 0xC>((int)v, id));
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
+// Exact sum of a u64 over the wave, in every lane: the same DPP steps on
+// both halves, the 64-bit add carrying between them (the lanes a row mask
+// leaves out add 0).
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_total_u64(uint64_t v) {
+    v += dpp_u64<kDppQuad1032>(v);
+    v += dpp_u64<kDppQuad2301>(v);
+    v += dpp_u64<kDppRowHalfMirror>(v);
+    v += dpp_u64<kDppRowMirror>(v);
+    v += dpp_u64<kDppRowBcast15, 0xA>(v);
+    v += dpp_u64<kDppRowBcast31, 0xC>(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_ext_u32<false>(v); }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_ext_u32<true>(v); }
 
@@ -1674,8 +1694,7 @@ __device__ __forceinline__ int merge_row(const FloorParams& a, int rs, MergeShar
         zs += ms.mhist[4 * lane + q];
         wm[q] = (double)ms.mhist[4 * lane + q];
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o, 64);
+    zs = wave_total_u64(zs);
     uint32_t fkey = kstar;
     double kept = (double)zs;
     if (a.top_p < 1.0) {
