@@ -56,10 +56,12 @@ def _run(lib, wl, noalloc):
 
 def test_noalloc_matches_workspace_entry_point(lib):
     # The headline workload, then a smaller one (fewer requests, positions
-    # and tokens) on the same scratch, then a ragged one with one-hot drafts.
+    # and tokens) on the same scratch, then a ragged one, rows of a single
+    # tile (the final kernel's one-tile variant), and one-hot drafts.
     cases = [workloads.make("headline", set_index=3),
              workloads.make("peaked", set_index=5),
-             workloads.make("ragged", set_index=2, B=24, V=50000)]
+             workloads.make("ragged", set_index=2, B=24, V=50000),
+             workloads.make("tiny", set_index=4, B=16)]
     oh = workloads.make("peaked", set_index=6, B=5)
     oh.draft = None
     cases.append(oh)
