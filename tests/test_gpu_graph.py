@@ -27,8 +27,8 @@ def _gpu():
     sd.load(build_if_missing=False)
 
 
-def _inputs(set_index):
-    wl = workloads.make("peaked", set_index=set_index)
+def _inputs(set_index, name="peaked"):
+    wl = workloads.make(name, set_index=set_index, B=(16 if name == "tiny" else None))
     return wl, dict(t=dev_logits(wl.target), d=dev_logits(wl.draft),
                     toks=torch.from_numpy(wl.draft_tokens).cuda(), u=torch.from_numpy(wl.uniforms).cuda())
 
@@ -45,11 +45,12 @@ def _replay_and_check(g, outs, ref, eager_other):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("name", ["peaked", "tiny"])          # tiny: rows of a single tile
 @pytest.mark.parametrize("processed", [False, True])
-def test_verify_graph_replays(processed):
+def test_verify_graph_replays(processed, name):
     import speculative_decoding_verification_10_amd as sd
-    wl, x = _inputs(11)
-    _, y = _inputs(12)
+    wl, x = _inputs(11, name)
+    _, y = _inputs(12, name)
     code = 1 if wl.dtype == "bf16" else 0
     kw = dict(top_k=30, top_p=0.9) if processed else {}
     nbytes = (sd._lib.load().specdec_verify_processed_workspace_bytes(wl.B, wl.K, wl.V, code, 0) if processed
