@@ -437,19 +437,30 @@ __device__ __forceinline__ float residual_direct(float xp, float xq, const ResCo
 // wave the signed sum and the near-tie p mass.  The slab test's two sums are
 // reduced together per slab; the four slabs' masses and q parts together
 // after the last.
-template <int DT>
+template <int DT, bool ONE>
 __device__ __forceinline__ void residual_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll],
-                                               const u32x4 (&rq)[kUnroll], const ResConst& k, StepShared& sh) {
+                                               const u32x4 (&rq)[kUnroll], const ResConst& k, int tile,
+                                               StepShared& sh) {
     constexpr int E = Elem<DT>::E;
     static_assert(kUnroll == 4, "the four slabs of a wave are reduced together");
     const int w = threadIdx.x >> 6;
     const bool lead = (threadIdx.x & 63) == 0;
+    const int wv0 = tile * kTileVec + w * kSlab;          // the wave's first vector of its first slab
     double dsum = 0.0;
     float xsum = 0.0f;
     double rs[kUnroll];                                   // per slab: the lane's mass
     float qs[kUnroll];                                    //           and q part
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+        if (ONE && wv0 + u * kThreads >= a.NV) {
+            // A one-tile row's slab wholly past the row's end (uniform over
+            // the wave): its -inf padding sums to zero; the work is skipped.
+            // (Short rows are mostly padding; a long row's last tile keeps
+            // the unbranched loop, which measured faster there.)
+            rs[u] = 0.0;
+            qs[u] = 0.0f;
+            continue;
+        }
         float ep[E], eq[E], av[E];
         float cp = 0.0f, ca = 0.0f;
         {
@@ -529,12 +540,14 @@ __device__ void put_slabs(const VerifyParams& a, const u32x4 (&rp)[kUnroll], con
     const int w = threadIdx.x >> 6;
     const bool lead = (threadIdx.x & 63) == 0;
     if (d.mode == kResidual) {
-        residual_slabs<DT>(a, rp, rq, res_const(d, d.rho, d.K0), sh);
+        residual_slabs<DT, ONE>(a, rp, rq, res_const(d, d.rho, d.K0), tile, sh);
     } else {
         const ResConst k{};
         double rsd[kUnroll], ts[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
+            rsd[u] = 0.0;
+            if (ONE && (threadIdx.x >> 6) * kSlab + u * kThreads >= a.NV) continue;   // (as above)
             float r[E];
             final_masses<DT>(rp[u], rq[u], d, k, v0 + u * kThreads, a.sc, r);
             rsd[u] = (double)pairwise_sum<E>(r);
